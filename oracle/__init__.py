@@ -1,0 +1,24 @@
+"""CPU oracle for the int4 GPTQ and dense GEMMs -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the package smoke check and the benchmark's CPU-baseline leg
+may import this package.  The library itself never calls it, and it calls
+nothing of the library: the two share no code.
+"""
+from .qgemm_oracle import (  # noqa: F401
+    GROUP_SIZE,
+    TOL_ABS,
+    TOL_REL,
+    fp16_value,
+    bf16_value,
+    unpack_qweight,
+    unpack_qzeros,
+    dequant,
+    qgemm_int4,
+    qgemm_int4_at,
+    dense,
+    dense_at,
+    grid_bracket,
+    round_to_grid,
+    accept,
+    compare,
+)

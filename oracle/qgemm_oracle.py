@@ -1,0 +1,229 @@
+"""Plain, slow, fp64 CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, the package smoke check and the benchmark's CPU-baseline leg may
+import this module.  It shares no code with the GPU library.
+
+What it computes
+----------------
+* int4 GPTQ linear layer (the GPTQModel NF12 pull request, "What changed" and
+  "Accuracy"; the mi50grad README, "Model": GPTQ-Int4 with group size 128).
+  The weight of output column j at input row i is w = (q - z) * s, where q is
+  the 4-bit code of (i, j), and z (4-bit) and s (fp16) are shared by the 128
+  consecutive rows of i's group.  Storage:
+    qweight uint32 [k/8][n]:   word (r, j) holds the codes of rows 8r..8r+7 of
+                               column j, row 8r+t in bits 4t..4t+3;
+    qzeros  uint32 [k/128][n/8]: word (g, c) holds the zeros of columns
+                               8c..8c+7, column 8c+t in bits 4t..4t+3;
+    scales  fp16   [k/128][n].
+  Y[m][n] = X[m][k] . W, W[k][n] the dequantised weights.  The oracle forms W
+  in fp32 (exact: |q - z| <= 15 has 4 bits and s has 11) and accumulates the
+  products of the bf16 activations with it in fp64.
+* dense products C = op(A) op(B) with fp32-accumulating bf16/fp16 inputs (the
+  BC-250 tuned-GEMM post, "Where the time went" and "Checking the results are
+  right": forward, input-gradient and weight-gradient products, each checked
+  against a float64 product on the CPU).  Row-major layouts:
+    NT: C[M][N] = A[M][K] . B[N][K]^T   (forward)
+    NN: C[M][N] = A[M][K] . B[K][N]     (input gradient)
+    TN: C[M][N] = A[K][M]^T . B[K][N]   (weight gradient)
+* acceptance of an output y against the fp64 value r (the NF12 pull request,
+  "Accuracy": zero violations of |err| <= 2e-3 + 2e-3 |ref|).  Read together
+  with its statement that the rms error it sees is the BF16 rounding floor, an
+  output is accepted when it meets that bound OR is one of the two output-dtype
+  numbers that bracket r (a faithful rounding).  A correctly rounded bf16 value
+  of a reference with |r| above about 2 can miss the literal bound, whose
+  relative part is below bf16's half-ulp, so the literal formula alone would
+  reject exact results.
+
+Every floating-point decoding here is written from the IEEE field definitions,
+not taken from a library conversion.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP_SIZE = 128
+TOL_ABS = 2e-3
+TOL_REL = 2e-3
+
+# significand bits (with the implicit one) and the smallest normal exponent
+_GRID = {"bf16": (8, -126), "fp16": (11, -14)}
+
+
+# ----------------------------------------------------------------------------
+# IEEE decoders (fields -> value), fp64
+# ----------------------------------------------------------------------------
+def _decode(bits, exp_bits: int, man_bits: int) -> np.ndarray:
+    b = np.asarray(bits).astype(np.int64)
+    bias = (1 << (exp_bits - 1)) - 1
+    sign = np.where((b >> (exp_bits + man_bits)) & 1, -1.0, 1.0)
+    e = (b >> man_bits) & ((1 << exp_bits) - 1)
+    f = (b & ((1 << man_bits) - 1)).astype(np.float64)
+    frac = f / float(1 << man_bits)
+    with np.errstate(over="ignore", invalid="ignore"):
+        normal = sign * (1.0 + frac) * np.exp2((e - bias).astype(np.float64))
+        subnormal = sign * frac * np.exp2(float(1 - bias))
+        special = np.where(f == 0, sign * np.inf, np.nan)
+    top = (1 << exp_bits) - 1
+    return np.where(e == 0, subnormal, np.where(e == top, special, normal))
+
+
+def fp16_value(bits) -> np.ndarray:
+    """IEEE binary16 bit patterns -> fp64 values (1 sign, 5 exponent, 10 fraction bits)."""
+    return _decode(bits, 5, 10)
+
+
+def bf16_value(bits) -> np.ndarray:
+    """bfloat16 bit patterns -> fp64 values (1 sign, 8 exponent, 7 fraction bits)."""
+    return _decode(bits, 8, 7)
+
+
+def _value(bits, dtype: str) -> np.ndarray:
+    return bf16_value(bits) if dtype == "bf16" else fp16_value(bits)
+
+
+# ----------------------------------------------------------------------------
+# int4 GPTQ weights
+# ----------------------------------------------------------------------------
+def unpack_qweight(qweight, k: int, n: int) -> np.ndarray:
+    """q[i][j] = floor(qweight[i // 8][j] / 16^(i mod 8)) mod 16, as int64 [k][n]."""
+    qw = np.asarray(qweight, dtype=np.uint32).astype(np.int64)
+    assert qw.shape == (k // 8, n)
+    q = np.empty((k, n), dtype=np.int64)
+    for t in range(8):
+        q[t::8, :] = (qw // (16 ** t)) % 16
+    return q
+
+
+def unpack_qzeros(qzeros, groups: int, n: int) -> np.ndarray:
+    """z[g][j] = floor(qzeros[g][j // 8] / 16^(j mod 8)) mod 16, as int64 [groups][n]."""
+    qz = np.asarray(qzeros, dtype=np.uint32).astype(np.int64)
+    assert qz.shape == (groups, n // 8)
+    z = np.empty((groups, n), dtype=np.int64)
+    for t in range(8):
+        z[:, t::8] = (qz // (16 ** t)) % 16
+    return z
+
+
+def dequant(qweight, scales, qzeros, k: int, n: int, group_size: int = GROUP_SIZE,
+            cols=None) -> np.ndarray:
+    """W32[i][j] = fp32((q[i][j] - z[g][j]) * s[g][j]), g = i // group_size.
+
+    Returns fp32 [k][n] (or [k][len(cols)] for a column subset).  The product of a
+    4-bit integer and an fp16 scale is exact in fp32; this is asserted.
+    """
+    groups = k // group_size
+    q = unpack_qweight(qweight, k, n)
+    z = unpack_qzeros(qzeros, groups, n)
+    s = fp16_value(np.asarray(scales).reshape(groups, n))
+    if cols is not None:
+        cols = np.asarray(cols)
+        q, z, s = q[:, cols], z[:, cols], s[:, cols]
+    g = np.arange(k) // group_size
+    w64 = (q - z[g, :]).astype(np.float64) * s[g, :]
+    w32 = w64.astype(np.float32)
+    if not np.array_equal(w32.astype(np.float64), w64):
+        raise AssertionError("(q - z) * s is not exact in fp32")
+    return w32
+
+
+def qgemm_int4(x_bits, qweight, scales, qzeros, m: int, k: int, n: int,
+               group_size: int = GROUP_SIZE) -> np.ndarray:
+    """Y64[m][n] = sum_i x[r][i] * W32[i][j], fp64 accumulation of bf16 x and fp32 W."""
+    if m == 0 or n == 0:
+        return np.zeros((m, n))
+    if k == 0:
+        return np.zeros((m, n))
+    x = bf16_value(np.asarray(x_bits)[:, :k])
+    w = dequant(qweight, scales, qzeros, k, n, group_size).astype(np.float64)
+    return x @ w
+
+
+def qgemm_int4_at(x_bits, qweight, scales, qzeros, k: int, n: int, rows, cols,
+                  group_size: int = GROUP_SIZE) -> np.ndarray:
+    """Y64 restricted to the given rows and columns: [len(rows)][len(cols)]."""
+    x = bf16_value(np.asarray(x_bits)[np.asarray(rows), :k])
+    w = dequant(qweight, scales, qzeros, k, n, group_size, cols=cols).astype(np.float64)
+    return x @ w
+
+
+# ----------------------------------------------------------------------------
+# dense products
+# ----------------------------------------------------------------------------
+def _ops(layout: str, a, b, dtype: str):
+    A = _value(a, dtype)
+    B = _value(b, dtype)
+    if layout == "NT":
+        return A, B.T
+    if layout == "NN":
+        return A, B
+    if layout == "TN":
+        return A.T, B
+    raise ValueError(layout)
+
+
+def dense(layout: str, dtype: str, a_bits, b_bits, M: int, N: int, K: int) -> np.ndarray:
+    """C64[M][N] = op(A) . op(B) over the stored bf16/fp16 values, fp64."""
+    opA, opB = _ops(layout, a_bits, b_bits, dtype)
+    assert opA.shape == (M, K) and opB.shape == (K, N)
+    if K == 0:
+        return np.zeros((M, N))
+    return opA @ opB
+
+
+def dense_at(layout: str, dtype: str, a_bits, b_bits, rows, cols) -> np.ndarray:
+    """C64 restricted to the given rows and columns."""
+    opA, opB = _ops(layout, a_bits, b_bits, dtype)
+    return opA[np.asarray(rows), :] @ opB[:, np.asarray(cols)]
+
+
+# ----------------------------------------------------------------------------
+# the output grid and the acceptance rule
+# ----------------------------------------------------------------------------
+def _ulp(r: np.ndarray, dtype: str) -> np.ndarray:
+    p, emin = _GRID[dtype]
+    mant, E = np.frexp(np.abs(r))   # |r| = mant * 2^E, mant in [0.5, 1)
+    e = np.maximum(E.astype(np.int64) - 1, emin)
+    return np.exp2((e - (p - 1)).astype(np.float64))
+
+
+def grid_bracket(r, dtype: str):
+    """The two output-dtype numbers lo <= r <= hi adjacent on that dtype's grid."""
+    r = np.asarray(r, dtype=np.float64)
+    u = _ulp(r, dtype)
+    return np.floor(r / u) * u, np.ceil(r / u) * u
+
+
+def round_to_grid(r, dtype: str) -> np.ndarray:
+    """r rounded to the nearest output-dtype number, ties to even significand."""
+    r = np.asarray(r, dtype=np.float64)
+    u = _ulp(r, dtype)
+    return np.rint(r / u) * u
+
+
+def accept(y, r, dtype: str) -> np.ndarray:
+    """Per element: |y - r| <= 2e-3 + 2e-3 |r|, or y is a faithful rounding of r."""
+    y = np.asarray(y, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    lo, hi = grid_bracket(r, dtype)
+    literal = np.abs(y - r) <= TOL_ABS + TOL_REL * np.abs(r)
+    return literal | (y == lo) | (y == hi)
+
+
+def compare(y_bits, r, dtype: str) -> dict:
+    """Compare output bit patterns with the fp64 reference; summary statistics."""
+    y = _value(y_bits, dtype)
+    r = np.asarray(r, dtype=np.float64)
+    ok = accept(y, r, dtype)
+    literal = np.abs(y - r) <= TOL_ABS + TOL_REL * np.abs(r)
+    nr = float(np.sqrt(np.sum(r * r)))
+    rms_rel = float(np.sqrt(np.sum((y - r) ** 2)) / nr) if nr > 0 else float(
+        np.sqrt(np.sum(y * y)))
+    ulps = np.abs(y - round_to_grid(r, dtype)) / _ulp(r, dtype)
+    return {
+        "n": int(r.size),
+        "rejected": int(r.size - np.count_nonzero(ok)),
+        "literal_violations": int(r.size - np.count_nonzero(literal)),
+        "rms_rel": rms_rel,
+        "max_ulp": float(np.max(ulps)) if r.size else 0.0,
+        "nonfinite": int(np.count_nonzero(~np.isfinite(y))),
+    }
