@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the int4 GPTQ small-M products on one MI355X.
+
+A step is one pass over the small-M workload: Y = X . W^T with GPTQ int4
+weights (group 128) for (k, n) in {(4096, 4096), (2048, 8192)} and m in
+{1, 8, 15} tokens -- six calls through the C ABI, each taking its dispatch
+path (GEMV for m = 1, the fused small-M kernel otherwise).
+
+Inputs are resident in HBM before timing starts.  In the default cold regime
+every call reads a different copy of its weights, rotating through enough
+copies (>= 512 MiB per shape, twice the 256 MB Infinity Cache) that the
+weights stream from HBM; --regime warm reuses one copy (cache-resident).
+
+Prints ONE JSON line: effective GB/s over the whole step (algorithmic bytes /
+time), per-call microseconds and GB/s, the roofline of the dominant kernel
+measured live with HIP events on the launch stream, and the CPU oracle timed
+on a bounded sample of the same workload.  ``--suite FILE`` also times every
+int4 and dense workload shape and writes them to FILE.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "qgemm µs & eff. HBM GB/s at m=1/8; TFLOPS (% MFMA peak) at m>=512"
+HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA
+LLC_BYTES = 256 << 20
+SMALL_M = [(4096, 4096), (2048, 8192)]
+SMALL_M_TOKENS = [1, 8, 15]
+
+
+def int4_bytes(m, k, n):
+    """Algorithmic bytes of one int4 call: every tensor touched once."""
+    g = k // 128
+    return k * n // 2 + g * n * 2 + g * n // 2 + 2 * m * k + 2 * m * n
+
+
+def dense_bytes(M, N, K):
+    return 2 * (M * K + N * K + M * N)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--regime", choices=["cold", "warm"], default="cold")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="wall time budget of the CPU oracle sample (0 disables)")
+    p.add_argument("--suite", default=None, help="also time all workload shapes into this JSON file")
+    return p.parse_args()
+
+
+class Int4Case:
+    """One int4 product with `copies` resident copies of its weights."""
+
+    def __init__(self, qg, torch, m, k, n, seed, copies):
+        from qgemm_inputs import int4_inputs
+        import numpy as np
+
+        self.m, self.k, self.n = m, k, n
+        d = int4_inputs(m, k, n, seed=seed)
+        self.host = d
+        dev = torch.device("cuda")
+        self.x = torch.from_numpy(d["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+        qw = torch.from_numpy(d["qweight"].view(np.int32)).to(dev)
+        sc = torch.from_numpy(d["scales"].view(np.int16)).to(dev).view(torch.float16)
+        qz = torch.from_numpy(d["qzeros"].view(np.int32)).to(dev)
+        self.w = [(qw, sc, qz)] + [(qw.clone(), sc.clone(), qz.clone()) for _ in range(copies - 1)]
+        self.y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        self.i = 0
+        self.qg = qg
+        self.kernel = qg.describe_int4(m, n, k).split(" ")[0]
+        self.bytes = int4_bytes(m, k, n)
+        self.flops = 2 * m * n * k
+
+    def launch(self, path="auto"):
+        qw, sc, qz = self.w[self.i % len(self.w)]
+        self.i += 1
+        self.qg.qgemm_int4(self.x, qw, sc, qz, out=self.y, path=path)
+
+
+def copies_for(bytes_per_copy, regime):
+    if regime == "warm":
+        return 1
+    return max(2, -(-2 * LLC_BYTES // bytes_per_copy))
+
+
+def time_us(torch, fn, iters):
+    """Average microseconds per call of fn() over iters back-to-back calls on the stream."""
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(iters):
+        fn()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / iters
+
+
+def cpu_baseline(cases, seconds):
+    """The CPU oracle, as it stands, on the same inputs until `seconds` have passed."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    t0 = time.perf_counter()
+    done_bytes, calls = 0, 0
+    while True:
+        for c in cases:
+            d = c.host
+            oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], c.m, c.k, c.n)
+            done_bytes += c.bytes
+            calls += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d oracle calls cycling over the six small-M products (%.1f s, numpy with "
+                      "a %d-thread BLAS)" % (calls, el, threads)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import int4_weight_only_gptq_amd as qg
+
+    qg.load()
+    torch.cuda.init()
+
+    cases = []
+    for si, (k, n) in enumerate(SMALL_M):
+        for mi, m in enumerate(SMALL_M_TOKENS):
+            nb = int4_bytes(0, k, n)
+            cases.append(Int4Case(qg, torch, m, k, n, seed=(1001 * 65536) + 3 * si + mi,
+                                  copies=copies_for(nb, args.regime)))
+    torch.cuda.synchronize()
+
+    # per-call timing (each case back to back), then the whole step
+    for c in cases:
+        for _ in range(args.warmup):
+            c.launch()
+    per_case = []
+    for c in cases:
+        us = time_us(torch, c.launch, args.steps)
+        per_case.append({"m": c.m, "k": c.k, "n": c.n, "kernel": c.kernel, "us": round(us, 3),
+                         "gbps": round(c.bytes / us / 1e3, 1), "bytes": c.bytes})
+
+    def step():
+        for c in cases:
+            c.launch()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    step_us = time_us(torch, step, args.steps)
+    step_bytes = sum(c.bytes for c in cases)
+    value = step_bytes / step_us / 1e3
+
+    # dominant kernel: largest share of the step; its average launch duration is
+    # the event-timed average over its calls in the per-call runs above
+    agg = {}
+    for pc in per_case:
+        a = agg.setdefault(pc["kernel"], {"us": 0.0, "bytes": 0, "launches": 0})
+        a["us"] += pc["us"]
+        a["bytes"] += pc["bytes"]
+        a["launches"] += 1
+    dom = max(agg, key=lambda name: agg[name]["us"])
+    a = agg[dom]
+    avg_us, avg_bytes = a["us"] / a["launches"], a["bytes"] / a["launches"]
+    achieved = avg_bytes / avg_us / 1e3
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "avg_launch_us": round(avg_us, 3), "bytes_per_launch": int(avg_bytes),
+                "traffic": None}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_us / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "int4 GPTQ small-M: k x n in {4096x4096, 2048x8192}, m in "
+                               "{1, 8, 15}, group 128, bf16 activations",
+                   "regime": args.regime, "calls_per_step": len(cases),
+                   "parallelism": "none (1 GPU)"},
+        "cases": per_case,
+        "roofline": roofline,
+    }
+    if args.suite:
+        out["suite_file"] = args.suite
+        run_suite(qg, torch, args, args.suite)
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(cases, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def run_suite(qg, torch, args, path):
+    """Time every int4 and dense workload shape (auto path) into a JSON file."""
+    import numpy as np
+    from qgemm_inputs import dense_cases, dense_inputs, int4_cases
+
+    rows = []
+    iters = max(10, args.steps // 4)
+    for cfg in (0, 1, 2, 4):
+        for (_, m, k, n, seed) in int4_cases(cfg):
+            c = Int4Case(qg, torch, m, k, n, seed, copies_for(int4_bytes(0, k, n), args.regime))
+            for _ in range(3):
+                c.launch()
+            us = time_us(torch, c.launch, iters)
+            rows.append({"kind": "int4", "m": m, "k": k, "n": n, "kernel": c.kernel, "us": us,
+                         "gbps": c.bytes / us / 1e3, "tflops": c.flops / us / 1e6,
+                         "mfma_frac": c.flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS})
+            print("suite int4", rows[-1], file=sys.stderr, flush=True)
+            del c
+            torch.cuda.empty_cache()
+    for case in dense_cases(3):
+        d = dense_inputs(case["layout"], case["dtype"], case["M"], case["N"], case["K"], case["seed"])
+        dt = torch.bfloat16 if case["dtype"] == "bf16" else torch.float16
+        a = torch.from_numpy(d["a"].view(np.int16)).cuda().view(dt)
+        b = torch.from_numpy(d["b"].view(np.int16)).cuda().view(dt)
+        out = qg.gemm_dense(case["layout"], a, b)
+        us = time_us(torch, lambda: qg.gemm_dense(case["layout"], a, b, out=out), iters)
+        M, N, K = case["M"], case["N"], case["K"]
+        rows.append({"kind": "dense", "role": case["role"], "layout": case["layout"],
+                     "dtype": case["dtype"], "M": M, "N": N, "K": K, "us": us,
+                     "gbps": dense_bytes(M, N, K) / us / 1e3, "tflops": 2 * M * N * K / us / 1e6,
+                     "mfma_frac": 2 * M * N * K / us / 1e6 / MFMA_BF16_PEAK_TFLOPS})
+        print("suite dense", rows[-1], file=sys.stderr, flush=True)
+    with open(path, "w") as f:
+        json.dump({"regime": args.regime, "rows": rows}, f, indent=1)
+
+
+if __name__ == "__main__":
+    main()

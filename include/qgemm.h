@@ -1,0 +1,153 @@
+/*
+ * qgemm.h -- C ABI of the MI355X (gfx950) int4 GPTQ and dense GEMM library.
+ *
+ * The products are the linear-layer matmuls of the pages:
+ *   - the GPTQ int4 weight-only linear layer (GPTQModel pull request #3645,
+ *     "What changed": one fused kernel for m <= 15 tokens, the matrix-core
+ *     kernel from m = 16; mi50grad README, "Project Structure" and "Model":
+ *     an int4 GEMV with a DPP reduction, GPTQ-Int4 with group size 128);
+ *   - the dense bf16/fp16 training products with fp32 accumulation (BC-250
+ *     tuned-GEMM post, "Where the time went": forward, input-gradient and
+ *     weight-gradient products, each a different memory layout).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates no memory, keeps no state between calls and may be called from
+ *     several host threads at once.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it and the call returns without waiting.
+ *   - Matrices are row-major; a leading dimension (ld*) is the distance in
+ *     elements between consecutive rows and must be >= the row length.
+ *   - Every argument is validated on the host before anything is launched.  An
+ *     invalid call returns a non-zero qg_status and enqueues nothing.  After a
+ *     launch, a HIP launch error is reported as QG_ERR_HIP; the HIP error code is
+ *     then available from qg_last_hip_error() on the calling thread.
+ *   - Sizes of zero are valid: m == 0 or n == 0 enqueue nothing (pointers may be
+ *     NULL); k == 0 writes zeros to the output.
+ *   - No C++ exception crosses this boundary.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QG_ABI_VERSION 1
+
+/* Return codes (qg_status values, returned as int32_t). */
+#define QG_OK 0
+#define QG_ERR_NULL 1        /* a required pointer is NULL                         */
+#define QG_ERR_SHAPE 2       /* negative size, ld too small, k % 128 or n % 8 != 0 */
+#define QG_ERR_ALIGN 3       /* a pointer or leading dimension is misaligned       */
+#define QG_ERR_DTYPE 4       /* unknown dtype code                                 */
+#define QG_ERR_LAYOUT 5      /* unknown layout code                                */
+#define QG_ERR_UNSUPPORTED 6 /* group size != 128, or a forced path that cannot take m */
+#define QG_ERR_HIP 7         /* the HIP runtime rejected a launch                  */
+
+/* dtype codes of gemm_dense */
+#define QG_BF16 0
+#define QG_FP16 1
+
+/* layout codes of gemm_dense (row-major definitions, see gemm_dense) */
+#define QG_NT 0
+#define QG_NN 1
+#define QG_TN 2
+
+/* path codes of qgemm_int4_path */
+#define QG_PATH_AUTO 0  /* m == 1: GEMV; 2 <= m <= 16: fused small-M; m > 16: MFMA tiles */
+#define QG_PATH_GEMV 1  /* m must be 1                                                   */
+#define QG_PATH_FUSED 2 /* 1 <= m <= 16                                                   */
+#define QG_PATH_MFMA 3  /* any m >= 1                                                    */
+
+/* Version of this ABI (QG_ABI_VERSION of the built library). */
+int32_t qg_abi_version(void);
+
+/* Static, NUL-terminated description of a qg_status value. */
+const char* qg_status_str(int32_t status);
+
+/* HIP error code (hipError_t as int) of the last QG_ERR_HIP on this thread. */
+int32_t qg_last_hip_error(void);
+
+/*
+ * qgemm_int4 -- Y = X . W^T with GPTQ int4 weights (GPTQModel #3645, "What
+ * changed" and "Accuracy"; mi50grad README, "Model": group size 128).
+ *
+ *   Y[r][j] = bf16_rne( sum_i X[r][i] * W[i][j] ),  accumulated in fp32,
+ *   W[i][j] = (q[i][j] - z[i/128][j]) * s[i/128][j]  (exact in fp32).
+ *
+ *   x        bf16 [m][ldx], ldx >= k, ldx % 8 == 0, 16-byte aligned.
+ *   qweight  uint32 [k/8][n], 16-byte aligned.  Word (r, j) holds the 4-bit
+ *            codes of rows 8r..8r+7 of output column j; row 8r+t is in bits
+ *            4t..4t+3 (least significant nibble first).
+ *   scales   fp16 bit patterns [k/128][n], 8-byte aligned.
+ *   qzeros   uint32 [k/128][n/8], 4-byte aligned.  Word (g, c) holds the 4-bit
+ *            zero points of columns 8c..8c+7; column 8c+t in bits 4t..4t+3.
+ *            The stored nibble is z itself (no +1 offset).
+ *   y        bf16 [m][ldy] output, ldy >= n, ldy % 4 == 0, 8-byte aligned.
+ *   m >= 0 tokens, n >= 0 output columns (n % 8 == 0), k >= 0 input rows
+ *   (k % 128 == 0), group_size must be 128.
+ *
+ * The path is chosen from m (see QG_PATH_AUTO).  x and y must not overlap the
+ * weights.  Errors: QG_ERR_NULL, QG_ERR_SHAPE, QG_ERR_ALIGN, QG_ERR_UNSUPPORTED,
+ * QG_ERR_HIP.
+ */
+int32_t qgemm_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
+                   const uint32_t* qzeros, void* y, int64_t ldy, int64_t m, int64_t n, int64_t k,
+                   int32_t group_size, void* stream);
+
+/*
+ * qgemm_int4_path -- qgemm_int4 with the kernel path forced (QG_PATH_* code),
+ * for same-process A/B measurement and per-path testing.  A path that cannot
+ * take m returns QG_ERR_UNSUPPORTED.  Same arguments and results otherwise.
+ */
+int32_t qgemm_int4_path(const void* x, int64_t ldx, const uint32_t* qweight,
+                        const uint16_t* scales, const uint32_t* qzeros, void* y, int64_t ldy,
+                        int64_t m, int64_t n, int64_t k, int32_t group_size, int32_t path,
+                        void* stream);
+
+/*
+ * qgemm_int4_describe -- names the kernel and launch shape that qgemm_int4_path
+ * would use for (m, n, k, path), e.g. "fused_int4_kernel<8,1> grid=256
+ * block=1024 lds=32768", into buf (NUL-terminated, truncated to len bytes).
+ * Launches nothing.  Errors: QG_ERR_NULL (buf), QG_ERR_SHAPE, QG_ERR_UNSUPPORTED.
+ */
+int32_t qgemm_int4_describe(int64_t m, int64_t n, int64_t k, int32_t path, char* buf, int64_t len);
+
+/*
+ * qgemm_int4_dequant -- the dequantised weights themselves, for a bit-exact
+ * check of the decode every int4 path shares (same storage as qgemm_int4):
+ *
+ *   w[i][j] = (float)(q[i][j] - z[i/128][j]) * s[i/128][j],  fp32 [k][n], n-contiguous.
+ *
+ * w must be 16-byte aligned.  Errors as qgemm_int4.
+ */
+int32_t qgemm_int4_dequant(const uint32_t* qweight, const uint16_t* scales,
+                           const uint32_t* qzeros, float* w, int64_t n, int64_t k,
+                           int32_t group_size, void* stream);
+
+/*
+ * gemm_dense -- C = op(A) . op(B) in bf16 or fp16 with fp32 accumulation
+ * (BC-250 tuned-GEMM post, "Where the time went" and "Tuning the kernels": the
+ * three products of a linear layer, each a different memory layout, with FP32
+ * accumulation).  Row-major definitions:
+ *
+ *   QG_NT  forward:          C[M][N] = A[M][K] . B[N][K]^T   (lda >= K, ldb >= K)
+ *   QG_NN  input gradient:   C[M][N] = A[M][K] . B[K][N]     (lda >= K, ldb >= N)
+ *   QG_TN  weight gradient:  C[M][N] = A[K][M]^T . B[K][N]   (lda >= M, ldb >= N)
+ *
+ * A, B and C share the dtype (QG_BF16 or QG_FP16); C is rounded to nearest even
+ * from the fp32 accumulator, ldc >= N.  Pointers must be 2-byte aligned; any
+ * sizes are accepted (1x1x1 included).  Errors: QG_ERR_NULL, QG_ERR_SHAPE,
+ * QG_ERR_ALIGN, QG_ERR_DTYPE, QG_ERR_LAYOUT, QG_ERR_HIP.
+ */
+int32_t gemm_dense(int32_t layout, int32_t dtype, int64_t M, int64_t N, int64_t K, const void* A,
+                   int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

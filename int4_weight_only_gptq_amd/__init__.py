@@ -1,0 +1,160 @@
+"""Python binding of the gfx950 int4 GPTQ / dense GEMM library (C ABI in include/qgemm.h).
+
+Argument marshalling only: torch tensors supply device pointers, shapes and
+strides, and torch's current HIP stream is passed through.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.  The
+library must have been built (``python -m int4_weight_only_gptq_amd.build``);
+loading fails loudly otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["load", "lib_path", "QGemmError", "qgemm_int4", "qgemm_int4_dequant", "gemm_dense", "describe_int4",
+           "abi_version", "PATHS", "LAYOUTS"]
+
+_LIB_NAME = "libqgemm_gfx950.so"
+_lib = None
+
+PATHS = {"auto": 0, "gemv": 1, "fused": 2, "mfma": 3}
+LAYOUTS = {"NT": 0, "NN": 1, "TN": 2}
+_DTYPES = {"bf16": 0, "fp16": 1}
+
+
+class QGemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _lib.qg_status_str(status).decode() if _lib is not None else "status %d" % status
+        if status == 7 and _lib is not None:
+            msg += " (hipError %d)" % _lib.qg_last_hip_error()
+        super().__init__("%s: %s" % (where, msg))
+        self.status = status
+
+
+def lib_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), _LIB_NAME)
+
+
+def load():
+    """Load the built library (binds to the HIP runtime torch has loaded)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  -- the library must share torch's HIP runtime
+
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError("%s is not built; run python -m int4_weight_only_gptq_amd.build" % path)
+    lib = ctypes.CDLL(path)
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    lib.qg_abi_version.restype = i32
+    lib.qg_abi_version.argtypes = []
+    lib.qg_status_str.restype = ctypes.c_char_p
+    lib.qg_status_str.argtypes = [i32]
+    lib.qg_last_hip_error.restype = i32
+    lib.qg_last_hip_error.argtypes = []
+    int4_args = [vp, i64, vp, vp, vp, vp, i64, i64, i64, i64, i32]
+    lib.qgemm_int4.restype = i32
+    lib.qgemm_int4.argtypes = int4_args + [vp]
+    lib.qgemm_int4_path.restype = i32
+    lib.qgemm_int4_path.argtypes = int4_args + [i32, vp]
+    lib.qgemm_int4_describe.restype = i32
+    lib.qgemm_int4_describe.argtypes = [i64, i64, i64, i32, ctypes.c_char_p, i64]
+    lib.qgemm_int4_dequant.restype = i32
+    lib.qgemm_int4_dequant.argtypes = [vp, vp, vp, vp, i64, i64, i32, vp]
+    lib.gemm_dense.restype = i32
+    lib.gemm_dense.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return load().qg_abi_version()
+
+
+def _stream(t, stream):
+    import torch
+
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ld(t) -> int:
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+
+
+def _check(status, where):
+    if status != 0:
+        raise QGemmError(status, where)
+
+
+def qgemm_int4(x, qweight, scales, qzeros, out=None, group_size: int = 128, path: str = "auto",
+               stream=None):
+    """Y[m][n] (bf16) = X[m][k] (bf16) . dequant(W)^T, W given in GPTQ int4 storage.
+
+    qweight int32/uint32 [k/8][n]; scales fp16 [k/128][n]; qzeros int32/uint32
+    [k/128][n/8].  ``path`` forces a kernel ("gemv", "fused", "mfma") or "auto".
+    """
+    import torch
+
+    lib = load()
+    m, k = x.shape
+    n = qweight.shape[1]
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    st = lib.qgemm_int4_path(x.data_ptr(), _ld(x), qweight.data_ptr(), scales.data_ptr(),
+                             qzeros.data_ptr(), out.data_ptr(), _ld(out), m, n, k, group_size,
+                             PATHS[path], _stream(x, stream))
+    _check(st, "qgemm_int4")
+    return out
+
+
+def describe_int4(m: int, n: int, k: int, path: str = "auto") -> str:
+    """Kernel and launch shape qgemm_int4 uses for (m, n, k, path); launches nothing."""
+    lib = load()
+    buf = ctypes.create_string_buffer(256)
+    _check(lib.qgemm_int4_describe(m, n, k, PATHS[path], buf, 256), "qgemm_int4_describe")
+    return buf.value.decode()
+
+
+def qgemm_int4_dequant(qweight, scales, qzeros, out=None, group_size: int = 128, stream=None):
+    """fp32 [k][n] dequantised weights (q - z) * s."""
+    import torch
+
+    lib = load()
+    k, n = qweight.shape[0] * 8, qweight.shape[1]
+    if out is None:
+        out = torch.empty((k, n), dtype=torch.float32, device=qweight.device)
+    st = lib.qgemm_int4_dequant(qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(),
+                                out.data_ptr(), n, k, group_size, _stream(qweight, stream))
+    _check(st, "qgemm_int4_dequant")
+    return out
+
+
+def gemm_dense(layout: str, a, b, out=None, stream=None):
+    """C = op(A) . op(B) for layout "NT", "NN" or "TN" (row-major, see qgemm.h)."""
+    import torch
+
+    lib = load()
+    if a.dtype != b.dtype or a.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("A and B must share dtype bf16 or fp16")
+    dtype = "bf16" if a.dtype == torch.bfloat16 else "fp16"
+    if layout == "NT":
+        (M, K), N = a.shape, b.shape[0]
+    elif layout == "NN":
+        (M, K), N = a.shape, b.shape[1]
+    elif layout == "TN":
+        (K, M), N = a.shape, b.shape[1]
+    else:
+        raise ValueError(layout)
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    st = lib.gemm_dense(LAYOUTS[layout], _DTYPES[dtype], M, N, K, a.data_ptr(), _ld(a),
+                        b.data_ptr(), _ld(b), out.data_ptr(), _ld(out), _stream(a, stream))
+    _check(st, "gemm_dense")
+    return out

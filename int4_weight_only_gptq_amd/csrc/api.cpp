@@ -1,0 +1,151 @@
+// C ABI of the library: argument validation, path choice and launch.
+// Declarations and the contract of each entry point are in include/qgemm.h.
+#include "qgemm.h"
+
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+int32_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return QG_OK;
+  g_last_hip_error = (int32_t)e;
+  return QG_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Validation shared by the int4 entry points; returns QG_OK or the error.
+int32_t check_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
+                   const uint32_t* qzeros, const void* y, int64_t ldy, int64_t m, int64_t n,
+                   int64_t k, int32_t group_size) {
+  if (m < 0 || n < 0 || k < 0) return QG_ERR_SHAPE;
+  if (group_size != 128) return QG_ERR_UNSUPPORTED;
+  if (k % 128 != 0 || n % 8 != 0) return QG_ERR_SHAPE;
+  // the kernels index with 32-bit column and row counts
+  if (n > (int64_t)1 << 30 || k > (int64_t)1 << 30) return QG_ERR_SHAPE;
+  if (m == 0 || n == 0) return QG_OK;
+  if (y == nullptr) return QG_ERR_NULL;
+  if (ldy < n) return QG_ERR_SHAPE;
+  if (!aligned(y, 8) || ldy % 4 != 0) return QG_ERR_ALIGN;
+  if (k == 0) return QG_OK;
+  if (x == nullptr || qweight == nullptr || scales == nullptr || qzeros == nullptr) return QG_ERR_NULL;
+  if (ldx < k) return QG_ERR_SHAPE;
+  if (!aligned(x, 16) || ldx % 8 != 0) return QG_ERR_ALIGN;
+  if (!aligned(qweight, 16) || !aligned(scales, 8) || !aligned(qzeros, 4)) return QG_ERR_ALIGN;
+  return QG_OK;
+}
+
+int32_t run_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
+                 const uint32_t* qzeros, void* y, int64_t ldy, int64_t m, int64_t n, int64_t k,
+                 int32_t group_size, int32_t path, void* stream) {
+  int32_t st = check_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size);
+  if (st != QG_OK) return st;
+  if (path < QG_PATH_AUTO || path > QG_PATH_MFMA) return QG_ERR_UNSUPPORTED;
+  if (path == QG_PATH_GEMV && m > 1) return QG_ERR_UNSUPPORTED;
+  if (path == QG_PATH_FUSED && m > 16) return QG_ERR_UNSUPPORTED;
+  if (m == 0 || n == 0) return QG_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (k == 0) return hip_status(qg::launch_zero16((uint16_t*)y, m, n, ldy, s));
+  const qg::Int4Args a{(const uint16_t*)x, ldx, qweight, scales, qzeros, (uint16_t*)y, ldy, m, n, k};
+  if (path == QG_PATH_AUTO) path = m == 1 ? QG_PATH_GEMV : (m <= 16 ? QG_PATH_FUSED : QG_PATH_MFMA);
+  switch (path) {
+    case QG_PATH_GEMV: return hip_status(qg::launch_gemv_int4(a, s));
+    case QG_PATH_FUSED: return hip_status(qg::launch_fused_int4(a, s));
+    default: return hip_status(qg::launch_mfma_int4(a, s));
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t qg_abi_version(void) { return QG_ABI_VERSION; }
+
+const char* qg_status_str(int32_t status) {
+  switch (status) {
+    case QG_OK: return "ok";
+    case QG_ERR_NULL: return "a required pointer is NULL";
+    case QG_ERR_SHAPE: return "invalid shape or leading dimension";
+    case QG_ERR_ALIGN: return "misaligned pointer or leading dimension";
+    case QG_ERR_DTYPE: return "unknown dtype";
+    case QG_ERR_LAYOUT: return "unknown layout";
+    case QG_ERR_UNSUPPORTED: return "unsupported group size or path for this m";
+    case QG_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int32_t qg_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t qgemm_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
+                   const uint32_t* qzeros, void* y, int64_t ldy, int64_t m, int64_t n, int64_t k,
+                   int32_t group_size, void* stream) {
+  return run_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size, QG_PATH_AUTO, stream);
+}
+
+int32_t qgemm_int4_path(const void* x, int64_t ldx, const uint32_t* qweight,
+                        const uint16_t* scales, const uint32_t* qzeros, void* y, int64_t ldy,
+                        int64_t m, int64_t n, int64_t k, int32_t group_size, int32_t path,
+                        void* stream) {
+  return run_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size, path, stream);
+}
+
+int32_t qgemm_int4_describe(int64_t m, int64_t n, int64_t k, int32_t path, char* buf, int64_t len) {
+  if (buf == nullptr || len <= 0) return QG_ERR_NULL;
+  buf[0] = 0;
+  if (m < 0 || n < 0 || k < 0 || k % 128 != 0 || n % 8 != 0) return QG_ERR_SHAPE;
+  if (path < QG_PATH_AUTO || path > QG_PATH_MFMA) return QG_ERR_UNSUPPORTED;
+  if ((path == QG_PATH_GEMV && m > 1) || (path == QG_PATH_FUSED && m > 16)) return QG_ERR_UNSUPPORTED;
+  if (m == 0 || n == 0) {
+    snprintf(buf, (size_t)len, "none");
+    return QG_OK;
+  }
+  if (k == 0) {
+    snprintf(buf, (size_t)len, "zero16_kernel");
+    return QG_OK;
+  }
+  if (path == QG_PATH_AUTO) path = m == 1 ? QG_PATH_GEMV : (m <= 16 ? QG_PATH_FUSED : QG_PATH_MFMA);
+  qg::describe_int4(m, n, k, path, buf, (size_t)len);
+  return QG_OK;
+}
+
+int32_t qgemm_int4_dequant(const uint32_t* qweight, const uint16_t* scales,
+                           const uint32_t* qzeros, float* w, int64_t n, int64_t k,
+                           int32_t group_size, void* stream) {
+  if (n < 0 || k < 0) return QG_ERR_SHAPE;
+  if (group_size != 128) return QG_ERR_UNSUPPORTED;
+  if (k % 128 != 0 || n % 8 != 0) return QG_ERR_SHAPE;
+  if (n == 0 || k == 0) return QG_OK;
+  if (qweight == nullptr || scales == nullptr || qzeros == nullptr || w == nullptr) return QG_ERR_NULL;
+  if (!aligned(qweight, 16) || !aligned(scales, 8) || !aligned(qzeros, 4) || !aligned(w, 16))
+    return QG_ERR_ALIGN;
+  return hip_status(qg::launch_dequant(qweight, scales, qzeros, w, n, k, (hipStream_t)stream));
+}
+
+int32_t gemm_dense(int32_t layout, int32_t dtype, int64_t M, int64_t N, int64_t K, const void* A,
+                   int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
+  if (layout < QG_NT || layout > QG_TN) return QG_ERR_LAYOUT;
+  if (dtype != QG_BF16 && dtype != QG_FP16) return QG_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0) return QG_ERR_SHAPE;
+  if (M == 0 || N == 0) return QG_OK;
+  if (C == nullptr) return QG_ERR_NULL;
+  if (ldc < N) return QG_ERR_SHAPE;
+  if (!aligned(C, 2)) return QG_ERR_ALIGN;
+  if (K > 0) {
+    if (A == nullptr || B == nullptr) return QG_ERR_NULL;
+    const int64_t a_row = layout == QG_TN ? M : K;
+    const int64_t b_row = layout == QG_NT ? K : N;
+    if (lda < a_row || ldb < b_row) return QG_ERR_SHAPE;
+    if (!aligned(A, 2) || !aligned(B, 2)) return QG_ERR_ALIGN;
+  }
+  const qg::DenseArgs a{layout, dtype, M, N, K, (const uint16_t*)A, lda, (const uint16_t*)B, ldb,
+                        (uint16_t*)C, ldc};
+  return hip_status(qg::launch_dense(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Shared device-side definitions for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kGroup = 128;     // rows of k sharing one scale and zero
+constexpr int kWave = 64;       // CDNA wavefront
+
+// bf16 bit pattern of 1.0 in both halves of a dword.
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
+// bf16 bit pattern of 128.0; OR-ing a 4-bit code q into its low mantissa bits
+// gives the bf16 value 128 + q exactly (the ulp of [128, 256) is 1).
+constexpr uint32_t kBias128x2 = 0x43004300u;
+
+// Four dwords holding the eight codes of one qweight word as bf16 pairs
+// (128 + q_t, 128 + q_{t+4}), t = 0..3.  The k order inside the MFMA operand is
+// therefore 0,4,1,5,2,6,3,7; the activation operand uses the same order
+// (see x_pairs_permuted), so the contraction over k is unchanged.
+__device__ __forceinline__ u32x4 codes_as_bf16_pairs(uint32_t w) {
+  u32x4 r;
+  r[0] = (w & 0x000F000Fu) | kBias128x2;
+  r[1] = ((w >> 4) & 0x000F000Fu) | kBias128x2;
+  r[2] = ((w >> 8) & 0x000F000Fu) | kBias128x2;
+  r[3] = ((w >> 12) & 0x000F000Fu) | kBias128x2;
+  return r;
+}
+
+// Eight consecutive bf16 activations (four dwords, x0..x7) reordered to the
+// pairs (x_t, x_{t+4}), t = 0..3, matching codes_as_bf16_pairs.
+__device__ __forceinline__ u32x4 x_pairs_permuted(u32x4 d) {
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(d[2], d[0], 0x05040100u);
+  r[1] = __builtin_amdgcn_perm(d[2], d[0], 0x07060302u);
+  r[2] = __builtin_amdgcn_perm(d[3], d[1], 0x05040100u);
+  r[3] = __builtin_amdgcn_perm(d[3], d[1], 0x07060302u);
+  return r;
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// fp32 -> bf16 bit pattern, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  _Float16 a = (_Float16)lo, b = (_Float16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ f32x4 mfma16_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Sum of a value over the four 16-lane rows of the wave (lanes l, l^16, l^32,
+// l^48), using the gfx950 row-swap permutes; every lane gets the total.
+__device__ __forceinline__ float sum_over_rows(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  auto p32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  float s = __builtin_bit_cast(float, (uint32_t)p32[0]) + __builtin_bit_cast(float, (uint32_t)p32[1]);
+  uint32_t us = __builtin_bit_cast(uint32_t, s);
+  auto p16 = __builtin_amdgcn_permlane16_swap(us, us, false, false);
+  return __builtin_bit_cast(float, (uint32_t)p16[0]) + __builtin_bit_cast(float, (uint32_t)p16[1]);
+}
+
+}  // namespace qg

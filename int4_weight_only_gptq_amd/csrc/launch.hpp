@@ -1,0 +1,47 @@
+// Internal launchers (host side) of the gfx950 kernels.  Arguments are already
+// validated by the C ABI layer; every launcher only enqueues work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+struct Int4Args {
+  const uint16_t* x;
+  int64_t ldx;
+  const uint32_t* qweight;
+  const uint16_t* scales;
+  const uint32_t* qzeros;
+  uint16_t* y;
+  int64_t ldy;
+  int64_t m, n, k;
+};
+
+hipError_t launch_dequant(const uint32_t* qweight, const uint16_t* scales, const uint32_t* qzeros,
+                          float* w, int64_t n, int64_t k, hipStream_t stream);
+hipError_t launch_gemv_int4(const Int4Args& a, hipStream_t stream);
+hipError_t launch_fused_int4(const Int4Args& a, hipStream_t stream);
+hipError_t launch_mfma_int4(const Int4Args& a, hipStream_t stream);
+
+// Text description of the kernel and launch shape of a path (1 GEMV, 2 fused, 3 MFMA).
+void describe_int4(int64_t m, int64_t n, int64_t k, int path, char* buf, size_t len);
+
+// Writes zeros to a rows x cols matrix of 16-bit elements with leading dimension ld.
+hipError_t launch_zero16(uint16_t* p, int64_t rows, int64_t cols, int64_t ld, hipStream_t stream);
+
+struct DenseArgs {
+  int layout;  // 0 NT, 1 NN, 2 TN
+  int dtype;   // 0 bf16, 1 fp16
+  int64_t M, N, K;
+  const uint16_t* A;
+  int64_t lda;
+  const uint16_t* B;
+  int64_t ldb;
+  uint16_t* C;
+  int64_t ldc;
+};
+
+hipError_t launch_dense(const DenseArgs& a, hipStream_t stream);
+
+}  // namespace qg

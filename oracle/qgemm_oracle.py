@@ -112,12 +112,20 @@ def dequant(qweight, scales, qzeros, k: int, n: int, group_size: int = GROUP_SIZ
     4-bit integer and an fp16 scale is exact in fp32; this is asserted.
     """
     groups = k // group_size
-    q = unpack_qweight(qweight, k, n)
-    z = unpack_qzeros(qzeros, groups, n)
-    s = fp16_value(np.asarray(scales).reshape(groups, n))
-    if cols is not None:
+    qweight = np.asarray(qweight)
+    scales = np.asarray(scales).reshape(groups, n)
+    qzeros = np.asarray(qzeros)
+    if cols is None:
+        q = unpack_qweight(qweight, k, n)
+        z = unpack_qzeros(qzeros, groups, n)
+        s = fp16_value(scales)
+    else:
+        # the same definitions, evaluated only for the requested columns
         cols = np.asarray(cols)
-        q, z, s = q[:, cols], z[:, cols], s[:, cols]
+        q = unpack_qweight(qweight[:, cols], k, len(cols))
+        zw = qzeros[:, cols // 8].astype(np.int64)
+        z = (zw // (16 ** (cols % 8))[None, :]) % 16
+        s = fp16_value(scales[:, cols])
     g = np.arange(k) // group_size
     w64 = (q - z[g, :]).astype(np.float64) * s[g, :]
     w32 = w64.astype(np.float32)

@@ -1,0 +1,129 @@
+"""C ABI contract checks that need no GPU: the library loads, exports every entry
+point include/qgemm.h declares, and rejects invalid arguments with the exact
+status code before anything is launched (no compute call is made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import int4_weight_only_gptq_amd as qg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemm.h")
+
+OK, NULL, SHAPE, ALIGN, DTYPE, LAYOUT, UNSUP = 0, 1, 2, 3, 4, 5, 6
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^(?:int32_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def defines(prefix):
+    text = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"#define\s+(%s\w*)\s+(\d+)" % prefix, text)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return qg.load()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "qg_abi_version", "qg_status_str", "qg_last_hip_error", "qgemm_int4", "qgemm_int4_path",
+        "qgemm_int4_describe", "qgemm_int4_dequant", "gemm_dense"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", qg.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s(\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_header_codes_match_binding():
+    assert defines("QG_PATH_") == {"QG_PATH_AUTO": 0, "QG_PATH_GEMV": 1, "QG_PATH_FUSED": 2,
+                                   "QG_PATH_MFMA": 3}
+    assert {k: v for k, v in defines("QG_").items() if k in ("QG_NT", "QG_NN", "QG_TN")} == {
+        "QG_NT": qg.LAYOUTS["NT"], "QG_NN": qg.LAYOUTS["NN"], "QG_TN": qg.LAYOUTS["TN"]}
+
+
+def test_version_and_status_strings(lib):
+    assert lib.qg_abi_version() == defines("QG_ABI")["QG_ABI_VERSION"]
+    for code in range(8):
+        assert lib.qg_status_str(code)
+    assert lib.qg_status_str(99) == b"unknown status"
+
+
+# Fake device addresses: validation rejects the call before any use of them.
+A16 = 0x10000          # 16-byte aligned
+MIS = 0x10002          # 2-byte aligned only
+
+
+def int4(lib, x=A16, ldx=256, qw=A16, sc=A16, qz=A16, y=A16, ldy=64, m=1, n=64, k=256, gs=128,
+         path=0):
+    return lib.qgemm_int4_path(x, ldx, qw, sc, qz, y, ldy, m, n, k, gs, path, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(m=-1), SHAPE), (dict(n=-8), SHAPE), (dict(k=-128), SHAPE),
+    (dict(gs=64), UNSUP), (dict(k=200), SHAPE), (dict(n=60), SHAPE),
+    (dict(x=0), NULL), (dict(qw=0), NULL), (dict(sc=0), NULL), (dict(qz=0), NULL), (dict(y=0), NULL),
+    (dict(ldx=128), SHAPE), (dict(ldy=32), SHAPE),
+    (dict(x=MIS), ALIGN), (dict(ldx=260), ALIGN), (dict(qw=A16 + 4), ALIGN),
+    (dict(sc=A16 + 2), ALIGN), (dict(qz=A16 + 2), ALIGN), (dict(y=A16 + 2), ALIGN),
+    (dict(ldy=66), ALIGN),
+    (dict(path=1, m=2), UNSUP), (dict(path=2, m=17), UNSUP), (dict(path=9), UNSUP),
+])
+def test_int4_rejects_invalid_arguments(lib, kw, code):
+    assert int4(lib, **kw) == code
+
+
+def test_int4_empty_problems_are_noops(lib):
+    # m == 0 or n == 0: nothing is launched, NULL pointers allowed
+    assert int4(lib, m=0, x=0, qw=0, sc=0, qz=0, y=0) == OK
+    assert int4(lib, n=0, x=0, qw=0, sc=0, qz=0, y=0) == OK
+
+
+def test_dequant_rejects_invalid_arguments(lib):
+    d = lib.qgemm_int4_dequant
+    assert d(A16, A16, A16, A16, 64, 100, 128, None) == SHAPE
+    assert d(A16, A16, A16, A16, 64, 128, 32, None) == UNSUP
+    assert d(0, A16, A16, A16, 64, 128, 128, None) == NULL
+    assert d(A16, A16, A16, A16 + 4, 64, 128, 128, None) == ALIGN
+    assert d(0, 0, 0, 0, 0, 128, 128, None) == OK
+
+
+@pytest.mark.parametrize("args,code", [
+    ((3, 0, 4, 4, 4, A16, 4, A16, 4, A16, 4), LAYOUT),
+    ((0, 2, 4, 4, 4, A16, 4, A16, 4, A16, 4), DTYPE),
+    ((0, 0, -1, 4, 4, A16, 4, A16, 4, A16, 4), SHAPE),
+    ((0, 0, 4, 4, 4, 0, 4, A16, 4, A16, 4), NULL),
+    ((0, 0, 4, 4, 4, A16, 4, A16, 4, 0, 4), NULL),
+    ((0, 0, 4, 4, 4, A16, 3, A16, 4, A16, 4), SHAPE),      # NT: lda >= K
+    ((2, 0, 8, 4, 4, A16, 4, A16, 4, A16, 4), SHAPE),      # TN: lda >= M
+    ((1, 0, 4, 8, 4, A16, 4, A16, 4, A16, 8), SHAPE),      # NN: ldb >= N
+    ((0, 0, 4, 4, 4, A16, 4, A16, 4, A16, 3), SHAPE),      # ldc >= N
+    ((0, 0, 4, 4, 4, A16 + 1, 4, A16, 4, A16, 4), ALIGN),
+    ((0, 0, 0, 4, 4, 0, 4, 0, 4, 0, 4), OK),
+])
+def test_dense_rejects_invalid_arguments(lib, args, code):
+    assert lib.gemm_dense(*args, None) == code
+
+
+def test_describe_names_the_dispatch(lib):
+    assert qg.describe_int4(1, 4096, 4096).startswith("gemv_int4_kernel<1>")
+    assert qg.describe_int4(8, 4096, 4096).startswith("fused_int4_kernel<8,1>")
+    assert qg.describe_int4(16, 28672, 4096).startswith("fused_int4_kernel<16,4>")
+    assert qg.describe_int4(17, 5120, 25600).startswith("mfma_int4_kernel")
+    assert qg.describe_int4(1, 4096, 4096, "mfma").startswith("mfma_int4_kernel")
+    assert qg.describe_int4(0, 64, 128) == "none"
+    assert qg.describe_int4(3, 64, 0) == "zero16_kernel"
+    with pytest.raises(qg.QGemmError):
+        qg.describe_int4(2, 64, 128, "gemv")

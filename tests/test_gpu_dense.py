@@ -1,0 +1,127 @@
+"""GPU parity of the dense bf16/fp16 NT/NN/TN products against the CPU oracle.
+
+Bar: zero rejections by the oracle's rule (|err| <= 2e-3 + 2e-3 |ref| or a
+faithful rounding in the output dtype), no non-finite values, and rms_rel at
+the rounding floor of the dtype (2.5e-3 bf16, 5e-4 fp16).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from qgemm_inputs import dense_cases, dense_inputs, f32_to_bf16_bits, f64_to_fp16_bits
+
+from gpu_helpers import dev, host_u16, sample_indices, say
+
+pytestmark = pytest.mark.gpu
+
+RMS_GATE = {"bf16": 2.5e-3, "fp16": 5e-4}
+
+
+def tdtype(dtype):
+    import torch
+
+    return torch.bfloat16 if dtype == "bf16" else torch.float16
+
+
+def run(qg, layout, a, b, out=None):
+    import torch
+
+    c = qg.gemm_dense(layout, a, b, out=out)
+    torch.cuda.synchronize()
+    return c
+
+
+def assert_accepted(c_bits, ref, dtype, what):
+    rep = oracle.compare(c_bits, ref, dtype)
+    say(what, rep)
+    assert rep["nonfinite"] == 0, (what, rep)
+    assert rep["rejected"] == 0, (what, rep)
+    if ref.size >= 64 and np.sqrt(np.mean(ref * ref)) > 0:
+        assert rep["rms_rel"] < RMS_GATE[dtype], (what, rep)
+
+
+SHAPES = [(1, 1, 1), (3, 5, 7), (16, 16, 16), (128, 128, 64), (130, 264, 200), (256, 136, 520),
+          (64, 16, 1024), (16, 1024, 64), (1000, 8, 16)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_shapes_match_oracle(gpu_lib, layout, dtype):
+    for i, (M, N, K) in enumerate(SHAPES):
+        say("dense", layout, dtype, M, N, K)
+        d = dense_inputs(layout, dtype, M, N, K, seed=500 + i)
+        a, b = dev(d["a"], tdtype(dtype)), dev(d["b"], tdtype(dtype))
+        c = host_u16(run(gpu_lib, layout, a, b))
+        ref = oracle.dense(layout, dtype, d["a"], d["b"], M, N, K)
+        assert_accepted(c, ref, dtype, (layout, dtype, M, N, K))
+
+
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_identity_is_exact(gpu_lib, layout):
+    M = N = K = 136
+    d = dense_inputs(layout, "bf16", M, N, K, seed=601, std=1.0)
+    eye = f32_to_bf16_bits(np.eye(K))
+    a = dev(d["a"], tdtype("bf16"))
+    c = host_u16(run(gpu_lib, layout, a, dev(eye, tdtype("bf16"))))
+    expect = d["a"] if layout != "TN" else d["a"].T
+    assert np.array_equal(c, expect)
+
+
+def test_fp16_subnormal_inputs(gpu_lib):
+    # every A value subnormal; B = 2^k powers keep the products exact
+    M, N, K = 32, 32, 64
+    rng = np.random.default_rng(7)
+    a = rng.integers(1, 0x400, size=(M, K)).astype(np.uint16)          # subnormal bit patterns
+    b = f64_to_fp16_bits(2.0 ** rng.integers(0, 8, size=(N, K)))
+    c = host_u16(run(gpu_lib, "NT", dev(a, tdtype("fp16")), dev(b, tdtype("fp16"))))
+    ref = oracle.dense("NT", "fp16", a, b, M, N, K)
+    assert_accepted(c, ref, "fp16", "subnormal")
+    assert np.count_nonzero(c) > 0.9 * c.size
+
+
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_unaligned_and_strided_operands(gpu_lib, layout):
+    import torch
+
+    M, N, K = 37, 45, 53
+    d = dense_inputs(layout, "bf16", M, N, K, seed=602)
+    pa = torch.zeros((d["a"].shape[0], d["a"].shape[1] + 3), dtype=torch.bfloat16, device="cuda")
+    pb = torch.zeros((d["b"].shape[0], d["b"].shape[1] + 5), dtype=torch.bfloat16, device="cuda")
+    pa[:, 1:1 + d["a"].shape[1]] = dev(d["a"], torch.bfloat16)
+    pb[:, 2:2 + d["b"].shape[1]] = dev(d["b"], torch.bfloat16)
+    big = torch.full((M + 2, N + 6), 3.0, dtype=torch.bfloat16, device="cuda")
+    out = big[1:M + 1, 3:3 + N]
+    run(gpu_lib, layout, pa[:, 1:1 + d["a"].shape[1]], pb[:, 2:2 + d["b"].shape[1]], out=out)
+    ref = oracle.dense(layout, "bf16", d["a"], d["b"], M, N, K)
+    assert_accepted(host_u16(out), ref, "bf16", ("strided", layout))
+    g = big.float().cpu().numpy()
+    g[1:M + 1, 3:3 + N] = 3.0
+    assert np.all(g == 3.0)
+
+
+def test_k_zero_writes_zeros(gpu_lib):
+    import torch
+
+    a = torch.zeros((4, 0), dtype=torch.float16, device="cuda")
+    b = torch.zeros((8, 0), dtype=torch.float16, device="cuda")
+    out = torch.full((4, 8), 1.0, dtype=torch.float16, device="cuda")
+    run(gpu_lib, "NT", a, b, out=out)
+    assert torch.all(out == 0)
+
+
+# ----------------------------------------------------------------------------
+# the training trio at full size (t = 1024 and 4096), sampled outputs
+# ----------------------------------------------------------------------------
+FULL = [c for c in dense_cases(3) if c["t"] in (1024, 4096)]
+
+
+@pytest.mark.parametrize("case", FULL, ids=["%s-%s-%s-t%d-w%dx%d" % (c["role"], c["layout"], c["dtype"], c["t"], *c["w"]) for c in FULL])
+def test_training_products_sampled(gpu_lib, case):
+    layout, dtype, M, N, K = case["layout"], case["dtype"], case["M"], case["N"], case["K"]
+    say("trio", case)
+    d = dense_inputs(layout, dtype, M, N, K, seed=case["seed"])
+    c = host_u16(run(gpu_lib, layout, dev(d["a"], tdtype(dtype)), dev(d["b"], tdtype(dtype))))
+    rows = sample_indices(M, 48, case["seed"])
+    cols = sample_indices(N, 48, case["seed"] + 1)
+    ref = oracle.dense_at(layout, dtype, d["a"], d["b"], rows, cols)
+    assert_accepted(c[np.ix_(rows, cols)], ref, dtype, case["role"])

@@ -1,0 +1,190 @@
+"""GPU parity of the int4 GPTQ paths against the CPU oracle (through the C ABI).
+
+Bar: dequantised weights bit-exact; products accepted element by element by
+the oracle's rule (|err| <= 2e-3 + 2e-3 |ref| or a faithful bf16 rounding),
+with zero rejections, no non-finite values and rms_rel at the bf16 rounding
+floor.  One-hot rows and blocked sums are exact and compared bitwise.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from qgemm_inputs import f32_to_bf16_bits, int4_cases, int4_inputs
+
+from gpu_helpers import dev, host_u16, host_u32, sample_indices, say, upload_int4
+
+pytestmark = pytest.mark.gpu
+
+RMS_GATE = 2.5e-3
+
+
+def run(qg, t, path="auto", out=None):
+    import torch
+
+    y = qg.qgemm_int4(t["x"], t["qweight"], t["scales"], t["qzeros"], out=out, path=path)
+    torch.cuda.synchronize()
+    return y
+
+
+def assert_accepted(y_bits, ref, what):
+    rep = oracle.compare(y_bits, ref, "bf16")
+    say(what, rep)
+    assert rep["nonfinite"] == 0, (what, rep)
+    assert rep["rejected"] == 0, (what, rep)
+    if np.sqrt(np.mean(ref * ref)) > 0.05:
+        assert rep["rms_rel"] < RMS_GATE, (what, rep)
+
+
+# ----------------------------------------------------------------------------
+# dequant: bit-exact
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("k,n", [(128, 8), (1152, 776), (4096, 4096), (896, 4864)])
+def test_dequant_bit_exact(gpu_lib, k, n):
+    say("dequant", k, n)
+    d = int4_inputs(1, k, n, seed=100 + k + n)
+    t = upload_int4(d)
+    w = gpu_lib.qgemm_int4_dequant(t["qweight"], t["scales"], t["qzeros"])
+    ref = oracle.dequant(d["qweight"], d["scales"], d["qzeros"], k, n)
+    assert np.array_equal(host_u32(w), ref.view(np.uint32))
+
+
+# ----------------------------------------------------------------------------
+# every path on shapes the oracle finishes quickly: several tiles + ragged tails
+# ----------------------------------------------------------------------------
+SMALL_SHAPES = [(128, 8), (1152, 776), (2048, 1040), (128, 12296), (256, 24584)]
+PATH_MS = {
+    "gemv": [1],
+    "fused": [1, 2, 3, 4, 5, 7, 8, 9, 12, 15, 16],
+    "mfma": [1, 16, 17, 33, 130, 257],
+    "auto": [1, 6, 16, 17, 200],
+}
+
+
+@pytest.mark.parametrize("k,n", SMALL_SHAPES)
+@pytest.mark.parametrize("path", ["gemv", "fused", "mfma", "auto"])
+def test_paths_match_oracle(gpu_lib, path, k, n):
+    for m in PATH_MS[path]:
+        if m * n * k > 2 ** 31:
+            continue
+        say("path", path, "m", m, "k", k, "n", n)
+        d = int4_inputs(m, k, n, seed=7 * m + k + n)
+        y = run(gpu_lib, upload_int4(d), path)
+        ref = oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], m, k, n)
+        assert_accepted(host_u16(y), ref, (path, m, k, n))
+
+
+# ----------------------------------------------------------------------------
+# exact cases, compared bitwise
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("path", ["gemv", "fused", "mfma"])
+def test_one_hot_rows_are_exact(gpu_lib, path):
+    k, n = 1152, 776
+    rows = [200] if path == "gemv" else [0, 7, 8, 127, 128, 1151]
+    d = int4_inputs(1, k, n, seed=31)
+    x = np.zeros((len(rows), k), dtype=np.uint16)
+    for r, i in enumerate(rows):
+        x[r, i] = 0x3F80
+    d["x"] = x
+    say("one-hot", path, rows)
+    y = host_u16(run(gpu_lib, upload_int4(d), path))
+    w = oracle.dequant(d["qweight"], d["scales"], d["qzeros"], k, n)
+    expect = f32_to_bf16_bits(w[rows, :])
+    assert np.array_equal(y, expect)
+
+
+@pytest.mark.parametrize("path", ["gemv", "fused", "mfma"])
+def test_blocked_sum_is_exact(gpu_lib, path):
+    # X = 1 on group 2 only and q - z = 5: Y = bf16(640 * s[2][j]) exactly
+    k, n = 640, 264
+    m = 1 if path == "gemv" else 3
+    d = int4_inputs(m, k, n, seed=32)
+    d["x"] = np.zeros((m, k), dtype=np.uint16)
+    d["x"][:, 256:384] = 0x3F80
+    d["qweight"] = np.full((k // 8, n), 0x77777777, dtype=np.uint32)
+    d["qzeros"] = np.full((k // 128, n // 8), 0x22222222, dtype=np.uint32)
+    say("blocked", path)
+    y = host_u16(run(gpu_lib, upload_int4(d), path))
+    s2 = oracle.fp16_value(d["scales"][2])
+    assert np.array_equal(y, np.repeat(f32_to_bf16_bits(640.0 * s2)[None, :], m, axis=0))
+
+
+@pytest.mark.parametrize("path", ["gemv", "fused", "mfma"])
+def test_codes_equal_zeros_give_zero(gpu_lib, path):
+    # w = 0 everywhere.  The kernels subtract the zero point through the group sum
+    # of the activations, so the result is zero up to fp32 rounding of that
+    # cancellation (far below the acceptance bound), not bitwise.
+    k, n = 1024, 136
+    m = 1 if path == "gemv" else 5
+    d = int4_inputs(m, k, n, seed=33)
+    z = oracle.unpack_qzeros(d["qzeros"], k // 128, n)
+    zrow = z[np.arange(k // 8) // 16, :].astype(np.uint32)
+    d["qweight"] = (zrow * np.uint32(0x11111111)).astype(np.uint32)
+    assert np.all(oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], m, k, n) == 0)
+    say("q==z", path)
+    y = oracle.bf16_value(host_u16(run(gpu_lib, upload_int4(d), path)))
+    assert np.max(np.abs(y)) < 1e-4
+
+
+def test_strided_x_and_y_with_guard_bands(gpu_lib):
+    import torch
+
+    m, k, n = 5, 1024, 520
+    d = int4_inputs(m, k, n, seed=34)
+    t = upload_int4(d)
+    xs = torch.zeros((m, k + 64), dtype=torch.bfloat16, device="cuda")
+    xs[:, :k] = t["x"]
+    t["x"] = xs[:, :k]
+    for path in ["fused", "mfma"]:
+        big = torch.full((m + 2, n + 24), -777.0, dtype=torch.bfloat16, device="cuda")
+        out = big[1:m + 1, 8:8 + n]
+        say("strided", path)
+        run(gpu_lib, t, path, out=out)
+        ref = oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], m, k, n)
+        assert_accepted(host_u16(out), ref, ("strided", path))
+        b = big.float().cpu().numpy()
+        b[1:m + 1, 8:8 + n] = -777.0
+        assert np.all(b == -777.0), "write outside the output view"
+
+
+def test_k_zero_writes_zeros_and_m_zero_is_noop(gpu_lib):
+    import torch
+
+    t = {"x": torch.zeros((3, 0), dtype=torch.bfloat16, device="cuda"),
+         "qweight": torch.zeros((0, 64), dtype=torch.int32, device="cuda"),
+         "scales": torch.zeros((0, 64), dtype=torch.float16, device="cuda"),
+         "qzeros": torch.zeros((0, 8), dtype=torch.int32, device="cuda")}
+    out = torch.full((3, 64), 5.0, dtype=torch.bfloat16, device="cuda")
+    run(gpu_lib, t, out=out)
+    assert torch.all(out == 0)
+    e = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    t0 = dict(t, x=torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda"))
+    run(gpu_lib, t0, out=e)
+
+
+def test_deterministic(gpu_lib):
+    m, k, n = 8, 2048, 1040
+    d = int4_inputs(m, k, n, seed=35)
+    t = upload_int4(d)
+    for path in ["fused", "mfma"]:
+        a = host_u16(run(gpu_lib, t, path))
+        b = host_u16(run(gpu_lib, t, path))
+        assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------------------
+# full workload sizes, the launch configuration the benchmark times (auto path),
+# checked on sampled outputs the oracle computes one by one
+# ----------------------------------------------------------------------------
+FULL = [(c, case) for c in (0, 1, 2, 4) for case in int4_cases(c)]
+
+
+@pytest.mark.parametrize("cfg,case", FULL, ids=["c%d-m%d-k%d-n%d" % (c, x[1], x[2], x[3]) for c, x in FULL])
+def test_full_size_sampled(gpu_lib, cfg, case):
+    _, m, k, n, seed = case
+    say("full", cfg, m, k, n)
+    d = int4_inputs(m, k, n, seed=seed)
+    y = host_u16(run(gpu_lib, upload_int4(d)))
+    rows = sample_indices(m, 24, seed)
+    cols = sample_indices(n, 160, seed + 1)
+    ref = oracle.qgemm_int4_at(d["x"], d["qweight"], d["scales"], d["qzeros"], k, n, rows, cols)
+    assert_accepted(y[np.ix_(rows, cols)], ref, ("full", cfg, m, k, n))
