@@ -93,8 +93,29 @@ def copies_for(bytes_per_copy, regime):
     return max(2, -(-2 * LLC_BYTES // bytes_per_copy))
 
 
-def time_us(torch, fn, iters):
-    """Average microseconds per call of fn() over iters back-to-back calls on the stream."""
+def time_us(torch, fn, iters, graph=True):
+    """Average microseconds per call of fn() over iters back-to-back calls.
+
+    With graph=True the iters calls are captured once into a HIP graph on the
+    launch stream and the timed region is one replay of it, so host launch cost
+    (Python, ctypes) is not on the clock; HIP events bracket the replay on the
+    same stream.  graph=False times eager launches from Python.
+    """
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(iters):
+                fn()
+        g.replay()                       # warm replay
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        g.replay()
+        e1.record(s)
+        e1.synchronize()
+        del g
+        return e0.elapsed_time(e1) * 1e3 / iters
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
@@ -103,6 +124,18 @@ def time_us(torch, fn, iters):
     e1.record(s)
     e1.synchronize()
     return e0.elapsed_time(e1) * 1e3 / iters
+
+
+def copy_peak_gbps(torch, nbytes=2 << 30):
+    """Measured device copy bandwidth (read + write bytes / time), torch's copy kernel."""
+    a = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    us = time_us(torch, lambda: b.copy_(a), 10, graph=False)
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / us / 1e3
 
 
 def cpu_baseline(cases, seconds):
@@ -156,8 +189,18 @@ def main():
     per_case = []
     for c in cases:
         us = time_us(torch, c.launch, args.steps)
+        eager = time_us(torch, c.launch, args.steps, graph=False)
         per_case.append({"m": c.m, "k": c.k, "n": c.n, "kernel": c.kernel, "us": round(us, 3),
-                         "gbps": round(c.bytes / us / 1e3, 1), "bytes": c.bytes})
+                         "gbps": round(c.bytes / us / 1e3, 1), "bytes": c.bytes,
+                         "eager_us": round(eager, 3)})
+    # floor: the smallest kernel the same entry point launches (k = 0 -> a zero fill of 1 x 8)
+    fx = torch.empty((1, 0), dtype=torch.bfloat16, device="cuda")
+    fw = torch.empty((0, 8), dtype=torch.int32, device="cuda")
+    fs = torch.empty((0, 8), dtype=torch.float16, device="cuda")
+    fz = torch.empty((0, 1), dtype=torch.int32, device="cuda")
+    fy = torch.empty((1, 8), dtype=torch.bfloat16, device="cuda")
+    floor_us = time_us(torch, lambda: qg.qgemm_int4(fx, fw, fs, fz, out=fy), args.steps)
+    copy_gbps = copy_peak_gbps(torch)
 
     def step():
         for c in cases:
@@ -197,8 +240,12 @@ def main():
                    "regime": args.regime, "calls_per_step": len(cases),
                    "parallelism": "none (1 GPU)"},
         "cases": per_case,
+        "timing": "HIP graph replay of back-to-back launches, HIP events on the launch stream",
+        "floor_us": round(floor_us, 3),
+        "copy_gbps": round(copy_gbps, 1),
         "roofline": roofline,
     }
+    roofline["frac_of_copy"] = round(achieved / copy_gbps, 4)
     if args.suite:
         out["suite_file"] = args.suite
         run_suite(qg, torch, args, args.suite)

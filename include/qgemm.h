@@ -89,14 +89,24 @@ int32_t qg_last_hip_error(void);
  *   y        bf16 [m][ldy] output, ldy >= n, ldy % 4 == 0, 8-byte aligned.
  *   m >= 0 tokens, n >= 0 output columns (n % 8 == 0), k >= 0 input rows
  *   (k % 128 == 0), group_size must be 128.
+ *   workspace, workspace_bytes
+ *            optional device scratch (16-byte aligned) that lets the m <= 16
+ *            paths split k over several workgroups; qgemm_int4_workspace_size
+ *            gives the size that enables the split.  Its first 64 KiB
+ *            hold the split's counters: they must be zero before the first use
+ *            with this library, and each call leaves them zero again (the rest
+ *            holds per-call partial sums).  NULL or a smaller
+ *            size is valid: the call then runs without the split (same
+ *            accuracy contract, fewer workgroups, summation order may differ).
+ *            Calls that share a workspace must not run concurrently.
  *
  * The path is chosen from m (see QG_PATH_AUTO).  x and y must not overlap the
- * weights.  Errors: QG_ERR_NULL, QG_ERR_SHAPE, QG_ERR_ALIGN, QG_ERR_UNSUPPORTED,
- * QG_ERR_HIP.
+ * weights or the workspace.  Errors: QG_ERR_NULL, QG_ERR_SHAPE, QG_ERR_ALIGN,
+ * QG_ERR_UNSUPPORTED, QG_ERR_HIP.
  */
 int32_t qgemm_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
                    const uint32_t* qzeros, void* y, int64_t ldy, int64_t m, int64_t n, int64_t k,
-                   int32_t group_size, void* stream);
+                   int32_t group_size, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * qgemm_int4_path -- qgemm_int4 with the kernel path forced (QG_PATH_* code),
@@ -106,15 +116,25 @@ int32_t qgemm_int4(const void* x, int64_t ldx, const uint32_t* qweight, const ui
 int32_t qgemm_int4_path(const void* x, int64_t ldx, const uint32_t* qweight,
                         const uint16_t* scales, const uint32_t* qzeros, void* y, int64_t ldy,
                         int64_t m, int64_t n, int64_t k, int32_t group_size, int32_t path,
-                        void* stream);
+                        void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * qgemm_int4_workspace_size -- bytes of workspace with which qgemm_int4_path
+ * (m, n, k, path) runs its preferred k split; 0 when it uses none.  Negative
+ * sizes or n % 8, k % 128 != 0 return -QG_ERR_SHAPE; an invalid path returns
+ * -QG_ERR_UNSUPPORTED.  Launches nothing.
+ */
+int64_t qgemm_int4_workspace_size(int64_t m, int64_t n, int64_t k, int32_t path);
 
 /*
  * qgemm_int4_describe -- names the kernel and launch shape that qgemm_int4_path
- * would use for (m, n, k, path), e.g. "fused_int4_kernel<8,1> grid=256
- * block=1024 lds=32768", into buf (NUL-terminated, truncated to len bytes).
- * Launches nothing.  Errors: QG_ERR_NULL (buf), QG_ERR_SHAPE, QG_ERR_UNSUPPORTED.
+ * would use for (m, n, k, path) with a workspace of workspace_bytes, e.g.
+ * "skinny_int4_kernel<8,mfma,1> grid=512 block=256 lds=40960 ksplit=8 groups=4",
+ * into buf (NUL-terminated, truncated to len bytes).  Launches nothing.
+ * Errors: QG_ERR_NULL (buf), QG_ERR_SHAPE, QG_ERR_UNSUPPORTED.
  */
-int32_t qgemm_int4_describe(int64_t m, int64_t n, int64_t k, int32_t path, char* buf, int64_t len);
+int32_t qgemm_int4_describe(int64_t m, int64_t n, int64_t k, int32_t path, int64_t workspace_bytes,
+                            char* buf, int64_t len);
 
 /*
  * qgemm_int4_dequant -- the dequantised weights themselves, for a bit-exact

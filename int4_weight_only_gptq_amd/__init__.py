@@ -12,6 +12,7 @@ import ctypes
 import os
 
 __all__ = ["load", "lib_path", "QGemmError", "qgemm_int4", "qgemm_int4_dequant", "gemm_dense", "describe_int4",
+           "workspace_size",
            "abi_version", "PATHS", "LAYOUTS"]
 
 _LIB_NAME = "libqgemm_gfx950.so"
@@ -55,11 +56,13 @@ def load():
     lib.qg_last_hip_error.argtypes = []
     int4_args = [vp, i64, vp, vp, vp, vp, i64, i64, i64, i64, i32]
     lib.qgemm_int4.restype = i32
-    lib.qgemm_int4.argtypes = int4_args + [vp]
+    lib.qgemm_int4.argtypes = int4_args + [vp, i64, vp]
     lib.qgemm_int4_path.restype = i32
-    lib.qgemm_int4_path.argtypes = int4_args + [i32, vp]
+    lib.qgemm_int4_path.argtypes = int4_args + [i32, vp, i64, vp]
+    lib.qgemm_int4_workspace_size.restype = i64
+    lib.qgemm_int4_workspace_size.argtypes = [i64, i64, i64, i32]
     lib.qgemm_int4_describe.restype = i32
-    lib.qgemm_int4_describe.argtypes = [i64, i64, i64, i32, ctypes.c_char_p, i64]
+    lib.qgemm_int4_describe.argtypes = [i64, i64, i64, i32, i64, ctypes.c_char_p, i64]
     lib.qgemm_int4_dequant.restype = i32
     lib.qgemm_int4_dequant.argtypes = [vp, vp, vp, vp, i64, i64, i32, vp]
     lib.gemm_dense.restype = i32
@@ -91,12 +94,39 @@ def _check(status, where):
         raise QGemmError(status, where)
 
 
+_workspaces = {}
+
+
+def workspace_size(m: int, n: int, k: int, path: str = "auto") -> int:
+    """Bytes of workspace that let the m <= 16 paths split k (0 if none is used)."""
+    size = load().qgemm_int4_workspace_size(m, n, k, PATHS[path])
+    if size < 0:
+        raise QGemmError(-size, "qgemm_int4_workspace_size")
+    return size
+
+
+def _workspace(device, stream_handle, nbytes):
+    """A zero-filled scratch tensor per (device, stream), grown on demand."""
+    import torch
+
+    if nbytes <= 0:
+        return None
+    key = (device.index, stream_handle)
+    t = _workspaces.get(key)
+    if t is None or t.numel() < nbytes:
+        t = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = t
+    return t
+
+
 def qgemm_int4(x, qweight, scales, qzeros, out=None, group_size: int = 128, path: str = "auto",
-               stream=None):
+               workspace=None, stream=None):
     """Y[m][n] (bf16) = X[m][k] (bf16) . dequant(W)^T, W given in GPTQ int4 storage.
 
     qweight int32/uint32 [k/8][n]; scales fp16 [k/128][n]; qzeros int32/uint32
     [k/128][n/8].  ``path`` forces a kernel ("gemv", "fused", "mfma") or "auto".
+    ``workspace``: None = a cached zero-filled buffer of the size the library
+    asks for; False = no workspace (no k split); or a caller-owned uint8 tensor.
     """
     import torch
 
@@ -107,18 +137,28 @@ def qgemm_int4(x, qweight, scales, qzeros, out=None, group_size: int = 128, path
         raise TypeError("x must be bfloat16")
     if out is None:
         out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    sh = _stream(x, stream)
+    if workspace is None:
+        workspace = _workspace(x.device, sh, workspace_size(m, n, k, path))
+    if workspace is None or workspace is False:
+        wptr, wbytes = None, 0
+    else:
+        wptr, wbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     st = lib.qgemm_int4_path(x.data_ptr(), _ld(x), qweight.data_ptr(), scales.data_ptr(),
                              qzeros.data_ptr(), out.data_ptr(), _ld(out), m, n, k, group_size,
-                             PATHS[path], _stream(x, stream))
+                             PATHS[path], wptr, wbytes, sh)
     _check(st, "qgemm_int4")
     return out
 
 
-def describe_int4(m: int, n: int, k: int, path: str = "auto") -> str:
+def describe_int4(m: int, n: int, k: int, path: str = "auto", workspace_bytes=None) -> str:
     """Kernel and launch shape qgemm_int4 uses for (m, n, k, path); launches nothing."""
     lib = load()
+    if workspace_bytes is None:
+        workspace_bytes = workspace_size(m, n, k, path)
     buf = ctypes.create_string_buffer(256)
-    _check(lib.qgemm_int4_describe(m, n, k, PATHS[path], buf, 256), "qgemm_int4_describe")
+    _check(lib.qgemm_int4_describe(m, n, k, PATHS[path], workspace_bytes, buf, 256),
+           "qgemm_int4_describe")
     return buf.value.decode()
 
 

@@ -40,22 +40,35 @@ int32_t check_int4(const void* x, int64_t ldx, const uint32_t* qweight, const ui
   return QG_OK;
 }
 
-int32_t run_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
-                 const uint32_t* qzeros, void* y, int64_t ldy, int64_t m, int64_t n, int64_t k,
-                 int32_t group_size, int32_t path, void* stream) {
-  int32_t st = check_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size);
-  if (st != QG_OK) return st;
+int32_t resolve_path(int64_t m, int32_t path) {
+  if (path == QG_PATH_AUTO) return m == 1 ? QG_PATH_GEMV : (m <= 16 ? QG_PATH_FUSED : QG_PATH_MFMA);
+  return path;
+}
+
+int32_t check_path(int64_t m, int32_t path) {
   if (path < QG_PATH_AUTO || path > QG_PATH_MFMA) return QG_ERR_UNSUPPORTED;
   if (path == QG_PATH_GEMV && m > 1) return QG_ERR_UNSUPPORTED;
   if (path == QG_PATH_FUSED && m > 16) return QG_ERR_UNSUPPORTED;
+  return QG_OK;
+}
+
+int32_t run_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
+                 const uint32_t* qzeros, void* y, int64_t ldy, int64_t m, int64_t n, int64_t k,
+                 int32_t group_size, int32_t path, void* ws, int64_t ws_bytes, void* stream) {
+  int32_t st = check_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size);
+  if (st != QG_OK) return st;
+  st = check_path(m, path);
+  if (st != QG_OK) return st;
+  if (ws_bytes < 0) return QG_ERR_SHAPE;
+  if (ws != nullptr && !aligned(ws, 16)) return QG_ERR_ALIGN;
   if (m == 0 || n == 0) return QG_OK;
   hipStream_t s = (hipStream_t)stream;
   if (k == 0) return hip_status(qg::launch_zero16((uint16_t*)y, m, n, ldy, s));
   const qg::Int4Args a{(const uint16_t*)x, ldx, qweight, scales, qzeros, (uint16_t*)y, ldy, m, n, k};
-  if (path == QG_PATH_AUTO) path = m == 1 ? QG_PATH_GEMV : (m <= 16 ? QG_PATH_FUSED : QG_PATH_MFMA);
-  switch (path) {
-    case QG_PATH_GEMV: return hip_status(qg::launch_gemv_int4(a, s));
-    case QG_PATH_FUSED: return hip_status(qg::launch_fused_int4(a, s));
+  if (ws == nullptr) ws_bytes = 0;
+  switch (resolve_path(m, path)) {
+    case QG_PATH_GEMV: return hip_status(qg::launch_gemv_int4(a, ws, ws_bytes, s));
+    case QG_PATH_FUSED: return hip_status(qg::launch_fused_int4(a, ws, ws_bytes, s));
     default: return hip_status(qg::launch_mfma_int4(a, s));
   }
 }
@@ -84,23 +97,32 @@ int32_t qg_last_hip_error(void) { return g_last_hip_error; }
 
 int32_t qgemm_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
                    const uint32_t* qzeros, void* y, int64_t ldy, int64_t m, int64_t n, int64_t k,
-                   int32_t group_size, void* stream) {
-  return run_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size, QG_PATH_AUTO, stream);
+                   int32_t group_size, void* workspace, int64_t workspace_bytes, void* stream) {
+  return run_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size, QG_PATH_AUTO,
+                  workspace, workspace_bytes, stream);
 }
 
 int32_t qgemm_int4_path(const void* x, int64_t ldx, const uint32_t* qweight,
                         const uint16_t* scales, const uint32_t* qzeros, void* y, int64_t ldy,
                         int64_t m, int64_t n, int64_t k, int32_t group_size, int32_t path,
-                        void* stream) {
-  return run_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size, path, stream);
+                        void* workspace, int64_t workspace_bytes, void* stream) {
+  return run_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size, path, workspace,
+                  workspace_bytes, stream);
 }
 
-int32_t qgemm_int4_describe(int64_t m, int64_t n, int64_t k, int32_t path, char* buf, int64_t len) {
+int64_t qgemm_int4_workspace_size(int64_t m, int64_t n, int64_t k, int32_t path) {
+  if (m < 0 || n < 0 || k < 0 || k % 128 != 0 || n % 8 != 0) return -QG_ERR_SHAPE;
+  if (n > (int64_t)1 << 30 || k > (int64_t)1 << 30) return -QG_ERR_SHAPE;
+  if (check_path(m, path) != QG_OK) return -QG_ERR_UNSUPPORTED;
+  return qg::workspace_int4(m, n, k, resolve_path(m, path));
+}
+
+int32_t qgemm_int4_describe(int64_t m, int64_t n, int64_t k, int32_t path, int64_t workspace_bytes,
+                            char* buf, int64_t len) {
   if (buf == nullptr || len <= 0) return QG_ERR_NULL;
   buf[0] = 0;
   if (m < 0 || n < 0 || k < 0 || k % 128 != 0 || n % 8 != 0) return QG_ERR_SHAPE;
-  if (path < QG_PATH_AUTO || path > QG_PATH_MFMA) return QG_ERR_UNSUPPORTED;
-  if ((path == QG_PATH_GEMV && m > 1) || (path == QG_PATH_FUSED && m > 16)) return QG_ERR_UNSUPPORTED;
+  if (check_path(m, path) != QG_OK) return QG_ERR_UNSUPPORTED;
   if (m == 0 || n == 0) {
     snprintf(buf, (size_t)len, "none");
     return QG_OK;
@@ -109,8 +131,8 @@ int32_t qgemm_int4_describe(int64_t m, int64_t n, int64_t k, int32_t path, char*
     snprintf(buf, (size_t)len, "zero16_kernel");
     return QG_OK;
   }
-  if (path == QG_PATH_AUTO) path = m == 1 ? QG_PATH_GEMV : (m <= 16 ? QG_PATH_FUSED : QG_PATH_MFMA);
-  qg::describe_int4(m, n, k, path, buf, (size_t)len);
+  qg::describe_int4(m, n, k, resolve_path(m, path), workspace_bytes < 0 ? 0 : workspace_bytes, buf,
+                    (size_t)len);
   return QG_OK;
 }
 

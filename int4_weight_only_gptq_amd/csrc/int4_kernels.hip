@@ -96,190 +96,275 @@ __device__ __forceinline__ void load_group_meta(const uint16_t* __restrict__ sca
   for (int c = 0; c < CPL; ++c) bz[c] = (float)(128u + ((zw >> (4 * c)) & 15u));
 }
 
+// Raw group metadata of CPL consecutive columns: their fp16 scales and the
+// word holding their zero nibbles.  Loaded in the load phase and decoded only
+// where it is used, so the loads do not force an early wait on everything in
+// flight.
+template <int CPL>
+struct Meta {
+  uint32_t s[CPL == 4 ? 2 : 1];
+  uint32_t z;
+};
+
+template <int CPL>
+__device__ __forceinline__ Meta<CPL> load_meta(const uint16_t* __restrict__ scales,
+                                               const uint32_t* __restrict__ qzeros, int64_t n,
+                                               int64_t g, int64_t col) {
+  Meta<CPL> r;
+  const uint16_t* sp = scales + g * n + col;
+  if constexpr (CPL == 4) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(sp);
+    r.s[0] = v[0];
+    r.s[1] = v[1];
+  } else if constexpr (CPL == 2) {
+    r.s[0] = *reinterpret_cast<const uint32_t*>(sp);
+  } else {
+    r.s[0] = *sp;
+  }
+  r.z = qzeros[g * (n >> 3) + (col >> 3)];
+  return r;
+}
+
+// zshift = 4 * (col % 8): the nibble of the first of the CPL columns.
+template <int CPL>
+__device__ __forceinline__ void decode_meta(const Meta<CPL>& mt, int zshift, float (&s)[CPL],
+                                            float (&bz)[CPL]) {
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    s[c] = half_bits_to_float((mt.s[c >> 1] >> (16 * (c & 1))) & 0xFFFFu);
+    bz[c] = (float)(128u + ((mt.z >> (zshift + 4 * c)) & 15u));
+  }
+}
+
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
                                          c, false);
 }
 
 // ---------------------------------------------------------------------------
-// m = 1 GEMV (VALU).  A workgroup owns 16*CPL output columns; its waves split
-// the k groups.  Lane (cl = lane % 16, ks = lane / 16) reads CPL consecutive
-// words of word-row 4s + ks (s = 0..3 within a group), so the 16 lanes of a row
-// read 64*CPL contiguous bytes.  Products use v_dot2_f32_bf16 on the pairs of
-// (128 + q) and the activations; the per-group offset correction and scale are
-// applied per lane.  The four 16-lane rows are then summed with the gfx950
-// row-swap permutes and the waves through LDS.
+// Skinny kernel for m <= 16 tokens (M known at compile time).
+//
+// A workgroup of W waves owns one strip of 16 * CPL output columns and a range
+// of k groups (its k-slice; the whole of k unless the k split is on).  Lane
+// (cl = lane % 16, ks = lane / 16) reads the CPL consecutive words of columns
+// CPL * cl .. CPL * cl + CPL - 1 of word-row 4s + ks (k-step s of a group), so a
+// wave-load covers 4 word-rows x 64 * CPL contiguous bytes.  Wave w takes
+// groups w, w + W, w + 2W, ... of the slice and software-pipelines them: the
+// loads of its next group are in flight while it computes the current one.
+//
+// DOT = true (m = 1, the GEMV): per lane v_dot2_f32_bf16 on (128 + q) pairs
+// against the activation slice staged once in LDS, per-group offset
+// correction and scale per lane, then the four 16-lane rows summed with the
+// row-swap permutes.
+// DOT = false: the 16x16x32 bf16 MFMA, operand A = activations loaded per lane
+// (token = lane % 16, zero for tokens >= M), operand B = the codes of one word
+// (8 consecutive k of one column = one lane's B slice); tile c of a lane is
+// column CPL * cl + c of the strip.  A second MFMA against a ones operand
+// gives the per-token group sums for the offset correction.
+//
+// The W wave partials [M][16 * CPL] are summed in LDS.  With ksplit > 1 the
+// workgroup partial goes to the workspace and the last workgroup of the strip
+// to arrive (counter) adds the ksplit partials in k order and writes Y.
+// Blocks are numbered so that consecutive strips, and all k-slices of a
+// strip, land on the same XCD (block b runs on XCD b % 8).
 // ---------------------------------------------------------------------------
-template <int CPL>
-__global__ __launch_bounds__(1024) void gemv_int4_kernel(const uint16_t* __restrict__ x,
-                                                         const uint32_t* __restrict__ qweight,
-                                                         const uint16_t* __restrict__ scales,
-                                                         const uint32_t* __restrict__ qzeros,
-                                                         uint16_t* __restrict__ y, int n, int k) {
-  constexpr int NB = 16 * CPL;
-  __shared__ float plane[16][NB];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-  const int cl = lane & 15, ks = lane >> 4;
-  const int64_t col = (int64_t)blockIdx.x * NB + CPL * cl;
-  const bool live = col < n;
-  const int G = k >> 7;
-  const int g0 = (wave * G) / nwaves, g1 = ((wave + 1) * G) / nwaves;
-  const uint32_t* qp = qweight + (live ? col : 0);
+constexpr int64_t kTicketBytes = 64 << 10;   // counters of up to 16384 strips
+constexpr int SK_MAX_SPLIT = 16;              // k-slices per strip at most
+constexpr int SK_MAX_WAVES = 16;
+constexpr size_t kSkinnyMaxLds = 150 << 10;    // of the 160 KiB of a gfx950 CU
 
-  float total[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) total[c] = 0.f;
+template <int M, bool DOT, int CPL>
+struct GroupRegs {
+  uint32_t w[4][CPL];                  // codes of the 4 k-steps
+  u32x4 xa[DOT ? 1 : 4];               // MFMA: the A slices of the 4 k-steps
+  Meta<CPL> meta;
+};
 
-  for (int g = g0; g < g1; ++g) {
-    u32x4 xv[4];
-    uint32_t wv[4][CPL];
+// gok: the group is in range; live: this lane's columns are in range; xrow:
+// this lane supplies activation row (token) cl.  The activation row does not
+// depend on the lane's columns.
+template <int M, bool DOT, int CPL>
+__device__ __forceinline__ void load_group(GroupRegs<M, DOT, CPL>& r, bool gok, bool live, bool xrow,
+                                           const uint32_t* __restrict__ qp,
+                                           const uint16_t* __restrict__ xp,
+                                           const uint16_t* __restrict__ scales,
+                                           const uint32_t* __restrict__ qzeros, int64_t n,
+                                           int64_t g, int64_t col, int ks) {
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  const bool ok = gok && live;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int64_t r = (int64_t)g * 16 + 4 * s + ks;
-      xv[s] = *reinterpret_cast<const u32x4*>(x + 8 * r);
-      if (live) {
-        load_words<CPL>(qp + r * n, wv[s]);
-      } else {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) wv[s][c] = 0u;
-      }
-    }
-    float sc[CPL], bz[CPL];
-    if (live) {
-      load_group_meta<CPL>(scales, qzeros, n, g, col, sc, bz);
+  for (int s = 0; s < 4; ++s) {
+    if (ok) {
+      load_words<CPL>(qp + (g * 16 + 4 * s + ks) * n, r.w[s]);
     } else {
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) { sc[c] = 0.f; bz[c] = 0.f; }
+      for (int c = 0; c < CPL; ++c) r.w[s][c] = 0u;
     }
-    float d[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) d[c] = 0.f;
-    float xs = 0.f;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const u32x4 a = x_pairs_permuted(xv[s]);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) xs = dot2_bf16(a[t], kOnesBf16x2, xs);
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const u32x4 b = codes_as_bf16_pairs(wv[s][c]);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) d[c] = dot2_bf16(b[t], a[t], d[c]);
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) total[c] += sc[c] * (d[c] - bz[c] * xs);
+    if constexpr (!DOT)
+      r.xa[s] = (gok && xrow) ? *reinterpret_cast<const u32x4*>(xp + 8 * (g * 16 + 4 * s + ks)) : zero4;
   }
-
+  if (ok) {
+    r.meta = load_meta<CPL>(scales, qzeros, n, g, col);
+  } else {
+    r.meta.z = 0u;
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) total[c] = sum_over_rows(total[c]);
-  if (ks == 0 && live) {
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) plane[wave][CPL * cl + c] = total[c];
-  }
-  __syncthreads();
-  if ((int)threadIdx.x < NB) {
-    const int64_t cc = (int64_t)blockIdx.x * NB + threadIdx.x;
-    if (cc < n) {
-      float acc = 0.f;
-      for (int w = 0; w < nwaves; ++w) acc += plane[w][threadIdx.x];
-      y[cc] = (uint16_t)f32_to_bf16_bits(acc);
-    }
+    for (int i = 0; i < (CPL == 4 ? 2 : 1); ++i) r.meta.s[i] = 0u;
   }
 }
 
-// ---------------------------------------------------------------------------
-// Fused small-M kernel, M = 1..16 tokens known at compile time.  Same column
-// ownership and word stream as the GEMV; the contraction runs on the
-// 16x16x32 bf16 MFMA: operand A = activations (row = token, rows >= M are
-// zero), operand B = the codes of one word per lane (8 consecutive k of one
-// column is exactly one lane's B slice).  Tile c of a lane holds column
-// 16*CPL*block + CPL*(lane%16) + c.  A second MFMA against a ones operand
-// gives the per-token group sums for the offset correction.  Accumulators are
-// compile-time sized VGPR arrays; the cross-wave partial plane holds M tokens.
-// ---------------------------------------------------------------------------
-template <int M, int CPL>
-__global__ __launch_bounds__(1024) void fused_int4_kernel(
+template <int M, bool DOT, int CPL>
+__global__ __launch_bounds__(1024) void skinny_int4_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
-    uint16_t* __restrict__ y, int64_t ldy, int n, int k) {
-  constexpr int NB = 16 * CPL;
-  constexpr int VMAX = M < 4 ? M : 4;   // accumulator rows that can hold a token
-  extern __shared__ float plane[];      // [nwaves][M][NB]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    uint16_t* __restrict__ y, int64_t ldy, int n, int k, int nstrips, int ksplit, int gwg,
+    int items_per_xcd, float* __restrict__ partials, uint32_t* __restrict__ tickets) {
+  static_assert(!DOT || M == 1, "the VALU variant computes one token");
+  constexpr int SW = 16 * CPL;                 // strip width in columns
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  float* plane = reinterpret_cast<float*>(smem);                 // [W][M][SW]
+  u32x4* xl = reinterpret_cast<u32x4*>(smem + (size_t)SK_MAX_WAVES * M * SW * 4);  // DOT: [k-slice chunks]
+  __shared__ int last_flag;
+
+  const int item = (blockIdx.x & 7) * items_per_xcd + (blockIdx.x >> 3);
+  const int strip = item / ksplit, kslice = item - strip * ksplit;
+  if (strip >= nstrips) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   const int cl = lane & 15, ks = lane >> 4;
-  const int64_t col = (int64_t)blockIdx.x * NB + CPL * cl;
+  const int G = k >> 7;
+  const int gbeg = kslice * gwg, gend = min(G, gbeg + gwg);
+  const int64_t col = (int64_t)strip * SW + CPL * cl;
   const bool live = col < n;
   const bool xrow = cl < M;
-  const int G = k >> 7;
-  const int g0 = (wave * G) / nwaves, g1 = ((wave + 1) * G) / nwaves;
   const uint32_t* qp = qweight + (live ? col : 0);
   const uint16_t* xp = x + (xrow ? (int64_t)cl * ldx : 0);
+  const int zshift = (int)(col & 7) * 4;
   const u32x4 ones = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+  if constexpr (DOT) {
+    // the activation row of this k-slice, in pair order, once per workgroup
+    const int chunks = (gend - gbeg) * 16;
+    for (int c = tid; c < chunks; c += blockDim.x)
+      xl[c] = x_pairs_permuted(*reinterpret_cast<const u32x4*>(x + (int64_t)gbeg * 128 + 8 * c));
+    __syncthreads();
+  }
 
   f32x4 total[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) total[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int g = g0; g < g1; ++g) {
-    u32x4 xv[4];
-    uint32_t wv[4][CPL];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int64_t r = (int64_t)g * 16 + 4 * s + ks;
-      xv[s] = xrow ? *reinterpret_cast<const u32x4*>(xp + 8 * r) : zero4;
-      if (live) {
-        load_words<CPL>(qp + r * n, wv[s]);
-      } else {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) wv[s][c] = 0u;
-      }
-    }
+  GroupRegs<M, DOT, CPL> cur, nxt;
+  int g = gbeg + wave;
+  load_group<M, DOT, CPL>(cur, g < gend, live, xrow, qp, xp, scales, qzeros, n, g, col, ks);
+  for (; g < gend; g += nw) {
+    const int gn = g + nw;
+    load_group<M, DOT, CPL>(nxt, gn < gend, live, xrow, qp, xp, scales, qzeros, n, gn, col, ks);
     float sc[CPL], bz[CPL];
-    if (live) {
-      load_group_meta<CPL>(scales, qzeros, n, g, col, sc, bz);
+    if constexpr (DOT) {
+      float d[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) d[c] = 0.f;
+      float xs = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 a = xl[(g - gbeg) * 16 + 4 * s + ks];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) xs = dot2_bf16(a[t], kOnesBf16x2, xs);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const u32x4 bq = codes_as_bf16_pairs(cur.w[s][c]);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) d[c] = dot2_bf16(bq[t], a[t], d[c]);
+        }
+      }
+      decode_meta<CPL>(cur.meta, zshift, sc, bz);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) total[c][0] += sc[c] * (d[c] - bz[c] * xs);
     } else {
+      constexpr int VMAX = M < 4 ? M : 4;
+      f32x4 acc[CPL];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) { sc[c] = 0.f; bz[c] = 0.f; }
+      for (int c = 0; c < CPL; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 xsum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 a = x_pairs_permuted(cur.xa[s]);
+        xsum = mfma16_bf16(a, ones, xsum);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[c] = mfma16_bf16(a, codes_as_bf16_pairs(cur.w[s][c]), acc[c]);
+      }
+      decode_meta<CPL>(cur.meta, zshift, sc, bz);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int v = 0; v < VMAX; ++v) total[c][v] += sc[c] * (acc[c][v] - bz[c] * xsum[v]);
     }
-    f32x4 acc[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 xsum = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const u32x4 a = x_pairs_permuted(xv[s]);
-      xsum = mfma16_bf16(a, ones, xsum);
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) acc[c] = mfma16_bf16(a, codes_as_bf16_pairs(wv[s][c]), acc[c]);
-    }
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-#pragma unroll
-      for (int v = 0; v < VMAX; ++v) total[c][v] += sc[c] * (acc[c][v] - bz[c] * xsum[v]);
-    }
+    cur = nxt;
   }
 
-  // accumulator (c, v) of this lane is token 4*ks + v, column CPL*cl + c of the block
+  // wave partials [M][SW] -> LDS plane -> sum over the waves
+  if constexpr (DOT) {
 #pragma unroll
-  for (int v = 0; v < VMAX; ++v) {
-    const int token = 4 * ks + v;
-    if (token < M && live) {
+    for (int c = 0; c < CPL; ++c) total[c][0] = sum_over_rows(total[c][0]);
+    if (ks == 0) {
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) plane[(wave * M + token) * NB + CPL * cl + c] = total[c][v];
+      for (int c = 0; c < CPL; ++c) plane[wave * SW + CPL * cl + c] = total[c][0];
+    }
+  } else {
+    constexpr int VMAX = M < 4 ? M : 4;
+#pragma unroll
+    for (int v = 0; v < VMAX; ++v) {
+      const int token = 4 * ks + v;
+      if (token < M) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) plane[(wave * M + token) * SW + CPL * cl + c] = total[c][v];
+      }
     }
   }
   __syncthreads();
-  for (int o = threadIdx.x; o < M * NB; o += blockDim.x) {
-    const int token = o / NB, cc = o - token * NB;
-    const int64_t cg = (int64_t)blockIdx.x * NB + cc;
-    if (cg < n) {
-      float acc = 0.f;
-      for (int w = 0; w < nwaves; ++w) acc += plane[(w * M + token) * NB + cc];
-      y[(int64_t)token * ldy + cg] = (uint16_t)f32_to_bf16_bits(acc);
+
+  float* mine = ksplit > 1 ? partials + ((int64_t)strip * ksplit + kslice) * (M * SW) : nullptr;
+  for (int o = tid; o < M * SW; o += blockDim.x) {
+    const int token = o / SW, cc = o - token * SW;
+    float v = 0.f;
+    for (int w = 0; w < nw; ++w) v += plane[(w * M + token) * SW + cc];
+    const int64_t cg = (int64_t)strip * SW + cc;
+    if (ksplit == 1) {
+      if (cg < n) y[(int64_t)token * ldy + cg] = (uint16_t)f32_to_bf16_bits(v);
+    } else {
+      // agent-coherent store: visible to any workgroup once it has completed
+      __hip_atomic_store(&mine[o], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+  if (ksplit == 1) return;
+
+  // split k: the last workgroup of the strip adds the partials in k order.
+  // Every thread waits for its partial stores to complete before the barrier,
+  // then one counter increment per workgroup; partials are only written and
+  // read with agent-coherent accesses, so no cache-wide maintenance is needed.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0)
+    last_flag = __hip_atomic_fetch_add(&tickets[strip], 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(ksplit - 1);
+  __syncthreads();
+  if (!last_flag) return;
+  const float* base = partials + (int64_t)strip * ksplit * (M * SW);
+  for (int o = tid; o < M * SW; o += blockDim.x) {
+    const int token = o / SW, cc = o - token * SW;
+    const int64_t cg = (int64_t)strip * SW + cc;
+    float part[SK_MAX_SPLIT];
+#pragma unroll
+    for (int p = 0; p < SK_MAX_SPLIT; ++p)       // all loads in flight, then add in k order
+      part[p] = p < ksplit ? __hip_atomic_load(&base[p * (M * SW) + o], __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)
+                           : 0.f;
+    float v = 0.f;
+#pragma unroll
+    for (int p = 0; p < SK_MAX_SPLIT; ++p) v += part[p];
+    if (cg < n) y[(int64_t)token * ldy + cg] = (uint16_t)f32_to_bf16_bits(v);
+  }
+  if (tid == 0) __hip_atomic_store(&tickets[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -426,70 +511,100 @@ __global__ __launch_bounds__(256) void mfma_int4_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// launch shapes
+// launch shapes of the skinny kernel
 // ---------------------------------------------------------------------------
-static int pick_cpl(int64_t n) {
-  // widest per-lane load that still gives enough workgroups for 256 CUs
-  if ((n + 63) / 64 >= 384) return 4;
-  if ((n + 31) / 32 >= 384) return 2;
-  return 1;
+#ifndef QG_SKINNY_MIN_STRIPS
+#define QG_SKINNY_MIN_STRIPS 256   // strips wanted before widening them
+#endif
+#ifndef QG_SKINNY_MAX_GPW
+#define QG_SKINNY_MAX_GPW 6        // groups per wave above which k is split
+#endif
+
+int64_t split_workspace_bytes(int64_t nstrips, int64_t ksplit, int64_t m, int cpl) {
+  return kTicketBytes + nstrips * ksplit * m * 16 * cpl * 4;
 }
 
-static int pick_waves(int64_t k) {
-  const int64_t groups = k / 128;
-  return (int)(groups < 16 ? (groups < 1 ? 1 : groups) : 16);
+SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes, bool dot) {
+  SkinnyPlan p{};
+  const int64_t G = k / 128;
+  // widest strip that still leaves enough strips for the CUs
+  p.cpl = 1;
+  if ((n + 63) / 64 >= QG_SKINNY_MIN_STRIPS) p.cpl = 4;
+  else if ((n + 31) / 32 >= QG_SKINNY_MIN_STRIPS) p.cpl = 2;
+  const int sw = 16 * p.cpl;
+  p.nstrips = (int)((n + sw - 1) / sw);
+  p.waves = (int)(G < 2 ? 1 : (G / 2 < SK_MAX_WAVES ? G / 2 : SK_MAX_WAVES));
+  // k split only when each wave would otherwise walk a long chain of groups
+  int64_t ks = 1;
+  const int64_t per_wave = (G + p.waves - 1) / p.waves;
+  if (per_wave > QG_SKINNY_MAX_GPW && (int64_t)p.nstrips * 4 <= kTicketBytes) {
+    ks = (per_wave + 3) / 4;
+    if (ks > SK_MAX_SPLIT) ks = SK_MAX_SPLIT;
+  }
+  int64_t gwg = (G + ks - 1) / ks;
+  ks = G > 0 ? (G + gwg - 1) / gwg : 1;
+  int64_t need = ks > 1 ? split_workspace_bytes(p.nstrips, ks, m, p.cpl) : 0;
+  if (need > workspace_bytes) {       // no room for the partials: one slice per strip
+    ks = 1;
+    gwg = G;
+    need = 0;
+  }
+  p.ksplit = (int)ks;
+  p.gwg = (int)gwg;
+  p.ws_bytes = need;
+  const int64_t items = (int64_t)p.nstrips * p.ksplit;
+  p.items_per_xcd = (int)((items + 7) / 8);
+  p.blocks = (int64_t)p.items_per_xcd * 8;
+  p.lds = (size_t)SK_MAX_WAVES * m * sw * 4 + (dot ? (size_t)gwg * 16 * 16 : 0);
+  return p;
 }
 
-hipError_t launch_gemv_int4(const Int4Args& a, hipStream_t stream) {
-  const int cpl = pick_cpl(a.n);
-  const int nw = pick_waves(a.k);
-  const unsigned blocks = (unsigned)((a.n + 16 * cpl - 1) / (16 * cpl));
-  const dim3 grid(blocks), block(64 * nw);
-  const int n = (int)a.n, k = (int)a.k;
-  if (cpl == 4)
-    gemv_int4_kernel<4><<<grid, block, 0, stream>>>(a.x, a.qweight, a.scales, a.qzeros, a.y, n, k);
-  else if (cpl == 2)
-    gemv_int4_kernel<2><<<grid, block, 0, stream>>>(a.x, a.qweight, a.scales, a.qzeros, a.y, n, k);
-  else
-    gemv_int4_kernel<1><<<grid, block, 0, stream>>>(a.x, a.qweight, a.scales, a.qzeros, a.y, n, k);
+template <int M, bool DOT, int CPL>
+static void skinny_launch(const Int4Args& a, const SkinnyPlan& p, void* ws, hipStream_t stream) {
+  uint32_t* tickets = (uint32_t*)ws;
+  float* partials = ws ? (float*)((char*)ws + kTicketBytes) : nullptr;
+  skinny_int4_kernel<M, DOT, CPL><<<dim3((unsigned)p.blocks), dim3(64 * p.waves), p.lds, stream>>>(
+      a.x, a.ldx, a.qweight, a.scales, a.qzeros, a.y, a.ldy, (int)a.n, (int)a.k, p.nstrips,
+      p.ksplit, p.gwg, p.items_per_xcd, partials, tickets);
+}
+
+template <int M, bool DOT>
+static void skinny_launch_c(const Int4Args& a, const SkinnyPlan& p, void* ws, hipStream_t stream) {
+  if (p.cpl == 4) skinny_launch<M, DOT, 4>(a, p, ws, stream);
+  else if (p.cpl == 2) skinny_launch<M, DOT, 2>(a, p, ws, stream);
+  else skinny_launch<M, DOT, 1>(a, p, ws, stream);
+}
+
+hipError_t launch_gemv_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream) {
+  const SkinnyPlan p = plan_skinny(1, a.n, a.k, ws ? ws_bytes : 0, true);
+  if (p.lds <= kSkinnyMaxLds) {
+    skinny_launch_c<1, true>(a, p, ws, stream);
+  } else {
+    // the k-slice's activations do not fit in LDS: the MFMA variant needs none
+    skinny_launch_c<1, false>(a, plan_skinny(1, a.n, a.k, ws ? ws_bytes : 0, false), ws, stream);
+  }
   return hipGetLastError();
 }
 
-template <int M, int CPL>
-static void fused_launch(const Int4Args& a, int nw, hipStream_t stream) {
-  const unsigned blocks = (unsigned)((a.n + 16 * CPL - 1) / (16 * CPL));
-  const size_t lds = (size_t)nw * M * 16 * CPL * sizeof(float);
-  fused_int4_kernel<M, CPL><<<dim3(blocks), dim3(64 * nw), lds, stream>>>(
-      a.x, a.ldx, a.qweight, a.scales, a.qzeros, a.y, a.ldy, (int)a.n, (int)a.k);
-}
-
-template <int M>
-static void fused_launch_m(const Int4Args& a, hipStream_t stream) {
-  const int cpl = pick_cpl(a.n);
-  const int nw = pick_waves(a.k);
-  if (cpl == 4) fused_launch<M, 4>(a, nw, stream);
-  else if (cpl == 2) fused_launch<M, 2>(a, nw, stream);
-  else fused_launch<M, 1>(a, nw, stream);
-}
-
-hipError_t launch_fused_int4(const Int4Args& a, hipStream_t stream) {
+hipError_t launch_fused_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream) {
+  const SkinnyPlan p = plan_skinny(a.m, a.n, a.k, ws ? ws_bytes : 0, false);
   switch (a.m) {
-    case 1: fused_launch_m<1>(a, stream); break;
-    case 2: fused_launch_m<2>(a, stream); break;
-    case 3: fused_launch_m<3>(a, stream); break;
-    case 4: fused_launch_m<4>(a, stream); break;
-    case 5: fused_launch_m<5>(a, stream); break;
-    case 6: fused_launch_m<6>(a, stream); break;
-    case 7: fused_launch_m<7>(a, stream); break;
-    case 8: fused_launch_m<8>(a, stream); break;
-    case 9: fused_launch_m<9>(a, stream); break;
-    case 10: fused_launch_m<10>(a, stream); break;
-    case 11: fused_launch_m<11>(a, stream); break;
-    case 12: fused_launch_m<12>(a, stream); break;
-    case 13: fused_launch_m<13>(a, stream); break;
-    case 14: fused_launch_m<14>(a, stream); break;
-    case 15: fused_launch_m<15>(a, stream); break;
-    case 16: fused_launch_m<16>(a, stream); break;
+    case 1: skinny_launch_c<1, false>(a, p, ws, stream); break;
+    case 2: skinny_launch_c<2, false>(a, p, ws, stream); break;
+    case 3: skinny_launch_c<3, false>(a, p, ws, stream); break;
+    case 4: skinny_launch_c<4, false>(a, p, ws, stream); break;
+    case 5: skinny_launch_c<5, false>(a, p, ws, stream); break;
+    case 6: skinny_launch_c<6, false>(a, p, ws, stream); break;
+    case 7: skinny_launch_c<7, false>(a, p, ws, stream); break;
+    case 8: skinny_launch_c<8, false>(a, p, ws, stream); break;
+    case 9: skinny_launch_c<9, false>(a, p, ws, stream); break;
+    case 10: skinny_launch_c<10, false>(a, p, ws, stream); break;
+    case 11: skinny_launch_c<11, false>(a, p, ws, stream); break;
+    case 12: skinny_launch_c<12, false>(a, p, ws, stream); break;
+    case 13: skinny_launch_c<13, false>(a, p, ws, stream); break;
+    case 14: skinny_launch_c<14, false>(a, p, ws, stream); break;
+    case 15: skinny_launch_c<15, false>(a, p, ws, stream); break;
+    case 16: skinny_launch_c<16, false>(a, p, ws, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -505,16 +620,20 @@ hipError_t launch_mfma_int4(const Int4Args& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-void describe_int4(int64_t m, int64_t n, int64_t k, int path, char* buf, size_t len) {
+int64_t workspace_int4(int64_t m, int64_t n, int64_t k, int path) {
+  if (path == 3 || m == 0 || n == 0 || k == 0) return 0;
+  return plan_skinny(m, n, k, INT64_MAX, path == 1).ws_bytes;
+}
+
+void describe_int4(int64_t m, int64_t n, int64_t k, int path, int64_t ws_bytes, char* buf,
+                   size_t len) {
   if (path == 1 || path == 2) {
-    const int cpl = pick_cpl(n), nw = pick_waves(k);
-    const long long blocks = (n + 16 * cpl - 1) / (16 * cpl);
-    if (path == 1)
-      snprintf(buf, len, "gemv_int4_kernel<%d> grid=%lld block=%d lds=%d", cpl, blocks, 64 * nw,
-               16 * 16 * cpl * 4);
-    else
-      snprintf(buf, len, "fused_int4_kernel<%lld,%d> grid=%lld block=%d lds=%lld", (long long)m, cpl,
-               blocks, 64 * nw, (long long)nw * m * 16 * cpl * 4);
+    SkinnyPlan p = plan_skinny(path == 1 ? 1 : m, n, k, ws_bytes, path == 1);
+    const bool dot = path == 1 && p.lds <= kSkinnyMaxLds;
+    if (path == 1 && !dot) p = plan_skinny(1, n, k, ws_bytes, false);
+    snprintf(buf, len, "skinny_int4_kernel<%lld,%s,%d> grid=%lld block=%d lds=%lld ksplit=%d groups=%d",
+             path == 1 ? 1LL : (long long)m, dot ? "dot" : "mfma", p.cpl, (long long)p.blocks,
+             64 * p.waves, (long long)p.lds, p.ksplit, p.gwg);
   } else {
     const long long tiles = ((m + TBM - 1) / TBM) * ((n + TBN - 1) / TBN);
     snprintf(buf, len, "mfma_int4_kernel grid=%lld block=256 lds=%d", tiles,

@@ -20,12 +20,26 @@ struct Int4Args {
 
 hipError_t launch_dequant(const uint32_t* qweight, const uint16_t* scales, const uint32_t* qzeros,
                           float* w, int64_t n, int64_t k, hipStream_t stream);
-hipError_t launch_gemv_int4(const Int4Args& a, hipStream_t stream);
-hipError_t launch_fused_int4(const Int4Args& a, hipStream_t stream);
+// Launch shape of the skinny (m <= 16) kernel: strips of 16 * cpl columns,
+// `waves` waves per workgroup, k split into `ksplit` slices of `gwg` groups.
+struct SkinnyPlan {
+  int cpl, nstrips, waves, ksplit, gwg, items_per_xcd;
+  int64_t blocks;
+  size_t lds;
+  int64_t ws_bytes;
+};
+SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes, bool dot);
+int64_t split_workspace_bytes(int64_t nstrips, int64_t ksplit, int64_t m, int cpl);
+
+// ws may be NULL (then no k split); ws_bytes is its size.
+hipError_t launch_gemv_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream);
+hipError_t launch_fused_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream);
 hipError_t launch_mfma_int4(const Int4Args& a, hipStream_t stream);
 
-// Text description of the kernel and launch shape of a path (1 GEMV, 2 fused, 3 MFMA).
-void describe_int4(int64_t m, int64_t n, int64_t k, int path, char* buf, size_t len);
+// Workspace bytes a path (1 GEMV, 2 fused, 3 MFMA) can use; 0 if none.
+int64_t workspace_int4(int64_t m, int64_t n, int64_t k, int path);
+// Text description of the kernel and launch shape of a path.
+void describe_int4(int64_t m, int64_t n, int64_t k, int path, int64_t ws_bytes, char* buf, size_t len);
 
 // Writes zeros to a rows x cols matrix of 16-bit elements with leading dimension ld.
 hipError_t launch_zero16(uint16_t* p, int64_t rows, int64_t cols, int64_t ld, hipStream_t stream);

@@ -19,7 +19,7 @@ OK, NULL, SHAPE, ALIGN, DTYPE, LAYOUT, UNSUP = 0, 1, 2, 3, 4, 5, 6
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^(?:int32_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^(?:int32_t|int64_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
 
 
 def defines(prefix):
@@ -35,7 +35,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "qg_abi_version", "qg_status_str", "qg_last_hip_error", "qgemm_int4", "qgemm_int4_path",
-        "qgemm_int4_describe", "qgemm_int4_dequant", "gemm_dense"])
+        "qgemm_int4_workspace_size", "qgemm_int4_describe", "qgemm_int4_dequant", "gemm_dense"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -67,8 +67,8 @@ MIS = 0x10002          # 2-byte aligned only
 
 
 def int4(lib, x=A16, ldx=256, qw=A16, sc=A16, qz=A16, y=A16, ldy=64, m=1, n=64, k=256, gs=128,
-         path=0):
-    return lib.qgemm_int4_path(x, ldx, qw, sc, qz, y, ldy, m, n, k, gs, path, None)
+         path=0, ws=None, wsb=0):
+    return lib.qgemm_int4_path(x, ldx, qw, sc, qz, y, ldy, m, n, k, gs, path, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -80,6 +80,7 @@ def int4(lib, x=A16, ldx=256, qw=A16, sc=A16, qz=A16, y=A16, ldy=64, m=1, n=64, 
     (dict(sc=A16 + 2), ALIGN), (dict(qz=A16 + 2), ALIGN), (dict(y=A16 + 2), ALIGN),
     (dict(ldy=66), ALIGN),
     (dict(path=1, m=2), UNSUP), (dict(path=2, m=17), UNSUP), (dict(path=9), UNSUP),
+    (dict(ws=A16 + 8, wsb=1024), ALIGN), (dict(wsb=-1), SHAPE),
 ])
 def test_int4_rejects_invalid_arguments(lib, kw, code):
     assert int4(lib, **kw) == code
@@ -118,12 +119,26 @@ def test_dense_rejects_invalid_arguments(lib, args, code):
 
 
 def test_describe_names_the_dispatch(lib):
-    assert qg.describe_int4(1, 4096, 4096).startswith("gemv_int4_kernel<1>")
-    assert qg.describe_int4(8, 4096, 4096).startswith("fused_int4_kernel<8,1>")
-    assert qg.describe_int4(16, 28672, 4096).startswith("fused_int4_kernel<16,4>")
+    # 4096 columns: 256 strips of 16, 16 waves splitting 32 groups, no k split
+    assert qg.describe_int4(1, 4096, 4096) == (
+        "skinny_int4_kernel<1,dot,1> grid=256 block=1024 lds=%d ksplit=1 groups=32" % (16 * 64 + 32 * 256))
+    assert qg.describe_int4(8, 8192, 2048).startswith("skinny_int4_kernel<8,mfma,2> grid=256 block=512")
+    assert qg.describe_int4(16, 28672, 4096).startswith("skinny_int4_kernel<16,mfma,4> grid=448 block=1024")
+    # a long k with few strips is split: 200 groups over 16 waves -> 4 slices of 50
+    assert "ksplit=4 groups=50" in qg.describe_int4(16, 5120, 25600)
+    assert "ksplit=1 groups=200" in qg.describe_int4(16, 5120, 25600, workspace_bytes=0)
     assert qg.describe_int4(17, 5120, 25600).startswith("mfma_int4_kernel")
     assert qg.describe_int4(1, 4096, 4096, "mfma").startswith("mfma_int4_kernel")
     assert qg.describe_int4(0, 64, 128) == "none"
     assert qg.describe_int4(3, 64, 0) == "zero16_kernel"
     with pytest.raises(qg.QGemmError):
         qg.describe_int4(2, 64, 128, "gemv")
+
+
+def test_workspace_size(lib):
+    # 64 KiB of counters, then 320 strips x 4 slices x 16 tokens x 16 columns x 4 bytes
+    assert qg.workspace_size(16, 5120, 25600) == 65536 + 320 * 4 * 16 * 16 * 4
+    assert qg.workspace_size(8, 4096, 4096) == 0           # no split needed
+    assert qg.workspace_size(17, 4096, 4096) == 0          # MFMA tiles use none
+    assert lib.qgemm_int4_workspace_size(8, 60, 4096, 0) == -SHAPE
+    assert lib.qgemm_int4_workspace_size(8, 64, 4096, 1) == -UNSUP

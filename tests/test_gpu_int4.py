@@ -18,10 +18,11 @@ pytestmark = pytest.mark.gpu
 RMS_GATE = 2.5e-3
 
 
-def run(qg, t, path="auto", out=None):
+def run(qg, t, path="auto", out=None, workspace=None):
     import torch
 
-    y = qg.qgemm_int4(t["x"], t["qweight"], t["scales"], t["qzeros"], out=out, path=path)
+    y = qg.qgemm_int4(t["x"], t["qweight"], t["scales"], t["qzeros"], out=out, path=path,
+                      workspace=workspace)
     torch.cuda.synchronize()
     return y
 
@@ -135,15 +136,15 @@ def test_strided_x_and_y_with_guard_bands(gpu_lib):
     xs[:, :k] = t["x"]
     t["x"] = xs[:, :k]
     for path in ["fused", "mfma"]:
-        big = torch.full((m + 2, n + 24), -777.0, dtype=torch.bfloat16, device="cuda")
+        big = torch.full((m + 2, n + 24), -384.0, dtype=torch.bfloat16, device="cuda")
         out = big[1:m + 1, 8:8 + n]
         say("strided", path)
         run(gpu_lib, t, path, out=out)
         ref = oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], m, k, n)
         assert_accepted(host_u16(out), ref, ("strided", path))
         b = big.float().cpu().numpy()
-        b[1:m + 1, 8:8 + n] = -777.0
-        assert np.all(b == -777.0), "write outside the output view"
+        b[1:m + 1, 8:8 + n] = -384.0
+        assert np.all(b == -384.0), "write outside the output view"
 
 
 def test_k_zero_writes_zeros_and_m_zero_is_noop(gpu_lib):
@@ -161,6 +162,49 @@ def test_k_zero_writes_zeros_and_m_zero_is_noop(gpu_lib):
     run(gpu_lib, t0, out=e)
 
 
+SPLIT_SHAPES = [(16384, 520), (20480, 776)]       # long k, few strips: the k split is on
+
+
+@pytest.mark.parametrize("k,n", SPLIT_SHAPES)
+@pytest.mark.parametrize("path,m", [("gemv", 1), ("fused", 1), ("fused", 8), ("fused", 16)])
+def test_split_k_with_and_without_workspace(gpu_lib, path, m, k, n):
+    d = int4_inputs(m, k, n, seed=36 + m + n)
+    t = upload_int4(d)
+    ref = oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], m, k, n)
+    for ws in (None, False):
+        say("split", path, m, k, n, "ws" if ws is None else "no-ws",
+            gpu_lib.describe_int4(m, n, k, path, None if ws is None else 0))
+        y = run(gpu_lib, t, path, workspace=ws)
+        assert_accepted(host_u16(y), ref, ("split", path, m, k, n, ws))
+
+
+def test_gemv_long_k_falls_back_when_lds_is_short(gpu_lib):
+    m, k, n = 1, 76800, 16
+    desc = gpu_lib.describe_int4(m, n, k, "gemv", 0)
+    say("long-k", desc)
+    assert "mfma" in desc          # the activation slice would not fit in LDS
+    d = int4_inputs(m, k, n, seed=39)
+    y = run(gpu_lib, upload_int4(d), "gemv", workspace=False)
+    ref = oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], m, k, n)
+    assert_accepted(host_u16(y), ref, ("long-k", m, k, n))
+
+
+def test_shared_workspace_across_shapes_and_counters_reset(gpu_lib):
+    import torch
+
+    ws = torch.zeros(8 << 20, dtype=torch.uint8, device="cuda")
+    shapes = [(8, 16384, 520), (1, 20480, 776), (15, 1152, 776), (16, 16384, 1040), (3, 896, 4864),
+              (8, 16384, 520)]
+    for i, (m, k, n) in enumerate(shapes):
+        say("shared-ws", m, k, n, gpu_lib.describe_int4(m, n, k, workspace_bytes=ws.numel()))
+        d = int4_inputs(m, k, n, seed=40 + i)
+        y = run(gpu_lib, upload_int4(d), workspace=ws)
+        ref = oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], m, k, n)
+        assert_accepted(host_u16(y), ref, ("shared-ws", m, k, n))
+        # the split's counters (the first 64 KiB) are back at zero
+        assert int(torch.count_nonzero(ws[:65536])) == 0
+
+
 def test_deterministic(gpu_lib):
     m, k, n = 8, 2048, 1040
     d = int4_inputs(m, k, n, seed=35)
@@ -169,6 +213,13 @@ def test_deterministic(gpu_lib):
         a = host_u16(run(gpu_lib, t, path))
         b = host_u16(run(gpu_lib, t, path))
         assert np.array_equal(a, b)
+    m1 = int4_inputs(1, k, n, seed=37)
+    t1 = upload_int4(m1)
+    assert np.array_equal(host_u16(run(gpu_lib, t1, "gemv")), host_u16(run(gpu_lib, t1, "gemv")))
+    # with the k split on, partials are added in k order: still deterministic
+    d2 = int4_inputs(8, 16384, 520, seed=38)
+    t2 = upload_int4(d2)
+    assert np.array_equal(host_u16(run(gpu_lib, t2, "fused")), host_u16(run(gpu_lib, t2, "fused")))
 
 
 # ----------------------------------------------------------------------------
