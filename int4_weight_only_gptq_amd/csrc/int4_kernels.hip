@@ -170,7 +170,6 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // ---------------------------------------------------------------------------
 constexpr int64_t kTicketBytes = 64 << 10;   // counters of up to 16384 strips
 constexpr int SK_MAX_SPLIT = 16;              // k-slices per strip at most
-constexpr int SK_MAX_WAVES = 16;
 constexpr size_t kSkinnyMaxLds = 150 << 10;    // of the 160 KiB of a gfx950 CU
 
 template <int M, bool DOT, int CPL>
@@ -221,15 +220,16 @@ __global__ __launch_bounds__(1024) void skinny_int4_kernel(
   static_assert(!DOT || M == 1, "the VALU variant computes one token");
   constexpr int SW = 16 * CPL;                 // strip width in columns
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  float* plane = reinterpret_cast<float*>(smem);                 // [W][M][SW]
-  u32x4* xl = reinterpret_cast<u32x4*>(smem + (size_t)SK_MAX_WAVES * M * SW * 4);  // DOT: [k-slice chunks]
+  const int nw = blockDim.x >> 6;
+  float* plane = reinterpret_cast<float*>(smem);                          // [nw][M][SW]
+  u32x4* xl = reinterpret_cast<u32x4*>(smem + (size_t)nw * M * SW * 4);   // DOT: [k-slice chunks]
   __shared__ int last_flag;
 
   const int item = (blockIdx.x & 7) * items_per_xcd + (blockIdx.x >> 3);
   const int strip = item / ksplit, kslice = item - strip * ksplit;
   if (strip >= nstrips) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cl = lane & 15, ks = lane >> 4;
   const int G = k >> 7;
   const int gbeg = kslice * gwg, gend = min(G, gbeg + gwg);
@@ -240,6 +240,11 @@ __global__ __launch_bounds__(1024) void skinny_int4_kernel(
   const uint16_t* xp = x + (xrow ? (int64_t)cl * ldx : 0);
   const int zshift = (int)(col & 7) * 4;
   const u32x4 ones = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
+
+  // first group's loads go out before anything waits
+  GroupRegs<M, DOT, CPL> cur, nxt;
+  int g = gbeg + wave;
+  load_group<M, DOT, CPL>(cur, g < gend, live, xrow, qp, xp, scales, qzeros, n, g, col, ks);
 
   if constexpr (DOT) {
     // the activation row of this k-slice, in pair order, once per workgroup
@@ -253,9 +258,6 @@ __global__ __launch_bounds__(1024) void skinny_int4_kernel(
 #pragma unroll
   for (int c = 0; c < CPL; ++c) total[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  GroupRegs<M, DOT, CPL> cur, nxt;
-  int g = gbeg + wave;
-  load_group<M, DOT, CPL>(cur, g < gend, live, xrow, qp, xp, scales, qzeros, n, g, col, ks);
   for (; g < gend; g += nw) {
     const int gn = g + nw;
     load_group<M, DOT, CPL>(nxt, gn < gend, live, xrow, qp, xp, scales, qzeros, n, gn, col, ks);
@@ -516,6 +518,9 @@ __global__ __launch_bounds__(256) void mfma_int4_kernel(
 #ifndef QG_SKINNY_MIN_STRIPS
 #define QG_SKINNY_MIN_STRIPS 256   // strips wanted before widening them
 #endif
+#ifndef QG_SKINNY_WAVES
+#define QG_SKINNY_WAVES 16         // waves per workgroup at most
+#endif
 #ifndef QG_SKINNY_MAX_GPW
 #define QG_SKINNY_MAX_GPW 6        // groups per wave above which k is split
 #endif
@@ -533,7 +538,9 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes,
   else if ((n + 31) / 32 >= QG_SKINNY_MIN_STRIPS) p.cpl = 2;
   const int sw = 16 * p.cpl;
   p.nstrips = (int)((n + sw - 1) / sw);
-  p.waves = (int)(G < 2 ? 1 : (G / 2 < SK_MAX_WAVES ? G / 2 : SK_MAX_WAVES));
+  // many strips: 8-wave workgroups so that two fit on a CU; few: 16 waves
+  const int64_t wcap = p.nstrips >= 384 ? (QG_SKINNY_WAVES < 8 ? QG_SKINNY_WAVES : 8) : QG_SKINNY_WAVES;
+  p.waves = (int)(G < 2 ? 1 : (G / 2 < wcap ? G / 2 : wcap));
   // k split only when each wave would otherwise walk a long chain of groups
   int64_t ks = 1;
   const int64_t per_wave = (G + p.waves - 1) / p.waves;
@@ -555,7 +562,7 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes,
   const int64_t items = (int64_t)p.nstrips * p.ksplit;
   p.items_per_xcd = (int)((items + 7) / 8);
   p.blocks = (int64_t)p.items_per_xcd * 8;
-  p.lds = (size_t)SK_MAX_WAVES * m * sw * 4 + (dot ? (size_t)gwg * 16 * 16 : 0);
+  p.lds = (size_t)p.waves * m * sw * 4 + (dot ? (size_t)gwg * 16 * 16 : 0);
   return p;
 }
 
