@@ -16,8 +16,13 @@
 
 namespace qg {
 
-constexpr int DBM = 128, DBN = 128, DBK = 64;
-constexpr int DSTRIDE = DBK + 8;   // 16-bit elements per LDS row
+constexpr int DBK = 64;
+constexpr int DSTRIDE = DBK + 8;   // 16-bit elements per LDS row (144 bytes)
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding and ignores the other counters (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 // 8 x 8 transpose of 16-bit elements: in[r] holds row r (8 elements), out[j]
 // receives column j = (in[0][j], in[1][j], ..., in[7][j]).
@@ -30,37 +35,13 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
   }
 }
 
-// Stage a K-contiguous operand tile (rows x DBK) from global memory.
-// rows = 128: 1024 chunks of 8 elements, 4 per thread.
-__device__ __forceinline__ void load_kcontig(const uint16_t* __restrict__ p, int64_t ld, int64_t row0,
-                                             int64_t rows, int64_t k0, int64_t K, u32x4 (&reg)[4]) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
-    const int r = c >> 3, kc = c & 7;
-    const int64_t gr = row0 + r, gk = k0 + 8 * kc;
-    reg[i] = (gr < rows && gk < K) ? *reinterpret_cast<const u32x4*>(p + gr * ld + gk)
-                                   : u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
-__device__ __forceinline__ void store_kcontig(uint16_t* lds, const u32x4 (&reg)[4]) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
-    const int r = c >> 3, kc = c & 7;
-    *reinterpret_cast<u32x4*>(&lds[r * DSTRIDE + 8 * kc]) = reg[i];
-  }
-}
-
-// Stage an MN-contiguous operand tile: memory [K][rows], 8 k-blocks x 16
-// row-blocks of 8 x 8 = 128 blocks; threads 0..127 of `half` take one each.
+// Stage an MN-contiguous operand tile: memory [K][rows], 8 k-blocks x rows/8
+// row-blocks of 8 x 8 elements; block `slot` is (k-block slot % 8, row-block
+// slot / 8), one per thread.
 __device__ __forceinline__ void load_mncontig(const uint16_t* __restrict__ p, int64_t ld, int64_t row0,
                                               int64_t rows, int64_t k0, int64_t K, int slot,
                                               u32x4 (&reg)[8]) {
-  const int kb = slot >> 4, rb = slot & 15;
+  const int kb = slot & 7, rb = slot >> 3;
   const int64_t gr = row0 + 8 * rb;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -71,113 +52,357 @@ __device__ __forceinline__ void load_mncontig(const uint16_t* __restrict__ p, in
 }
 
 __device__ __forceinline__ void store_mncontig(uint16_t* lds, int slot, const u32x4 (&reg)[8]) {
-  const int kb = slot >> 4, rb = slot & 15;
+  const int kb = slot & 7, rb = slot >> 3;
   u32x4 t[8];
   transpose8x8(reg, t);
 #pragma unroll
   for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(&lds[(8 * rb + j) * DSTRIDE + 8 * kb]) = t[j];
 }
 
-template <int LAYOUT, int DTYPE>
-__global__ __launch_bounds__(256) void dense_mfma_kernel(const uint16_t* __restrict__ A, int64_t lda,
+// Tile kernel: BM x BN output tile per workgroup of 4 waves (2 x 2, each
+// BM/2 x BN/2 = FM x FN MFMA tiles of 16 x 16), k tiles of 64 double-buffered in
+// LDS with one barrier per k tile: the next tile's global loads are in flight
+// while the current one is multiplied, and are written to the other buffer
+// after.  B fragment c of a wave holds columns wn0 + 16c + lane % 16, the
+// standard mapping (lanes 0..15 read 16 consecutive LDS rows, conflict-free
+// with the 144-byte row pitch).  The epilogue converts the accumulators into an
+// output tile in LDS and writes it with 16-byte row-contiguous stores.
+// Workgroup b works on tile (b % 8) * tiles_per_xcd + b / 8, so each XCD gets
+// a contiguous, row-major range of tiles (shared A panels in its L2).
+template <int BM, int BN>
+struct DenseSmem {
+  static constexpr int kA = BM * DSTRIDE, kB = BN * DSTRIDE;          // halves per buffer
+  static constexpr int kMain = 2 * (kA + kB);                          // two buffers
+  static constexpr int kOut = BM * (BN + 8);                           // epilogue tile
+  static constexpr int kHalves = kMain > kOut ? kMain : kOut;
+};
+
+template <int LAYOUT, int DTYPE, int BM, int BN>
+__global__ __launch_bounds__(256) void dense_tile_kernel(const uint16_t* __restrict__ A, int64_t lda,
                                                          const uint16_t* __restrict__ B, int64_t ldb,
-                                                         uint16_t* __restrict__ C, int64_t ldc,
-                                                         int M, int N, int K, int tiles_m) {
+                                                         uint16_t* __restrict__ C, int64_t ldc, int M,
+                                                         int N, int K, int tiles_n, int tiles,
+                                                         int tiles_per_xcd, int vec_store) {
   constexpr bool A_T = (LAYOUT == 2);            // A stored [K][M]
   constexpr bool B_T = (LAYOUT != 0);            // B stored [K][N]
-  __shared__ __attribute__((aligned(16))) uint16_t a_lds[DBM * DSTRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t b_lds[DBN * DSTRIDE];
+  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
+  constexpr int ACH = BM / 32, BCH = BN / 32;    // 16-byte chunks per thread, K-contiguous staging
+  using SM = DenseSmem<BM, BN>;
+  extern __shared__ __attribute__((aligned(16))) uint16_t dsm[];
 
+  const int t = (blockIdx.x & 7) * tiles_per_xcd + (blockIdx.x >> 3);
+  if (t >= tiles) return;
+  const int tm = t / tiles_n, tn = t - tm * tiles_n;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int cl = lane & 15, ks = lane >> 4;
-  const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
-  const int64_t m0 = (int64_t)tm * DBM, n0 = (int64_t)tn * DBN;
-  const int wm0 = (wave & 1) * 64, wn0 = (wave >> 1) * 64;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int wm0 = (wave & 1) * WM, wn0 = (wave >> 1) * WN;
 
-  // register staging for the next k tile
-  u32x4 ra[A_T ? 8 : 4];
-  u32x4 rb[B_T ? 8 : 4];
-  // threads 0..127 stage A blocks and 128..255 B blocks when both are transposed;
-  // when only one is transposed, every thread stages the K-contiguous one and
-  // threads 0..127 the transposed one.
+  u32x4 ra[A_T ? 8 : ACH];
+  u32x4 rb[B_T ? 8 : BCH];
   auto load = [&](int64_t k0) {
     if constexpr (A_T) {
-      if (tid < 128) load_mncontig(A, lda, m0, M, k0, K, tid, ra);
+      if (tid < BM) load_mncontig(A, lda, m0, M, k0, K, tid, ra);
     } else {
-      load_kcontig(A, lda, m0, M, k0, K, ra);
+#pragma unroll
+      for (int i = 0; i < ACH; ++i) {
+        const int c = tid + 256 * i, r = c >> 3, kc = c & 7;
+        const int64_t gr = m0 + r, gk = k0 + 8 * kc;
+        ra[i] = (gr < M && gk < K) ? *reinterpret_cast<const u32x4*>(A + gr * lda + gk) : u32x4{0u, 0u, 0u, 0u};
+      }
     }
     if constexpr (B_T) {
-      const int slot = A_T ? tid - 128 : tid;
-      if (slot >= 0 && slot < 128) load_mncontig(B, ldb, n0, N, k0, K, slot, rb);
+      if (tid < BN) load_mncontig(B, ldb, n0, N, k0, K, tid, rb);
     } else {
-      load_kcontig(B, ldb, n0, N, k0, K, rb);
+#pragma unroll
+      for (int i = 0; i < BCH; ++i) {
+        const int c = tid + 256 * i, r = c >> 3, kc = c & 7;
+        const int64_t gr = n0 + r, gk = k0 + 8 * kc;
+        rb[i] = (gr < N && gk < K) ? *reinterpret_cast<const u32x4*>(B + gr * ldb + gk) : u32x4{0u, 0u, 0u, 0u};
+      }
     }
   };
-  auto store = [&]() {
+  auto store = [&](int buf) {
+    uint16_t* la = dsm + buf * SM::kA;
+    uint16_t* lb = dsm + 2 * SM::kA + buf * SM::kB;
     if constexpr (A_T) {
-      if (tid < 128) store_mncontig(a_lds, tid, ra);
+      if (tid < BM) store_mncontig(la, tid, ra);
     } else {
-      store_kcontig(a_lds, ra);
+#pragma unroll
+      for (int i = 0; i < ACH; ++i) {
+        const int c = tid + 256 * i, r = c >> 3, kc = c & 7;
+        *reinterpret_cast<u32x4*>(&la[r * DSTRIDE + 8 * kc]) = ra[i];
+      }
     }
     if constexpr (B_T) {
-      const int slot = A_T ? tid - 128 : tid;
-      if (slot >= 0 && slot < 128) store_mncontig(b_lds, slot, rb);
+      if (tid < BN) store_mncontig(lb, tid, rb);
     } else {
-      store_kcontig(b_lds, rb);
+#pragma unroll
+      for (int i = 0; i < BCH; ++i) {
+        const int c = tid + 256 * i, r = c >> 3, kc = c & 7;
+        *reinterpret_cast<u32x4*>(&lb[r * DSTRIDE + 8 * kc]) = rb[i];
+      }
     }
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[FM][FN];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < FM; ++f)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[f][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < FN; ++c) acc[f][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int ktiles = (K + DBK - 1) / DBK;
-  if (ktiles > 0) load(0);
+  load(0);
+  store(0);
+  __syncthreads();
   for (int kt = 0; kt < ktiles; ++kt) {
-    __syncthreads();
-    store();
-    __syncthreads();
+    const int buf = kt & 1;
     if (kt + 1 < ktiles) load((int64_t)(kt + 1) * DBK);
+    const uint16_t* la = dsm + buf * SM::kA;
+    const uint16_t* lb = dsm + 2 * SM::kA + buf * SM::kB;
 #pragma unroll
     for (int s = 0; s < DBK / 32; ++s) {
-      u32x4 a[4], b[4];
+      u32x4 a[FM], b[FN];
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
-        a[f] = *reinterpret_cast<const u32x4*>(&a_lds[(wm0 + 16 * f + cl) * DSTRIDE + 32 * s + 8 * ks]);
+      for (int f = 0; f < FM; ++f)
+        a[f] = *reinterpret_cast<const u32x4*>(&la[(wm0 + 16 * f + cl) * DSTRIDE + 32 * s + 8 * ks]);
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        b[c] = *reinterpret_cast<const u32x4*>(&b_lds[(wn0 + 4 * cl + c) * DSTRIDE + 32 * s + 8 * ks]);
+      for (int c = 0; c < FN; ++c)
+        b[c] = *reinterpret_cast<const u32x4*>(&lb[(wn0 + 16 * c + cl) * DSTRIDE + 32 * s + 8 * ks]);
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
+      for (int f = 0; f < FM; ++f)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < FN; ++c)
           acc[f][c] = DTYPE == 0 ? mfma16_bf16(a[f], b[c], acc[f][c]) : mfma16_f16(a[f], b[c], acc[f][c]);
+    }
+    if (kt + 1 < ktiles) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: accumulators -> output tile in LDS -> 16-byte stores
+  constexpr int OP = BN + 8;                     // halves per LDS output row
+#pragma unroll
+  for (int f = 0; f < FM; ++f)
+#pragma unroll
+    for (int c = 0; c < FN; ++c)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = wm0 + 16 * f + 4 * ks + v, col = wn0 + 16 * c + cl;
+        uint16_t h;
+        if constexpr (DTYPE == 0) h = (uint16_t)f32_to_bf16_bits(acc[f][c][v]);
+        else h = __builtin_bit_cast(uint16_t, (_Float16)acc[f][c][v]);
+        dsm[row * OP + col] = h;
+      }
+  __syncthreads();
+  constexpr int CPR = BN / 8;                    // 16-byte chunks per tile row
+  for (int c = tid; c < BM * CPR; c += 256) {
+    const int r = c / CPR, cc = c - r * CPR;
+    const int64_t gr = m0 + r, gc = n0 + 8 * cc;
+    if (gr >= M || gc >= N) continue;
+    const uint16_t* src = &dsm[r * OP + 8 * cc];
+    if (vec_store && gc + 8 <= N) {
+      *reinterpret_cast<u32x4*>(C + gr * ldc + gc) = *reinterpret_cast<const u32x4*>(src);
+    } else {
+      for (int e = 0; e < 8 && gc + e < N; ++e) C[gr * ldc + gc + e] = src[e];
+    }
+  }
+}
+
+// Pipeline kernel for all three layouts (K % 64 == 0, operands 16-byte
+// vectorizable).  Tile BM x BN per workgroup of 4 waves (2 x 2, each
+// (BM/2) x (BN/2)), k tiles of 64 in a STAGES-deep ring of LDS buffers filled
+// by direct global-to-LDS loads (no staging registers): while tile kt is
+// multiplied, tiles kt+1 .. kt+STAGES-1 are in flight.  One barrier per k tile.
+//
+// Operand tiles are stored in LDS in their memory orientation, in 16-byte
+// chunks, with an XOR swizzle instead of padding (a direct load fills 64
+// consecutive chunks per instruction):
+//  * K-contiguous operand (A of NT/NN, B of NT): rows = m or n, 8 chunks of 8 k;
+//    chunk c of row r sits at 8r + (c ^ (r & 7)).  A fragment is one 16-byte
+//    read of row (lane % 16), chunk 4s + lane / 16.
+//  * MN-contiguous operand (A of TN, B of NN and TN): rows = k, R/8 chunks of
+//    8 m or n; chunk c of row k sits at k*R/8 + (c ^ f(k)), f(k) = 2((k & 3) |
+//    ((k >> 1) & 4)).  A fragment is two transposing reads
+//    (ds_read_b64_tr_b16): in each 16-lane group, lane 4r + q supplies columns
+//    4q..4q+3 of k-row r and lane j receives column j of the 4 rows, i.e. 4
+//    consecutive k of one column; the swizzle puts the 16 rows one read
+//    touches two to a bank slot (the minimum for 512 bytes).
+// Rows or columns past M or N load a clamped valid address; their results
+// are discarded.
+__device__ __forceinline__ int swz(int r, int c) { return 8 * r + (c ^ (r & 7)); }
+__device__ __forceinline__ int fmn(int k) { return 2 * ((k & 3) | ((k >> 1) & 4)); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef s16x4 __attribute__((address_space(3))) lds_s16x4;
+
+// 8 consecutive k of column `col` (0 .. R-1) from an MN-contiguous stage
+// region with R columns (R/8 chunks per k-row); kb = first k (multiple of 8).
+template <int R>
+__device__ __forceinline__ u32x4 read_mn_frag(const u32x4* region, int kb, int col0, int lane) {
+  const int j = lane & 15, r = j >> 2, q = j & 3;
+  const int c = (col0 >> 3) + (q >> 1);
+  const int k1 = kb + r, k2 = kb + 4 + r;
+  const uint16_t* h1 = reinterpret_cast<const uint16_t*>(region + k1 * (R / 8) + (c ^ fmn(k1))) + 4 * (q & 1);
+  const uint16_t* h2 = reinterpret_cast<const uint16_t*>(region + k2 * (R / 8) + (c ^ fmn(k2))) + 4 * (q & 1);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(h1));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(h2));
+  u32x4 out;
+  out[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+  out[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+  out[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+  out[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+  return out;
+}
+
+template <int LAYOUT, int DTYPE, int BM, int BN, int STAGES>
+__global__ __launch_bounds__(256) void dense_pipe_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+    uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_n, int tiles,
+    int tiles_per_xcd, int vec_store) {
+  constexpr bool A_MN = (LAYOUT == 2);           // A stored [K][M]
+  constexpr bool B_MN = (LAYOUT != 0);           // B stored [K][N]
+  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
+  constexpr int A_SLOTS = BM * 8, B_SLOTS = BN * 8;           // 16-byte chunks per stage
+  constexpr int STAGE = A_SLOTS + B_SLOTS;
+  constexpr int A_LOADS = A_SLOTS / 256, B_LOADS = B_SLOTS / 256;   // per thread per stage
+  constexpr int LOADS = A_LOADS + B_LOADS;
+  static_assert(LOADS * (STAGES - 2) <= 63, "vmcnt range");
+  extern __shared__ __attribute__((aligned(16))) u32x4 psm[];
+
+  const int t = (blockIdx.x & 7) * tiles_per_xcd + (blockIdx.x >> 3);
+  if (t >= tiles) return;
+  const int tm = t / tiles_n, tn = t - tm * tiles_n;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cl = lane & 15, ks = lane >> 4;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int wm0 = (wave & 1) * WM, wn0 = (wave >> 1) * WN;
+
+  // source of each of this thread's chunks (chunk tid + 256 i of the operand's
+  // stage region), at k tile 0; later tiles add k0 (K-contiguous) or k0 * ld
+  const uint16_t* asrc[A_LOADS];
+  const uint16_t* bsrc[B_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) {
+    const int slot = tid + 256 * i;
+    if constexpr (A_MN) {
+      const int k = slot / (BM / 8), c = (slot % (BM / 8)) ^ fmn(k);
+      const int64_t gm = m0 + 8 * c < M ? m0 + 8 * c : (int64_t)M - 8;
+      asrc[i] = A + (int64_t)k * lda + gm;
+    } else {
+      const int r = slot >> 3, c = (slot & 7) ^ (r & 7);
+      const int64_t gr = m0 + r < M ? m0 + r : (int64_t)M - 1;
+      asrc[i] = A + gr * lda + 8 * c;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) {
+    const int slot = tid + 256 * i;
+    if constexpr (B_MN) {
+      const int k = slot / (BN / 8), c = (slot % (BN / 8)) ^ fmn(k);
+      const int64_t gn = n0 + 8 * c < N ? n0 + 8 * c : (int64_t)N - 8;
+      bsrc[i] = B + (int64_t)k * ldb + gn;
+    } else {
+      const int r = slot >> 3, c = (slot & 7) ^ (r & 7);
+      const int64_t gr = n0 + r < N ? n0 + r : (int64_t)N - 1;
+      bsrc[i] = B + gr * ldb + 8 * c;
+    }
+  }
+  const int64_t astep = A_MN ? (int64_t)DBK * lda : DBK;      // source advance per k tile
+  const int64_t bstep = B_MN ? (int64_t)DBK * ldb : DBK;
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int f = 0; f < FM; ++f)
+#pragma unroll
+    for (int c = 0; c < FN; ++c) acc[f][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int ktiles = K / DBK;
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st) {
+    if (st < ktiles) {
+      u32x4* base = psm + (size_t)st * STAGE;           // one stage of direct loads:
+#pragma unroll                                           // each wave-instruction fills
+      for (int i = 0; i < A_LOADS; ++i)                  // 64 consecutive chunks
+        __builtin_amdgcn_global_load_lds((void*)(asrc[i] + st * astep), (void*)(base + 256 * i + 64 * wave), 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < B_LOADS; ++i)
+        __builtin_amdgcn_global_load_lds((void*)(bsrc[i] + st * bstep), (void*)(base + A_SLOTS + 256 * i + 64 * wave), 16, 0, 0);
     }
   }
 
-  // lane (cl, ks) holds rows 4*ks + v of tile f and columns wn0 + 4*cl + c
-  const int64_t col = n0 + wn0 + 4 * cl;
-  if (col < N) {
+  for (int kt = 0; kt < ktiles; ++kt) {
+    // the oldest stage (kt) has landed once at most (STAGES - 2) stages remain in flight
+    if (kt + STAGES - 2 < ktiles) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * (STAGES - 2)));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    // every wave has waited for its own loads of stage kt, and has finished
+    // reading stage kt-1 (whose buffer the next issue refills): a plain
+    // barrier suffices (a fenced one would drain all stages in flight)
+    __builtin_amdgcn_s_barrier();
+    if (kt + STAGES - 1 < ktiles) {
+      const int st = kt + STAGES - 1;
+      u32x4* base = psm + (size_t)(st % STAGES) * STAGE;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
+      for (int i = 0; i < A_LOADS; ++i)
+        __builtin_amdgcn_global_load_lds((void*)(asrc[i] + st * astep), (void*)(base + 256 * i + 64 * wave), 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < B_LOADS; ++i)
+        __builtin_amdgcn_global_load_lds((void*)(bsrc[i] + st * bstep), (void*)(base + A_SLOTS + 256 * i + 64 * wave), 16, 0, 0);
+    }
+    const u32x4* la = psm + (size_t)(kt % STAGES) * STAGE;
+    const u32x4* lb = la + A_SLOTS;
+#pragma unroll
+    for (int s = 0; s < DBK / 32; ++s) {
+      const int ch = 4 * s + ks;
+      u32x4 a[FM], b[FN];
+#pragma unroll
+      for (int f = 0; f < FM; ++f) {
+        if constexpr (A_MN) a[f] = read_mn_frag<BM>(la, 32 * s + 8 * ks, wm0 + 16 * f, lane);
+        else a[f] = la[swz(wm0 + 16 * f + cl, ch)];
+      }
+#pragma unroll
+      for (int c = 0; c < FN; ++c) {
+        if constexpr (B_MN) b[c] = read_mn_frag<BN>(lb, 32 * s + 8 * ks, wn0 + 16 * c, lane);
+        else b[c] = lb[swz(wn0 + 16 * c + cl, ch)];
+      }
+#pragma unroll
+      for (int f = 0; f < FM; ++f)
+#pragma unroll
+        for (int c = 0; c < FN; ++c)
+          acc[f][c] = DTYPE == 0 ? mfma16_bf16(a[f], b[c], acc[f][c]) : mfma16_f16(a[f], b[c], acc[f][c]);
+    }
+  }
+  __syncthreads();
+
+  // epilogue: accumulators -> output tile in LDS -> 16-byte stores
+  uint16_t* osm = reinterpret_cast<uint16_t*>(psm);
+  constexpr int OP = BN + 8;
+#pragma unroll
+  for (int f = 0; f < FM; ++f)
+#pragma unroll
+    for (int c = 0; c < FN; ++c)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int64_t row = m0 + wm0 + 16 * f + 4 * ks + v;
-        if (row < M) {
-          u32x2 o;
-          if constexpr (DTYPE == 0) {
-            o[0] = pack_bf16x2(acc[f][0][v], acc[f][1][v]);
-            o[1] = pack_bf16x2(acc[f][2][v], acc[f][3][v]);
-          } else {
-            o[0] = pack_f16x2(acc[f][0][v], acc[f][1][v]);
-            o[1] = pack_f16x2(acc[f][2][v], acc[f][3][v]);
-          }
-          *reinterpret_cast<u32x2*>(C + row * ldc + col) = o;
-        }
+        const int row = wm0 + 16 * f + 4 * ks + v, col = wn0 + 16 * c + cl;
+        uint16_t h;
+        if constexpr (DTYPE == 0) h = (uint16_t)f32_to_bf16_bits(acc[f][c][v]);
+        else h = __builtin_bit_cast(uint16_t, (_Float16)acc[f][c][v]);
+        osm[row * OP + col] = h;
       }
+  __syncthreads();
+  constexpr int CPR = BN / 8;
+  for (int c = tid; c < BM * CPR; c += 256) {
+    const int r = c / CPR, cc = c - r * CPR;
+    const int64_t gr = m0 + r, gc = n0 + 8 * cc;
+    if (gr >= M || gc >= N) continue;
+    const uint16_t* src = &osm[r * OP + 8 * cc];
+    if (vec_store && gc + 8 <= N) {
+      *reinterpret_cast<u32x4*>(C + gr * ldc + gc) = *reinterpret_cast<const u32x4*>(src);
+    } else {
+      for (int e = 0; e < 8 && gc + e < N; ++e) C[gr * ldc + gc + e] = src[e];
     }
   }
 }
@@ -209,28 +434,60 @@ __global__ __launch_bounds__(256) void dense_generic_kernel(const uint16_t* __re
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Whether the MFMA kernel's vector loads/stores fit this problem.
+// Whether the tile kernel's 16-byte operand loads fit this problem.
 static bool mfma_fits(const DenseArgs& a) {
-  if (!aligned16(a.A) || !aligned16(a.B) || ((uintptr_t)a.C & 7u)) return false;
-  if (a.lda % 8 || a.ldb % 8 || a.ldc % 4 || a.N % 4) return false;
+  if (!aligned16(a.A) || !aligned16(a.B)) return false;
+  if (a.lda % 8 || a.ldb % 8) return false;
   const int64_t a_contig = a.layout == 2 ? a.M : a.K;
   const int64_t b_contig = a.layout == 0 ? a.K : a.N;
   if (a_contig % 8 || b_contig % 8) return false;
   return a.M < (1LL << 31) && a.N < (1LL << 31) && a.K < (1LL << 31);
 }
 
+#ifndef QG_DENSE_BIG_MIN_TILES
+#define QG_DENSE_BIG_MIN_TILES 160     // 256 x 128 tiles wanted before using them
+#endif
+
+template <int LAYOUT, int DTYPE, int BM, int BN>
+static void tile_launch(const DenseArgs& a, hipStream_t stream) {
+  const int tiles_m = (int)((a.M + BM - 1) / BM), tiles_n = (int)((a.N + BN - 1) / BN);
+  const int tiles = tiles_m * tiles_n, per_xcd = (tiles + 7) / 8;
+  const int vec = aligned16(a.C) && a.ldc % 8 == 0;
+  const size_t lds = (size_t)DenseSmem<BM, BN>::kHalves * 2;
+  dense_tile_kernel<LAYOUT, DTYPE, BM, BN><<<dim3((unsigned)(per_xcd * 8)), dim3(256), lds, stream>>>(
+      a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, vec);
+}
+
+#ifndef QG_DENSE_PIPE_STAGES
+#define QG_DENSE_PIPE_STAGES 3
+#endif
+
+template <int LAYOUT, int DTYPE, int BM, int BN, int STAGES>
+static void pipe_launch(const DenseArgs& a, hipStream_t stream) {
+  const int tiles_m = (int)((a.M + BM - 1) / BM), tiles_n = (int)((a.N + BN - 1) / BN);
+  const int tiles = tiles_m * tiles_n, per_xcd = (tiles + 7) / 8;
+  const int vec = aligned16(a.C) && a.ldc % 8 == 0;
+  const size_t main_bytes = (size_t)STAGES * (BM + BN) * 8 * 16;
+  const size_t out_bytes = (size_t)BM * (BN + 8) * 2;
+  const size_t lds = main_bytes > out_bytes ? main_bytes : out_bytes;
+  dense_pipe_kernel<LAYOUT, DTYPE, BM, BN, STAGES><<<dim3((unsigned)(per_xcd * 8)), dim3(256), lds, stream>>>(
+      a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, vec);
+}
+
 template <int LAYOUT, int DTYPE>
 static void dense_dispatch(const DenseArgs& a, hipStream_t stream) {
-  const uint16_t* A = a.A;
-  const uint16_t* B = a.B;
-  if (mfma_fits(a)) {
-    const int tiles_m = (int)((a.M + DBM - 1) / DBM), tiles_n = (int)((a.N + DBN - 1) / DBN);
-    dense_mfma_kernel<LAYOUT, DTYPE><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, stream>>>(
-        A, a.lda, B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_m);
+  if (mfma_fits(a) && a.K % DBK == 0 && a.M >= 128 && a.N >= 128) {
+    const int64_t big = ((a.M + 255) / 256) * ((a.N + 127) / 128);
+    if (big >= QG_DENSE_BIG_MIN_TILES) pipe_launch<LAYOUT, DTYPE, 256, 128, QG_DENSE_PIPE_STAGES>(a, stream);
+    else pipe_launch<LAYOUT, DTYPE, 128, 128, 4>(a, stream);
+  } else if (mfma_fits(a)) {
+    const int64_t big = ((a.M + 255) / 256) * ((a.N + 127) / 128);
+    if (big >= QG_DENSE_BIG_MIN_TILES) tile_launch<LAYOUT, DTYPE, 256, 128>(a, stream);
+    else tile_launch<LAYOUT, DTYPE, 128, 128>(a, stream);
   } else {
     const int64_t total = a.M * a.N;
     dense_generic_kernel<LAYOUT, DTYPE><<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(
-        A, a.lda, B, a.ldb, a.C, a.ldc, a.M, a.N, a.K);
+        a.A, a.lda, a.B, a.ldb, a.C, a.ldc, a.M, a.N, a.K);
   }
 }
 

@@ -142,3 +142,11 @@ def test_workspace_size(lib):
     assert qg.workspace_size(17, 4096, 4096) == 0          # MFMA tiles use none
     assert lib.qgemm_int4_workspace_size(8, 60, 4096, 0) == -SHAPE
     assert lib.qgemm_int4_workspace_size(8, 64, 4096, 1) == -UNSUP
+
+
+def test_library_has_no_undefined_kernel_symbols(lib):
+    # a kernel whose host-side stub was dropped at compile time links but fails to load
+    out = subprocess.run(["nm", "-D", "--undefined-only", qg.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    bad = [ln for ln in out.splitlines() if "qg" in ln or "device_stub" in ln]
+    assert not bad, bad

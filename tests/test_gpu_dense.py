@@ -56,6 +56,35 @@ def test_shapes_match_oracle(gpu_lib, layout, dtype):
         assert_accepted(c, ref, dtype, (layout, dtype, M, N, K))
 
 
+# shapes for the pipelined kernel (K % 64 == 0): ragged M and N edges, both tile sizes
+PIPE_SHAPES = [(128, 128, 64), (200, 264, 128), (1000, 136, 192), (2000, 2600, 64)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_pipeline_shapes_match_oracle(gpu_lib, layout, dtype):
+    for i, (M, N, K) in enumerate(PIPE_SHAPES):
+        say("pipe", layout, dtype, M, N, K)
+        d = dense_inputs(layout, dtype, M, N, K, seed=700 + i)
+        c = host_u16(run(gpu_lib, layout, dev(d["a"], tdtype(dtype)), dev(d["b"], tdtype(dtype))))
+        if M * N <= 300000:
+            ref = oracle.dense(layout, dtype, d["a"], d["b"], M, N, K)
+            assert_accepted(c, ref, dtype, (layout, dtype, M, N, K))
+        else:
+            rows, cols = sample_indices(M, 96, i), sample_indices(N, 96, i + 1)
+            ref = oracle.dense_at(layout, dtype, d["a"], d["b"], rows, cols)
+            assert_accepted(c[np.ix_(rows, cols)], ref, dtype, (layout, dtype, M, N, K))
+
+
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_pipeline_identity_is_exact(gpu_lib, layout):
+    M = N = K = 256
+    d = dense_inputs(layout, "bf16", M, N, K, seed=611, std=1.0)
+    eye = f32_to_bf16_bits(np.eye(K))
+    c = host_u16(run(gpu_lib, layout, dev(d["a"], tdtype("bf16")), dev(eye, tdtype("bf16"))))
+    assert np.array_equal(c, d["a"] if layout != "TN" else d["a"].T)
+
+
 @pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
 def test_identity_is_exact(gpu_lib, layout):
     M = N = K = 136
