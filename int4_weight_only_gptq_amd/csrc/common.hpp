@@ -27,12 +27,25 @@ constexpr uint32_t kBias128x2 = 0x43004300u;
 // (128 + q_t, 128 + q_{t+4}), t = 0..3.  The k order inside the MFMA operand is
 // therefore 0,4,1,5,2,6,3,7; the activation operand uses the same order
 // (see x_pairs_permuted), so the contraction over k is unchanged.
+//
+// The mask and the bias are passed through an empty asm so that they sit in
+// VGPRs: a VOP3 instruction takes no literal on gfx9, and with both as
+// literals the compiler emits an AND and an OR per dword instead of one
+// v_and_or_b32.  (No instruction is written in asm: the compiler's hazard
+// tracking does not see inside asm, and an asm VALU write can race an MFMA
+// still writing the same register.)
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
 __device__ __forceinline__ u32x4 codes_as_bf16_pairs(uint32_t w) {
+  const uint32_t mask = in_vgpr(0x000F000Fu), bias = in_vgpr(kBias128x2);
   u32x4 r;
-  r[0] = (w & 0x000F000Fu) | kBias128x2;
-  r[1] = ((w >> 4) & 0x000F000Fu) | kBias128x2;
-  r[2] = ((w >> 8) & 0x000F000Fu) | kBias128x2;
-  r[3] = ((w >> 12) & 0x000F000Fu) | kBias128x2;
+  r[0] = (w & mask) | bias;
+  r[1] = ((w >> 4) & mask) | bias;
+  r[2] = ((w >> 8) & mask) | bias;
+  r[3] = ((w >> 12) & mask) | bias;
   return r;
 }
 
@@ -89,5 +102,15 @@ __device__ __forceinline__ float sum_over_rows(float v) {
   auto p16 = __builtin_amdgcn_permlane16_swap(us, us, false, false);
   return __builtin_bit_cast(float, (uint32_t)p16[0]) + __builtin_bit_cast(float, (uint32_t)p16[1]);
 }
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding and ignores the other counters (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// Slot of 16-byte chunk c (8 bf16 of k) of row r in a K-contiguous LDS tile of
+// 8 chunks per row: the XOR spreads the 16 rows one MFMA operand read touches
+// over distinct banks.
+__device__ __forceinline__ int swz(int r, int c) { return 8 * r + (c ^ (r & 7)); }
 
 }  // namespace qg

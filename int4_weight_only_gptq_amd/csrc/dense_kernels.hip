@@ -19,11 +19,6 @@ namespace qg {
 constexpr int DBK = 64;
 constexpr int DSTRIDE = DBK + 8;   // 16-bit elements per LDS row (144 bytes)
 
-// s_waitcnt immediate that waits until at most n vector-memory operations are
-// outstanding and ignores the other counters (gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
 // 8 x 8 transpose of 16-bit elements: in[r] holds row r (8 elements), out[j]
 // receives column j = (in[0][j], in[1][j], ..., in[7][j]).
 __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
@@ -230,7 +225,6 @@ __global__ __launch_bounds__(256) void dense_tile_kernel(const uint16_t* __restr
 //    touches two to a bank slot (the minimum for 512 bytes).
 // Rows or columns past M or N load a clamped valid address; their results
 // are discarded.
-__device__ __forceinline__ int swz(int r, int c) { return 8 * r + (c ^ (r & 7)); }
 __device__ __forceinline__ int fmn(int k) { return 2 * ((k & 3) | ((k >> 1) & 4)); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));

@@ -1,5 +1,5 @@
 // int4 GPTQ kernels for gfx950: dequant, the m = 1 GEMV, the fused small-M
-// kernel and the LDS-tiled MFMA kernel.
+// kernel and the pipelined MFMA kernel for larger m.
 //
 // Storage (GPTQ-Int4, group size 128): qweight uint32 [k/8][n] with row 8r+t
 // of column j in bits 4t..4t+3 of word (r, j); qzeros uint32 [k/128][n/8] with
@@ -72,28 +72,6 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[CPL]
   } else {
     w[0] = *p;
   }
-}
-
-// Scales of CPL consecutive columns (fp32) and their zero points plus 128.
-template <int CPL>
-__device__ __forceinline__ void load_group_meta(const uint16_t* __restrict__ scales,
-                                                const uint32_t* __restrict__ qzeros, int64_t n,
-                                                int64_t g, int64_t col, float (&s)[CPL],
-                                                float (&bz)[CPL]) {
-  const uint16_t* sp = scales + g * n + col;
-  if constexpr (CPL == 4) {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(sp);
-    s[0] = half_bits_to_float(v[0] & 0xFFFFu); s[1] = half_bits_to_float(v[0] >> 16);
-    s[2] = half_bits_to_float(v[1] & 0xFFFFu); s[3] = half_bits_to_float(v[1] >> 16);
-  } else if constexpr (CPL == 2) {
-    const uint32_t v = *reinterpret_cast<const uint32_t*>(sp);
-    s[0] = half_bits_to_float(v & 0xFFFFu); s[1] = half_bits_to_float(v >> 16);
-  } else {
-    s[0] = half_bits_to_float(*sp);
-  }
-  const uint32_t zw = qzeros[g * (n >> 3) + (col >> 3)] >> ((col & 7) * 4);
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) bz[c] = (float)(128u + ((zw >> (4 * c)) & 15u));
 }
 
 // Raw group metadata of CPL consecutive columns: their fp16 scales and the
@@ -370,144 +348,225 @@ __global__ __launch_bounds__(1024) void skinny_int4_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// LDS-tiled MFMA kernel for m > 16.  Workgroup tile 128 tokens x 128 columns,
-// four waves in 2 x 2 (64 x 64 each, 4 x 4 MFMA tiles of 16 x 16).  One k group
-// (128 rows) per iteration: the activation tile (128 x 128 bf16, stored in
-// the permuted pair order) and the packed words (16 x 128) are staged in LDS;
-// the next group's global loads are in flight while the current one computes.
-// Each wave turns its words into bf16 B operands itself; the per-token group
-// sums come from v_dot2 on the A operands it already holds.
+// Pipelined MFMA kernel for m > 16.
+//
+// Workgroup tile BM x BN = (NWM * 16 * FM) tokens x (NWN * 64) columns; wave
+// (wm, wn) owns 16 * FM tokens x 64 columns as FM x 4 MFMA tiles of 16 x 16.
+// Within a wave's 64 columns, N-fragment c holds columns 4 * l + c (l = lane
+// % 16), so one 16-byte LDS read gives a lane the words of its four columns and
+// the output of four adjacent columns lands in one lane.
+//
+// The k loop walks stages of 64 rows (half a quantization group).  Each stage
+// is copied global -> LDS with direct loads (global_load_lds, no register
+// round trip), STAGES deep:
+//   activations  BM x 64 bf16, K-contiguous, XOR-swizzled 16-byte chunks
+//   codes        8 word rows x BN columns (the qweight words of those 64 rows)
+//   metadata     the group's BN fp16 scales and BN / 8 zero words
+// The oldest stage is consumed once the wave's vmcnt shows its loads landed
+// and a plain s_barrier shows every wave is past the previous stage.
+//
+// Per 32-row k step a wave turns each column's word into the bf16 pairs
+// 128 + q (codes_as_bf16_pairs), reorders its activation fragments to the
+// same pair order, and accumulates; a ones-MFMA on the raw activation
+// fragments gives the per-token group sums in the accumulator layout.  After
+// both stages of a group: total += s * (acc - (128 + z) * sum_x), fp32.
 // ---------------------------------------------------------------------------
-constexpr int TBM = 128, TBN = 128;
-constexpr int XS_STRIDE = 128 + 8;   // bf16 per LDS row of the activation tile
-constexpr int WS_STRIDE = 128 + 4;   // words per LDS row of the code tile
+template <int NWM, int NWN, int FM>
+struct PipeShape {
+  static constexpr int T = 64 * NWM * NWN;               // threads
+  static constexpr int BM = NWM * 16 * FM, BN = NWN * 64;
+  static constexpr int X_SLOTS = BM * 8;                 // 16-byte activation chunks per stage
+  static constexpr int XL = X_SLOTS / T;                 // per thread
+  static constexpr bool W16 = (2 * BN) % T == 0;         // words as 16-byte chunks, else dwords
+  static constexpr int WL = W16 ? 2 * BN / T : 8 * BN / T;
+  static constexpr int LOADS = XL + WL + 1;              // direct loads per thread per stage
+  static constexpr int X_DW = 4 * X_SLOTS, W_DW = 8 * BN, M_DW = T;
+  static constexpr int STAGE_DW = X_DW + W_DW + M_DW;    // dwords of LDS per stage
+  static constexpr int OP = BN + 8;                      // output tile row pitch (bf16)
+  static_assert(X_SLOTS % T == 0, "activation chunks per thread");
+  static_assert((8 * BN) % T == 0, "word loads per thread");
+  static_assert(T >= BN / 2 + BN / 8, "metadata slots");
+};
 
-__global__ __launch_bounds__(256) void mfma_int4_kernel(
+template <int NWM, int NWN, int FM, int STAGES>
+__global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(2))) void int4_pipe_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
-    uint16_t* __restrict__ y, int64_t ldy, int m, int n, int k, int tiles_m) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs_lds[TBM * XS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint32_t ws_lds[16 * WS_STRIDE];
+    uint16_t* __restrict__ y, int64_t ldy, int m, int n, int k, int tiles_n, int tiles,
+    int tiles_per_xcd, int vec_store) {
+  using S = PipeShape<NWM, NWN, FM>;
+  constexpr int T = S::T, BM = S::BM, BN = S::BN, XL = S::XL, WL = S::WL, LOADS = S::LOADS;
+  static_assert(LOADS * (STAGES - 2) <= 63, "vmcnt range");
+  extern __shared__ __attribute__((aligned(16))) uint32_t psm_i4[];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int t = (blockIdx.x & 7) * tiles_per_xcd + (blockIdx.x >> 3);
+  if (t >= tiles) return;
+  const int tm = t / tiles_n, tn = t - tm * tiles_n;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cl = lane & 15, ks = lane >> 4;
-  const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
-  const int m0 = tm * TBM, n0 = tn * TBN;
-  const int wm0 = (wave & 1) * 64, wn0 = (wave >> 1) * 64;
-  const int G = k >> 7;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int wm0 = (wave % NWM) * 16 * FM, wn0 = (wave / NWM) * 64;
 
-  // staging assignment: activation chunks (row, 8-wide k chunk), word chunks
-  u32x4 xreg[8];
-  u32x4 wreg[2];
-  auto load_tiles = [&](int g) {
+  // this thread's direct-load sources at stage 0
+  const uint16_t* xsrc[XL];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 4, kc = c & 15;
-      const int tok = m0 + row;
-      xreg[i] = tok < m ? *reinterpret_cast<const u32x4*>(x + (int64_t)tok * ldx + (int64_t)g * 128 + 8 * kc)
-                        : u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int i = 0; i < XL; ++i) {
+    const int slot = tid + T * i;
+    const int r = slot >> 3, c = (slot & 7) ^ (r & 7);
+    const int gr = m0 + r < m ? m0 + r : m - 1;
+    xsrc[i] = x + (int64_t)gr * ldx + 8 * c;
+  }
+  const uint32_t* wsrc[WL];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i;
-      const int wr = c >> 5, cc = c & 31;
-      const int colw = n0 + 4 * cc;
-      wreg[i] = colw < n ? *reinterpret_cast<const u32x4*>(qweight + ((int64_t)g * 16 + wr) * n + colw)
-                         : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_tiles = [&]() {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 4, kc = c & 15;
-      *reinterpret_cast<u32x4*>(&xs_lds[row * XS_STRIDE + 8 * kc]) = x_pairs_permuted(xreg[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i;
-      const int wr = c >> 5, cc = c & 31;
-      *reinterpret_cast<u32x4*>(&ws_lds[wr * WS_STRIDE + 4 * cc]) = wreg[i];
-    }
-  };
-
-  const int64_t mycol = (int64_t)n0 + wn0 + 4 * cl;   // columns mycol + c, c = 0..3
-  const bool colok = mycol < n;
-
-  f32x4 total[4][4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) total[f][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (G > 0) load_tiles(0);
-  for (int g = 0; g < G; ++g) {
-    __syncthreads();
-    store_tiles();
-    __syncthreads();
-    if (g + 1 < G) load_tiles(g + 1);
-    float sc[4], bz[4];
-    if (colok) {
-      load_group_meta<4>(scales, qzeros, n, g, mycol, sc, bz);
+  for (int i = 0; i < WL; ++i) {
+    const int slot = tid + T * i;
+    if constexpr (S::W16) {
+      const int wr = slot / (BN / 4), cc = slot % (BN / 4);
+      const int col = n0 + 4 * cc < n ? n0 + 4 * cc : n - 4;
+      wsrc[i] = qweight + (int64_t)wr * n + col;
     } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) { sc[c] = 0.f; bz[c] = 0.f; }
-    }
-
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[f][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float xsp[4] = {0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4 a[4];
-#pragma unroll
-      for (int f = 0; f < 4; ++f)
-        a[f] = *reinterpret_cast<const u32x4*>(&xs_lds[(wm0 + 16 * f + cl) * XS_STRIDE + 32 * s + 8 * ks]);
-      const u32x4 wv = *reinterpret_cast<const u32x4*>(&ws_lds[(4 * s + ks) * WS_STRIDE + wn0 + 4 * cl]);
-      u32x4 b[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) b[c] = codes_as_bf16_pairs(wv[c]);
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) xsp[f] = dot2_bf16(a[f][t], kOnesBf16x2, xsp[f]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[f][c] = mfma16_bf16(a[f], b[c], acc[f][c]);
-      }
-    }
-    // group sums per token: A rows are lane % 16, accumulator rows are 4*ks + v
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const float rs = sum_over_rows(xsp[f]);
-      float xsv[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) xsv[v] = __shfl(rs, 4 * ks + v);
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) total[f][c][v] += sc[c] * (acc[f][c][v] - bz[c] * xsv[v]);
+      const int wr = slot / BN, cw = slot % BN;
+      const int col = n0 + cw < n ? n0 + cw : n - 1;
+      wsrc[i] = qweight + (int64_t)wr * n + col;
     }
   }
+  const uint32_t* msrc;
+  int64_t mstep;   // dwords per group row
+  {
+    const int nz = n >> 3;
+    if (tid < BN / 2) {
+      const int col = n0 + 2 * tid < n ? n0 + 2 * tid : n - 2;
+      msrc = reinterpret_cast<const uint32_t*>(scales + col);
+      mstep = n >> 1;
+    } else {
+      const int j = tid < BN / 2 + BN / 8 ? tid - BN / 2 : 0;
+      const int zc = (n0 >> 3) + j < nz ? (n0 >> 3) + j : nz - 1;
+      msrc = qzeros + zc;
+      mstep = nz;
+    }
+  }
+  const int64_t wstep = 8 * (int64_t)n;   // words per stage of 64 rows
 
-  if (colok) {
+  auto issue = [&](int st) {
+    uint32_t* base = psm_i4 + (size_t)(st % STAGES) * S::STAGE_DW;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
+    for (int i = 0; i < XL; ++i)
+      __builtin_amdgcn_global_load_lds((void*)(xsrc[i] + 64 * st),
+                                       (void*)(base + 4 * (T * i + 64 * wave)), 16, 0, 0);
+    uint32_t* wbase = base + S::X_DW;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int tok = m0 + wm0 + 16 * f + 4 * ks + v;
-        if (tok < m) {
-          u32x2 o;
-          o[0] = pack_bf16x2(total[f][0][v], total[f][1][v]);
-          o[1] = pack_bf16x2(total[f][2][v], total[f][3][v]);
-          *reinterpret_cast<u32x2*>(y + (int64_t)tok * ldy + mycol) = o;
+    for (int i = 0; i < WL; ++i) {
+      if constexpr (S::W16)
+        __builtin_amdgcn_global_load_lds((void*)(wsrc[i] + wstep * st),
+                                         (void*)(wbase + 4 * (T * i + 64 * wave)), 16, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds((void*)(wsrc[i] + wstep * st),
+                                         (void*)(wbase + T * i + 64 * wave), 4, 0, 0);
+    }
+    __builtin_amdgcn_global_load_lds((void*)(msrc + mstep * (st >> 1)),
+                                     (void*)(wbase + S::W_DW + 64 * wave), 4, 0, 0);
+  };
+
+  f32x4 total[FM][4], acc[FM][4], xs[FM];
+#pragma unroll
+  for (int f = 0; f < FM; ++f)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) total[f][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4 ones = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
+
+  const int ktiles = k >> 6;
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < ktiles) issue(st);
+
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < (ktiles >> 1); ++g) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kt = 2 * g + h;
+      if (kt + STAGES - 2 < ktiles) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * (STAGES - 2)));
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      }
+      // every wave's loads of stage kt have landed and every wave has
+      // finished reading stage kt - 1, whose buffer the next issue refills
+      __builtin_amdgcn_s_barrier();
+      if (kt + STAGES - 1 < ktiles) issue(kt + STAGES - 1);
+
+      const uint32_t* st = psm_i4 + (size_t)(kt % STAGES) * S::STAGE_DW;
+      const u32x4* la = reinterpret_cast<const u32x4*>(st);
+      const uint32_t* lw = st + S::X_DW;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int ch = 4 * s + ks;   // 8-row chunk of k within the stage
+        const bool first = h == 0 && s == 0;   // first k step of the group
+        u32x4 a[FM];
+#pragma unroll
+        for (int f = 0; f < FM; ++f) a[f] = la[swz(wm0 + 16 * f + cl, ch)];
+        const u32x4 wv = *reinterpret_cast<const u32x4*>(lw + ch * BN + wn0 + 4 * cl);
+        u32x4 b[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) b[c] = codes_as_bf16_pairs(wv[c]);
+#pragma unroll
+        for (int f = 0; f < FM; ++f) {
+          xs[f] = mfma16_bf16(a[f], ones, first ? zero : xs[f]);
+          const u32x4 ap = x_pairs_permuted(a[f]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[f][c] = mfma16_bf16(ap, b[c], first ? zero : acc[f][c]);
         }
       }
+      if (h == 1) {
+        // end of group g: scale and remove the 128 + z offset
+        const uint32_t* lm = lw + S::W_DW;
+        const int col = wn0 + 4 * cl;
+        const u32x2 sv = *reinterpret_cast<const u32x2*>(lm + (col >> 1));
+        const uint32_t zw = lm[BN / 2 + (col >> 3)] >> (4 * (col & 7));
+        float sc[4], bz[4];
+        sc[0] = half_bits_to_float(sv[0] & 0xFFFFu);
+        sc[1] = half_bits_to_float(sv[0] >> 16);
+        sc[2] = half_bits_to_float(sv[1] & 0xFFFFu);
+        sc[3] = half_bits_to_float(sv[1] >> 16);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bz[c] = (float)(128u + ((zw >> (4 * c)) & 15u));
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              total[f][c][v] = __builtin_fmaf(sc[c], __builtin_fmaf(-bz[c], xs[f][v], acc[f][c][v]),
+                                              total[f][c][v]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // output tile through LDS, then 16-byte (or 8-byte) row stores
+  uint16_t* osm = reinterpret_cast<uint16_t*>(psm_i4);
+#pragma unroll
+  for (int f = 0; f < FM; ++f)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = wm0 + 16 * f + 4 * ks + v;
+      u32x2 o;
+      o[0] = pack_bf16x2(total[f][0][v], total[f][1][v]);
+      o[1] = pack_bf16x2(total[f][2][v], total[f][3][v]);
+      *reinterpret_cast<u32x2*>(&osm[row * S::OP + wn0 + 4 * cl]) = o;
+    }
+  __syncthreads();
+  constexpr int CPR = BN / 8;
+  for (int c = tid; c < BM * CPR; c += T) {
+    const int r = c / CPR, cc = c - r * CPR;
+    const int gr = m0 + r, gc = n0 + 8 * cc;
+    if (gr >= m || gc >= n) continue;
+    const uint16_t* src = &osm[r * S::OP + 8 * cc];
+    uint16_t* dst = y + (int64_t)gr * ldy + gc;
+    if (vec_store) {
+      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+    } else {
+      reinterpret_cast<u32x2*>(dst)[0] = reinterpret_cast<const u32x2*>(src)[0];
+      reinterpret_cast<u32x2*>(dst)[1] = reinterpret_cast<const u32x2*>(src)[1];
     }
   }
 }
@@ -617,13 +676,57 @@ hipError_t launch_fused_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipS
   return hipGetLastError();
 }
 
+// Launch shapes of the pipelined kernel, smallest tile first.
+struct PipeCfg {
+  int bm, bn, stages, threads;
+  size_t lds;
+};
+
+template <int NWM, int NWN, int FM, int STAGES>
+static PipeCfg pipe_cfg() {
+  using S = PipeShape<NWM, NWN, FM>;
+  size_t lds = (size_t)STAGES * S::STAGE_DW * 4;
+  const size_t out = (size_t)S::BM * S::OP * 2;
+  return PipeCfg{S::BM, S::BN, STAGES, S::T, lds > out ? lds : out};
+}
+
+#ifndef QG_PIPE_BIG_MIN_TILES
+#define QG_PIPE_BIG_MIN_TILES 256   // 256-token tiles wanted before using them
+#endif
+
+// 0: 64 x 128, 1: 128 x 128, 2: 256 x 128
+static int pick_pipe(int64_t m, int64_t n) {
+  const int64_t tn = (n + 127) / 128;
+  if (((m + 255) / 256) * tn >= QG_PIPE_BIG_MIN_TILES) return 2;
+  if (m > 64) return 1;
+  return 0;
+}
+
+static PipeCfg pipe_cfg_of(int which) {
+  switch (which) {
+    case 2: return pipe_cfg<4, 2, 4, 4>();
+    case 1: return pipe_cfg<2, 2, 4, 4>();
+    default: return pipe_cfg<1, 2, 4, 4>();
+  }
+}
+
+template <int NWM, int NWN, int FM, int STAGES>
+static void pipe_launch(const Int4Args& a, hipStream_t stream) {
+  const PipeCfg c = pipe_cfg<NWM, NWN, FM, STAGES>();
+  const int tiles_m = (int)((a.m + c.bm - 1) / c.bm), tiles_n = (int)((a.n + c.bn - 1) / c.bn);
+  const int tiles = tiles_m * tiles_n, per_xcd = (tiles + 7) / 8;
+  const int vec = ((uintptr_t)a.y & 15u) == 0 && a.ldy % 8 == 0;
+  int4_pipe_kernel<NWM, NWN, FM, STAGES><<<dim3((unsigned)(per_xcd * 8)), dim3(c.threads), c.lds, stream>>>(
+      a.x, a.ldx, a.qweight, a.scales, a.qzeros, a.y, a.ldy, (int)a.m, (int)a.n, (int)a.k, tiles_n,
+      tiles, per_xcd, vec);
+}
+
 hipError_t launch_mfma_int4(const Int4Args& a, hipStream_t stream) {
-  const int tiles_m = (int)((a.m + TBM - 1) / TBM);
-  const int tiles_n = (int)((a.n + TBN - 1) / TBN);
-  const unsigned blocks = (unsigned)tiles_m * (unsigned)tiles_n;
-  mfma_int4_kernel<<<dim3(blocks), dim3(256), 0, stream>>>(a.x, a.ldx, a.qweight, a.scales,
-                                                            a.qzeros, a.y, a.ldy, (int)a.m,
-                                                            (int)a.n, (int)a.k, tiles_m);
+  switch (pick_pipe(a.m, a.n)) {
+    case 2: pipe_launch<4, 2, 4, 4>(a, stream); break;
+    case 1: pipe_launch<2, 2, 4, 4>(a, stream); break;
+    default: pipe_launch<1, 2, 4, 4>(a, stream); break;
+  }
   return hipGetLastError();
 }
 
@@ -642,9 +745,10 @@ void describe_int4(int64_t m, int64_t n, int64_t k, int path, int64_t ws_bytes, 
              path == 1 ? 1LL : (long long)m, dot ? "dot" : "mfma", p.cpl, (long long)p.blocks,
              64 * p.waves, (long long)p.lds, p.ksplit, p.gwg);
   } else {
-    const long long tiles = ((m + TBM - 1) / TBM) * ((n + TBN - 1) / TBN);
-    snprintf(buf, len, "mfma_int4_kernel grid=%lld block=256 lds=%d", tiles,
-             (int)(TBM * XS_STRIDE * 2 + 16 * WS_STRIDE * 4));
+    const PipeCfg c = pipe_cfg_of(pick_pipe(m, n));
+    const long long tiles = ((m + c.bm - 1) / c.bm) * ((n + c.bn - 1) / c.bn);
+    snprintf(buf, len, "int4_pipe_kernel<%d,%d,%d> grid=%lld block=%d lds=%lld", c.bm, c.bn, c.stages,
+             ((tiles + 7) / 8) * 8, c.threads, (long long)c.lds);
   }
 }
 

@@ -127,8 +127,14 @@ def test_describe_names_the_dispatch(lib):
     # a long k with few strips is split: 200 groups over 16 waves -> 4 slices of 50
     assert "ksplit=4 groups=50" in qg.describe_int4(16, 5120, 25600)
     assert "ksplit=1 groups=200" in qg.describe_int4(16, 5120, 25600, workspace_bytes=0)
-    assert qg.describe_int4(17, 5120, 25600).startswith("mfma_int4_kernel")
-    assert qg.describe_int4(1, 4096, 4096, "mfma").startswith("mfma_int4_kernel")
+    # pipelined MFMA kernel: 64-token tiles for small m, 256 x 128 once there are enough of them
+    # (lds = 4 stages x (activations + words + metadata) dwords x 4 bytes)
+    assert qg.describe_int4(17, 5120, 25600) == (
+        "int4_pipe_kernel<64,128,4> grid=40 block=128 lds=%d" % (4 * (2048 + 1024 + 128) * 4))
+    assert qg.describe_int4(100, 5120, 25600).startswith("int4_pipe_kernel<128,128,4> grid=40 block=256")
+    assert qg.describe_int4(2048, 5120, 25600) == (
+        "int4_pipe_kernel<256,128,4> grid=320 block=512 lds=%d" % (4 * (8192 + 1024 + 512) * 4))
+    assert qg.describe_int4(1, 4096, 4096, "mfma").startswith("int4_pipe_kernel<64,128,4> grid=32 ")
     assert qg.describe_int4(0, 64, 128) == "none"
     assert qg.describe_int4(3, 64, 0) == "zero16_kernel"
     with pytest.raises(qg.QGemmError):
