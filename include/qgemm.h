@@ -40,7 +40,7 @@ extern "C" {
 /* Return codes (qg_status values, returned as int32_t). */
 #define QG_OK 0
 #define QG_ERR_NULL 1        /* a required pointer is NULL                         */
-#define QG_ERR_SHAPE 2       /* negative size, ld too small, k % 128 or n % 8 != 0 */
+#define QG_ERR_SHAPE 2       /* bad size or ld (see each call), k % 128, n % 8    */
 #define QG_ERR_ALIGN 3       /* a pointer or leading dimension is misaligned       */
 #define QG_ERR_DTYPE 4       /* unknown dtype code                                 */
 #define QG_ERR_LAYOUT 5      /* unknown layout code                                */
@@ -78,7 +78,7 @@ int32_t qg_last_hip_error(void);
  *   Y[r][j] = bf16_rne( sum_i X[r][i] * W[i][j] ),  accumulated in fp32,
  *   W[i][j] = (q[i][j] - z[i/128][j]) * s[i/128][j]  (exact in fp32).
  *
- *   x        bf16 [m][ldx], ldx >= k, ldx % 8 == 0, 16-byte aligned.
+ *   x        bf16 [m][ldx], k <= ldx <= 2^22, ldx % 8 == 0, 16-byte aligned.
  *   qweight  uint32 [k/8][n], 16-byte aligned.  Word (r, j) holds the 4-bit
  *            codes of rows 8r..8r+7 of output column j; row 8r+t is in bits
  *            4t..4t+3 (least significant nibble first).
@@ -87,8 +87,8 @@ int32_t qg_last_hip_error(void);
  *            zero points of columns 8c..8c+7; column 8c+t in bits 4t..4t+3.
  *            The stored nibble is z itself (no +1 offset).
  *   y        bf16 [m][ldy] output, ldy >= n, ldy % 4 == 0, 8-byte aligned.
- *   m >= 0 tokens, n >= 0 output columns (n % 8 == 0), k >= 0 input rows
- *   (k % 128 == 0), group_size must be 128.
+ *   m >= 0 tokens, 0 <= n <= 2^26 output columns (n % 8 == 0), 0 <= k <= 2^22
+ *   input rows (k % 128 == 0), group_size must be 128.
  *   workspace, workspace_bytes
  *            optional device scratch (16-byte aligned) that lets the m <= 16
  *            paths split k over several workgroups; qgemm_int4_workspace_size

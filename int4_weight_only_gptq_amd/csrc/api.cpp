@@ -26,15 +26,16 @@ int32_t check_int4(const void* x, int64_t ldx, const uint32_t* qweight, const ui
   if (m < 0 || n < 0 || k < 0) return QG_ERR_SHAPE;
   if (group_size != 128) return QG_ERR_UNSUPPORTED;
   if (k % 128 != 0 || n % 8 != 0) return QG_ERR_SHAPE;
-  // the kernels index with 32-bit column and row counts
-  if (n > (int64_t)1 << 30 || k > (int64_t)1 << 30) return QG_ERR_SHAPE;
+  // the kernels address a stage of activations and codes with 32-bit byte
+  // offsets: 256 rows of x (ldx <= 2^22) and 8 word rows of qweight (n <= 2^26)
+  if (n > (int64_t)1 << 26 || k > (int64_t)1 << 22) return QG_ERR_SHAPE;
   if (m == 0 || n == 0) return QG_OK;
   if (y == nullptr) return QG_ERR_NULL;
   if (ldy < n) return QG_ERR_SHAPE;
   if (!aligned(y, 8) || ldy % 4 != 0) return QG_ERR_ALIGN;
   if (k == 0) return QG_OK;
   if (x == nullptr || qweight == nullptr || scales == nullptr || qzeros == nullptr) return QG_ERR_NULL;
-  if (ldx < k) return QG_ERR_SHAPE;
+  if (ldx < k || ldx > (int64_t)1 << 22) return QG_ERR_SHAPE;
   if (!aligned(x, 16) || ldx % 8 != 0) return QG_ERR_ALIGN;
   if (!aligned(qweight, 16) || !aligned(scales, 8) || !aligned(qzeros, 4)) return QG_ERR_ALIGN;
   return QG_OK;

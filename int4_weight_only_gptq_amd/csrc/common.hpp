@@ -113,4 +113,36 @@ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4
 // over distinct banks.
 __device__ __forceinline__ int swz(int r, int c) { return 8 * r + (c ^ (r & 7)); }
 
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// also wait for every direct global->LDS load in flight).  The empty asm with a
+// memory clobber keeps the compiler from moving LDS reads or writes across it:
+// the s_barrier builtin itself is not a memory operation to the compiler.
+// Visibility of another wave's direct loads is the caller's job: each wave
+// waits for its own loads (vmcnt) before the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct global -> LDS copy through a raw buffer resource on `base`: 16 or 4
+// bytes per lane from base + voff into lds + lane * bytes (lds is the wave's
+// base slot; the hardware adds the lane offset).  The resource covers 2^32 - 1
+// bytes from base, so voff must stay below 4 GiB; the resource is formed in
+// SGPRs from a wave-uniform base.  The bodies exist only in the device pass:
+// the host pass cannot form buffer resources or address-space-3 pointers.
+__device__ __forceinline__ void buffer_to_lds16(const void* base, uint32_t voff, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, -1, 0x00020000),
+                                           (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+#endif
+}
+
+__device__ __forceinline__ void buffer_to_lds4(const void* base, uint32_t voff, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, -1, 0x00020000),
+                                           (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
+#endif
+}
+
 }  // namespace qg

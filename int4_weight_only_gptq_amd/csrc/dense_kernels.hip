@@ -335,7 +335,7 @@ __global__ __launch_bounds__(256) void dense_pipe_kernel(
     // every wave has waited for its own loads of stage kt, and has finished
     // reading stage kt-1 (whose buffer the next issue refills): a plain
     // barrier suffices (a fenced one would drain all stages in flight)
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
     if (kt + STAGES - 1 < ktiles) {
       const int st = kt + STAGES - 1;
       u32x4* base = psm + (size_t)(st % STAGES) * STAGE;

@@ -357,7 +357,7 @@ __global__ __launch_bounds__(1024) void skinny_int4_kernel(
 // the output of four adjacent columns lands in one lane.
 //
 // The k loop walks stages of 64 rows (half a quantization group).  Each stage
-// is copied global -> LDS with direct loads (global_load_lds, no register
+// is copied global -> LDS with direct buffer loads (no register
 // round trip), STAGES deep:
 //   activations  BM x 64 bf16, K-contiguous, XOR-swizzled 16-byte chunks
 //   codes        8 word rows x BN columns (the qweight words of those 64 rows)
@@ -385,7 +385,7 @@ struct PipeShape {
   static constexpr int OP = BN + 8;                      // output tile row pitch (bf16)
   static_assert(X_SLOTS % T == 0, "activation chunks per thread");
   static_assert((8 * BN) % T == 0, "word loads per thread");
-  static_assert(T >= BN / 2 + BN / 8, "metadata slots");
+  static_assert(BN == 128 && T >= 128, "metadata: one wave of scales, one of zero words");
 };
 
 template <int NWM, int NWN, int FM, int STAGES>
@@ -402,69 +402,64 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
   const int t = (blockIdx.x & 7) * tiles_per_xcd + (blockIdx.x >> 3);
   if (t >= tiles) return;
   const int tm = t / tiles_n, tn = t - tm * tiles_n;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases stay scalar
   const int cl = lane & 15, ks = lane >> 4;
   const int m0 = tm * BM, n0 = tn * BN;
   const int wm0 = (wave % NWM) * 16 * FM, wn0 = (wave / NWM) * 64;
 
-  // this thread's direct-load sources at stage 0
-  const uint16_t* xsrc[XL];
+  // Direct loads go through buffer resources (base in SGPRs, rebased per
+  // stage) with one fixed 32-bit byte offset per lane and load, so a stage's
+  // issue costs no vector ALU work.  Rows past m and columns past n load a
+  // clamped valid address; their results are discarded.
+  uint32_t xoff[XL];
 #pragma unroll
   for (int i = 0; i < XL; ++i) {
     const int slot = tid + T * i;
     const int r = slot >> 3, c = (slot & 7) ^ (r & 7);
-    const int gr = m0 + r < m ? m0 + r : m - 1;
-    xsrc[i] = x + (int64_t)gr * ldx + 8 * c;
+    const int rl = m0 + r < m ? r : m - 1 - m0;
+    xoff[i] = (uint32_t)(((int64_t)rl * ldx + 8 * c) * 2);
   }
-  const uint32_t* wsrc[WL];
+  uint32_t woff[WL];
 #pragma unroll
   for (int i = 0; i < WL; ++i) {
     const int slot = tid + T * i;
+    int wr, cw;
     if constexpr (S::W16) {
-      const int wr = slot / (BN / 4), cc = slot % (BN / 4);
-      const int col = n0 + 4 * cc < n ? n0 + 4 * cc : n - 4;
-      wsrc[i] = qweight + (int64_t)wr * n + col;
+      wr = slot / (BN / 4);
+      cw = n0 + 4 * (slot % (BN / 4)) < n ? 4 * (slot % (BN / 4)) : n - 4 - n0;
     } else {
-      const int wr = slot / BN, cw = slot % BN;
-      const int col = n0 + cw < n ? n0 + cw : n - 1;
-      wsrc[i] = qweight + (int64_t)wr * n + col;
+      wr = slot / BN;
+      cw = n0 + slot % BN < n ? slot % BN : n - 1 - n0;
     }
+    woff[i] = (uint32_t)(((int64_t)wr * n + cw) * 4);
   }
-  const uint32_t* msrc;
-  int64_t mstep;   // dwords per group row
-  {
-    const int nz = n >> 3;
-    if (tid < BN / 2) {
-      const int col = n0 + 2 * tid < n ? n0 + 2 * tid : n - 2;
-      msrc = reinterpret_cast<const uint32_t*>(scales + col);
-      mstep = n >> 1;
-    } else {
-      const int j = tid < BN / 2 + BN / 8 ? tid - BN / 2 : 0;
-      const int zc = (n0 >> 3) + j < nz ? (n0 >> 3) + j : nz - 1;
-      msrc = qzeros + zc;
-      mstep = nz;
-    }
+  // metadata: wave 0 loads the group's BN scales (BN / 2 dwords), every other
+  // wave the BN / 8 zero words (only wave 1's land where they are read)
+  uint32_t moff;
+  if (wave == 0) {
+    moff = (uint32_t)((n0 + 2 * lane < n ? 2 * lane : n - 2 - n0) * 2);
+  } else {
+    moff = (uint32_t)(((n0 >> 3) + lane < (n >> 3) ? lane : (n >> 3) - 1 - (n0 >> 3)) * 4);
   }
-  const int64_t wstep = 8 * (int64_t)n;   // words per stage of 64 rows
+  const uint16_t* xbase = x + (int64_t)m0 * ldx;
+  const uint32_t* wbase0 = qweight + n0;
 
   auto issue = [&](int st) {
     uint32_t* base = psm_i4 + (size_t)(st % STAGES) * S::STAGE_DW;
+    const uint16_t* xs_base = xbase + 64 * (int64_t)st;
 #pragma unroll
-    for (int i = 0; i < XL; ++i)
-      __builtin_amdgcn_global_load_lds((void*)(xsrc[i] + 64 * st),
-                                       (void*)(base + 4 * (T * i + 64 * wave)), 16, 0, 0);
-    uint32_t* wbase = base + S::X_DW;
+    for (int i = 0; i < XL; ++i) buffer_to_lds16(xs_base, xoff[i], base + 4 * (T * i + 64 * wave));
+    uint32_t* wl = base + S::X_DW;
+    const uint32_t* ws_base = wbase0 + 8 * (int64_t)st * n;
 #pragma unroll
     for (int i = 0; i < WL; ++i) {
-      if constexpr (S::W16)
-        __builtin_amdgcn_global_load_lds((void*)(wsrc[i] + wstep * st),
-                                         (void*)(wbase + 4 * (T * i + 64 * wave)), 16, 0, 0);
-      else
-        __builtin_amdgcn_global_load_lds((void*)(wsrc[i] + wstep * st),
-                                         (void*)(wbase + T * i + 64 * wave), 4, 0, 0);
+      if constexpr (S::W16) buffer_to_lds16(ws_base, woff[i], wl + 4 * (T * i + 64 * wave));
+      else buffer_to_lds4(ws_base, woff[i], wl + T * i + 64 * wave);
     }
-    __builtin_amdgcn_global_load_lds((void*)(msrc + mstep * (st >> 1)),
-                                     (void*)(wbase + S::W_DW + 64 * wave), 4, 0, 0);
+    const int64_t g = st >> 1;
+    buffer_to_lds4(wave == 0 ? (const void*)(scales + g * n + n0) : (const void*)(qzeros + g * (n >> 3) + (n0 >> 3)),
+                   moff, wl + S::W_DW + 64 * wave);
   };
 
   f32x4 total[FM][4], acc[FM][4], xs[FM];
@@ -475,60 +470,83 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
   const u32x4 ones = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
 
   const int ktiles = k >> 6;
+  // raw fragments of one k step: FM activation chunks and one 16-byte word read
+  u32x4 fa[FM], fw;
+  auto read_step = [&](int kt, int s) {
+    const uint32_t* st = psm_i4 + (size_t)(kt % STAGES) * S::STAGE_DW;
+    const u32x4* la = reinterpret_cast<const u32x4*>(st);
 #pragma unroll
-  for (int st = 0; st < STAGES - 1; ++st)
+    for (int f = 0; f < FM; ++f) fa[f] = la[swz(wm0 + 16 * f + cl, 4 * s + ks)];
+    fw = *reinterpret_cast<const u32x4*>(st + S::X_DW + (4 * s + ks) * BN + wn0 + 4 * cl);
+  };
+
+  // all STAGES buffers start filling; stage 0 must land before the first read
+#pragma unroll
+  for (int st = 0; st < STAGES; ++st)
     if (st < ktiles) issue(st);
+  if (ktiles >= STAGES) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * (STAGES - 1)));
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+  lds_barrier();
+  read_step(0, 0);
 
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   for (int g = 0; g < (ktiles >> 1); ++g) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int kt = 2 * g + h;
-      if (kt + STAGES - 2 < ktiles) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * (STAGES - 2)));
-      } else {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      }
-      // every wave's loads of stage kt have landed and every wave has
-      // finished reading stage kt - 1, whose buffer the next issue refills
-      __builtin_amdgcn_s_barrier();
-      if (kt + STAGES - 1 < ktiles) issue(kt + STAGES - 1);
-
-      const uint32_t* st = psm_i4 + (size_t)(kt % STAGES) * S::STAGE_DW;
-      const u32x4* la = reinterpret_cast<const u32x4*>(st);
-      const uint32_t* lw = st + S::X_DW;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const int ch = 4 * s + ks;   // 8-row chunk of k within the stage
+        // reorder / decode this step's fragments (their LDS reads were issued
+        // one step earlier, under the previous step's MFMAs)
+        u32x4 ap[FM], b[4];
+#pragma unroll
+        for (int f = 0; f < FM; ++f) ap[f] = x_pairs_permuted(fa[f]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) b[c] = codes_as_bf16_pairs(fw[c]);
+        if (s == 0) read_step(kt, 1);
         const bool first = h == 0 && s == 0;   // first k step of the group
-        u32x4 a[FM];
-#pragma unroll
-        for (int f = 0; f < FM; ++f) a[f] = la[swz(wm0 + 16 * f + cl, ch)];
-        const u32x4 wv = *reinterpret_cast<const u32x4*>(lw + ch * BN + wn0 + 4 * cl);
-        u32x4 b[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) b[c] = codes_as_bf16_pairs(wv[c]);
+        // the ones-MFMA sums the reordered activations; a sum's order does not matter
 #pragma unroll
         for (int f = 0; f < FM; ++f) {
-          xs[f] = mfma16_bf16(a[f], ones, first ? zero : xs[f]);
-          const u32x4 ap = x_pairs_permuted(a[f]);
+          xs[f] = mfma16_bf16(ap[f], ones, first ? zero : xs[f]);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) acc[f][c] = mfma16_bf16(ap, b[c], first ? zero : acc[f][c]);
+          for (int c = 0; c < 4; ++c) acc[f][c] = mfma16_bf16(ap[f], b[c], first ? zero : acc[f][c]);
         }
       }
+      // the group's scales and zeros, read while stage kt is still ours
+      float sc[4], bz[4];
       if (h == 1) {
-        // end of group g: scale and remove the 128 + z offset
-        const uint32_t* lm = lw + S::W_DW;
+        const uint32_t* lm = psm_i4 + (size_t)(kt % STAGES) * S::STAGE_DW + S::X_DW + S::W_DW;
         const int col = wn0 + 4 * cl;
         const u32x2 sv = *reinterpret_cast<const u32x2*>(lm + (col >> 1));
         const uint32_t zw = lm[BN / 2 + (col >> 3)] >> (4 * (col & 7));
-        float sc[4], bz[4];
         sc[0] = half_bits_to_float(sv[0] & 0xFFFFu);
         sc[1] = half_bits_to_float(sv[0] >> 16);
         sc[2] = half_bits_to_float(sv[1] & 0xFFFFu);
         sc[3] = half_bits_to_float(sv[1] >> 16);
 #pragma unroll
         for (int c = 0; c < 4; ++c) bz[c] = (float)(128u + ((zw >> (4 * c)) & 15u));
+      }
+      // Stage kt is fully read (fragments and metadata sit in registers).  With
+      // the MFMAs above in flight: wait for this wave's loads of stage kt + 1,
+      // meet the other waves (after which every wave is done with stage kt and
+      // all of stage kt + 1 has landed), refill stage kt's buffer with stage
+      // kt + STAGES and read the first fragments of stage kt + 1.
+      if (kt + 1 < ktiles) {
+        if (kt + STAGES - 1 < ktiles) {
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * (STAGES - 2)));
+        } else {
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+        lds_barrier();
+        if (kt + STAGES < ktiles) issue(kt + STAGES);
+        read_step(kt + 1, 0);
+      }
+      if (h == 1) {
+        // end of group g: scale and remove the 128 + z offset
 #pragma unroll
         for (int f = 0; f < FM; ++f)
 #pragma unroll

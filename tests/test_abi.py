@@ -81,6 +81,9 @@ def int4(lib, x=A16, ldx=256, qw=A16, sc=A16, qz=A16, y=A16, ldy=64, m=1, n=64, 
     (dict(ldy=66), ALIGN),
     (dict(path=1, m=2), UNSUP), (dict(path=2, m=17), UNSUP), (dict(path=9), UNSUP),
     (dict(ws=A16 + 8, wsb=1024), ALIGN), (dict(wsb=-1), SHAPE),
+    # 32-bit stage offsets: ldx and k at most 2^22, n at most 2^26
+    (dict(ldx=(1 << 22) + 8), SHAPE), (dict(k=(1 << 22) + 128, ldx=(1 << 22) + 128), SHAPE),
+    (dict(n=(1 << 26) + 8, ldy=(1 << 26) + 8), SHAPE),
 ])
 def test_int4_rejects_invalid_arguments(lib, kw, code):
     assert int4(lib, **kw) == code
