@@ -401,6 +401,230 @@ __global__ __launch_bounds__(256) void dense_pipe_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Products with one output dimension of at most 16 (the rank-16 LoRA factors:
+// C[t][16] = X . A_l^T, dU = dY . B_l, dB_l = dY^T . U, dA_l = dU^T . X).
+// They stream one large operand once and are bound by HBM, so the kernel is
+// built for bytes in flight, not for MFMA throughput: one workgroup owns a
+// 16 x 16 output tile, its W waves take interleaved 32-row k steps (U of
+// them per round, all loads issued before any MFMA), and the W partial
+// tiles are summed through LDS at the end.
+//
+// A K-contiguous operand (A of NT and NN, B of NT) is loaded straight into
+// the MFMA fragment (lane: row l % 16, 8 consecutive k).  An M/N-contiguous
+// one (B of NN and TN, A of TN) is loaded as 32 k-rows x 16 columns (64
+// lanes x 16 bytes) into a wave-private LDS buffer and read back transposed
+// with ds_read_b64_tr_b16 (two reads of 4 k-rows each); no barrier is needed
+// since only the wave itself touches its buffer.
+// ---------------------------------------------------------------------------
+constexpr int SK_W = 16;
+
+// 8 consecutive k (kb .. kb+7) of column j (0..15) from a wave buffer of
+// 32 k-rows x 16 columns (k-row k at chunks 2k, 2k+1).
+__device__ __forceinline__ u32x4 read16_frag(const u32x4* buf, int kb, int lane) {
+  const int j = lane & 15, r = j >> 2, q = j & 3;
+  const uint16_t* h1 = reinterpret_cast<const uint16_t*>(buf + 2 * (kb + r) + (q >> 1)) + 4 * (q & 1);
+  const uint16_t* h2 = reinterpret_cast<const uint16_t*>(buf + 2 * (kb + 4 + r) + (q >> 1)) + 4 * (q & 1);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(h1));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(h2));
+  u32x4 out;
+  out[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+  out[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+  out[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+  out[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+  return out;
+}
+
+// Raw 16 bytes of operand P for k step k0: a fragment (K-contiguous: row
+// r0 + l % 16, k0 + 8 (l / 16)) or a staging chunk (MN-contiguous: k-row
+// k0 + l / 2, columns r0 + 8 (l % 2)).  Past K: zeros (they enter the sum);
+// past the row / column count: a clamped valid address (result discarded).
+template <bool MN>
+__device__ __forceinline__ u32x4 load_sk(const uint16_t* __restrict__ p, int64_t ld, int rows, int K,
+                                         int r0, int k0, int lane) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  if constexpr (MN) {
+    const int kr = k0 + (lane >> 1);
+    int c = r0 + 8 * (lane & 1);
+    if (c >= rows) c = r0;                 // a whole chunk past the end (rows % 8 == 0)
+    return kr < K ? *reinterpret_cast<const u32x4*>(p + (int64_t)kr * ld + c) : z;
+  } else {
+    const int r = r0 + (lane & 15) < rows ? r0 + (lane & 15) : rows - 1;
+    const int kc = k0 + 8 * (lane >> 4);
+    return kc < K ? *reinterpret_cast<const u32x4*>(p + (int64_t)r * ld + kc) : z;
+  }
+}
+
+// U k steps per round per wave: 4 when at most one operand is staged, 2 when
+// both are (TN), so that the LDS of two workgroups fits on a CU.
+template <int LAYOUT, int DTYPE>
+__global__ __launch_bounds__(64 * SK_W) void dense_splitk16_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+    uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_n, int tiles,
+    int tiles_per_xcd) {
+  constexpr bool A_MN = (LAYOUT == 2), B_MN = (LAYOUT != 0);
+  constexpr int U = (A_MN && B_MN) ? 2 : 4;
+  constexpr int NSTAGED = (A_MN ? 1 : 0) + (B_MN ? 1 : 0);
+  constexpr int STAGE_CHUNKS = SK_W * U * 64 * NSTAGED;   // 16-byte chunks
+  constexpr int RED_CHUNKS = SK_W * 64;                    // f32x4 partial tiles
+  __shared__ u32x4 smem[STAGE_CHUNKS > RED_CHUNKS ? STAGE_CHUNKS : RED_CHUNKS];
+  // consecutive tiles (adjacent 16-wide strips) run on one XCD and share its L2
+  const int t = (blockIdx.x & 7) * tiles_per_xcd + (blockIdx.x >> 3);
+  if (t >= tiles) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i0 = (t / tiles_n) * 16, j0 = (t % tiles_n) * 16;
+  const int ksteps = (K + 31) >> 5;
+  u32x4* sa = smem + (size_t)wave * U * 64 * NSTAGED;   // this wave's staging buffers
+  u32x4* sb = sa + (A_MN ? U * 64 : 0);
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = wave; s0 < ksteps; s0 += SK_W * U) {
+    u32x4 ra[U], rb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k0 = 32 * (s0 + SK_W * u);   // past K loads zeros
+      ra[u] = load_sk<A_MN>(A, lda, M, K, i0, k0, lane);
+      rb[u] = load_sk<B_MN>(B, ldb, N, K, j0, k0, lane);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if constexpr (A_MN) sa[64 * u + lane] = ra[u];
+      if constexpr (B_MN) sb[64 * u + lane] = rb[u];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kb = 8 * (lane >> 4);
+      const u32x4 a = A_MN ? read16_frag(sa + 64 * u, kb, lane) : ra[u];
+      const u32x4 b = B_MN ? read16_frag(sb + 64 * u, kb, lane) : rb[u];
+      acc = DTYPE == 0 ? mfma16_bf16(a, b, acc) : mfma16_f16(a, b, acc);
+    }
+  }
+  f32x4* red = reinterpret_cast<f32x4*>(smem);
+  __syncthreads();   // staging buffers are reused for the partial tiles
+  red[wave * 64 + lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4 tot = red[lane];
+#pragma unroll
+    for (int w = 1; w < SK_W; ++w) tot += red[w * 64 + lane];
+    const int col = j0 + (lane & 15);
+    if (col < N) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = i0 + 4 * (lane >> 4) + v;
+        if (row < M) {
+          uint16_t h;
+          if constexpr (DTYPE == 0) h = (uint16_t)f32_to_bf16_bits(tot[v]);
+          else h = __builtin_bit_cast(uint16_t, (_Float16)tot[v]);
+          C[(int64_t)row * ldc + col] = h;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Products with K <= 32 (Y += U . B_l^T and dX += dU . A_l of a rank-16
+// adapter): a rank-K outer product whose cost is writing C.  Each wave owns a
+// 64 x 64 tile of C and does one k step of 16 MFMAs; N-fragment c of a 64-column
+// block holds columns 4 * l + c (l = lane % 16), so a lane ends with 4
+// adjacent columns of 16 rows and 16 lanes store one 128-byte row segment.
+// A (K-contiguous) and NT's B load straight into fragments; NN's B ([K][N])
+// is staged per wave (K rows x 64 columns) and read back transposed.
+// ---------------------------------------------------------------------------
+template <int LAYOUT, int DTYPE>
+__global__ __launch_bounds__(256) void dense_smallk_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+    uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_n, int tiles,
+    int tiles_per_xcd, int vec_store) {
+  constexpr bool B_MN = (LAYOUT == 1);
+  __shared__ u32x4 bstage[B_MN ? 4 * 256 : 1];   // per wave: 32 k-rows x 64 columns
+  const int t = (blockIdx.x & 7) * tiles_per_xcd + (blockIdx.x >> 3);
+  if (t >= tiles) return;
+  const int lane = threadIdx.x & 63, cl = lane & 15, ks = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m0 = (t / tiles_n) * 64, n0 = (t % tiles_n) * 256 + 64 * wave;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+
+  u32x4 a[4], b[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int r = m0 + 16 * f + cl < M ? m0 + 16 * f + cl : M - 1;
+    a[f] = 8 * ks < K ? *reinterpret_cast<const u32x4*>(A + (int64_t)r * lda + 8 * ks) : z;
+  }
+  if constexpr (!B_MN) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int col = n0 + 4 * cl + c < N ? n0 + 4 * cl + c : N - 1;
+      b[c] = 8 * ks < K ? *reinterpret_cast<const u32x4*>(B + (int64_t)col * ldb + 8 * ks) : z;
+    }
+  } else {
+    // Stage rows k of B[k][n0 .. n0+63] with the columns reordered so that
+    // position 16 (col % 4) + col / 4 holds column col: fragment c's columns
+    // 4 l + c then sit at positions 16 c .. 16 c + 15.  A 16-byte chunk of
+    // columns 8 ch .. 8 ch + 7 becomes the pairs (x_e, x_{e+4}), e = 0..3, at
+    // positions 16 e + 2 ch (+1).  Past K zeros, past N a clamped chunk.
+    uint32_t* buf = reinterpret_cast<uint32_t*>(bstage + 256 * wave);   // 32 rows x 32 dwords
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int kr = 8 * p + (lane >> 3), ch = lane & 7;
+      int c0 = n0 + 8 * ch;
+      if (c0 >= N) c0 = N - 8;
+      const u32x4 v = kr < K ? *reinterpret_cast<const u32x4*>(B + (int64_t)kr * ldb + c0) : z;
+      const u32x4 pv = x_pairs_permuted(v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) buf[32 * kr + 8 * e + ch] = pv[e];
+    }
+    // fragment c: 8 consecutive k of position 16 c + (lane % 16), two
+    // transposing reads of 4 k-rows each (lane 4 r + q addresses row r,
+    // positions 4 q .. 4 q + 3 of the 16)
+    const uint16_t* hb = reinterpret_cast<const uint16_t*>(buf);
+    const int r = cl >> 2, q = cl & 3;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(hb + (8 * ks + r) * 64 + 16 * c + 4 * q));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(hb + (8 * ks + 4 + r) * 64 + 16 * c + 4 * q));
+      b[c][0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+      b[c][1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+      b[c][2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+      b[c][3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+    }
+  }
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      acc[f][c] = DTYPE == 0 ? mfma16_bf16(a[f], b[c], f32x4{0.f, 0.f, 0.f, 0.f})
+                             : mfma16_f16(a[f], b[c], f32x4{0.f, 0.f, 0.f, 0.f});
+
+  const int col = n0 + 4 * cl;
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = m0 + 16 * f + 4 * ks + v;
+      if (row >= M || col >= N) continue;
+      uint16_t h[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (DTYPE == 0) h[c] = (uint16_t)f32_to_bf16_bits(acc[f][c][v]);
+        else h[c] = __builtin_bit_cast(uint16_t, (_Float16)acc[f][c][v]);
+      }
+      uint16_t* dst = C + (int64_t)row * ldc + col;
+      if (vec_store && col + 4 <= N) {
+        u32x2 o;
+        o[0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+        o[1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+        *reinterpret_cast<u32x2*>(dst) = o;
+      } else {
+        for (int c = 0; c < 4 && col + c < N; ++c) dst[c] = h[c];
+      }
+    }
+}
+
 // Any shape, any alignment: one thread per output element, fp32 accumulation.
 template <int DTYPE>
 __device__ __forceinline__ float load_elem(const uint16_t* p) {
@@ -468,9 +692,24 @@ static void pipe_launch(const DenseArgs& a, hipStream_t stream) {
       a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, vec);
 }
 
+#ifndef QG_SPLITK16_MIN_K
+#define QG_SPLITK16_MIN_K 256     // k below which the 16 x 16 split-k tile is not worth it
+#endif
+
 template <int LAYOUT, int DTYPE>
 static void dense_dispatch(const DenseArgs& a, hipStream_t stream) {
-  if (mfma_fits(a) && a.K % DBK == 0 && a.M >= 128 && a.N >= 128) {
+  if (mfma_fits(a) && (a.M <= 16 || a.N <= 16) && a.K >= QG_SPLITK16_MIN_K) {
+    const int tiles_n = (int)((a.N + 15) / 16);
+    const int tiles = (int)(((a.M + 15) / 16) * tiles_n), per_xcd = (tiles + 7) / 8;
+    dense_splitk16_kernel<LAYOUT, DTYPE><<<dim3((unsigned)(per_xcd * 8)), dim3(64 * SK_W), 0, stream>>>(
+        a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd);
+  } else if (LAYOUT != 2 && mfma_fits(a) && a.K <= 32 && a.M >= 64 && a.N >= 256) {
+    const int tiles_n = (int)((a.N + 255) / 256);
+    const int tiles = (int)(((a.M + 63) / 64) * tiles_n), per_xcd = (tiles + 7) / 8;
+    const int vec = ((uintptr_t)a.C & 7u) == 0 && a.ldc % 4 == 0;
+    dense_smallk_kernel<LAYOUT, DTYPE><<<dim3((unsigned)(per_xcd * 8)), dim3(256), 0, stream>>>(
+        a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, vec);
+  } else if (mfma_fits(a) && a.K % DBK == 0 && a.M >= 128 && a.N >= 128) {
     const int64_t big = ((a.M + 255) / 256) * ((a.N + 127) / 128);
     if (big >= QG_DENSE_BIG_MIN_TILES) pipe_launch<LAYOUT, DTYPE, 256, 128, QG_DENSE_PIPE_STAGES>(a, stream);
     else pipe_launch<LAYOUT, DTYPE, 128, 128, 4>(a, stream);

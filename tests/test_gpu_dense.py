@@ -76,6 +76,42 @@ def test_pipeline_shapes_match_oracle(gpu_lib, layout, dtype):
             assert_accepted(c[np.ix_(rows, cols)], ref, dtype, (layout, dtype, M, N, K))
 
 
+# shapes for the 16 x 16 split-k kernel (one of M, N <= 16, K >= 256): k tails
+# inside a 32-row step, ragged 16-tiles, K not a multiple of 8 (TN only: K is
+# then a row count), and both orientations of the skinny side
+SPLITK_SHAPES = [(1000, 16, 2056), (16, 1000, 4104), (9, 24, 520), (40, 3, 1024), (24, 9, 1001),
+                 (2048, 16, 256), (16, 16, 8200)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_splitk16_shapes_match_oracle(gpu_lib, layout, dtype):
+    for i, (M, N, K) in enumerate(SPLITK_SHAPES):
+        if K % 8 and layout != "TN":
+            continue          # K is a contiguous dimension there; other kernels cover it
+        say("splitk16", layout, dtype, M, N, K)
+        d = dense_inputs(layout, dtype, M, N, K, seed=900 + i)
+        c = host_u16(run(gpu_lib, layout, dev(d["a"], tdtype(dtype)), dev(d["b"], tdtype(dtype))))
+        ref = oracle.dense(layout, dtype, d["a"], d["b"], M, N, K)
+        assert_accepted(c, ref, dtype, (layout, dtype, M, N, K))
+
+
+# shapes for the K <= 32 outer-product kernel (NT and NN, M >= 64, N >= 256):
+# ragged 64 x 256 tiles and waves past N, K below one 32-row step
+SMALLK_SHAPES = [(64, 256, 16), (100, 264, 16), (130, 520, 24), (67, 1000, 8), (200, 304, 32)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_smallk_shapes_match_oracle(gpu_lib, layout, dtype):
+    for i, (M, N, K) in enumerate(SMALLK_SHAPES):
+        say("smallk", layout, dtype, M, N, K)
+        d = dense_inputs(layout, dtype, M, N, K, seed=950 + i)
+        c = host_u16(run(gpu_lib, layout, dev(d["a"], tdtype(dtype)), dev(d["b"], tdtype(dtype))))
+        ref = oracle.dense(layout, dtype, d["a"], d["b"], M, N, K)
+        assert_accepted(c, ref, dtype, (layout, dtype, M, N, K))
+
+
 @pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
 def test_pipeline_identity_is_exact(gpu_lib, layout):
     M = N = K = 256
