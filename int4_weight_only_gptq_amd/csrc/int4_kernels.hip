@@ -131,9 +131,9 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // loads of its next group are in flight while it computes the current one.
 //
 // DOT = true (m = 1, the GEMV): per lane v_dot2_f32_bf16 on (128 + q) pairs
-// against the activation slice staged once in LDS, per-group offset
-// correction and scale per lane, then the four 16-lane rows summed with the
-// row-swap permutes.
+// against the 8 activations of its word-row (one load the 16 lanes of a row
+// share), per-group offset correction and scale per lane, then the four
+// 16-lane rows summed with the row-swap permutes.
 // DOT = false: the 16x16x32 bf16 MFMA, operand A = activations loaded per lane
 // (token = lane % 16, zero for tokens >= M), operand B = the codes of one word
 // (8 consecutive k of one column = one lane's B slice); tile c of a lane is
@@ -148,12 +148,11 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // ---------------------------------------------------------------------------
 constexpr int64_t kTicketBytes = 64 << 10;   // counters of up to 16384 strips
 constexpr int SK_MAX_SPLIT = 16;              // k-slices per strip at most
-constexpr size_t kSkinnyMaxLds = 150 << 10;    // of the 160 KiB of a gfx950 CU
 
 template <int M, bool DOT, int CPL>
 struct GroupRegs {
   uint32_t w[4][CPL];                  // codes of the 4 k-steps
-  u32x4 xa[DOT ? 1 : 4];               // MFMA: the A slices of the 4 k-steps
+  u32x4 xa[4];                         // activations of the 4 k-steps (MFMA: the A slices)
   Meta<CPL> meta;
 };
 
@@ -177,8 +176,9 @@ __device__ __forceinline__ void load_group(GroupRegs<M, DOT, CPL>& r, bool gok, 
 #pragma unroll
       for (int c = 0; c < CPL; ++c) r.w[s][c] = 0u;
     }
-    if constexpr (!DOT)
-      r.xa[s] = (gok && xrow) ? *reinterpret_cast<const u32x4*>(xp + 8 * (g * 16 + 4 * s + ks)) : zero4;
+    // MFMA: token cl's 8 k of this lane's word-row; GEMV: the one token's 8 k
+    // (the same address for the 16 lanes of a row: one broadcast load)
+    r.xa[s] = (gok && xrow) ? *reinterpret_cast<const u32x4*>(xp + 8 * (g * 16 + 4 * s + ks)) : zero4;
   }
   if (ok) {
     r.meta = load_meta<CPL>(scales, qzeros, n, g, col);
@@ -200,7 +200,6 @@ __global__ __launch_bounds__(1024) void skinny_int4_kernel(
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int nw = blockDim.x >> 6;
   float* plane = reinterpret_cast<float*>(smem);                          // [nw][M][SW]
-  u32x4* xl = reinterpret_cast<u32x4*>(smem + (size_t)nw * M * SW * 4);   // DOT: [k-slice chunks]
   __shared__ int last_flag;
 
   const int item = (blockIdx.x & 7) * items_per_xcd + (blockIdx.x >> 3);
@@ -213,9 +212,10 @@ __global__ __launch_bounds__(1024) void skinny_int4_kernel(
   const int gbeg = kslice * gwg, gend = min(G, gbeg + gwg);
   const int64_t col = (int64_t)strip * SW + CPL * cl;
   const bool live = col < n;
-  const bool xrow = cl < M;
+  // MFMA: the lane supplies token cl (zeros past M); GEMV: every lane the one token
+  const bool xrow = DOT || cl < M;
   const uint32_t* qp = qweight + (live ? col : 0);
-  const uint16_t* xp = x + (xrow ? (int64_t)cl * ldx : 0);
+  const uint16_t* xp = x + (!DOT && xrow ? (int64_t)cl * ldx : 0);
   const int zshift = (int)(col & 7) * 4;
   const u32x4 ones = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
 
@@ -223,14 +223,6 @@ __global__ __launch_bounds__(1024) void skinny_int4_kernel(
   GroupRegs<M, DOT, CPL> cur, nxt;
   int g = gbeg + wave;
   load_group<M, DOT, CPL>(cur, g < gend, live, xrow, qp, xp, scales, qzeros, n, g, col, ks);
-
-  if constexpr (DOT) {
-    // the activation row of this k-slice, in pair order, once per workgroup
-    const int chunks = (gend - gbeg) * 16;
-    for (int c = tid; c < chunks; c += blockDim.x)
-      xl[c] = x_pairs_permuted(*reinterpret_cast<const u32x4*>(x + (int64_t)gbeg * 128 + 8 * c));
-    __syncthreads();
-  }
 
   f32x4 total[CPL];
 #pragma unroll
@@ -247,7 +239,7 @@ __global__ __launch_bounds__(1024) void skinny_int4_kernel(
       float xs = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const u32x4 a = xl[(g - gbeg) * 16 + 4 * s + ks];
+        const u32x4 a = x_pairs_permuted(cur.xa[s]);
 #pragma unroll
         for (int t = 0; t < 4; ++t) xs = dot2_bf16(a[t], kOnesBf16x2, xs);
 #pragma unroll
@@ -639,7 +631,8 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes,
   const int64_t items = (int64_t)p.nstrips * p.ksplit;
   p.items_per_xcd = (int)((items + 7) / 8);
   p.blocks = (int64_t)p.items_per_xcd * 8;
-  p.lds = (size_t)p.waves * m * sw * 4 + (dot ? (size_t)gwg * 16 * 16 : 0);
+  p.lds = (size_t)p.waves * m * sw * 4;   // the wave partial plane
+  (void)dot;
   return p;
 }
 
@@ -660,13 +653,7 @@ static void skinny_launch_c(const Int4Args& a, const SkinnyPlan& p, void* ws, hi
 }
 
 hipError_t launch_gemv_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream) {
-  const SkinnyPlan p = plan_skinny(1, a.n, a.k, ws ? ws_bytes : 0, true);
-  if (p.lds <= kSkinnyMaxLds) {
-    skinny_launch_c<1, true>(a, p, ws, stream);
-  } else {
-    // the k-slice's activations do not fit in LDS: the MFMA variant needs none
-    skinny_launch_c<1, false>(a, plan_skinny(1, a.n, a.k, ws ? ws_bytes : 0, false), ws, stream);
-  }
+  skinny_launch_c<1, true>(a, plan_skinny(1, a.n, a.k, ws ? ws_bytes : 0, true), ws, stream);
   return hipGetLastError();
 }
 
@@ -756,9 +743,8 @@ int64_t workspace_int4(int64_t m, int64_t n, int64_t k, int path) {
 void describe_int4(int64_t m, int64_t n, int64_t k, int path, int64_t ws_bytes, char* buf,
                    size_t len) {
   if (path == 1 || path == 2) {
-    SkinnyPlan p = plan_skinny(path == 1 ? 1 : m, n, k, ws_bytes, path == 1);
-    const bool dot = path == 1 && p.lds <= kSkinnyMaxLds;
-    if (path == 1 && !dot) p = plan_skinny(1, n, k, ws_bytes, false);
+    const SkinnyPlan p = plan_skinny(path == 1 ? 1 : m, n, k, ws_bytes, path == 1);
+    const bool dot = path == 1;
     snprintf(buf, len, "skinny_int4_kernel<%lld,%s,%d> grid=%lld block=%d lds=%lld ksplit=%d groups=%d",
              path == 1 ? 1LL : (long long)m, dot ? "dot" : "mfma", p.cpl, (long long)p.blocks,
              64 * p.waves, (long long)p.lds, p.ksplit, p.gwg);

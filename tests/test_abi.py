@@ -124,7 +124,7 @@ def test_dense_rejects_invalid_arguments(lib, args, code):
 def test_describe_names_the_dispatch(lib):
     # 4096 columns: 256 strips of 16, 16 waves splitting 32 groups, no k split
     assert qg.describe_int4(1, 4096, 4096) == (
-        "skinny_int4_kernel<1,dot,1> grid=256 block=1024 lds=%d ksplit=1 groups=32" % (16 * 64 + 32 * 256))
+        "skinny_int4_kernel<1,dot,1> grid=256 block=1024 lds=%d ksplit=1 groups=32" % (16 * 64))
     assert qg.describe_int4(8, 8192, 2048).startswith("skinny_int4_kernel<8,mfma,2> grid=256 block=512")
     assert qg.describe_int4(16, 28672, 4096).startswith("skinny_int4_kernel<16,mfma,4> grid=448 block=512")
     # a long k with few strips is split: 200 groups over 16 waves -> 4 slices of 50

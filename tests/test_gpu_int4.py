@@ -178,11 +178,12 @@ def test_split_k_with_and_without_workspace(gpu_lib, path, m, k, n):
         assert_accepted(host_u16(y), ref, ("split", path, m, k, n, ws))
 
 
-def test_gemv_long_k_falls_back_when_lds_is_short(gpu_lib):
+def test_gemv_long_k_without_workspace(gpu_lib):
+    # 600 groups on one 16-column strip, no k split: each wave walks a long chain
     m, k, n = 1, 76800, 16
     desc = gpu_lib.describe_int4(m, n, k, "gemv", 0)
     say("long-k", desc)
-    assert "mfma" in desc          # the activation slice would not fit in LDS
+    assert "dot" in desc and "ksplit=1" in desc
     d = int4_inputs(m, k, n, seed=39)
     y = run(gpu_lib, upload_int4(d), "gemv", workspace=False)
     ref = oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], m, k, n)
