@@ -32,6 +32,15 @@ METRIC = "qgemm µs & eff. HBM GB/s at m=1/8; TFLOPS (% MFMA peak) at m>=512"
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA
 LLC_BYTES = 256 << 20
+# HBM traffic of the small-M kernels, measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+# and scaled by the same counters on a copy of known size; valid only while the
+# kernel sources hash to the value recorded with the counters.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "skinny_int4_small_m_traffic.md")
+KERNEL_SOURCES = ["int4_weight_only_gptq_amd/csrc/int4_kernels.hip",
+                  "int4_weight_only_gptq_amd/csrc/common.hpp",
+                  "int4_weight_only_gptq_amd/csrc/launch.hpp",
+                  "int4_weight_only_gptq_amd/build.py"]
+
 SMALL_M = [(4096, 4096), (2048, 8192)]
 SMALL_M_TOKENS = [1, 8, 15]
 
@@ -124,6 +133,34 @@ def time_us(torch, fn, iters, graph=True):
     e1.record(s)
     e1.synchronize()
     return e0.elapsed_time(e1) * 1e3 / iters
+
+
+def kernel_source_sha256():
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter profile, or None
+    when there is none for it or the kernel sources changed since it was taken."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    start = text.find("```json")
+    if start < 0:
+        return None
+    end = text.find("```", start + 7)
+    data = json.loads(text[start + 7:end])
+    if data.get("source_sha256") != kernel_source_sha256():
+        return None
+    k = data.get("kernels", {}).get(kernel)
+    return None if k is None else int(k["fetch_bytes"] + k["write_bytes"])
 
 
 def copy_peak_gbps(torch, nbytes=2 << 30):
@@ -228,7 +265,7 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "avg_launch_us": round(avg_us, 3), "bytes_per_launch": int(avg_bytes),
-                "traffic": None}
+                "traffic": measured_traffic(dom)}
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
