@@ -696,6 +696,26 @@ static void pipe_launch(const DenseArgs& a, hipStream_t stream) {
 #define QG_SPLITK16_MIN_K 256     // k below which the 16 x 16 split-k tile is not worth it
 #endif
 
+// Tile of the pipelined kernel: each of these runs one workgroup per CU, so a
+// launch takes ceil(tiles / 256) rounds of one tile time.  Measured tile times
+// relative to 256 x 128: 256 x 256 (128 x 128 per wave, accumulators in AGPRs)
+// costs 1.4-1.6x for twice the work, 128 x 128 about 0.6x for half of it.
+// 0: 128 x 128, 1: 256 x 128, 2: 256 x 256.
+#ifndef QG_DENSE_T256X256
+#define QG_DENSE_T256X256 1.5
+#endif
+#ifndef QG_DENSE_T128X128
+#define QG_DENSE_T128X128 0.6
+#endif
+static int pick_pipe_tile(int64_t M, int64_t N) {
+  auto rounds = [](int64_t tiles) { return (double)((tiles + 255) / 256); };
+  const double c2 = rounds(((M + 255) / 256) * ((N + 255) / 256)) * QG_DENSE_T256X256;
+  const double c1 = rounds(((M + 255) / 256) * ((N + 127) / 128));
+  const double c0 = rounds(((M + 127) / 128) * ((N + 127) / 128)) * QG_DENSE_T128X128;
+  if (c2 < c1 && c2 < c0) return 2;
+  return c1 <= c0 ? 1 : 0;
+}
+
 template <int LAYOUT, int DTYPE>
 static void dense_dispatch(const DenseArgs& a, hipStream_t stream) {
   if (mfma_fits(a) && (a.M <= 16 || a.N <= 16) && a.K >= QG_SPLITK16_MIN_K) {
@@ -710,9 +730,11 @@ static void dense_dispatch(const DenseArgs& a, hipStream_t stream) {
     dense_smallk_kernel<LAYOUT, DTYPE><<<dim3((unsigned)(per_xcd * 8)), dim3(256), 0, stream>>>(
         a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, vec);
   } else if (mfma_fits(a) && a.K % DBK == 0 && a.M >= 128 && a.N >= 128) {
-    const int64_t big = ((a.M + 255) / 256) * ((a.N + 127) / 128);
-    if (big >= QG_DENSE_BIG_MIN_TILES) pipe_launch<LAYOUT, DTYPE, 256, 128, QG_DENSE_PIPE_STAGES>(a, stream);
-    else pipe_launch<LAYOUT, DTYPE, 128, 128, 4>(a, stream);
+    switch (pick_pipe_tile(a.M, a.N)) {
+      case 2: pipe_launch<LAYOUT, DTYPE, 256, 256, 2>(a, stream); break;
+      case 1: pipe_launch<LAYOUT, DTYPE, 256, 128, QG_DENSE_PIPE_STAGES>(a, stream); break;
+      default: pipe_launch<LAYOUT, DTYPE, 128, 128, 4>(a, stream); break;
+    }
   } else if (mfma_fits(a)) {
     const int64_t big = ((a.M + 255) / 256) * ((a.N + 127) / 128);
     if (big >= QG_DENSE_BIG_MIN_TILES) tile_launch<LAYOUT, DTYPE, 256, 128>(a, stream);
