@@ -226,6 +226,9 @@ __global__ __launch_bounds__(256) void dense_tile_kernel(const uint16_t* __restr
 // Rows or columns past M or N load a clamped valid address; their results
 // are discarded.
 __device__ __forceinline__ int fmn(int k) { return 2 * ((k & 3) | ((k >> 1) & 4)); }
+// the same XOR limited to a row of R / 8 chunks (R = 64: 8 chunks)
+template <int R>
+__device__ __forceinline__ int fmn_r(int k) { return fmn(k) & (R / 8 - 1); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef s16x4 __attribute__((address_space(3))) lds_s16x4;
@@ -237,8 +240,8 @@ __device__ __forceinline__ u32x4 read_mn_frag(const u32x4* region, int kb, int c
   const int j = lane & 15, r = j >> 2, q = j & 3;
   const int c = (col0 >> 3) + (q >> 1);
   const int k1 = kb + r, k2 = kb + 4 + r;
-  const uint16_t* h1 = reinterpret_cast<const uint16_t*>(region + k1 * (R / 8) + (c ^ fmn(k1))) + 4 * (q & 1);
-  const uint16_t* h2 = reinterpret_cast<const uint16_t*>(region + k2 * (R / 8) + (c ^ fmn(k2))) + 4 * (q & 1);
+  const uint16_t* h1 = reinterpret_cast<const uint16_t*>(region + k1 * (R / 8) + (c ^ fmn_r<R>(k1))) + 4 * (q & 1);
+  const uint16_t* h2 = reinterpret_cast<const uint16_t*>(region + k2 * (R / 8) + (c ^ fmn_r<R>(k2))) + 4 * (q & 1);
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(h1));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(h2));
   u32x4 out;
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(256) void dense_pipe_kernel(
   for (int i = 0; i < A_LOADS; ++i) {
     const int slot = tid + 256 * i;
     if constexpr (A_MN) {
-      const int k = slot / (BM / 8), c = (slot % (BM / 8)) ^ fmn(k);
+      const int k = slot / (BM / 8), c = (slot % (BM / 8)) ^ fmn_r<BM>(k);
       const int64_t gm = m0 + 8 * c < M ? m0 + 8 * c : (int64_t)M - 8;
       asrc[i] = A + (int64_t)k * lda + gm;
     } else {
@@ -293,7 +296,7 @@ __global__ __launch_bounds__(256) void dense_pipe_kernel(
   for (int i = 0; i < B_LOADS; ++i) {
     const int slot = tid + 256 * i;
     if constexpr (B_MN) {
-      const int k = slot / (BN / 8), c = (slot % (BN / 8)) ^ fmn(k);
+      const int k = slot / (BN / 8), c = (slot % (BN / 8)) ^ fmn_r<BN>(k);
       const int64_t gn = n0 + 8 * c < N ? n0 + 8 * c : (int64_t)N - 8;
       bsrc[i] = B + (int64_t)k * ldb + gn;
     } else {
@@ -699,21 +702,27 @@ static void pipe_launch(const DenseArgs& a, hipStream_t stream) {
 // Tile of the pipelined kernel: each of these runs one workgroup per CU, so a
 // launch takes ceil(tiles / 256) rounds of one tile time.  Measured tile times
 // relative to 256 x 128: 256 x 256 (128 x 128 per wave, accumulators in AGPRs)
-// costs 1.4-1.6x for twice the work, 128 x 128 about 0.6x for half of it.
-// 0: 128 x 128, 1: 256 x 128, 2: 256 x 256.
+// costs 1.4-1.6x for twice the work, 128 x 128 about 0.6x for half of it,
+// 64 x 128 about 0.4x for a quarter of it.
+// -1: 64 x 128, 0: 128 x 128, 1: 256 x 128, 2: 256 x 256.
 #ifndef QG_DENSE_T256X256
 #define QG_DENSE_T256X256 1.5
 #endif
 #ifndef QG_DENSE_T128X128
 #define QG_DENSE_T128X128 0.6
 #endif
+#ifndef QG_DENSE_T64X128
+#define QG_DENSE_T64X128 0.4
+#endif
 static int pick_pipe_tile(int64_t M, int64_t N) {
   auto rounds = [](int64_t tiles) { return (double)((tiles + 255) / 256); };
   const double c2 = rounds(((M + 255) / 256) * ((N + 255) / 256)) * QG_DENSE_T256X256;
   const double c1 = rounds(((M + 255) / 256) * ((N + 127) / 128));
   const double c0 = rounds(((M + 127) / 128) * ((N + 127) / 128)) * QG_DENSE_T128X128;
-  if (c2 < c1 && c2 < c0) return 2;
-  return c1 <= c0 ? 1 : 0;
+  const double cm = rounds(((M + 63) / 64) * ((N + 127) / 128)) * QG_DENSE_T64X128;
+  if (c2 < c1 && c2 < c0 && c2 < cm) return 2;
+  if (c1 <= c0 && c1 <= cm) return 1;
+  return c0 <= cm ? 0 : -1;
 }
 
 template <int LAYOUT, int DTYPE>
@@ -733,7 +742,8 @@ static void dense_dispatch(const DenseArgs& a, hipStream_t stream) {
     switch (pick_pipe_tile(a.M, a.N)) {
       case 2: pipe_launch<LAYOUT, DTYPE, 256, 256, 2>(a, stream); break;
       case 1: pipe_launch<LAYOUT, DTYPE, 256, 128, QG_DENSE_PIPE_STAGES>(a, stream); break;
-      default: pipe_launch<LAYOUT, DTYPE, 128, 128, 4>(a, stream); break;
+      case 0: pipe_launch<LAYOUT, DTYPE, 128, 128, 4>(a, stream); break;
+      default: pipe_launch<LAYOUT, DTYPE, 64, 128, 4>(a, stream); break;
     }
   } else if (mfma_fits(a)) {
     const int64_t big = ((a.M + 255) / 256) * ((a.N + 127) / 128);

@@ -56,9 +56,11 @@ def test_shapes_match_oracle(gpu_lib, layout, dtype):
         assert_accepted(c, ref, dtype, (layout, dtype, M, N, K))
 
 
-# shapes for the pipelined kernel (K % 64 == 0): ragged M and N edges, all three tile
-# sizes (2050 x 5624 takes 256 x 256 tiles: one round of 198 against two of 396)
-PIPE_SHAPES = [(128, 128, 64), (200, 264, 128), (1000, 136, 192), (2000, 2600, 64), (2050, 5624, 192)]
+# shapes for the pipelined kernel (K % 64 == 0): ragged M and N edges, all four tile
+# sizes (2050 x 5624 takes 256 x 256 tiles: one round of 198 against two of 396;
+# 1000 x 2000 takes 64 x 128 tiles: one round of 256)
+PIPE_SHAPES = [(128, 128, 64), (200, 264, 128), (1000, 136, 192), (2000, 2600, 64), (2050, 5624, 192),
+               (1000, 2000, 128)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
