@@ -90,15 +90,17 @@ int32_t qg_last_hip_error(void);
  *   m >= 0 tokens, 0 <= n <= 2^26 output columns (n % 8 == 0), 0 <= k <= 2^22
  *   input rows (k % 128 == 0), group_size must be 128.
  *   workspace, workspace_bytes
- *            optional device scratch (16-byte aligned) that lets the m <= 16
- *            paths split k over several workgroups; qgemm_int4_workspace_size
- *            gives the size that enables the split.  Its first 64 KiB
- *            hold the split's counters: they must be zero before the first use
- *            with this library, and each call leaves them zero again (the rest
- *            holds per-call partial sums).  NULL or a smaller
- *            size is valid: the call then runs without the split (same
- *            accuracy contract, fewer workgroups, summation order may differ).
- *            Calls that share a workspace must not run concurrently.
+ *            optional device scratch (16-byte aligned).  The m <= 16 paths
+ *            use it to split k over several workgroups; the MFMA path (m > 16)
+ *            to hold the activations in the decode's pair order and their
+ *            per-group sums (a preparation pass before the tiles run).
+ *            qgemm_int4_workspace_size gives the size that enables either.
+ *            Its first 64 KiB hold the split's counters: they must be zero
+ *            before the first use with this library, and each call leaves them
+ *            zero again (the rest holds per-call data).  NULL or a smaller size
+ *            is valid: the call then runs without the split / preparation
+ *            (same accuracy contract; the summation order may differ).  Calls
+ *            that share a workspace must not run concurrently.
  *
  * The path is chosen from m (see QG_PATH_AUTO).  x and y must not overlap the
  * weights or the workspace.  Errors: QG_ERR_NULL, QG_ERR_SHAPE, QG_ERR_ALIGN,

@@ -70,7 +70,7 @@ int32_t run_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint
   switch (resolve_path(m, path)) {
     case QG_PATH_GEMV: return hip_status(qg::launch_gemv_int4(a, ws, ws_bytes, s));
     case QG_PATH_FUSED: return hip_status(qg::launch_fused_int4(a, ws, ws_bytes, s));
-    default: return hip_status(qg::launch_mfma_int4(a, s));
+    default: return hip_status(qg::launch_mfma_int4(a, ws, ws_bytes, s));
   }
 }
 

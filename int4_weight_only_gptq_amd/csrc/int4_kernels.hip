@@ -363,30 +363,36 @@ __global__ __launch_bounds__(1024) void skinny_int4_kernel(
 // fragments gives the per-token group sums in the accumulator layout.  After
 // both stages of a group: total += s * (acc - (128 + z) * sum_x), fp32.
 // ---------------------------------------------------------------------------
-template <int NWM, int NWN, int FM>
+template <int NWM, int NWN, int FM, bool PREP>
 struct PipeShape {
   static constexpr int T = 64 * NWM * NWN;               // threads
+  static constexpr int NW = NWM * NWN;                   // waves
   static constexpr int BM = NWM * 16 * FM, BN = NWN * 64;
   static constexpr int X_SLOTS = BM * 8;                 // 16-byte activation chunks per stage
   static constexpr int XL = X_SLOTS / T;                 // per thread
   static constexpr bool W16 = (2 * BN) % T == 0;         // words as 16-byte chunks, else dwords
   static constexpr int WL = W16 ? 2 * BN / T : 8 * BN / T;
-  static constexpr int LOADS = XL + WL + 1;              // direct loads per thread per stage
-  static constexpr int X_DW = 4 * X_SLOTS, W_DW = 8 * BN, M_DW = T;
+  // metadata: 64-dword slots, one per wave and load: the BN scales (slot 0), the
+  // BN / 8 zero words (slot 1) and, with the prepared activations, the group
+  // sums of the BM tokens (slots 2 .. 2 + BM / 64 - 1); other slots are filler
+  static constexpr int MSLOTS = 2 + (PREP ? BM / 64 : 0);
+  static constexpr int ML = (MSLOTS + NW - 1) / NW;      // metadata loads per thread
+  static constexpr int LOADS = XL + WL + ML;             // direct loads per thread per stage
+  static constexpr int X_DW = 4 * X_SLOTS, W_DW = 8 * BN, M_DW = 64 * NW * ML;
   static constexpr int STAGE_DW = X_DW + W_DW + M_DW;    // dwords of LDS per stage
   static constexpr int OP = BN + 8;                      // output tile row pitch (bf16)
   static_assert(X_SLOTS % T == 0, "activation chunks per thread");
   static_assert((8 * BN) % T == 0, "word loads per thread");
-  static_assert(BN == 128 && T >= 128, "metadata: one wave of scales, one of zero words");
+  static_assert(BN == 128 && BM % 64 == 0, "metadata slots");
 };
 
-template <int NWM, int NWN, int FM, int STAGES>
+template <int NWM, int NWN, int FM, int STAGES, bool PREP>
 __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(2))) void int4_pipe_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
-    uint16_t* __restrict__ y, int64_t ldy, int m, int n, int k, int tiles_n, int tiles,
-    int tiles_per_xcd, int vec_store) {
-  using S = PipeShape<NWM, NWN, FM>;
+    const float* __restrict__ xsum, uint16_t* __restrict__ y, int64_t ldy, int m, int n, int k,
+    int tiles_n, int tiles, int tiles_per_xcd, int vec_store) {
+  using S = PipeShape<NWM, NWN, FM, PREP>;
   constexpr int T = S::T, BM = S::BM, BN = S::BN, XL = S::XL, WL = S::WL, LOADS = S::LOADS;
   static_assert(LOADS * (STAGES - 2) <= 63, "vmcnt range");
   extern __shared__ __attribute__((aligned(16))) uint32_t psm_i4[];
@@ -426,13 +432,21 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
     }
     woff[i] = (uint32_t)(((int64_t)wr * n + cw) * 4);
   }
-  // metadata: wave 0 loads the group's BN scales (BN / 2 dwords), every other
-  // wave the BN / 8 zero words (only wave 1's land where they are read)
-  uint32_t moff;
-  if (wave == 0) {
-    moff = (uint32_t)((n0 + 2 * lane < n ? 2 * lane : n - 2 - n0) * 2);
-  } else {
-    moff = (uint32_t)(((n0 >> 3) + lane < (n >> 3) ? lane : (n >> 3) - 1 - (n0 >> 3)) * 4);
+  // metadata slot j = NW * i + wave of load i: 0 scales, 1 zero words,
+  // 2.. the group sums of tokens m0 + 64 (j - 2) + lane; others: zero words
+  const int zlane = (n0 >> 3) + lane < (n >> 3) ? lane : (n >> 3) - 1 - (n0 >> 3);
+  uint32_t moff[S::ML];
+#pragma unroll
+  for (int i = 0; i < S::ML; ++i) {
+    const int j = S::NW * i + wave;
+    if (j == 0) {
+      moff[i] = (uint32_t)((n0 + 2 * lane < n ? 2 * lane : n - 2 - n0) * 2);
+    } else if (j >= 2 && j < S::MSLOTS) {
+      const int r = 64 * (j - 2) + lane;
+      moff[i] = (uint32_t)((m0 + r < m ? r : m - 1 - m0) * 4);
+    } else {
+      moff[i] = (uint32_t)(zlane * 4);
+    }
   }
   const uint16_t* xbase = x + (int64_t)m0 * ldx;
   const uint32_t* wbase0 = qweight + n0;
@@ -450,11 +464,17 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
       else buffer_to_lds4(ws_base, woff[i], wl + T * i + 64 * wave);
     }
     const int64_t g = st >> 1;
-    buffer_to_lds4(wave == 0 ? (const void*)(scales + g * n + n0) : (const void*)(qzeros + g * (n >> 3) + (n0 >> 3)),
-                   moff, wl + S::W_DW + 64 * wave);
+#pragma unroll
+    for (int i = 0; i < S::ML; ++i) {
+      const int j = S::NW * i + wave;
+      const void* base = j == 0 ? (const void*)(scales + g * n + n0)
+                       : (j >= 2 && j < S::MSLOTS) ? (const void*)(xsum + g * m + m0)
+                                                   : (const void*)(qzeros + g * (n >> 3) + (n0 >> 3));
+      buffer_to_lds4(base, moff[i], wl + S::W_DW + 64 * j);
+    }
   };
 
-  f32x4 total[FM][4], acc[FM][4], xs[FM];
+  f32x4 total[FM][4], acc[FM][4], xs[PREP ? 1 : FM];
 #pragma unroll
   for (int f = 0; f < FM; ++f)
 #pragma unroll
@@ -492,10 +512,11 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         // reorder / decode this step's fragments (their LDS reads were issued
-        // one step earlier, under the previous step's MFMAs)
+        // one step earlier, under the previous step's MFMAs); prepared
+        // activations are already in pair order
         u32x4 ap[FM], b[4];
 #pragma unroll
-        for (int f = 0; f < FM; ++f) ap[f] = x_pairs_permuted(fa[f]);
+        for (int f = 0; f < FM; ++f) ap[f] = PREP ? fa[f] : x_pairs_permuted(fa[f]);
 #pragma unroll
         for (int c = 0; c < 4; ++c) b[c] = codes_as_bf16_pairs(fw[c]);
         if (s == 0) read_step(kt, 1);
@@ -503,15 +524,20 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
         // the ones-MFMA sums the reordered activations; a sum's order does not matter
 #pragma unroll
         for (int f = 0; f < FM; ++f) {
-          xs[f] = mfma16_bf16(ap[f], ones, first ? zero : xs[f]);
+          if constexpr (!PREP) xs[f] = mfma16_bf16(ap[f], ones, first ? zero : xs[f]);
 #pragma unroll
           for (int c = 0; c < 4; ++c) acc[f][c] = mfma16_bf16(ap[f], b[c], first ? zero : acc[f][c]);
         }
       }
-      // the group's scales and zeros, read while stage kt is still ours
+      // the group's scales, zeros (and prepared group sums), read while stage
+      // kt is still ours
       float sc[4], bz[4];
+      f32x4 gs[FM];   // group sums of this lane's accumulator rows 4 ks + v
       if (h == 1) {
         const uint32_t* lm = psm_i4 + (size_t)(kt % STAGES) * S::STAGE_DW + S::X_DW + S::W_DW;
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+          gs[f] = PREP ? *reinterpret_cast<const f32x4*>(lm + 128 + wm0 + 16 * f + 4 * ks) : xs[PREP ? 0 : f];
         const int col = wn0 + 4 * cl;
         const u32x2 sv = *reinterpret_cast<const u32x2*>(lm + (col >> 1));
         const uint32_t zw = lm[BN / 2 + (col >> 3)] >> (4 * (col & 7));
@@ -545,7 +571,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
           for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-              total[f][c][v] = __builtin_fmaf(sc[c], __builtin_fmaf(-bz[c], xs[f][v], acc[f][c][v]),
+              total[f][c][v] = __builtin_fmaf(sc[c], __builtin_fmaf(-bz[c], gs[f][v], acc[f][c][v]),
                                               total[f][c][v]);
       }
     }
@@ -681,15 +707,45 @@ hipError_t launch_fused_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipS
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Activation preparation for the pipelined kernel (with a workspace): each
+// 8-element chunk of X copied in the pair order of codes_as_bf16_pairs, and the
+// fp32 sum of every 128-row group per token, xsum[g][token].  The MFMA loop
+// then needs neither the reorder nor a ones-MFMA.  Thread = (token, chunk);
+// the 16 threads of a group are 16 consecutive lanes (k % 128 == 0).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void int4_prep_kernel(const uint16_t* __restrict__ x, int64_t ldx, int m,
+                                                        int k, uint16_t* __restrict__ xp,
+                                                        float* __restrict__ xsum) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int cpr = k >> 3;
+  if (t >= (int64_t)m * cpr) return;   // whole 16-lane groups leave together
+  const int row = (int)(t / cpr), c = (int)(t - (int64_t)row * cpr);
+  const u32x4 v = *reinterpret_cast<const u32x4*>(x + (int64_t)row * ldx + 8 * c);
+  *reinterpret_cast<u32x4*>(xp + (int64_t)row * k + 8 * c) = x_pairs_permuted(v);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sum = dot2_bf16(v[i], kOnesBf16x2, sum);
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
+  if ((c & 15) == 0) xsum[(int64_t)(c >> 4) * m + row] = sum;
+}
+
+// Workspace of the pipelined path: the counters' 64 KiB (left untouched), the
+// prepared activations [m][k] bf16, then xsum [k/128][m] fp32.
+static int64_t prep_workspace_bytes(int64_t m, int64_t k) {
+  return kTicketBytes + m * k * 2 + (k / 128) * m * 4;
+}
+
 // Launch shapes of the pipelined kernel, smallest tile first.
 struct PipeCfg {
   int bm, bn, stages, threads;
   size_t lds;
 };
 
-template <int NWM, int NWN, int FM, int STAGES>
+template <int NWM, int NWN, int FM, int STAGES, bool PREP>
 static PipeCfg pipe_cfg() {
-  using S = PipeShape<NWM, NWN, FM>;
+  using S = PipeShape<NWM, NWN, FM, PREP>;
   size_t lds = (size_t)STAGES * S::STAGE_DW * 4;
   const size_t out = (size_t)S::BM * S::OP * 2;
   return PipeCfg{S::BM, S::BN, STAGES, S::T, lds > out ? lds : out};
@@ -707,36 +763,54 @@ static int pick_pipe(int64_t m, int64_t n) {
   return 0;
 }
 
+template <bool PREP>
 static PipeCfg pipe_cfg_of(int which) {
   switch (which) {
-    case 2: return pipe_cfg<4, 2, 4, 4>();
-    case 1: return pipe_cfg<2, 2, 4, 4>();
-    default: return pipe_cfg<1, 2, 4, 4>();
+    case 2: return pipe_cfg<4, 2, 4, 4, PREP>();
+    case 1: return pipe_cfg<2, 2, 4, 4, PREP>();
+    default: return pipe_cfg<1, 2, 4, 4, PREP>();
   }
 }
 
-template <int NWM, int NWN, int FM, int STAGES>
-static void pipe_launch(const Int4Args& a, hipStream_t stream) {
-  const PipeCfg c = pipe_cfg<NWM, NWN, FM, STAGES>();
+template <int NWM, int NWN, int FM, int STAGES, bool PREP>
+static void pipe_launch(const Int4Args& a, const uint16_t* x, int64_t ldx, const float* xsum,
+                        hipStream_t stream) {
+  const PipeCfg c = pipe_cfg<NWM, NWN, FM, STAGES, PREP>();
   const int tiles_m = (int)((a.m + c.bm - 1) / c.bm), tiles_n = (int)((a.n + c.bn - 1) / c.bn);
   const int tiles = tiles_m * tiles_n, per_xcd = (tiles + 7) / 8;
   const int vec = ((uintptr_t)a.y & 15u) == 0 && a.ldy % 8 == 0;
-  int4_pipe_kernel<NWM, NWN, FM, STAGES><<<dim3((unsigned)(per_xcd * 8)), dim3(c.threads), c.lds, stream>>>(
-      a.x, a.ldx, a.qweight, a.scales, a.qzeros, a.y, a.ldy, (int)a.m, (int)a.n, (int)a.k, tiles_n,
+  int4_pipe_kernel<NWM, NWN, FM, STAGES, PREP><<<dim3((unsigned)(per_xcd * 8)), dim3(c.threads), c.lds, stream>>>(
+      x, ldx, a.qweight, a.scales, a.qzeros, xsum, a.y, a.ldy, (int)a.m, (int)a.n, (int)a.k, tiles_n,
       tiles, per_xcd, vec);
 }
 
-hipError_t launch_mfma_int4(const Int4Args& a, hipStream_t stream) {
+template <bool PREP>
+static void pipe_dispatch(const Int4Args& a, const uint16_t* x, int64_t ldx, const float* xsum,
+                          hipStream_t stream) {
   switch (pick_pipe(a.m, a.n)) {
-    case 2: pipe_launch<4, 2, 4, 4>(a, stream); break;
-    case 1: pipe_launch<2, 2, 4, 4>(a, stream); break;
-    default: pipe_launch<1, 2, 4, 4>(a, stream); break;
+    case 2: pipe_launch<4, 2, 4, 4, PREP>(a, x, ldx, xsum, stream); break;
+    case 1: pipe_launch<2, 2, 4, 4, PREP>(a, x, ldx, xsum, stream); break;
+    default: pipe_launch<1, 2, 4, 4, PREP>(a, x, ldx, xsum, stream); break;
+  }
+}
+
+hipError_t launch_mfma_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream) {
+  if (ws != nullptr && ws_bytes >= prep_workspace_bytes(a.m, a.k)) {
+    uint16_t* xp = (uint16_t*)((char*)ws + kTicketBytes);
+    float* xsum = (float*)(xp + a.m * a.k);
+    const int64_t threads = a.m * (a.k / 8);
+    int4_prep_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(
+        a.x, a.ldx, (int)a.m, (int)a.k, xp, xsum);
+    pipe_dispatch<true>(a, xp, a.k, xsum, stream);
+  } else {
+    pipe_dispatch<false>(a, a.x, a.ldx, nullptr, stream);
   }
   return hipGetLastError();
 }
 
 int64_t workspace_int4(int64_t m, int64_t n, int64_t k, int path) {
-  if (path == 3 || m == 0 || n == 0 || k == 0) return 0;
+  if (m == 0 || n == 0 || k == 0) return 0;
+  if (path == 3) return prep_workspace_bytes(m, k);
   return plan_skinny(m, n, k, INT64_MAX, path == 1).ws_bytes;
 }
 
@@ -749,10 +823,11 @@ void describe_int4(int64_t m, int64_t n, int64_t k, int path, int64_t ws_bytes, 
              path == 1 ? 1LL : (long long)m, dot ? "dot" : "mfma", p.cpl, (long long)p.blocks,
              64 * p.waves, (long long)p.lds, p.ksplit, p.gwg);
   } else {
-    const PipeCfg c = pipe_cfg_of(pick_pipe(m, n));
+    const bool prep = ws_bytes >= prep_workspace_bytes(m, k);
+    const PipeCfg c = prep ? pipe_cfg_of<true>(pick_pipe(m, n)) : pipe_cfg_of<false>(pick_pipe(m, n));
     const long long tiles = ((m + c.bm - 1) / c.bm) * ((n + c.bn - 1) / c.bn);
-    snprintf(buf, len, "int4_pipe_kernel<%d,%d,%d> grid=%lld block=%d lds=%lld", c.bm, c.bn, c.stages,
-             ((tiles + 7) / 8) * 8, c.threads, (long long)c.lds);
+    snprintf(buf, len, "int4_pipe_kernel<%d,%d,%d,%s> grid=%lld block=%d lds=%lld", c.bm, c.bn, c.stages,
+             prep ? "prep" : "ones", ((tiles + 7) / 8) * 8, c.threads, (long long)c.lds);
   }
 }
 

@@ -34,7 +34,8 @@ int64_t split_workspace_bytes(int64_t nstrips, int64_t ksplit, int64_t m, int cp
 // ws may be NULL (then no k split); ws_bytes is its size.
 hipError_t launch_gemv_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream);
 hipError_t launch_fused_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream);
-hipError_t launch_mfma_int4(const Int4Args& a, hipStream_t stream);
+// With ws_bytes >= workspace_int4(m, n, k, 3): a preparation pass into ws first.
+hipError_t launch_mfma_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream);
 
 // Workspace bytes a path (1 GEMV, 2 fused, 3 MFMA) can use; 0 if none.
 int64_t workspace_int4(int64_t m, int64_t n, int64_t k, int path);

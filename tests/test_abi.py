@@ -132,12 +132,16 @@ def test_describe_names_the_dispatch(lib):
     assert "ksplit=1 groups=200" in qg.describe_int4(16, 5120, 25600, workspace_bytes=0)
     # pipelined MFMA kernel: 64-token tiles for small m, 256 x 128 once there are enough of them
     # (lds = 4 stages x (activations + words + metadata) dwords x 4 bytes)
+    # (with the workspace: prepared activations, the group sums ride in the metadata slots;
+    # without it: a ones-MFMA per fragment; 64-token tiles need a second metadata load)
     assert qg.describe_int4(17, 5120, 25600) == (
-        "int4_pipe_kernel<64,128,4> grid=40 block=128 lds=%d" % (4 * (2048 + 1024 + 128) * 4))
-    assert qg.describe_int4(100, 5120, 25600).startswith("int4_pipe_kernel<128,128,4> grid=40 block=256")
+        "int4_pipe_kernel<64,128,4,prep> grid=40 block=128 lds=%d" % (4 * (2048 + 1024 + 256) * 4))
+    assert qg.describe_int4(17, 5120, 25600, workspace_bytes=0) == (
+        "int4_pipe_kernel<64,128,4,ones> grid=40 block=128 lds=%d" % (4 * (2048 + 1024 + 128) * 4))
+    assert qg.describe_int4(100, 5120, 25600).startswith("int4_pipe_kernel<128,128,4,prep> grid=40 block=256")
     assert qg.describe_int4(2048, 5120, 25600) == (
-        "int4_pipe_kernel<256,128,4> grid=320 block=512 lds=%d" % (4 * (8192 + 1024 + 512) * 4))
-    assert qg.describe_int4(1, 4096, 4096, "mfma").startswith("int4_pipe_kernel<64,128,4> grid=32 ")
+        "int4_pipe_kernel<256,128,4,prep> grid=320 block=512 lds=%d" % (4 * (8192 + 1024 + 512) * 4))
+    assert qg.describe_int4(1, 4096, 4096, "mfma").startswith("int4_pipe_kernel<64,128,4,prep> grid=32 ")
     assert qg.describe_int4(0, 64, 128) == "none"
     assert qg.describe_int4(3, 64, 0) == "zero16_kernel"
     with pytest.raises(qg.QGemmError):
@@ -148,7 +152,8 @@ def test_workspace_size(lib):
     # 64 KiB of counters, then 320 strips x 4 slices x 16 tokens x 16 columns x 4 bytes
     assert qg.workspace_size(16, 5120, 25600) == 65536 + 320 * 4 * 16 * 16 * 4
     assert qg.workspace_size(8, 4096, 4096) == 0           # no split needed
-    assert qg.workspace_size(17, 4096, 4096) == 0          # MFMA tiles use none
+    # MFMA tiles: 64 KiB of counters (untouched), prepared activations, group sums
+    assert qg.workspace_size(17, 4096, 4096) == 65536 + 17 * 4096 * 2 + 32 * 17 * 4
     assert lib.qgemm_int4_workspace_size(8, 60, 4096, 0) == -SHAPE
     assert lib.qgemm_int4_workspace_size(8, 64, 4096, 1) == -UNSUP
 

@@ -57,19 +57,21 @@ PATH_MS = {
     "gemv": [1],
     "fused": [1, 2, 3, 4, 5, 7, 8, 9, 12, 15, 16],
     "mfma": [1, 16, 17, 33, 130, 257],
+    "mfma_nows": [17, 33, 130, 257],     # no workspace: the MFMA tiles without the preparation pass
     "auto": [1, 6, 16, 17, 200],
 }
 
 
 @pytest.mark.parametrize("k,n", SMALL_SHAPES)
-@pytest.mark.parametrize("path", ["gemv", "fused", "mfma", "auto"])
+@pytest.mark.parametrize("path", ["gemv", "fused", "mfma", "mfma_nows", "auto"])
 def test_paths_match_oracle(gpu_lib, path, k, n):
+    p, ws = ("mfma", False) if path == "mfma_nows" else (path, None)
     for m in PATH_MS[path]:
         if m * n * k > 2 ** 31:
             continue
         say("path", path, "m", m, "k", k, "n", n)
         d = int4_inputs(m, k, n, seed=7 * m + k + n)
-        y = run(gpu_lib, upload_int4(d), path)
+        y = run(gpu_lib, upload_int4(d), p, workspace=ws)
         ref = oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], m, k, n)
         assert_accepted(host_u16(y), ref, (path, m, k, n))
 
@@ -194,8 +196,9 @@ def test_shared_workspace_across_shapes_and_counters_reset(gpu_lib):
     import torch
 
     ws = torch.zeros(8 << 20, dtype=torch.uint8, device="cuda")
-    shapes = [(8, 16384, 520), (1, 20480, 776), (15, 1152, 776), (16, 16384, 1040), (3, 896, 4864),
-              (8, 16384, 520)]
+    # includes m > 16 calls, whose preparation pass writes past the counters
+    shapes = [(8, 16384, 520), (1, 20480, 776), (40, 2048, 520), (15, 1152, 776), (16, 16384, 1040),
+              (130, 1152, 776), (3, 896, 4864), (8, 16384, 520)]
     for i, (m, k, n) in enumerate(shapes):
         say("shared-ws", m, k, n, gpu_lib.describe_int4(m, n, k, workspace_bytes=ws.numel()))
         d = int4_inputs(m, k, n, seed=40 + i)
