@@ -751,16 +751,29 @@ static PipeCfg pipe_cfg() {
   return PipeCfg{S::BM, S::BN, STAGES, S::T, lds > out ? lds : out};
 }
 
-#ifndef QG_PIPE_BIG_MIN_TILES
-#define QG_PIPE_BIG_MIN_TILES 256   // 256-token tiles wanted before using them
+// Tile choice: a launch takes ceil(tiles / (256 CUs x workgroups per CU))
+// rounds; measured round times relative to 256 x 128 (one workgroup per CU):
+// 128 x 128 (one per CU) 0.62-0.66, 64 x 128 (three per CU, LDS-bound) 0.8-0.9.
+// 0: 64 x 128, 1: 128 x 128, 2: 256 x 128.
+#ifndef QG_PIPE_T128
+#define QG_PIPE_T128 0.65
 #endif
-
-// 0: 64 x 128, 1: 128 x 128, 2: 256 x 128
+#ifndef QG_PIPE_T64
+#define QG_PIPE_T64 0.85
+#endif
 static int pick_pipe(int64_t m, int64_t n) {
+#ifdef QG_PIPE_FORCE
+  (void)m; (void)n;
+  return QG_PIPE_FORCE;
+#else
   const int64_t tn = (n + 127) / 128;
-  if (((m + 255) / 256) * tn >= QG_PIPE_BIG_MIN_TILES) return 2;
-  if (m > 64) return 1;
-  return 0;
+  auto rounds = [](int64_t tiles, int per_cu) { return (double)((tiles + 256 * per_cu - 1) / (256 * per_cu)); };
+  const double c2 = rounds(((m + 255) / 256) * tn, 1);
+  const double c1 = rounds(((m + 127) / 128) * tn, 1) * QG_PIPE_T128;
+  const double c0 = rounds(((m + 63) / 64) * tn, 3) * QG_PIPE_T64;
+  if (c2 <= c1 && c2 <= c0) return 2;
+  return c1 <= c0 ? 1 : 0;
+#endif
 }
 
 template <bool PREP>

@@ -132,16 +132,20 @@ def test_describe_names_the_dispatch(lib):
     assert "ksplit=1 groups=200" in qg.describe_int4(16, 5120, 25600, workspace_bytes=0)
     # pipelined MFMA kernel: 64-token tiles for small m, 256 x 128 once there are enough of them
     # (lds = 4 stages x (activations + words + metadata) dwords x 4 bytes)
-    # (with the workspace: prepared activations, the group sums ride in the metadata slots;
-    # without it: a ones-MFMA per fragment; 64-token tiles need a second metadata load)
+    # pipelined MFMA kernel, tile by rounds on 256 CUs (64 x 128 fits three to a CU); with the
+    # workspace the activations are prepared and the group sums ride in the metadata slots,
+    # without it a ones-MFMA per fragment (64-token tiles need a second metadata load)
     assert qg.describe_int4(17, 5120, 25600) == (
-        "int4_pipe_kernel<64,128,4,prep> grid=40 block=128 lds=%d" % (4 * (2048 + 1024 + 256) * 4))
-    assert qg.describe_int4(17, 5120, 25600, workspace_bytes=0) == (
-        "int4_pipe_kernel<64,128,4,ones> grid=40 block=128 lds=%d" % (4 * (2048 + 1024 + 128) * 4))
-    assert qg.describe_int4(100, 5120, 25600).startswith("int4_pipe_kernel<128,128,4,prep> grid=40 block=256")
+        "int4_pipe_kernel<128,128,4,prep> grid=40 block=256 lds=%d" % (4 * (4096 + 1024 + 256) * 4))
+    # (arguments m, n, k) n = 5120, k = 25600 at m = 2048: 64 x 128, 1280 tiles
     assert qg.describe_int4(2048, 5120, 25600) == (
-        "int4_pipe_kernel<256,128,4,prep> grid=320 block=512 lds=%d" % (4 * (8192 + 1024 + 512) * 4))
-    assert qg.describe_int4(1, 4096, 4096, "mfma").startswith("int4_pipe_kernel<64,128,4,prep> grid=32 ")
+        "int4_pipe_kernel<64,128,4,prep> grid=1280 block=128 lds=%d" % (4 * (2048 + 1024 + 256) * 4))
+    assert qg.describe_int4(2048, 5120, 25600, workspace_bytes=0) == (
+        "int4_pipe_kernel<64,128,4,ones> grid=1280 block=128 lds=%d" % (4 * (2048 + 1024 + 128) * 4))
+    assert qg.describe_int4(512, 5120, 25600).startswith("int4_pipe_kernel<128,128,4,prep> grid=160 block=256")
+    assert qg.describe_int4(2048, 25600, 5120) == (
+        "int4_pipe_kernel<256,128,4,prep> grid=1600 block=512 lds=%d" % (4 * (8192 + 1024 + 512) * 4))
+    assert qg.describe_int4(1, 4096, 4096, "mfma").startswith("int4_pipe_kernel<128,128,4,prep> grid=32 ")
     assert qg.describe_int4(0, 64, 128) == "none"
     assert qg.describe_int4(3, 64, 0) == "zero16_kernel"
     with pytest.raises(qg.QGemmError):
