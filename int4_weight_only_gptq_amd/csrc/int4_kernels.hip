@@ -391,15 +391,22 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
     const uint16_t* __restrict__ x, int64_t ldx, const uint32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
     const float* __restrict__ xsum, uint16_t* __restrict__ y, int64_t ldy, int m, int n, int k,
-    int tiles_n, int tiles, int tiles_per_xcd, int vec_store) {
+    int tiles_n, int items, int items_per_xcd, int vec_store, int ksplit, int gps,
+    float* __restrict__ partials, uint32_t* __restrict__ tickets) {
   using S = PipeShape<NWM, NWN, FM, PREP>;
   constexpr int T = S::T, BM = S::BM, BN = S::BN, XL = S::XL, WL = S::WL, LOADS = S::LOADS;
   static_assert(LOADS * (STAGES - 2) <= 63, "vmcnt range");
   extern __shared__ __attribute__((aligned(16))) uint32_t psm_i4[];
+  __shared__ int last_slice;
 
-  const int t = (blockIdx.x & 7) * tiles_per_xcd + (blockIdx.x >> 3);
-  if (t >= tiles) return;
+  // item = tile * ksplit + k-slice; the slices of a tile are consecutive items,
+  // so they run on one XCD
+  const int item = (blockIdx.x & 7) * items_per_xcd + (blockIdx.x >> 3);
+  if (item >= items) return;
+  const int t = item / ksplit, kslice = item - t * ksplit;
   const int tm = t / tiles_n, tn = t - tm * tiles_n;
+  const int gbeg = kslice * gps, gend = min(k >> 7, gbeg + gps);   // this slice's groups
+  const int kt0 = 2 * gbeg;                                          // its first stage
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases stay scalar
   const int cl = lane & 15, ks = lane >> 4;
@@ -451,19 +458,19 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
   const uint16_t* xbase = x + (int64_t)m0 * ldx;
   const uint32_t* wbase0 = qweight + n0;
 
-  auto issue = [&](int st) {
+  auto issue = [&](int st) {   // local stage st = global stage kt0 + st
     uint32_t* base = psm_i4 + (size_t)(st % STAGES) * S::STAGE_DW;
-    const uint16_t* xs_base = xbase + 64 * (int64_t)st;
+    const uint16_t* xs_base = xbase + 64 * (int64_t)(kt0 + st);
 #pragma unroll
     for (int i = 0; i < XL; ++i) buffer_to_lds16(xs_base, xoff[i], base + 4 * (T * i + 64 * wave));
     uint32_t* wl = base + S::X_DW;
-    const uint32_t* ws_base = wbase0 + 8 * (int64_t)st * n;
+    const uint32_t* ws_base = wbase0 + 8 * (int64_t)(kt0 + st) * n;
 #pragma unroll
     for (int i = 0; i < WL; ++i) {
       if constexpr (S::W16) buffer_to_lds16(ws_base, woff[i], wl + 4 * (T * i + 64 * wave));
       else buffer_to_lds4(ws_base, woff[i], wl + T * i + 64 * wave);
     }
-    const int64_t g = st >> 1;
+    const int64_t g = (kt0 + st) >> 1;
 #pragma unroll
     for (int i = 0; i < S::ML; ++i) {
       const int j = S::NW * i + wave;
@@ -481,7 +488,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
     for (int c = 0; c < 4; ++c) total[f][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   const u32x4 ones = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
 
-  const int ktiles = k >> 6;
+  const int ktiles = 2 * (gend - gbeg);   // stages of this slice
   // raw fragments of one k step: FM activation chunks and one 16-byte word read
   u32x4 fa[FM], fw;
   auto read_step = [&](int kt, int s) {
@@ -575,6 +582,58 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
                                               total[f][c][v]);
       }
     }
+  }
+  if (ksplit > 1) {
+    // Split k: every slice stores its fp32 partial tile with agent-coherent
+    // stores and takes a ticket; the last slice of the tile to arrive adds the
+    // partials in slice order (deterministic) and writes Y.  No fences: the
+    // partials are only written and read with agent-coherent accesses, and
+    // every thread waits for its stores before the ticket is taken.
+    // fragment order: element pair (f, v, c / 2) of thread tid at
+    // ((f * 4 + v) * 2 + c / 2) * T + tid (8-byte words), so that each store
+    // instruction of a wave covers 512 contiguous bytes; the last slice reads
+    // with the same thread mapping
+    uint64_t* mine = reinterpret_cast<uint64_t*>(partials) + ((int64_t)t * ksplit + kslice) * (BM * BN / 2);
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          // (the element is copied to a scalar first: a bit cast applied to a
+          // vector element directly read element 0 whatever the index)
+          const float lo = total[f][2 * h2][v], hi = total[f][2 * h2 + 1][v];
+          const uint64_t pair = (uint64_t)__builtin_bit_cast(uint32_t, lo) |
+                                ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
+          __hip_atomic_store(&mine[((f * 4 + v) * 2 + h2) * T + tid], pair, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    if (tid == 0)
+      last_slice = __hip_atomic_fetch_add(&tickets[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   (uint32_t)(ksplit - 1);
+    __syncthreads();
+    if (!last_slice) return;
+    const uint64_t* base = reinterpret_cast<const uint64_t*>(partials) + (int64_t)t * ksplit * (BM * BN / 2);
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int o = ((f * 4 + v) * 2 + h2) * T + tid;
+          float s0 = 0.f, s1 = 0.f;
+          for (int p = 0; p < ksplit; ++p) {
+            const uint64_t pair = __hip_atomic_load(&base[(int64_t)p * (BM * BN / 2) + o], __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+            s0 += __builtin_bit_cast(float, (uint32_t)pair);
+            s1 += __builtin_bit_cast(float, (uint32_t)(pair >> 32));
+          }
+          total[f][2 * h2][v] = s0;
+          total[f][2 * h2 + 1][v] = s1;
+        }
+    if (tid == 0) __hip_atomic_store(&tickets[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
 
@@ -731,11 +790,9 @@ __global__ __launch_bounds__(256) void int4_prep_kernel(const uint16_t* __restri
   if ((c & 15) == 0) xsum[(int64_t)(c >> 4) * m + row] = sum;
 }
 
-// Workspace of the pipelined path: the counters' 64 KiB (left untouched), the
-// prepared activations [m][k] bf16, then xsum [k/128][m] fp32.
-static int64_t prep_workspace_bytes(int64_t m, int64_t k) {
-  return kTicketBytes + m * k * 2 + (k / 128) * m * 4;
-}
+// Workspace of the pipelined path: the counters (64 KiB; per-tile tickets of
+// the k split, zero between calls), the prepared activations [m][k] bf16,
+// xsum [k/128][m] fp32, then the split's fp32 partial tiles.
 
 // Launch shapes of the pipelined kernel, smallest tile first.
 struct PipeCfg {
@@ -751,29 +808,86 @@ static PipeCfg pipe_cfg() {
   return PipeCfg{S::BM, S::BN, STAGES, S::T, lds > out ? lds : out};
 }
 
-// Tile choice: a launch takes ceil(tiles / (256 CUs x workgroups per CU))
-// rounds; measured round times relative to 256 x 128 (one workgroup per CU):
-// 128 x 128 (one per CU) 0.62-0.66, 64 x 128 (three per CU, LDS-bound) 0.8-0.9.
-// 0: 64 x 128, 1: 128 x 128, 2: 256 x 128.
+// Plan of the pipelined path: tile, k split, preparation.  A launch takes
+// ceil(items / (256 CUs x workgroups per CU)) rounds; measured round times
+// relative to 256 x 128 (one workgroup per CU) with the whole of k: 128 x 128
+// (one per CU) 0.62-0.66, 64 x 128 (three per CU) 0.8-0.9.  A k slice of
+// 1/ks of the groups costs 1/ks of that plus the partial exchange; slices keep
+// at least QG_PIPE_MIN_GPS groups.  The split needs the preparation workspace
+// (it rides behind it) and at most 16384 tiles (the counters).
+// cfg 0: 64 x 128, 1: 128 x 128, 2: 256 x 128.
 #ifndef QG_PIPE_T128
 #define QG_PIPE_T128 0.65
 #endif
 #ifndef QG_PIPE_T64
 #define QG_PIPE_T64 0.85
 #endif
-static int pick_pipe(int64_t m, int64_t n) {
-#ifdef QG_PIPE_FORCE
-  (void)m; (void)n;
-  return QG_PIPE_FORCE;
-#else
-  const int64_t tn = (n + 127) / 128;
-  auto rounds = [](int64_t tiles, int per_cu) { return (double)((tiles + 256 * per_cu - 1) / (256 * per_cu)); };
-  const double c2 = rounds(((m + 255) / 256) * tn, 1);
-  const double c1 = rounds(((m + 127) / 128) * tn, 1) * QG_PIPE_T128;
-  const double c0 = rounds(((m + 63) / 64) * tn, 3) * QG_PIPE_T64;
-  if (c2 <= c1 && c2 <= c0) return 2;
-  return c1 <= c0 ? 1 : 0;
+#ifndef QG_PIPE_MIN_GPS
+#define QG_PIPE_MIN_GPS 8
 #endif
+// Costs in rounds of a full-k 256 x 128 tile (≈ 0.0192 us per k row on this
+// chip): a slice pays QG_PIPE_FILL stages of pipeline fill and drain, and a
+// split writes and re-reads items x BM x 128 fp32 partials at ~4 TB/s.
+#ifndef QG_PIPE_FILL
+#define QG_PIPE_FILL 3.0
+#endif
+#ifndef QG_PIPE_US_PER_K
+#define QG_PIPE_US_PER_K 0.0192
+#endif
+#ifndef QG_PIPE_PARTIAL_BPUS
+#define QG_PIPE_PARTIAL_BPUS 4.0e6   // bytes per microsecond of partial traffic
+#endif
+#ifndef QG_PIPE_MAX_SPLIT
+#define QG_PIPE_MAX_SPLIT 8
+#endif
+
+struct MfmaPlan {
+  int cfg, ksplit, gps;
+  bool prep;
+  int64_t tiles, ws_bytes;
+};
+
+static const int kCfgBM[3] = {64, 128, 256};
+
+static MfmaPlan plan_mfma(int64_t m, int64_t n, int64_t k, int64_t ws_bytes) {
+  const int64_t G = k / 128, tn = (n + 127) / 128;
+  // prepared activations, group sums, then (256-byte aligned) the split's partials
+  const int64_t prep_bytes = (kTicketBytes + m * k * 2 + G * m * 4 + 255) & ~(int64_t)255;
+  MfmaPlan best{2, 1, (int)G, ws_bytes >= prep_bytes, ((m + 255) / 256) * tn, 0};
+  best.ws_bytes = best.prep ? prep_bytes : 0;
+  double best_cost = 1e300;
+  const double tcost[3] = {QG_PIPE_T64, QG_PIPE_T128, 1.0};
+  const int per_cu[3] = {3, 1, 1};
+  for (int cfg = 0; cfg < 3; ++cfg) {
+    const int64_t tiles = ((m + kCfgBM[cfg] - 1) / kCfgBM[cfg]) * tn;
+    for (int ks = 1; ks <= QG_PIPE_MAX_SPLIT; ++ks) {
+      const int64_t gps = (G + ks - 1) / ks;
+      if (ks > 1 && (gps < QG_PIPE_MIN_GPS || (G + gps - 1) / gps != ks)) continue;
+      int64_t need = best.prep ? prep_bytes : 0;
+      if (ks > 1) {
+        if (!best.prep || tiles > kTicketBytes / 4) break;
+        need = prep_bytes + tiles * ks * kCfgBM[cfg] * 128 * 4;
+        if (need > ws_bytes) break;
+      }
+      const int64_t items = tiles * ks;
+      const double rounds = (double)((items + 256 * per_cu[cfg] - 1) / (256 * per_cu[cfg]));
+      const double round_us = QG_PIPE_US_PER_K * (double)k;                  // full-k 256 x 128 round
+      double cost = rounds * tcost[cfg] * (2.0 * gps + QG_PIPE_FILL) / (2.0 * G);
+      if (ks > 1) cost += (double)items * kCfgBM[cfg] * 128 * 4 * 2 / QG_PIPE_PARTIAL_BPUS / round_us;
+#ifdef QG_PIPE_FORCE
+      if (cfg != QG_PIPE_FORCE) continue;
+#endif
+      if (cost < best_cost - 1e-9) {
+        best_cost = cost;
+        best.cfg = cfg;
+        best.ksplit = ks;
+        best.gps = (int)gps;
+        best.tiles = tiles;
+        best.ws_bytes = need;
+      }
+    }
+  }
+  return best;
 }
 
 template <bool PREP>
@@ -786,44 +900,47 @@ static PipeCfg pipe_cfg_of(int which) {
 }
 
 template <int NWM, int NWN, int FM, int STAGES, bool PREP>
-static void pipe_launch(const Int4Args& a, const uint16_t* x, int64_t ldx, const float* xsum,
-                        hipStream_t stream) {
+static void pipe_launch(const Int4Args& a, const MfmaPlan& p, const uint16_t* x, int64_t ldx,
+                        const float* xsum, float* partials, uint32_t* tickets, hipStream_t stream) {
   const PipeCfg c = pipe_cfg<NWM, NWN, FM, STAGES, PREP>();
-  const int tiles_m = (int)((a.m + c.bm - 1) / c.bm), tiles_n = (int)((a.n + c.bn - 1) / c.bn);
-  const int tiles = tiles_m * tiles_n, per_xcd = (tiles + 7) / 8;
+  const int tiles_n = (int)((a.n + c.bn - 1) / c.bn);
+  const int items = (int)(p.tiles * p.ksplit), per_xcd = (items + 7) / 8;
   const int vec = ((uintptr_t)a.y & 15u) == 0 && a.ldy % 8 == 0;
   int4_pipe_kernel<NWM, NWN, FM, STAGES, PREP><<<dim3((unsigned)(per_xcd * 8)), dim3(c.threads), c.lds, stream>>>(
       x, ldx, a.qweight, a.scales, a.qzeros, xsum, a.y, a.ldy, (int)a.m, (int)a.n, (int)a.k, tiles_n,
-      tiles, per_xcd, vec);
+      items, per_xcd, vec, p.ksplit, p.gps, partials, tickets);
 }
 
 template <bool PREP>
-static void pipe_dispatch(const Int4Args& a, const uint16_t* x, int64_t ldx, const float* xsum,
-                          hipStream_t stream) {
-  switch (pick_pipe(a.m, a.n)) {
-    case 2: pipe_launch<4, 2, 4, 4, PREP>(a, x, ldx, xsum, stream); break;
-    case 1: pipe_launch<2, 2, 4, 4, PREP>(a, x, ldx, xsum, stream); break;
-    default: pipe_launch<1, 2, 4, 4, PREP>(a, x, ldx, xsum, stream); break;
+static void pipe_dispatch(const Int4Args& a, const MfmaPlan& p, const uint16_t* x, int64_t ldx,
+                          const float* xsum, float* partials, uint32_t* tickets, hipStream_t stream) {
+  switch (p.cfg) {
+    case 2: pipe_launch<4, 2, 4, 4, PREP>(a, p, x, ldx, xsum, partials, tickets, stream); break;
+    case 1: pipe_launch<2, 2, 4, 4, PREP>(a, p, x, ldx, xsum, partials, tickets, stream); break;
+    default: pipe_launch<1, 2, 4, 4, PREP>(a, p, x, ldx, xsum, partials, tickets, stream); break;
   }
 }
 
 hipError_t launch_mfma_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream) {
-  if (ws != nullptr && ws_bytes >= prep_workspace_bytes(a.m, a.k)) {
+  const MfmaPlan p = plan_mfma(a.m, a.n, a.k, ws ? ws_bytes : 0);
+  if (p.prep) {
+    uint32_t* tickets = (uint32_t*)ws;
     uint16_t* xp = (uint16_t*)((char*)ws + kTicketBytes);
     float* xsum = (float*)(xp + a.m * a.k);
+    float* partials = (float*)((char*)ws + ((kTicketBytes + a.m * a.k * 2 + (a.k / 128) * a.m * 4 + 255) & ~(int64_t)255));
     const int64_t threads = a.m * (a.k / 8);
     int4_prep_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(
         a.x, a.ldx, (int)a.m, (int)a.k, xp, xsum);
-    pipe_dispatch<true>(a, xp, a.k, xsum, stream);
+    pipe_dispatch<true>(a, p, xp, a.k, xsum, partials, tickets, stream);
   } else {
-    pipe_dispatch<false>(a, a.x, a.ldx, nullptr, stream);
+    pipe_dispatch<false>(a, p, a.x, a.ldx, nullptr, nullptr, nullptr, stream);
   }
   return hipGetLastError();
 }
 
 int64_t workspace_int4(int64_t m, int64_t n, int64_t k, int path) {
   if (m == 0 || n == 0 || k == 0) return 0;
-  if (path == 3) return prep_workspace_bytes(m, k);
+  if (path == 3) return plan_mfma(m, n, k, INT64_MAX).ws_bytes;
   return plan_skinny(m, n, k, INT64_MAX, path == 1).ws_bytes;
 }
 
@@ -836,11 +953,12 @@ void describe_int4(int64_t m, int64_t n, int64_t k, int path, int64_t ws_bytes, 
              path == 1 ? 1LL : (long long)m, dot ? "dot" : "mfma", p.cpl, (long long)p.blocks,
              64 * p.waves, (long long)p.lds, p.ksplit, p.gwg);
   } else {
-    const bool prep = ws_bytes >= prep_workspace_bytes(m, k);
-    const PipeCfg c = prep ? pipe_cfg_of<true>(pick_pipe(m, n)) : pipe_cfg_of<false>(pick_pipe(m, n));
-    const long long tiles = ((m + c.bm - 1) / c.bm) * ((n + c.bn - 1) / c.bn);
-    snprintf(buf, len, "int4_pipe_kernel<%d,%d,%d,%s> grid=%lld block=%d lds=%lld", c.bm, c.bn, c.stages,
-             prep ? "prep" : "ones", ((tiles + 7) / 8) * 8, c.threads, (long long)c.lds);
+    const MfmaPlan p = plan_mfma(m, n, k, ws_bytes);
+    const PipeCfg c = p.prep ? pipe_cfg_of<true>(p.cfg) : pipe_cfg_of<false>(p.cfg);
+    const long long items = p.tiles * p.ksplit;
+    snprintf(buf, len, "int4_pipe_kernel<%d,%d,%d,%s> grid=%lld block=%d lds=%lld ksplit=%d groups=%d", c.bm,
+             c.bn, c.stages, p.prep ? "prep" : "ones", ((items + 7) / 8) * 8, c.threads, (long long)c.lds,
+             p.ksplit, p.gps);
   }
 }
 

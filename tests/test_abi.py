@@ -132,20 +132,22 @@ def test_describe_names_the_dispatch(lib):
     assert "ksplit=1 groups=200" in qg.describe_int4(16, 5120, 25600, workspace_bytes=0)
     # pipelined MFMA kernel: 64-token tiles for small m, 256 x 128 once there are enough of them
     # (lds = 4 stages x (activations + words + metadata) dwords x 4 bytes)
-    # pipelined MFMA kernel, tile by rounds on 256 CUs (64 x 128 fits three to a CU); with the
-    # workspace the activations are prepared and the group sums ride in the metadata slots,
-    # without it a ones-MFMA per fragment (64-token tiles need a second metadata load)
+    # pipelined MFMA kernel: tile and k split by rounds on 256 CUs (64 x 128 fits three to a
+    # CU); with the workspace the activations are prepared and the group sums ride in the
+    # metadata slots, without it a ones-MFMA per fragment and no split
     assert qg.describe_int4(17, 5120, 25600) == (
-        "int4_pipe_kernel<128,128,4,prep> grid=40 block=256 lds=%d" % (4 * (4096 + 1024 + 256) * 4))
-    # (arguments m, n, k) n = 5120, k = 25600 at m = 2048: 64 x 128, 1280 tiles
-    assert qg.describe_int4(2048, 5120, 25600) == (
-        "int4_pipe_kernel<64,128,4,prep> grid=1280 block=128 lds=%d" % (4 * (2048 + 1024 + 256) * 4))
-    assert qg.describe_int4(2048, 5120, 25600, workspace_bytes=0) == (
-        "int4_pipe_kernel<64,128,4,ones> grid=1280 block=128 lds=%d" % (4 * (2048 + 1024 + 128) * 4))
-    assert qg.describe_int4(512, 5120, 25600).startswith("int4_pipe_kernel<128,128,4,prep> grid=160 block=256")
+        "int4_pipe_kernel<64,128,4,prep> grid=320 block=128 lds=%d ksplit=8 groups=25"
+        % (4 * (2048 + 1024 + 256) * 4))
+    assert qg.describe_int4(17, 5120, 25600, workspace_bytes=0) == (
+        "int4_pipe_kernel<128,128,4,ones> grid=40 block=256 lds=%d ksplit=1 groups=200"
+        % (4 * (4096 + 1024 + 256) * 4))
     assert qg.describe_int4(2048, 25600, 5120) == (
-        "int4_pipe_kernel<256,128,4,prep> grid=1600 block=512 lds=%d" % (4 * (8192 + 1024 + 512) * 4))
-    assert qg.describe_int4(1, 4096, 4096, "mfma").startswith("int4_pipe_kernel<128,128,4,prep> grid=32 ")
+        "int4_pipe_kernel<256,128,4,prep> grid=1600 block=512 lds=%d ksplit=1 groups=40"
+        % (4 * (8192 + 1024 + 512) * 4))
+    assert qg.describe_int4(512, 5120, 25600).startswith("int4_pipe_kernel<256,128,4,prep> grid=240 block=512")
+    assert qg.describe_int4(2048, 5120, 25600, workspace_bytes=0).startswith(
+        "int4_pipe_kernel<64,128,4,ones> grid=1280 block=128 lds=%d ksplit=1" % (4 * (2048 + 1024 + 128) * 4))
+    assert qg.describe_int4(1, 4096, 4096, "mfma").startswith("int4_pipe_kernel<128,128,4,prep> grid=128 ")
     assert qg.describe_int4(0, 64, 128) == "none"
     assert qg.describe_int4(3, 64, 0) == "zero16_kernel"
     with pytest.raises(qg.QGemmError):
@@ -156,8 +158,16 @@ def test_workspace_size(lib):
     # 64 KiB of counters, then 320 strips x 4 slices x 16 tokens x 16 columns x 4 bytes
     assert qg.workspace_size(16, 5120, 25600) == 65536 + 320 * 4 * 16 * 16 * 4
     assert qg.workspace_size(8, 4096, 4096) == 0           # no split needed
-    # MFMA tiles: 64 KiB of counters (untouched), prepared activations, group sums
-    assert qg.workspace_size(17, 4096, 4096) == 65536 + 17 * 4096 * 2 + 32 * 17 * 4
+    # MFMA tiles: 64 KiB of counters, prepared activations, group sums, then the k split's
+    # partial tiles (tiles x slices x BM x 128 fp32)
+    up = lambda b: (b + 255) // 256 * 256
+    assert qg.workspace_size(2048, 25600, 5120) == up(65536 + 2048 * 5120 * 2 + 40 * 2048 * 4)  # no split
+    desc = qg.describe_int4(17, 4096, 4096)
+    bm = int(desc.split("<")[1].split(",")[0])
+    ks = int(desc.split("ksplit=")[1].split()[0])
+    tiles = ((17 + bm - 1) // bm) * (4096 // 128)
+    assert ks > 1
+    assert qg.workspace_size(17, 4096, 4096) == up(65536 + 17 * 4096 * 2 + 32 * 17 * 4) + tiles * ks * bm * 128 * 4
     assert lib.qgemm_int4_workspace_size(8, 60, 4096, 0) == -SHAPE
     assert lib.qgemm_int4_workspace_size(8, 64, 4096, 1) == -UNSUP
 

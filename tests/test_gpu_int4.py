@@ -180,6 +180,25 @@ def test_split_k_with_and_without_workspace(gpu_lib, path, m, k, n):
         assert_accepted(host_u16(y), ref, ("split", path, m, k, n, ws))
 
 
+# MFMA tiles with a k split (few tiles, long k): partial tiles, per-tile tickets and
+# the ordered reduction by the last slice; the first shapes leave ragged tiles
+MFMA_SPLIT_SHAPES = [(33, 4096, 520), (130, 8192, 776), (17, 16384, 264), (64, 6144, 1040)]
+
+
+@pytest.mark.parametrize("m,k,n", MFMA_SPLIT_SHAPES)
+def test_mfma_split_k_matches_oracle(gpu_lib, m, k, n):
+    desc = gpu_lib.describe_int4(m, n, k, "mfma")
+    say("mfma-split", m, k, n, desc)
+    assert "ksplit=1 " not in desc + " "
+    d = int4_inputs(m, k, n, seed=50 + m + n)
+    t = upload_int4(d)
+    ref = oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], m, k, n)
+    y1 = run(gpu_lib, t, "mfma")
+    assert_accepted(host_u16(y1), ref, ("mfma-split", m, k, n))
+    y2 = run(gpu_lib, t, "mfma")            # the tickets were reset: same result again
+    assert np.array_equal(host_u16(y1), host_u16(y2))
+
+
 def test_gemv_long_k_without_workspace(gpu_lib):
     # 600 groups on one 16-column strip, no k split: each wave walks a long chain
     m, k, n = 1, 76800, 16
