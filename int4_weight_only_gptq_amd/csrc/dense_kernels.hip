@@ -12,6 +12,7 @@
 // elements), transposes it in registers with byte permutes and writes 8
 // K-contiguous rows.
 #include "common.hpp"
+#include <type_traits>
 #include "launch.hpp"
 
 namespace qg {
@@ -208,7 +209,8 @@ __global__ __launch_bounds__(256) void dense_tile_kernel(const uint16_t* __restr
 // vectorizable).  Tile BM x BN per workgroup of 4 waves (2 x 2, each
 // (BM/2) x (BN/2)), k tiles of 64 in a STAGES-deep ring of LDS buffers filled
 // by direct global-to-LDS loads (no staging registers): while tile kt is
-// multiplied, tiles kt+1 .. kt+STAGES-1 are in flight.  One barrier per k tile.
+// multiplied, tiles kt+1 .. kt+STAGES-1 are in flight.  One barrier per k tile,
+// operand fragments read one 32-k step ahead of the MFMAs that use them.
 //
 // Operand tiles are stored in LDS in their memory orientation, in 16-byte
 // chunks, with an XOR swizzle instead of padding (a direct load fills 64
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(256) void dense_pipe_kernel(
   constexpr int STAGE = A_SLOTS + B_SLOTS;
   constexpr int A_LOADS = A_SLOTS / 256, B_LOADS = B_SLOTS / 256;   // per thread per stage
   constexpr int LOADS = A_LOADS + B_LOADS;
-  static_assert(LOADS * (STAGES - 2) <= 63, "vmcnt range");
+  static_assert(LOADS * (STAGES - 1) <= 63, "vmcnt range");
   extern __shared__ __attribute__((aligned(16))) u32x4 psm[];
 
   const int t = (blockIdx.x & 7) * tiles_per_xcd + (blockIdx.x >> 3);
@@ -315,62 +317,154 @@ __global__ __launch_bounds__(256) void dense_pipe_kernel(
     for (int c = 0; c < FN; ++c) acc[f][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int ktiles = K / DBK;
-#pragma unroll
-  for (int st = 0; st < STAGES - 1; ++st) {
-    if (st < ktiles) {
-      u32x4* base = psm + (size_t)st * STAGE;           // one stage of direct loads:
-#pragma unroll                                           // each wave-instruction fills
-      for (int i = 0; i < A_LOADS; ++i)                  // 64 consecutive chunks
-        __builtin_amdgcn_global_load_lds((void*)(asrc[i] + st * astep), (void*)(base + 256 * i + 64 * wave), 16, 0, 0);
-#pragma unroll
-      for (int i = 0; i < B_LOADS; ++i)
-        __builtin_amdgcn_global_load_lds((void*)(bsrc[i] + st * bstep), (void*)(base + A_SLOTS + 256 * i + 64 * wave), 16, 0, 0);
-    }
-  }
-
-  for (int kt = 0; kt < ktiles; ++kt) {
-    // the oldest stage (kt) has landed once at most (STAGES - 2) stages remain in flight
-    if (kt + STAGES - 2 < ktiles) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * (STAGES - 2)));
-    } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
-    // every wave has waited for its own loads of stage kt, and has finished
-    // reading stage kt-1 (whose buffer the next issue refills): a plain
-    // barrier suffices (a fenced one would drain all stages in flight)
-    lds_barrier();
-    if (kt + STAGES - 1 < ktiles) {
-      const int st = kt + STAGES - 1;
-      u32x4* base = psm + (size_t)(st % STAGES) * STAGE;
-#pragma unroll
-      for (int i = 0; i < A_LOADS; ++i)
-        __builtin_amdgcn_global_load_lds((void*)(asrc[i] + st * astep), (void*)(base + 256 * i + 64 * wave), 16, 0, 0);
-#pragma unroll
-      for (int i = 0; i < B_LOADS; ++i)
-        __builtin_amdgcn_global_load_lds((void*)(bsrc[i] + st * bstep), (void*)(base + A_SLOTS + 256 * i + 64 * wave), 16, 0, 0);
-    }
+  // direct load j (0 .. LOADS-1) of stage st: each wave-instruction fills 64
+  // consecutive chunks of the stage's buffer
+  auto issue1 = [&](int st, int j) {
+    u32x4* base = psm + (size_t)(st % STAGES) * STAGE;
+    if (j < A_LOADS)
+      __builtin_amdgcn_global_load_lds((void*)(asrc[j] + st * astep), (void*)(base + 256 * j + 64 * wave), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds((void*)(bsrc[j - A_LOADS] + st * bstep),
+                                       (void*)(base + A_SLOTS + 256 * (j - A_LOADS) + 64 * wave), 16, 0, 0);
+  };
+  // operand fragment j (0 .. FM-1: rows of A, FM .. FM+FN-1: columns of B) of
+  // k step s (32 k) of stage kt
+  //
+  // An M/N-contiguous fragment (column col0 + l % 16 of 8 k-rows) takes two
+  // transposed 8-byte reads at k-rows kb + r and kb + 4 + r (r = (l % 16) / 4,
+  // kb = 32 s + 8 (l / 16)).  Both rows get the same chunk XOR of the stage
+  // layout, 2 (r | 4 (l / 16 % 2)), for either k step, and it only touches
+  // the even part of the chunk index, so a fragment's address is a per-lane
+  // base for its column group plus constant offsets for s and the row half.
+  const int r4 = (lane & 15) >> 2, q4 = lane & 3;
+  auto mn_base = [&](int R, int col0) {    // halfword offset in the operand region
+    const int x = (2 * (r4 | 4 * (ks & 1))) & (R / 8 - 1);
+    return ((8 * ks + r4) * (R / 8) + (((col0 >> 3) ^ x) | (q4 >> 1))) * 8 + 4 * (q4 & 1);
+  };
+  auto read_mn = [&](const u32x4* region, int R, int base, int s) {
+    const uint16_t* h = reinterpret_cast<const uint16_t*>(region) + base + 32 * s * R;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(h));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(h + 4 * R));
+    u32x4 out;
+    out[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+    out[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+    out[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+    out[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+    return out;
+  };
+  auto read1 = [&](int kt, int s, int j, u32x4 (&a)[FM], u32x4 (&b)[FN]) {
     const u32x4* la = psm + (size_t)(kt % STAGES) * STAGE;
     const u32x4* lb = la + A_SLOTS;
-#pragma unroll
-    for (int s = 0; s < DBK / 32; ++s) {
-      const int ch = 4 * s + ks;
-      u32x4 a[FM], b[FN];
-#pragma unroll
-      for (int f = 0; f < FM; ++f) {
-        if constexpr (A_MN) a[f] = read_mn_frag<BM>(la, 32 * s + 8 * ks, wm0 + 16 * f, lane);
-        else a[f] = la[swz(wm0 + 16 * f + cl, ch)];
-      }
-#pragma unroll
-      for (int c = 0; c < FN; ++c) {
-        if constexpr (B_MN) b[c] = read_mn_frag<BN>(lb, 32 * s + 8 * ks, wn0 + 16 * c, lane);
-        else b[c] = lb[swz(wn0 + 16 * c + cl, ch)];
-      }
-#pragma unroll
-      for (int f = 0; f < FM; ++f)
-#pragma unroll
-        for (int c = 0; c < FN; ++c)
-          acc[f][c] = DTYPE == 0 ? mfma16_bf16(a[f], b[c], acc[f][c]) : mfma16_f16(a[f], b[c], acc[f][c]);
+    const int ch = 4 * s + ks;
+    if (j < FM) {
+      if constexpr (A_MN) a[j] = read_mn(la, BM, mn_base(BM, wm0 + 16 * j), s);
+      else a[j] = la[swz(wm0 + 16 * j + cl, ch)];
+    } else {
+      const int c = j - FM;
+      if constexpr (B_MN) b[c] = read_mn(lb, BN, mn_base(BN, wn0 + 16 * c), s);
+      else b[c] = lb[swz(wn0 + 16 * c + cl, ch)];
     }
+  };
+  // the FN MFMAs of accumulator row f
+  auto mma_row = [&](int f, const u32x4 (&a)[FM], const u32x4 (&b)[FN]) {
+#pragma unroll
+    for (int c = 0; c < FN; ++c)
+      acc[f][c] = DTYPE == 0 ? mfma16_bf16(a[f], b[c], acc[f][c]) : mfma16_f16(a[f], b[c], acc[f][c]);
+  };
+  constexpr int NFRAG = FM + FN, RROWS = FM / 2;   // fragment reads spread over the first FM/2 rows
+
+  // Every buffer starts filled.  Per k tile kt (its first k step already in
+  // registers r0), with scheduling barriers fixing the order:
+  //  1. MFMA rows of the first k step, the second k step read into r1
+  //     between rows 0 .. FM/2-1;
+  //  2. one barrier: stage kt + 1 has landed for every wave, and nobody reads
+  //     stage kt any more (all reads of it are complete); stage kt's buffer
+  //     is refilled with stage kt + STAGES;
+  //  3. MFMA rows of the second k step, the first k step of kt + 1 read into
+  //     r0 between rows 0 .. FM/2-1.
+  // So the matrix unit waits for neither an operand read nor a load issue,
+  // only at the one barrier per k tile.  Where the barrier and the refill go
+  // is measured per operand form: with K-contiguous operands the barrier
+  // follows the first k step and the refill loads are spread over the rows of
+  // the second; with a transposed operand (whose loads take longer to land)
+  // the barrier comes right after the reads of r1, half-way through the
+  // first k step, and the refill is issued at once, a whole k tile before
+  // it is needed.
+  constexpr bool EARLY = A_MN || B_MN;
+#pragma unroll
+  for (int st = 0; st < STAGES; ++st)
+    if (st < ktiles)
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j) issue1(st, j);
+  if (ktiles >= STAGES) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * (STAGES - 1)));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  lds_barrier();
+  u32x4 r0a[FM], r0b[FN], r1a[FM], r1b[FN];
+#pragma unroll
+  for (int j = 0; j < NFRAG; ++j) read1(0, 0, j, r0a, r0b);
+  // one k tile; refill = kt + STAGES < ktiles, next = kt + 1 < ktiles, either
+  // compile-time (std::true_type / false_type) or run-time uniform flags
+  auto tile = [&](int kt, auto refill, auto next) {
+    constexpr int BAR_ROW = EARLY ? RROWS : FM;        // first-step rows before the barrier
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(63) & ~(0xF << 8));     // r0 complete
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < BAR_ROW; ++f) {
+      mma_row(f, r0a, r0b);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NFRAG; ++j)
+        if (j * RROWS / NFRAG == f) read1(kt, 1, j, r1a, r1b);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // stage kt + 1 landed (with a refill ahead, stages kt + 2 .. kt + STAGES - 1
+    // may stay in flight; without, fewer were issued and all are waited for),
+    // and this wave's reads of stage kt are complete
+    if (refill) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS * (STAGES - 2)) & ~(0xF << 8));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & ~(0xF << 8));
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (EARLY) {
+      if (refill) {
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) issue1(kt + STAGES, j);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int f = BAR_ROW; f < FM; ++f) mma_row(f, r0a, r0b);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+      mma_row(f, r1a, r1b);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!EARLY) {
+        if (refill) {
+#pragma unroll
+          for (int j = 0; j < LOADS; ++j)
+            if (j * FM / LOADS == f) issue1(kt + STAGES, j);
+        }
+      }
+      if (next) {
+#pragma unroll
+        for (int j = 0; j < NFRAG; ++j)
+          if (j * RROWS / NFRAG == f) read1(kt + 1, 0, j, r0a, r0b);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  if constexpr (!EARLY) {
+    // K-contiguous operands: the last tiles in loops of their own, branch-free
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    int kt = 0;
+    for (; kt + STAGES < ktiles; ++kt) tile(kt, T_{}, T_{});
+    for (; kt + 1 < ktiles; ++kt) tile(kt, F_{}, T_{});
+    tile(kt, F_{}, F_{});
+  } else {
+    // with transposed reads, separate loops made the register allocator
+    // shuffle accumulators between loops; one loop with uniform flags
+    for (int kt = 0; kt < ktiles; ++kt) tile(kt, kt + STAGES < ktiles, kt + 1 < ktiles);
   }
   __syncthreads();
 
