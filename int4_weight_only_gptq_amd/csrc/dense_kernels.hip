@@ -809,12 +809,15 @@ static void pipe_launch(const DenseArgs& a, hipStream_t stream) {
 #define QG_DENSE_T64X128 0.4
 #endif
 static int pick_pipe_tile(int64_t M, int64_t N) {
+#ifdef QG_DENSE_FORCE_TILE
+  return QG_DENSE_FORCE_TILE;       // tile sweeps
+#endif
   auto rounds = [](int64_t tiles) { return (double)((tiles + 255) / 256); };
   const double c2 = rounds(((M + 255) / 256) * ((N + 255) / 256)) * QG_DENSE_T256X256;
   const double c1 = rounds(((M + 255) / 256) * ((N + 127) / 128));
   const double c0 = rounds(((M + 127) / 128) * ((N + 127) / 128)) * QG_DENSE_T128X128;
   const double cm = rounds(((M + 63) / 64) * ((N + 127) / 128)) * QG_DENSE_T64X128;
-  if (c2 < c1 && c2 < c0 && c2 < cm) return 2;
+  if (c2 <= c1 && c2 < c0 && c2 < cm) return 2;     // ties: 256 x 256 measured 3-4% ahead
   if (c1 <= c0 && c1 <= cm) return 1;
   return c0 <= cm ? 0 : -1;
 }
