@@ -18,6 +18,9 @@ What it computes
   Y[m][n] = X[m][k] . W, W[k][n] the dequantised weights.  The oracle forms W
   in fp32 (exact: |q - z| <= 15 has 4 bits and s has 11) and accumulates the
   products of the bf16 activations with it in fp64.
+* the variant without a zero point (the mi50grad README, "Project Structure":
+  an AWQ GEMV variant that skips the zero-point subtraction): w = q * s, the
+  same storage without qzeros (passed as None here).
 * dense products C = op(A) op(B) with fp32-accumulating bf16/fp16 inputs (the
   BC-250 tuned-GEMM post, "Where the time went" and "Checking the results are
   right": forward, input-gradient and weight-gradient products, each checked
@@ -108,23 +111,27 @@ def dequant(qweight, scales, qzeros, k: int, n: int, group_size: int = GROUP_SIZ
             cols=None) -> np.ndarray:
     """W32[i][j] = fp32((q[i][j] - z[g][j]) * s[g][j]), g = i // group_size.
 
+    qzeros None: no zero point, W32[i][j] = fp32(q[i][j] * s[g][j]).
     Returns fp32 [k][n] (or [k][len(cols)] for a column subset).  The product of a
     4-bit integer and an fp16 scale is exact in fp32; this is asserted.
     """
     groups = k // group_size
     qweight = np.asarray(qweight)
     scales = np.asarray(scales).reshape(groups, n)
-    qzeros = np.asarray(qzeros)
     if cols is None:
         q = unpack_qweight(qweight, k, n)
-        z = unpack_qzeros(qzeros, groups, n)
+        z = (np.zeros((groups, n), dtype=np.int64) if qzeros is None
+             else unpack_qzeros(np.asarray(qzeros), groups, n))
         s = fp16_value(scales)
     else:
         # the same definitions, evaluated only for the requested columns
         cols = np.asarray(cols)
         q = unpack_qweight(qweight[:, cols], k, len(cols))
-        zw = qzeros[:, cols // 8].astype(np.int64)
-        z = (zw // (16 ** (cols % 8))[None, :]) % 16
+        if qzeros is None:
+            z = np.zeros((groups, len(cols)), dtype=np.int64)
+        else:
+            zw = np.asarray(qzeros)[:, cols // 8].astype(np.int64)
+            z = (zw // (16 ** (cols % 8))[None, :]) % 16
         s = fp16_value(scales[:, cols])
     g = np.arange(k) // group_size
     w64 = (q - z[g, :]).astype(np.float64) * s[g, :]

@@ -147,6 +147,17 @@ def test_dequant_hand_values():
         assert np.all(got == np.float32(w)), (parts, got[0, 0])
 
 
+def test_dequant_without_zero_point_hand_values():
+    for parts in _golden_lines("awq"):
+        q, sbits, w = int(parts[1]), int(parts[2], 16), float(parts[4])
+        qw = np.full((16, 8), q * 0x11111111, dtype=np.uint32)
+        sc = np.full((1, 8), sbits, dtype=np.uint16)
+        got = oracle.dequant(qw, sc, None, 128, 8)
+        assert np.all(got == np.float32(w)), (parts, got[0, 0])
+        sub = oracle.dequant(qw, sc, None, 128, 8, cols=np.array([3, 5]))
+        assert np.all(sub == np.float32(w))
+
+
 def test_dequant_group_index():
     # k = 256: group 0 (rows 0..127) has s = 0.5, z = 3; group 1 s = 0.25, z = 15
     k, n = 256, 8
@@ -250,6 +261,23 @@ def test_brute_force_small_int4():
                 terms.append(_bf16_py(d["x"][r, i]) * ((q - z) * s))
             exact = math.fsum(terms)
             assert abs(y[r, j] - exact) <= 1e-12 * max(1.0, abs(exact))
+
+
+def test_brute_force_small_int4_without_zero_point():
+    m, k, n = 2, 256, 8
+    d = int4_inputs(m, k, n, seed=17)
+    y = oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], None, m, k, n)
+    for r in range(m):
+        for j in range(n):
+            terms = []
+            for i in range(k):
+                q = (int(d["qweight"][i >> 3, j]) >> ((i & 7) << 2)) & 0xF
+                s = _fp16_py(d["scales"][i >> 7, j])
+                terms.append(_bf16_py(d["x"][r, i]) * (q * s))
+            exact = math.fsum(terms)
+            assert abs(y[r, j] - exact) <= 1e-12 * max(1.0, abs(exact))
+    part = oracle.qgemm_int4_at(d["x"], d["qweight"], d["scales"], None, k, n, [1], [2, 7])
+    np.testing.assert_allclose(part, y[np.ix_([1], [2, 7])], rtol=1e-14, atol=1e-14)
 
 
 def test_sampled_outputs_match_full():
