@@ -45,10 +45,10 @@ SMALL_M = [(4096, 4096), (2048, 8192)]
 SMALL_M_TOKENS = [1, 8, 15]
 
 
-def int4_bytes(m, k, n):
+def int4_bytes(m, k, n, zeros=True):
     """Algorithmic bytes of one int4 call: every tensor touched once."""
     g = k // 128
-    return k * n // 2 + g * n * 2 + g * n // 2 + 2 * m * k + 2 * m * n
+    return k * n // 2 + g * n * 2 + (g * n // 2 if zeros else 0) + 2 * m * k + 2 * m * n
 
 
 def dense_bytes(M, N, K):
@@ -70,7 +70,7 @@ def parse():
 class Int4Case:
     """One int4 product with `copies` resident copies of its weights."""
 
-    def __init__(self, qg, torch, m, k, n, seed, copies):
+    def __init__(self, qg, torch, m, k, n, seed, copies, zeros=True):
         from qgemm_inputs import int4_inputs
         import numpy as np
 
@@ -81,13 +81,14 @@ class Int4Case:
         self.x = torch.from_numpy(d["x"].view(np.int16)).to(dev).view(torch.bfloat16)
         qw = torch.from_numpy(d["qweight"].view(np.int32)).to(dev)
         sc = torch.from_numpy(d["scales"].view(np.int16)).to(dev).view(torch.float16)
-        qz = torch.from_numpy(d["qzeros"].view(np.int32)).to(dev)
-        self.w = [(qw, sc, qz)] + [(qw.clone(), sc.clone(), qz.clone()) for _ in range(copies - 1)]
+        qz = torch.from_numpy(d["qzeros"].view(np.int32)).to(dev) if zeros else None
+        self.w = [(qw, sc, qz)] + [(qw.clone(), sc.clone(), None if qz is None else qz.clone())
+                                   for _ in range(copies - 1)]
         self.y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         self.i = 0
         self.qg = qg
         self.kernel = qg.describe_int4(m, n, k).split(" ")[0]
-        self.bytes = int4_bytes(m, k, n)
+        self.bytes = int4_bytes(m, k, n, zeros)
         self.flops = 2 * m * n * k
 
     def launch(self, path="auto"):
@@ -310,6 +311,20 @@ def run_suite(qg, torch, args, path):
                          "gbps": c.bytes / us / 1e3, "tflops": c.flops / us / 1e6,
                          "mfma_frac": c.flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS})
             print("suite int4", rows[-1], file=sys.stderr, flush=True)
+            del c
+            torch.cuda.empty_cache()
+    # weights without a zero point (qzeros NULL) on the small-M and prefill shapes
+    for cfg in (1, 2):
+        for (_, m, k, n, seed) in int4_cases(cfg):
+            c = Int4Case(qg, torch, m, k, n, seed, copies_for(int4_bytes(0, k, n, False), args.regime),
+                         zeros=False)
+            for _ in range(3):
+                c.launch()
+            us = time_us(torch, c.launch, iters)
+            rows.append({"kind": "int4_nozero", "m": m, "k": k, "n": n, "kernel": c.kernel, "us": us,
+                         "gbps": c.bytes / us / 1e3, "tflops": c.flops / us / 1e6,
+                         "mfma_frac": c.flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS})
+            print("suite int4_nozero", rows[-1], file=sys.stderr, flush=True)
             del c
             torch.cuda.empty_cache()
     for case in dense_cases(3):

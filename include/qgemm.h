@@ -85,7 +85,10 @@ int32_t qg_last_hip_error(void);
  *   scales   fp16 bit patterns [k/128][n], 8-byte aligned.
  *   qzeros   uint32 [k/128][n/8], 4-byte aligned.  Word (g, c) holds the 4-bit
  *            zero points of columns 8c..8c+7; column 8c+t in bits 4t..4t+3.
- *            The stored nibble is z itself (no +1 offset).
+ *            The stored nibble is z itself (no +1 offset).  NULL: weights
+ *            without a zero point, W[i][j] = q[i][j] * s[i/128][j] (the AWQ
+ *            GEMV variant of the mi50grad README, "Project Structure", which
+ *            skips the zero-point subtraction); every path accepts it.
  *   y        bf16 [m][ldy] output, ldy >= n, ldy % 4 == 0, 8-byte aligned.
  *   m >= 0 tokens, 0 <= n <= 2^26 output columns (n % 8 == 0), 0 <= k <= 2^22
  *   input rows (k % 128 == 0), group_size must be 128.
@@ -144,7 +147,8 @@ int32_t qgemm_int4_describe(int64_t m, int64_t n, int64_t k, int32_t path, int64
  *
  *   w[i][j] = (float)(q[i][j] - z[i/128][j]) * s[i/128][j],  fp32 [k][n], n-contiguous.
  *
- * w must be 16-byte aligned.  Errors as qgemm_int4.
+ * qzeros NULL: z = 0, as in qgemm_int4.  w must be 16-byte aligned.  Errors as
+ * qgemm_int4.
  */
 int32_t qgemm_int4_dequant(const uint32_t* qweight, const uint16_t* scales,
                            const uint32_t* qzeros, float* w, int64_t n, int64_t k,

@@ -124,7 +124,8 @@ def qgemm_int4(x, qweight, scales, qzeros, out=None, group_size: int = 128, path
     """Y[m][n] (bf16) = X[m][k] (bf16) . dequant(W)^T, W given in GPTQ int4 storage.
 
     qweight int32/uint32 [k/8][n]; scales fp16 [k/128][n]; qzeros int32/uint32
-    [k/128][n/8].  ``path`` forces a kernel ("gemv", "fused", "mfma") or "auto".
+    [k/128][n/8], or None for weights without a zero point (w = q * s).
+    ``path`` forces a kernel ("gemv", "fused", "mfma") or "auto".
     ``workspace``: None = a cached zero-filled buffer of the size the library
     asks for; False = no workspace (no k split); or a caller-owned uint8 tensor.
     """
@@ -145,10 +146,14 @@ def qgemm_int4(x, qweight, scales, qzeros, out=None, group_size: int = 128, path
     else:
         wptr, wbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     st = lib.qgemm_int4_path(x.data_ptr(), _ld(x), qweight.data_ptr(), scales.data_ptr(),
-                             qzeros.data_ptr(), out.data_ptr(), _ld(out), m, n, k, group_size,
+                             _ptr(qzeros), out.data_ptr(), _ld(out), m, n, k, group_size,
                              PATHS[path], wptr, wbytes, sh)
     _check(st, "qgemm_int4")
     return out
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
 
 
 def describe_int4(m: int, n: int, k: int, path: str = "auto", workspace_bytes=None) -> str:
@@ -163,14 +168,14 @@ def describe_int4(m: int, n: int, k: int, path: str = "auto", workspace_bytes=No
 
 
 def qgemm_int4_dequant(qweight, scales, qzeros, out=None, group_size: int = 128, stream=None):
-    """fp32 [k][n] dequantised weights (q - z) * s."""
+    """fp32 [k][n] dequantised weights (q - z) * s (q * s when qzeros is None)."""
     import torch
 
     lib = load()
     k, n = qweight.shape[0] * 8, qweight.shape[1]
     if out is None:
         out = torch.empty((k, n), dtype=torch.float32, device=qweight.device)
-    st = lib.qgemm_int4_dequant(qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(),
+    st = lib.qgemm_int4_dequant(qweight.data_ptr(), scales.data_ptr(), _ptr(qzeros),
                                 out.data_ptr(), n, k, group_size, _stream(qweight, stream))
     _check(st, "qgemm_int4_dequant")
     return out

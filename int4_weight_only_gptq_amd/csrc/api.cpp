@@ -34,7 +34,7 @@ int32_t check_int4(const void* x, int64_t ldx, const uint32_t* qweight, const ui
   if (ldy < n) return QG_ERR_SHAPE;
   if (!aligned(y, 8) || ldy % 4 != 0) return QG_ERR_ALIGN;
   if (k == 0) return QG_OK;
-  if (x == nullptr || qweight == nullptr || scales == nullptr || qzeros == nullptr) return QG_ERR_NULL;
+  if (x == nullptr || qweight == nullptr || scales == nullptr) return QG_ERR_NULL;   // qzeros may be null
   if (ldx < k || ldx > (int64_t)1 << 22) return QG_ERR_SHAPE;
   if (!aligned(x, 16) || ldx % 8 != 0) return QG_ERR_ALIGN;
   if (!aligned(qweight, 16) || !aligned(scales, 8) || !aligned(qzeros, 4)) return QG_ERR_ALIGN;
@@ -144,7 +144,7 @@ int32_t qgemm_int4_dequant(const uint32_t* qweight, const uint16_t* scales,
   if (group_size != 128) return QG_ERR_UNSUPPORTED;
   if (k % 128 != 0 || n % 8 != 0) return QG_ERR_SHAPE;
   if (n == 0 || k == 0) return QG_OK;
-  if (qweight == nullptr || scales == nullptr || qzeros == nullptr || w == nullptr) return QG_ERR_NULL;
+  if (qweight == nullptr || scales == nullptr || w == nullptr) return QG_ERR_NULL;   // qzeros may be null
   if (!aligned(qweight, 16) || !aligned(scales, 8) || !aligned(qzeros, 4) || !aligned(w, 16))
     return QG_ERR_ALIGN;
   return hip_status(qg::launch_dequant(qweight, scales, qzeros, w, n, k, (hipStream_t)stream));

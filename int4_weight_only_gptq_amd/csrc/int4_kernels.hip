@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
   const int64_t col = (idx - r * quads) << 2;
   const u32x4 words = *reinterpret_cast<const u32x4*>(qweight + r * n + col);
   const int64_t g = r >> 4;
-  const uint32_t zw = qzeros[g * (n >> 3) + (col >> 3)] >> ((col & 7) * 4);
+  const uint32_t zw = qzeros ? qzeros[g * (n >> 3) + (col >> 3)] >> ((col & 7) * 4) : 0u;   // none: z = 0
   const u32x2 sw = *reinterpret_cast<const u32x2*>(scales + g * n + col);
   float s[4] = {half_bits_to_float(sw[0] & 0xFFFFu), half_bits_to_float(sw[0] >> 16),
                 half_bits_to_float(sw[1] & 0xFFFFu), half_bits_to_float(sw[1] >> 16)};
@@ -99,7 +99,7 @@ __device__ __forceinline__ Meta<CPL> load_meta(const uint16_t* __restrict__ scal
   } else {
     r.s[0] = *sp;
   }
-  r.z = qzeros[g * (n >> 3) + (col >> 3)];
+  r.z = qzeros ? qzeros[g * (n >> 3) + (col >> 3)] : 0u;   // no zero point: z = 0
   return r;
 }
 
@@ -474,10 +474,10 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int i = 0; i < S::ML; ++i) {
       const int j = S::NW * i + wave;
-      const void* base = j == 0 ? (const void*)(scales + g * n + n0)
-                       : (j >= 2 && j < S::MSLOTS) ? (const void*)(xsum + g * m + m0)
-                                                   : (const void*)(qzeros + g * (n >> 3) + (n0 >> 3));
-      buffer_to_lds4(base, moff[i], wl + S::W_DW + 64 * j);
+      // without zero points the zero-word slots stay unloaded (and unread)
+      if (j == 0) buffer_to_lds4(scales + g * n + n0, moff[i], wl + S::W_DW + 64 * j);
+      else if (j >= 2 && j < S::MSLOTS) buffer_to_lds4(xsum + g * m + m0, moff[i], wl + S::W_DW + 64 * j);
+      else if (qzeros) buffer_to_lds4(qzeros + g * (n >> 3) + (n0 >> 3), moff[i], wl + S::W_DW + 64 * j);
     }
   };
 
@@ -547,7 +547,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
           gs[f] = PREP ? *reinterpret_cast<const f32x4*>(lm + 128 + wm0 + 16 * f + 4 * ks) : xs[PREP ? 0 : f];
         const int col = wn0 + 4 * cl;
         const u32x2 sv = *reinterpret_cast<const u32x2*>(lm + (col >> 1));
-        const uint32_t zw = lm[BN / 2 + (col >> 3)] >> (4 * (col & 7));
+        const uint32_t zw = qzeros ? lm[BN / 2 + (col >> 3)] >> (4 * (col & 7)) : 0u;
         sc[0] = half_bits_to_float(sv[0] & 0xFFFFu);
         sc[1] = half_bits_to_float(sv[0] >> 16);
         sc[2] = half_bits_to_float(sv[1] & 0xFFFFu);

@@ -74,7 +74,9 @@ def int4(lib, x=A16, ldx=256, qw=A16, sc=A16, qz=A16, y=A16, ldy=64, m=1, n=64, 
 @pytest.mark.parametrize("kw,code", [
     (dict(m=-1), SHAPE), (dict(n=-8), SHAPE), (dict(k=-128), SHAPE),
     (dict(gs=64), UNSUP), (dict(k=200), SHAPE), (dict(n=60), SHAPE),
-    (dict(x=0), NULL), (dict(qw=0), NULL), (dict(sc=0), NULL), (dict(qz=0), NULL), (dict(y=0), NULL),
+    (dict(x=0), NULL), (dict(qw=0), NULL), (dict(sc=0), NULL), (dict(y=0), NULL),
+    # qzeros NULL is valid (no zero point): the call gets past the pointer checks
+    (dict(qz=0, x=MIS), ALIGN),
     (dict(ldx=128), SHAPE), (dict(ldy=32), SHAPE),
     (dict(x=MIS), ALIGN), (dict(ldx=260), ALIGN), (dict(qw=A16 + 4), ALIGN),
     (dict(sc=A16 + 2), ALIGN), (dict(qz=A16 + 2), ALIGN), (dict(y=A16 + 2), ALIGN),
@@ -101,6 +103,8 @@ def test_dequant_rejects_invalid_arguments(lib):
     assert d(A16, A16, A16, A16, 64, 128, 32, None) == UNSUP
     assert d(0, A16, A16, A16, 64, 128, 128, None) == NULL
     assert d(A16, A16, A16, A16 + 4, 64, 128, 128, None) == ALIGN
+    assert d(A16, A16, 0, A16 + 4, 64, 128, 128, None) == ALIGN     # qzeros NULL accepted
+    assert d(A16, A16, A16, 0, 64, 128, 128, None) == NULL
     assert d(0, 0, 0, 0, 0, 128, 128, None) == OK
 
 

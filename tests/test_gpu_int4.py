@@ -262,3 +262,44 @@ def test_full_size_sampled(gpu_lib, cfg, case):
     cols = sample_indices(n, 160, seed + 1)
     ref = oracle.qgemm_int4_at(d["x"], d["qweight"], d["scales"], d["qzeros"], k, n, rows, cols)
     assert_accepted(y[np.ix_(rows, cols)], ref, ("full", cfg, m, k, n))
+
+
+# ----------------------------------------------------------------------------
+# weights without a zero point (qzeros NULL: w = q * s), every path
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("k,n", [(128, 8), (1152, 776)])
+def test_dequant_without_zero_point_bit_exact(gpu_lib, k, n):
+    say("dequant-nozero", k, n)
+    d = int4_inputs(1, k, n, seed=300 + k + n)
+    t = upload_int4(d)
+    w = gpu_lib.qgemm_int4_dequant(t["qweight"], t["scales"], None)
+    ref = oracle.dequant(d["qweight"], d["scales"], None, k, n)
+    assert np.array_equal(host_u32(w), ref.view(np.uint32))
+
+
+NOZERO_CASES = [("gemv", 1, 1152, 776), ("fused", 2, 2048, 1040), ("fused", 8, 1152, 776),
+                ("fused", 15, 2048, 1040), ("fused", 16, 1152, 776), ("mfma", 17, 2048, 1040),
+                ("mfma", 130, 1152, 776), ("mfma_nows", 33, 2048, 1040),
+                ("gemv", 1, 16384, 520), ("fused", 8, 16384, 520), ("mfma", 33, 4096, 520)]
+
+
+@pytest.mark.parametrize("path,m,k,n", NOZERO_CASES)
+def test_paths_without_zero_point_match_oracle(gpu_lib, path, m, k, n):
+    p, ws = ("mfma", False) if path == "mfma_nows" else (path, None)
+    say("nozero", path, m, k, n, gpu_lib.describe_int4(m, n, k, p, None if ws is None else 0))
+    d = int4_inputs(m, k, n, seed=400 + m + k + n)
+    t = dict(upload_int4(d), qzeros=None)
+    y = run(gpu_lib, t, p, workspace=ws)
+    ref = oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], None, m, k, n)
+    assert_accepted(host_u16(y), ref, ("nozero", path, m, k, n))
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 4096, 4096), (15, 2048, 8192), (512, 5120, 25600)])
+def test_full_size_without_zero_point_sampled(gpu_lib, m, k, n):
+    say("nozero-full", m, k, n)
+    d = int4_inputs(m, k, n, seed=500 + m)
+    y = host_u16(run(gpu_lib, dict(upload_int4(d), qzeros=None)))
+    rows = sample_indices(m, 24, m)
+    cols = sample_indices(n, 160, m + 1)
+    ref = oracle.qgemm_int4_at(d["x"], d["qweight"], d["scales"], None, k, n, rows, cols)
+    assert_accepted(y[np.ix_(rows, cols)], ref, ("nozero-full", m, k, n))
