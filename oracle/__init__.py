@@ -17,6 +17,8 @@ from .qgemm_oracle import (  # noqa: F401
     qgemm_int4_at,
     dense,
     dense_at,
+    dense_batched,
+    dense_batched_at,
     grid_bracket,
     round_to_grid,
     accept,

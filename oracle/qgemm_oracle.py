@@ -28,6 +28,8 @@ What it computes
     NT: C[M][N] = A[M][K] . B[N][K]^T   (forward)
     NN: C[M][N] = A[M][K] . B[K][N]     (input gradient)
     TN: C[M][N] = A[K][M]^T . B[K][N]   (weight gradient)
+  and batches of them (the batched products inside attention), one product per
+  leading index.
 * acceptance of an output y against the fp64 value r (the NF12 pull request,
   "Accuracy": zero violations of |err| <= 2e-3 + 2e-3 |ref|).  Read together
   with its statement that the rms error it sees is the BF16 rounding floor, an
@@ -189,6 +191,26 @@ def dense_at(layout: str, dtype: str, a_bits, b_bits, rows, cols) -> np.ndarray:
     """C64 restricted to the given rows and columns."""
     opA, opB = _ops(layout, a_bits, b_bits, dtype)
     return opA[np.asarray(rows), :] @ opB[:, np.asarray(cols)]
+
+
+def dense_batched(layout: str, dtype: str, a_bits, b_bits, M: int, N: int, K: int) -> np.ndarray:
+    """C64[b] = op(A[b]) . op(B[b]) for b over the leading (batch) axis, fp64 [batch][M][N].
+
+    The batched attention products of the BC-250 tuned-GEMM post ("Tuning the
+    kernels", "Checking the results are right"): independent products of one
+    shape, each defined as `dense`.
+    """
+    a_bits, b_bits = np.asarray(a_bits), np.asarray(b_bits)
+    assert a_bits.shape[0] == b_bits.shape[0]
+    out = np.zeros((a_bits.shape[0], M, N))
+    for i in range(a_bits.shape[0]):
+        out[i] = dense(layout, dtype, a_bits[i], b_bits[i], M, N, K)
+    return out
+
+
+def dense_batched_at(layout: str, dtype: str, a_bits, b_bits, index, rows, cols) -> np.ndarray:
+    """C64[index] restricted to the given rows and columns."""
+    return dense_at(layout, dtype, np.asarray(a_bits)[index], np.asarray(b_bits)[index], rows, cols)
 
 
 # ----------------------------------------------------------------------------

@@ -12,5 +12,8 @@ from .gen import (  # noqa: F401
     f64_to_fp16_bits,
     int4_inputs,
     dense_inputs,
+    dense_batched_inputs,
 )
-from .configs import INT4_CONFIGS, DENSE_CONFIGS, int4_cases, dense_cases  # noqa: F401
+from .configs import (  # noqa: F401
+    INT4_CONFIGS, DENSE_CONFIGS, ATTENTION_CONFIG, int4_cases, dense_cases, attention_cases,
+)

@@ -7,7 +7,14 @@ dense shapes are the per-layer training products of the BC-250 tuned-GEMM post
 ("Tuning the kernels": every layer at 1,024, 2,048 and 4,096 tokens and the
 rank-16 LoRA matrices) for a model with hidden size 2048 and FFN size 5632.
 
-Seeds: case i of config c uses seed (1000 + c) * 65536 + i.
+The batched attention products (the same post tunes "the batched products
+inside attention" and validates batched attention shapes) are taken at the same
+token counts for one sequence whose hidden size 2048 is split into 32 heads of
+64 (the pages give no head layout; this split is a reading): per head the
+scores S = Q K^T, the output O = P V, and the gradients dP = dO V^T,
+dV = P^T dO, dQ = dS K and dK = dS^T Q.
+
+Seeds: case i of config c uses seed (1000 + c) * 65536 + i (attention: c = 5).
 """
 from __future__ import annotations
 
@@ -28,6 +35,10 @@ DENSE_CONFIGS = {
         # weight matrices W[n][k] of the FFN: up/gate [5632][2048], down [2048][5632]
         "weights": [(5632, 2048), (2048, 5632)], "dtypes": ["bf16", "fp16"], "lora_rank": 16},
 }
+
+
+ATTENTION_CONFIG = {"name": "batched attention products", "tokens": [1024, 2048, 4096], "heads": 32,
+                    "head_dim": 64, "dtypes": ["bf16", "fp16"], "std": 1.0}
 
 
 def seed_for(config: int, case: int) -> int:
@@ -76,4 +87,30 @@ def dense_cases(config: int = 3, with_lora: bool = True):
                                 "N": N, "K": K, "t": t, "w": (n, k),
                                 "seed": seed_for(config, i)})
                     i += 1
+    return out
+
+
+def attention_cases():
+    """List of dict(role, layout, dtype, batch, M, N, K, seed, t) of the attention products.
+
+    For t tokens, h heads of width d (operands [h][t][d] or [h][t][t]):
+      scores  NT  M=t N=t K=d     (Q K^T)
+      pv      NN  M=t N=d K=t     (P V)
+      dp      NT  M=t N=t K=d     (dO V^T)
+      dv      TN  M=t N=d K=t     (P^T dO)
+      dq      NN  M=t N=d K=t     (dS K)
+      dk      TN  M=t N=d K=t     (dS^T Q)
+    """
+    c = ATTENTION_CONFIG
+    h, d = c["heads"], c["head_dim"]
+    out = []
+    i = 0
+    for dtype in c["dtypes"]:
+        for t in c["tokens"]:
+            for role, layout, M, N, K in (("scores", "NT", t, t, d), ("pv", "NN", t, d, t),
+                                          ("dp", "NT", t, t, d), ("dv", "TN", t, d, t),
+                                          ("dq", "NN", t, d, t), ("dk", "TN", t, d, t)):
+                out.append({"role": role, "layout": layout, "dtype": dtype, "batch": h, "M": M,
+                            "N": N, "K": K, "t": t, "seed": seed_for(5, i)})
+                i += 1
     return out

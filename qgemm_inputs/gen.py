@@ -131,3 +131,13 @@ def dense_inputs(layout: str, dtype: str, M: int, N: int, K: int, seed: int,
     a = normal_bits(rng, sa, std, dtype)
     b = normal_bits(rng, sb, std, dtype)
     return {"a": a, "b": b, "layout": layout, "dtype": dtype, "M": M, "N": N, "K": K}
+
+
+def dense_batched_inputs(layout: str, dtype: str, batch: int, M: int, N: int, K: int, seed: int,
+                         std: float = 0.02) -> dict:
+    """Raw inputs of `batch` dense products: a [batch][...] then b [batch][...], N(0, std^2)."""
+    rng = SplitMix64(seed)
+    sa, sb = dense_shapes(layout, M, N, K)
+    a = normal_bits(rng, (batch,) + tuple(sa), std, dtype)
+    b = normal_bits(rng, (batch,) + tuple(sb), std, dtype)
+    return {"a": a, "b": b, "layout": layout, "dtype": dtype, "batch": batch, "M": M, "N": N, "K": K}

@@ -14,7 +14,8 @@ import numpy as np
 import pytest
 
 import oracle
-from qgemm_inputs import SplitMix64, f32_to_bf16_bits, f64_to_fp16_bits, int4_inputs, dense_inputs
+from qgemm_inputs import (SplitMix64, f32_to_bf16_bits, f64_to_fp16_bits, int4_inputs, dense_inputs,
+                          dense_batched_inputs)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -395,6 +396,35 @@ def test_dense_brute_force(layout, dtype):
                 b = d["b"][j, p] if layout == "NT" else d["b"][p, j]
                 terms.append(dec(a) * dec(b))
             assert abs(c[i, j] - math.fsum(terms)) <= 1e-14 * max(1.0, abs(c[i, j]))
+
+
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_dense_batched_brute_force(layout):
+    bt, M, N, K = 3, 2, 3, 4
+    d = dense_batched_inputs(layout, "fp16", bt, M, N, K, seed=24, std=1.0)
+    c = oracle.dense_batched(layout, "fp16", d["a"], d["b"], M, N, K)
+    assert c.shape == (bt, M, N)
+    for q in range(bt):
+        for i in range(M):
+            for j in range(N):
+                terms = []
+                for p in range(K):
+                    a = d["a"][q, i, p] if layout in ("NT", "NN") else d["a"][q, p, i]
+                    b = d["b"][q, j, p] if layout == "NT" else d["b"][q, p, j]
+                    terms.append(_fp16_py(a) * _fp16_py(b))
+                assert abs(c[q, i, j] - math.fsum(terms)) <= 1e-14 * max(1.0, abs(c[q, i, j]))
+    part = oracle.dense_batched_at(layout, "fp16", d["a"], d["b"], 2, [1], [0, 2])
+    assert np.array_equal(part, c[2][np.ix_([1], [0, 2])])
+
+
+def test_dense_batched_scaled_identities():
+    # B[q] = (q + 1) I: the products are the A[q] scaled by q + 1, exactly
+    bt, M = 4, 8
+    d = dense_batched_inputs("NN", "bf16", bt, M, M, M, seed=25, std=1.0)
+    eyes = np.stack([_store((q + 1) * np.eye(M), "bf16") for q in range(bt)])
+    c = oracle.dense_batched("NN", "bf16", d["a"], eyes, M, M, M)
+    for q in range(bt):
+        assert np.array_equal(c[q], (q + 1) * oracle.bf16_value(d["a"][q]))
 
 
 @pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
