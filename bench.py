@@ -340,6 +340,27 @@ def run_suite(qg, torch, args, path):
                      "gbps": dense_bytes(M, N, K) / us / 1e3, "tflops": 2 * M * N * K / us / 1e6,
                      "mfma_frac": 2 * M * N * K / us / 1e6 / MFMA_BF16_PEAK_TFLOPS})
         print("suite dense", rows[-1], file=sys.stderr, flush=True)
+    # batched attention products; operands drawn on the device from a seeded
+    # generator (timing only: the parity tests use the host generator)
+    from qgemm_inputs import attention_cases
+    for case in attention_cases():
+        dt = torch.bfloat16 if case["dtype"] == "bf16" else torch.float16
+        bt, M, N, K, layout = case["batch"], case["M"], case["N"], case["K"], case["layout"]
+        sa = (bt, M, K) if layout != "TN" else (bt, K, M)
+        sb = (bt, N, K) if layout == "NT" else (bt, K, N)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(case["seed"])
+        a = torch.randn(sa, generator=g, device="cuda", dtype=torch.float32).to(dt)
+        b = torch.randn(sb, generator=g, device="cuda", dtype=torch.float32).to(dt)
+        out = qg.gemm_dense_batched(layout, a, b)
+        us = time_us(torch, lambda: qg.gemm_dense_batched(layout, a, b, out=out), iters)
+        rows.append({"kind": "attention", "role": case["role"], "layout": layout, "dtype": case["dtype"],
+                     "batch": bt, "M": M, "N": N, "K": K, "us": us,
+                     "gbps": bt * dense_bytes(M, N, K) / us / 1e3, "tflops": 2 * bt * M * N * K / us / 1e6,
+                     "mfma_frac": 2 * bt * M * N * K / us / 1e6 / MFMA_BF16_PEAK_TFLOPS})
+        print("suite attention", rows[-1], file=sys.stderr, flush=True)
+        del a, b, out
+        torch.cuda.empty_cache()
     with open(path, "w") as f:
         json.dump({"regime": args.regime, "rows": rows}, f, indent=1)
 

@@ -172,6 +172,24 @@ int32_t qgemm_int4_dequant(const uint32_t* qweight, const uint16_t* scales,
 int32_t gemm_dense(int32_t layout, int32_t dtype, int64_t M, int64_t N, int64_t K, const void* A,
                    int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream);
 
+/*
+ * gemm_dense_batched -- `batch` independent gemm_dense products in one launch,
+ * the batched products inside attention that the BC-250 tuned-GEMM post tunes
+ * and validates ("Tuning the kernels", "Checking the results are right"):
+ *
+ *   C_b = op(A_b) . op(B_b),  A_b = A + b * stride_a, B_b = B + b * stride_b,
+ *   C_b = C + b * stride_c  (strides in elements), b = 0 .. batch-1,
+ *
+ * each product as gemm_dense defines it (same layouts, dtypes, rounding and
+ * leading dimensions).  0 <= batch <= 65535; strides >= 0 (an input stride of
+ * 0 reuses one operand for every product); when batch > 1 the outputs must not
+ * overlap: stride_c >= (M - 1) * ldc + N.  batch == 1 ignores the strides.
+ * Errors as gemm_dense.
+ */
+int32_t gemm_dense_batched(int32_t layout, int32_t dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
+                           const void* A, int64_t lda, int64_t stride_a, const void* B, int64_t ldb,
+                           int64_t stride_b, void* C, int64_t ldc, int64_t stride_c, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,7 +11,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["load", "lib_path", "QGemmError", "qgemm_int4", "qgemm_int4_dequant", "gemm_dense", "describe_int4",
+__all__ = ["load", "lib_path", "QGemmError", "qgemm_int4", "qgemm_int4_dequant", "gemm_dense",
+           "gemm_dense_batched", "describe_int4",
            "workspace_size",
            "abi_version", "PATHS", "LAYOUTS"]
 
@@ -67,6 +68,9 @@ def load():
     lib.qgemm_int4_dequant.argtypes = [vp, vp, vp, vp, i64, i64, i32, vp]
     lib.gemm_dense.restype = i32
     lib.gemm_dense.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
+    lib.gemm_dense_batched.restype = i32
+    lib.gemm_dense_batched.argtypes = [i32, i32, i64, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64,
+                                       i64, vp]
     _lib = lib
     return lib
 
@@ -202,4 +206,37 @@ def gemm_dense(layout: str, a, b, out=None, stream=None):
     st = lib.gemm_dense(LAYOUTS[layout], _DTYPES[dtype], M, N, K, a.data_ptr(), _ld(a),
                         b.data_ptr(), _ld(b), out.data_ptr(), _ld(out), _stream(a, stream))
     _check(st, "gemm_dense")
+    return out
+
+
+def gemm_dense_batched(layout: str, a, b, out=None, stream=None):
+    """C[i] = op(A[i]) . op(B[i]) for 3-D tensors [batch][rows][cols] (row-major per
+    matrix, last dimension contiguous; any batch strides, 0 to reuse one operand)."""
+    import torch
+
+    lib = load()
+    if a.dtype != b.dtype or a.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("A and B must share dtype bf16 or fp16")
+    if a.dim() != 3 or b.dim() != 3 or a.shape[0] != b.shape[0]:
+        raise ValueError("A and B must be [batch][rows][cols] with the same batch")
+    dtype = "bf16" if a.dtype == torch.bfloat16 else "fp16"
+    batch = a.shape[0]
+    if layout == "NT":
+        (M, K), N = a.shape[1:], b.shape[1]
+    elif layout == "NN":
+        (M, K), N = a.shape[1:], b.shape[2]
+    elif layout == "TN":
+        (K, M), N = a.shape[1:], b.shape[2]
+    else:
+        raise ValueError(layout)
+    if out is None:
+        out = torch.empty((batch, M, N), dtype=a.dtype, device=a.device)
+    for t in (a, b, out):
+        if t.shape[-1] > 1 and t.stride(-1) != 1:
+            raise ValueError("last dimension must be contiguous")
+    st = lib.gemm_dense_batched(LAYOUTS[layout], _DTYPES[dtype], batch, M, N, K,
+                                a.data_ptr(), a.stride(1), a.stride(0), b.data_ptr(), b.stride(1),
+                                b.stride(0), out.data_ptr(), out.stride(1), out.stride(0),
+                                _stream(a, stream))
+    _check(st, "gemm_dense_batched")
     return out

@@ -150,14 +150,17 @@ int32_t qgemm_int4_dequant(const uint32_t* qweight, const uint16_t* scales,
   return hip_status(qg::launch_dequant(qweight, scales, qzeros, w, n, k, (hipStream_t)stream));
 }
 
-int32_t gemm_dense(int32_t layout, int32_t dtype, int64_t M, int64_t N, int64_t K, const void* A,
-                   int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
+static int32_t run_dense(int32_t layout, int32_t dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
+                         const void* A, int64_t lda, int64_t sa, const void* B, int64_t ldb, int64_t sb,
+                         void* C, int64_t ldc, int64_t sc, void* stream) {
   if (layout < QG_NT || layout > QG_TN) return QG_ERR_LAYOUT;
   if (dtype != QG_BF16 && dtype != QG_FP16) return QG_ERR_DTYPE;
-  if (M < 0 || N < 0 || K < 0) return QG_ERR_SHAPE;
-  if (M == 0 || N == 0) return QG_OK;
+  if (M < 0 || N < 0 || K < 0 || batch < 0 || batch > 65535) return QG_ERR_SHAPE;
+  if (sa < 0 || sb < 0 || sc < 0) return QG_ERR_SHAPE;
+  if (M == 0 || N == 0 || batch == 0) return QG_OK;
   if (C == nullptr) return QG_ERR_NULL;
   if (ldc < N) return QG_ERR_SHAPE;
+  if (batch > 1 && sc < (M - 1) * ldc + N) return QG_ERR_SHAPE;     // outputs must not overlap
   if (!aligned(C, 2)) return QG_ERR_ALIGN;
   if (K > 0) {
     if (A == nullptr || B == nullptr) return QG_ERR_NULL;
@@ -166,9 +169,22 @@ int32_t gemm_dense(int32_t layout, int32_t dtype, int64_t M, int64_t N, int64_t 
     if (lda < a_row || ldb < b_row) return QG_ERR_SHAPE;
     if (!aligned(A, 2) || !aligned(B, 2)) return QG_ERR_ALIGN;
   }
+  if (batch == 1) sa = sb = sc = 0;
   const qg::DenseArgs a{layout, dtype, M, N, K, (const uint16_t*)A, lda, (const uint16_t*)B, ldb,
-                        (uint16_t*)C, ldc};
+                        (uint16_t*)C, ldc, batch, sa, sb, sc};
   return hip_status(qg::launch_dense(a, (hipStream_t)stream));
+}
+
+int32_t gemm_dense(int32_t layout, int32_t dtype, int64_t M, int64_t N, int64_t K, const void* A,
+                   int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
+  return run_dense(layout, dtype, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, stream);
+}
+
+int32_t gemm_dense_batched(int32_t layout, int32_t dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
+                           const void* A, int64_t lda, int64_t stride_a, const void* B, int64_t ldb,
+                           int64_t stride_b, void* C, int64_t ldc, int64_t stride_c, void* stream) {
+  return run_dense(layout, dtype, batch, M, N, K, A, lda, stride_a, B, ldb, stride_b, C, ldc, stride_c,
+                   stream);
 }
 
 }  // extern "C"

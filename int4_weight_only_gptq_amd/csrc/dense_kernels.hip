@@ -78,7 +78,10 @@ __global__ __launch_bounds__(256) void dense_tile_kernel(const uint16_t* __restr
                                                          const uint16_t* __restrict__ B, int64_t ldb,
                                                          uint16_t* __restrict__ C, int64_t ldc, int M,
                                                          int N, int K, int tiles_n, int tiles,
-                                                         int tiles_per_xcd, int vec_store) {
+                                                         int tiles_per_xcd, int vec_store, BatchStrides bs) {
+  A += blockIdx.y * bs.a;   // batch blockIdx.y
+  B += blockIdx.y * bs.b;
+  C += blockIdx.y * bs.c;
   constexpr bool A_T = (LAYOUT == 2);            // A stored [K][M]
   constexpr bool B_T = (LAYOUT != 0);            // B stored [K][N]
   constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
@@ -258,7 +261,10 @@ template <int LAYOUT, int DTYPE, int BM, int BN, int STAGES>
 __global__ __launch_bounds__(256) void dense_pipe_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_n, int tiles,
-    int tiles_per_xcd, int vec_store) {
+    int tiles_per_xcd, int vec_store, BatchStrides bs) {
+  A += blockIdx.y * bs.a;   // batch blockIdx.y
+  B += blockIdx.y * bs.b;
+  C += blockIdx.y * bs.c;
   constexpr bool A_MN = (LAYOUT == 2);           // A stored [K][M]
   constexpr bool B_MN = (LAYOUT != 0);           // B stored [K][N]
   constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
@@ -558,7 +564,10 @@ template <int LAYOUT, int DTYPE>
 __global__ __launch_bounds__(64 * SK_W) void dense_splitk16_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_n, int tiles,
-    int tiles_per_xcd) {
+    int tiles_per_xcd, BatchStrides bs) {
+  A += blockIdx.y * bs.a;   // batch blockIdx.y
+  B += blockIdx.y * bs.b;
+  C += blockIdx.y * bs.c;
   constexpr bool A_MN = (LAYOUT == 2), B_MN = (LAYOUT != 0);
   constexpr int U = (A_MN && B_MN) ? 2 : 4;
   constexpr int NSTAGED = (A_MN ? 1 : 0) + (B_MN ? 1 : 0);
@@ -634,7 +643,10 @@ template <int LAYOUT, int DTYPE>
 __global__ __launch_bounds__(256) void dense_smallk_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_n, int tiles,
-    int tiles_per_xcd, int vec_store) {
+    int tiles_per_xcd, int vec_store, BatchStrides bs) {
+  A += blockIdx.y * bs.a;   // batch blockIdx.y
+  B += blockIdx.y * bs.b;
+  C += blockIdx.y * bs.c;
   constexpr bool B_MN = (LAYOUT == 1);
   __shared__ u32x4 bstage[B_MN ? 4 * 256 : 1];   // per wave: 32 k-rows x 64 columns
   const int t = (blockIdx.x & 7) * tiles_per_xcd + (blockIdx.x >> 3);
@@ -733,7 +745,10 @@ template <int LAYOUT, int DTYPE>
 __global__ __launch_bounds__(256) void dense_generic_kernel(const uint16_t* __restrict__ A, int64_t lda,
                                                             const uint16_t* __restrict__ B, int64_t ldb,
                                                             uint16_t* __restrict__ C, int64_t ldc,
-                                                            int64_t M, int64_t N, int64_t K) {
+                                                            int64_t M, int64_t N, int64_t K, BatchStrides bs) {
+  A += blockIdx.y * bs.a;   // batch blockIdx.y
+  B += blockIdx.y * bs.b;
+  C += blockIdx.y * bs.c;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= M * N) return;
   const int64_t r = i / N, c = i - r * N;
@@ -749,10 +764,12 @@ __global__ __launch_bounds__(256) void dense_generic_kernel(const uint16_t* __re
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+static BatchStrides strides(const DenseArgs& a) { return BatchStrides{a.sa, a.sb, a.sc}; }
+
 // Whether the tile kernel's 16-byte operand loads fit this problem.
 static bool mfma_fits(const DenseArgs& a) {
   if (!aligned16(a.A) || !aligned16(a.B)) return false;
-  if (a.lda % 8 || a.ldb % 8) return false;
+  if (a.lda % 8 || a.ldb % 8 || a.sa % 8 || a.sb % 8) return false;
   const int64_t a_contig = a.layout == 2 ? a.M : a.K;
   const int64_t b_contig = a.layout == 0 ? a.K : a.N;
   if (a_contig % 8 || b_contig % 8) return false;
@@ -767,10 +784,10 @@ template <int LAYOUT, int DTYPE, int BM, int BN>
 static void tile_launch(const DenseArgs& a, hipStream_t stream) {
   const int tiles_m = (int)((a.M + BM - 1) / BM), tiles_n = (int)((a.N + BN - 1) / BN);
   const int tiles = tiles_m * tiles_n, per_xcd = (tiles + 7) / 8;
-  const int vec = aligned16(a.C) && a.ldc % 8 == 0;
+  const int vec = aligned16(a.C) && a.ldc % 8 == 0 && a.sc % 8 == 0;
   const size_t lds = (size_t)DenseSmem<BM, BN>::kHalves * 2;
-  dense_tile_kernel<LAYOUT, DTYPE, BM, BN><<<dim3((unsigned)(per_xcd * 8)), dim3(256), lds, stream>>>(
-      a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, vec);
+  dense_tile_kernel<LAYOUT, DTYPE, BM, BN><<<dim3((unsigned)(per_xcd * 8), (unsigned)a.batch), dim3(256), lds, stream>>>(
+      a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, vec, strides(a));
 }
 
 #ifndef QG_DENSE_PIPE_STAGES
@@ -781,12 +798,12 @@ template <int LAYOUT, int DTYPE, int BM, int BN, int STAGES>
 static void pipe_launch(const DenseArgs& a, hipStream_t stream) {
   const int tiles_m = (int)((a.M + BM - 1) / BM), tiles_n = (int)((a.N + BN - 1) / BN);
   const int tiles = tiles_m * tiles_n, per_xcd = (tiles + 7) / 8;
-  const int vec = aligned16(a.C) && a.ldc % 8 == 0;
+  const int vec = aligned16(a.C) && a.ldc % 8 == 0 && a.sc % 8 == 0;
   const size_t main_bytes = (size_t)STAGES * (BM + BN) * 8 * 16;
   const size_t out_bytes = (size_t)BM * (BN + 8) * 2;
   const size_t lds = main_bytes > out_bytes ? main_bytes : out_bytes;
-  dense_pipe_kernel<LAYOUT, DTYPE, BM, BN, STAGES><<<dim3((unsigned)(per_xcd * 8)), dim3(256), lds, stream>>>(
-      a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, vec);
+  dense_pipe_kernel<LAYOUT, DTYPE, BM, BN, STAGES><<<dim3((unsigned)(per_xcd * 8), (unsigned)a.batch), dim3(256), lds, stream>>>(
+      a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, vec, strides(a));
 }
 
 #ifndef QG_SPLITK16_MIN_K
@@ -808,11 +825,11 @@ static void pipe_launch(const DenseArgs& a, hipStream_t stream) {
 #ifndef QG_DENSE_T64X128
 #define QG_DENSE_T64X128 0.4
 #endif
-static int pick_pipe_tile(int64_t M, int64_t N) {
+static int pick_pipe_tile(int64_t M, int64_t N, int64_t batch) {
 #ifdef QG_DENSE_FORCE_TILE
   return QG_DENSE_FORCE_TILE;       // tile sweeps
 #endif
-  auto rounds = [](int64_t tiles) { return (double)((tiles + 255) / 256); };
+  auto rounds = [batch](int64_t tiles) { return (double)((tiles * batch + 255) / 256); };
   const double c2 = rounds(((M + 255) / 256) * ((N + 255) / 256)) * QG_DENSE_T256X256;
   const double c1 = rounds(((M + 255) / 256) * ((N + 127) / 128));
   const double c0 = rounds(((M + 127) / 128) * ((N + 127) / 128)) * QG_DENSE_T128X128;
@@ -827,16 +844,16 @@ static void dense_dispatch(const DenseArgs& a, hipStream_t stream) {
   if (mfma_fits(a) && (a.M <= 16 || a.N <= 16) && a.K >= QG_SPLITK16_MIN_K) {
     const int tiles_n = (int)((a.N + 15) / 16);
     const int tiles = (int)(((a.M + 15) / 16) * tiles_n), per_xcd = (tiles + 7) / 8;
-    dense_splitk16_kernel<LAYOUT, DTYPE><<<dim3((unsigned)(per_xcd * 8)), dim3(64 * SK_W), 0, stream>>>(
-        a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd);
+    dense_splitk16_kernel<LAYOUT, DTYPE><<<dim3((unsigned)(per_xcd * 8), (unsigned)a.batch), dim3(64 * SK_W), 0, stream>>>(
+        a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, strides(a));
   } else if (LAYOUT != 2 && mfma_fits(a) && a.K <= 32 && a.M >= 64 && a.N >= 256) {
     const int tiles_n = (int)((a.N + 255) / 256);
     const int tiles = (int)(((a.M + 63) / 64) * tiles_n), per_xcd = (tiles + 7) / 8;
-    const int vec = ((uintptr_t)a.C & 7u) == 0 && a.ldc % 4 == 0;
-    dense_smallk_kernel<LAYOUT, DTYPE><<<dim3((unsigned)(per_xcd * 8)), dim3(256), 0, stream>>>(
-        a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, vec);
+    const int vec = ((uintptr_t)a.C & 7u) == 0 && a.ldc % 4 == 0 && a.sc % 4 == 0;
+    dense_smallk_kernel<LAYOUT, DTYPE><<<dim3((unsigned)(per_xcd * 8), (unsigned)a.batch), dim3(256), 0, stream>>>(
+        a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, vec, strides(a));
   } else if (mfma_fits(a) && a.K % DBK == 0 && a.M >= 128 && a.N >= 128) {
-    switch (pick_pipe_tile(a.M, a.N)) {
+    switch (pick_pipe_tile(a.M, a.N, a.batch)) {
       case 2: pipe_launch<LAYOUT, DTYPE, 256, 256, 2>(a, stream); break;
       case 1: pipe_launch<LAYOUT, DTYPE, 256, 128, QG_DENSE_PIPE_STAGES>(a, stream); break;
       case 0: pipe_launch<LAYOUT, DTYPE, 128, 128, 4>(a, stream); break;
@@ -848,14 +865,20 @@ static void dense_dispatch(const DenseArgs& a, hipStream_t stream) {
     else tile_launch<LAYOUT, DTYPE, 128, 128>(a, stream);
   } else {
     const int64_t total = a.M * a.N;
-    dense_generic_kernel<LAYOUT, DTYPE><<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(
-        a.A, a.lda, a.B, a.ldb, a.C, a.ldc, a.M, a.N, a.K);
+    dense_generic_kernel<LAYOUT, DTYPE><<<dim3((unsigned)((total + 255) / 256), (unsigned)a.batch), dim3(256), 0, stream>>>(
+        a.A, a.lda, a.B, a.ldb, a.C, a.ldc, a.M, a.N, a.K, strides(a));
   }
 }
 
 hipError_t launch_dense(const DenseArgs& a, hipStream_t stream) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
-  if (a.K == 0) return launch_zero16(a.C, a.M, a.N, a.ldc, stream);
+  if (a.K == 0) {
+    for (int64_t b = 0; b < a.batch; ++b) {
+      const hipError_t e = launch_zero16(a.C + b * a.sc, a.M, a.N, a.ldc, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   switch (a.layout * 2 + a.dtype) {
     case 0: dense_dispatch<0, 0>(a, stream); break;
     case 1: dense_dispatch<0, 1>(a, stream); break;

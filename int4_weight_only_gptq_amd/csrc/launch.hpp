@@ -55,6 +55,13 @@ struct DenseArgs {
   int64_t ldb;
   uint16_t* C;
   int64_t ldc;
+  int64_t batch;           // >= 1 products, operand b at A + b sa, B + b sb, C + b sc
+  int64_t sa, sb, sc;      // batch strides in elements (0 when batch == 1)
+};
+
+// batch strides as one kernel argument
+struct BatchStrides {
+  int64_t a, b, c;
 };
 
 hipError_t launch_dense(const DenseArgs& a, hipStream_t stream);

@@ -35,7 +35,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "qg_abi_version", "qg_status_str", "qg_last_hip_error", "qgemm_int4", "qgemm_int4_path",
-        "qgemm_int4_workspace_size", "qgemm_int4_describe", "qgemm_int4_dequant", "gemm_dense"])
+        "qgemm_int4_workspace_size", "qgemm_int4_describe", "qgemm_int4_dequant", "gemm_dense",
+        "gemm_dense_batched"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -123,6 +124,23 @@ def test_dequant_rejects_invalid_arguments(lib):
 ])
 def test_dense_rejects_invalid_arguments(lib, args, code):
     assert lib.gemm_dense(*args, None) == code
+
+
+def batched(lib, layout=0, dtype=0, batch=2, M=4, N=4, K=4, A=A16, lda=4, sa=16, B=A16, ldb=4, sb=16,
+            C=A16, ldc=4, sc=16):
+    return lib.gemm_dense_batched(layout, dtype, batch, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, sc, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(layout=3), LAYOUT), (dict(dtype=2), DTYPE), (dict(batch=-1), SHAPE), (dict(batch=65536), SHAPE),
+    (dict(sa=-1), SHAPE), (dict(sb=-16), SHAPE), (dict(sc=-16), SHAPE),
+    (dict(sc=15), SHAPE),                       # outputs of consecutive products overlap
+    (dict(A=0), NULL), (dict(C=0), NULL), (dict(lda=3), SHAPE), (dict(B=A16 + 1), ALIGN),
+    (dict(batch=0, A=0, B=0, C=0), OK),         # nothing to do
+    (dict(sc=15, batch=1, A=MIS + 1), ALIGN),   # batch 1: no overlap check
+])
+def test_dense_batched_rejects_invalid_arguments(lib, kw, code):
+    assert batched(lib, **kw) == code
 
 
 def test_describe_names_the_dispatch(lib):
