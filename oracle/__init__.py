@@ -10,6 +10,7 @@ from .qgemm_oracle import (  # noqa: F401
     TOL_REL,
     fp16_value,
     bf16_value,
+    fp32_value,
     unpack_qweight,
     unpack_qzeros,
     dequant,
@@ -18,6 +19,9 @@ from .qgemm_oracle import (  # noqa: F401
     dense,
     dense_at,
     dense_batched,
+    dense_absdot,
+    accept_fp32,
+    compare_fp32,
     dense_batched_at,
     grid_bracket,
     round_to_grid,

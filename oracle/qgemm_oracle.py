@@ -29,7 +29,9 @@ What it computes
     NN: C[M][N] = A[M][K] . B[K][N]     (input gradient)
     TN: C[M][N] = A[K][M]^T . B[K][N]   (weight gradient)
   and batches of them (the batched products inside attention), one product per
-  leading index.
+  leading index; and the same products in FP32 (the post tunes and validates
+  FP32 in all three layouts), accepted under a dot-product error bound
+  (accept_fp32).
 * acceptance of an output y against the fp64 value r (the NF12 pull request,
   "Accuracy": zero violations of |err| <= 2e-3 + 2e-3 |ref|).  Read together
   with its statement that the rms error it sees is the BF16 rounding floor, an
@@ -82,7 +84,14 @@ def bf16_value(bits) -> np.ndarray:
     return _decode(bits, 8, 7)
 
 
+def fp32_value(bits) -> np.ndarray:
+    """IEEE binary32 bit patterns -> fp64 values (1 sign, 8 exponent, 23 fraction bits)."""
+    return _decode(bits, 8, 23)
+
+
 def _value(bits, dtype: str) -> np.ndarray:
+    if dtype == "fp32":
+        return fp32_value(bits)
     return bf16_value(bits) if dtype == "bf16" else fp16_value(bits)
 
 
@@ -193,6 +202,14 @@ def dense_at(layout: str, dtype: str, a_bits, b_bits, rows, cols) -> np.ndarray:
     return opA[np.asarray(rows), :] @ opB[:, np.asarray(cols)]
 
 
+def dense_absdot(layout: str, dtype: str, a_bits, b_bits, rows=None, cols=None) -> np.ndarray:
+    """|op(A)| . |op(B)| in fp64 (optionally restricted): the scale of the fp32 error bound."""
+    opA, opB = _ops(layout, a_bits, b_bits, dtype)
+    if rows is not None:
+        opA, opB = opA[np.asarray(rows), :], opB[:, np.asarray(cols)]
+    return np.abs(opA) @ np.abs(opB)
+
+
 def dense_batched(layout: str, dtype: str, a_bits, b_bits, M: int, N: int, K: int) -> np.ndarray:
     """C64[b] = op(A[b]) . op(B[b]) for b over the leading (batch) axis, fp64 [batch][M][N].
 
@@ -244,6 +261,31 @@ def accept(y, r, dtype: str) -> np.ndarray:
     lo, hi = grid_bracket(r, dtype)
     literal = np.abs(y - r) <= TOL_ABS + TOL_REL * np.abs(r)
     return literal | (y == lo) | (y == hi)
+
+
+# fp32 outputs (fp32 products and accumulation).  The pages validate FP32
+# products against a float64 CPU product without stating a tolerance; the bound
+# used is the classical one for a dot product of length K evaluated in
+# floating point with unit roundoff u = 2^-24, in any order of summation:
+#   |y - r| <= gamma_K * sum_i |a_i b_i|,   gamma_K = K u / (1 - K u),
+# plus K times the smallest subnormal for underflow in the products.
+def accept_fp32(y, r, absdot, K: int) -> np.ndarray:
+    u = 2.0 ** -24
+    gamma = K * u / (1.0 - K * u)
+    y = np.asarray(y, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    return np.abs(y - r) <= gamma * np.asarray(absdot, dtype=np.float64) + K * 2.0 ** -149
+
+
+def compare_fp32(y_bits, r, absdot, K: int) -> dict:
+    """Compare fp32 output bit patterns with the fp64 reference under accept_fp32."""
+    y = fp32_value(y_bits)
+    r = np.asarray(r, dtype=np.float64)
+    ok = accept_fp32(y, r, absdot, K)
+    nr = float(np.sqrt(np.sum(r * r)))
+    rms_rel = float(np.sqrt(np.sum((y - r) ** 2)) / nr) if nr > 0 else float(np.sqrt(np.sum(y * y)))
+    return {"n": int(r.size), "rejected": int(r.size - np.count_nonzero(ok)), "rms_rel": rms_rel,
+            "nonfinite": int(np.count_nonzero(~np.isfinite(y)))}
 
 
 def compare(y_bits, r, dtype: str) -> dict:

@@ -10,6 +10,7 @@ from .gen import (  # noqa: F401
     SplitMix64,
     f32_to_bf16_bits,
     f64_to_fp16_bits,
+    f64_to_fp32_bits,
     int4_inputs,
     dense_inputs,
     dense_batched_inputs,

@@ -101,11 +101,19 @@ def int4_inputs(m: int, k: int, n: int, seed: int, group_size: int = 128) -> dic
             "m": m, "k": k, "n": n, "group_size": group_size}
 
 
+def f64_to_fp32_bits(v) -> np.ndarray:
+    """Round fp64 values to IEEE binary32 bit patterns, RNE."""
+    return np.ascontiguousarray(np.asarray(v, dtype=np.float64).astype(np.float32)).view(np.uint32)
+
+
 def normal_bits(rng: SplitMix64, shape, std: float, dtype: str) -> np.ndarray:
     """A tensor of N(0, std^2) values rounded to the storage dtype, as bit patterns."""
     count = int(np.prod(shape)) if len(shape) else 1
     v = std * rng.normal(count)
-    bits = f32_to_bf16_bits(v) if dtype == "bf16" else f64_to_fp16_bits(v)
+    if dtype == "fp32":
+        bits = f64_to_fp32_bits(v)
+    else:
+        bits = f32_to_bf16_bits(v) if dtype == "bf16" else f64_to_fp16_bits(v)
     return bits.reshape(shape)
 
 

@@ -446,6 +446,59 @@ def test_dense_k1_outer_product_and_1x1x1():
     assert oracle.dense("TN", "bf16", one, one, 1, 1, 1).tolist() == [[2.25]]
 
 
+def test_fp32_decoder_matches_struct_unpack():
+    # special values, subnormals, extremes and a seeded sample of all patterns
+    rng = np.random.default_rng(3)
+    pats = np.concatenate([
+        np.array([0, 0x80000000, 1, 0x007FFFFF, 0x00800000, 0x3F800000, 0xBF800000, 0x7F7FFFFF,
+                  0xFF7FFFFF, 0x7F800000, 0xFF800000, 0x33800000], dtype=np.uint64),
+        rng.integers(0, 2 ** 32, size=20000, dtype=np.uint64)]).astype(np.uint32)
+    got = oracle.fp32_value(pats)
+    for b, g in zip(pats.tolist(), got.tolist()):
+        want = struct.unpack("<f", struct.pack("<I", b))[0]
+        if math.isnan(want):
+            assert math.isnan(g)
+        else:
+            assert g == want, (hex(b), g, want)
+
+
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_dense_fp32_brute_force(layout):
+    M, N, K = 3, 4, 6
+    d = dense_inputs(layout, "fp32", M, N, K, seed=26, std=1.0)
+    c = oracle.dense(layout, "fp32", d["a"], d["b"], M, N, K)
+    absd = oracle.dense_absdot(layout, "fp32", d["a"], d["b"])
+    dec = lambda v: struct.unpack("<f", struct.pack("<I", int(v)))[0]
+    for i in range(M):
+        for j in range(N):
+            terms = []
+            for p in range(K):
+                a = d["a"][i, p] if layout in ("NT", "NN") else d["a"][p, i]
+                b = d["b"][j, p] if layout == "NT" else d["b"][p, j]
+                terms.append(dec(a) * dec(b))
+            assert abs(c[i, j] - math.fsum(terms)) <= 1e-14 * max(1.0, abs(c[i, j]))
+            assert abs(absd[i, j] - math.fsum(abs(t) for t in terms)) <= 1e-14 * absd[i, j]
+
+
+def test_fp32_bound_accepts_fp32_sums_and_rejects_a_dropped_term():
+    M, N, K = 16, 16, 2048
+    d = dense_inputs("NT", "fp32", M, N, K, seed=27, std=1.0)
+    r = oracle.dense("NT", "fp32", d["a"], d["b"], M, N, K)
+    absd = oracle.dense_absdot("NT", "fp32", d["a"], d["b"])
+    a = oracle.fp32_value(d["a"]).astype(np.float32)
+    b = oracle.fp32_value(d["b"]).astype(np.float32)
+    # a plain sequential fp32 evaluation lies inside the bound
+    y = np.zeros((M, N), dtype=np.float32)
+    for p in range(K):
+        y = (y + np.outer(a[:, p], b[:, p]).astype(np.float32)).astype(np.float32)
+    rep = oracle.compare_fp32(y.view(np.uint32), r, absd, K)
+    assert rep["rejected"] == 0 and rep["rms_rel"] < 2e-5, rep
+    # a dropped k slice (8 of 2048 terms, the size of one lane's step) is outside it
+    y2 = (y - (a[:, 64:72].astype(np.float64) @ b[:, 64:72].T.astype(np.float64))).astype(np.float32)
+    rep2 = oracle.compare_fp32(y2.view(np.uint32), r, absd, K)
+    assert rep2["rejected"] > 0.9 * M * N, rep2
+
+
 def test_dense_fp16_subnormals_are_kept():
     a = np.array([[0x0001, 0x03FF]], dtype=np.uint16)       # 2^-24, largest subnormal
     b = np.array([[0x3C00], [0x4000]], dtype=np.uint16)     # [K][N] = [1; 2]
