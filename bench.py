@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "qgemm µs & eff. HBM GB/s at m=1/8; TFLOPS (% MFMA peak) at m>=512"
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3        # MI355X published dense fp32 (matrix and vector)
 LLC_BYTES = 256 << 20
 # HBM traffic of the small-M kernels, measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
 # and scaled by the same counters on a copy of known size; valid only while the
@@ -340,6 +341,25 @@ def run_suite(qg, torch, args, path):
                      "gbps": dense_bytes(M, N, K) / us / 1e3, "tflops": 2 * M * N * K / us / 1e6,
                      "mfma_frac": 2 * M * N * K / us / 1e6 / MFMA_BF16_PEAK_TFLOPS})
         print("suite dense", rows[-1], file=sys.stderr, flush=True)
+    # the FP32 training trio (fp32 products and accumulation) against the fp32 peak
+    for case in dense_cases(3, with_lora=False):
+        if case["dtype"] != "bf16":
+            continue
+        M, N, K, layout = case["M"], case["N"], case["K"], case["layout"]
+        sa = (M, K) if layout != "TN" else (K, M)
+        sb = (N, K) if layout == "NT" else (K, N)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(case["seed"])
+        a = torch.randn(sa, generator=g, device="cuda", dtype=torch.float32) * 0.02
+        b = torch.randn(sb, generator=g, device="cuda", dtype=torch.float32) * 0.02
+        out = qg.gemm_dense(layout, a, b)
+        us = time_us(torch, lambda: qg.gemm_dense(layout, a, b, out=out), iters)
+        rows.append({"kind": "dense_fp32", "role": case["role"], "layout": layout, "dtype": "fp32",
+                     "M": M, "N": N, "K": K, "us": us, "gbps": 2 * dense_bytes(M, N, K) / us / 1e3,
+                     "tflops": 2 * M * N * K / us / 1e6,
+                     "fp32_frac": 2 * M * N * K / us / 1e6 / FP32_PEAK_TFLOPS})
+        print("suite dense_fp32", rows[-1], file=sys.stderr, flush=True)
+        del a, b, out
     # batched attention products; operands drawn on the device from a seeded
     # generator (timing only: the parity tests use the host generator)
     from qgemm_inputs import attention_cases

@@ -50,6 +50,7 @@ extern "C" {
 /* dtype codes of gemm_dense */
 #define QG_BF16 0
 #define QG_FP16 1
+#define QG_FP32 2
 
 /* layout codes of gemm_dense (row-major definitions, see gemm_dense) */
 #define QG_NT 0
@@ -166,7 +167,9 @@ int32_t qgemm_int4_dequant(const uint32_t* qweight, const uint16_t* scales,
  *
  * A, B and C share the dtype (QG_BF16 or QG_FP16); C is rounded to nearest even
  * from the fp32 accumulator, ldc >= N.  Pointers must be 2-byte aligned; any
- * sizes are accepted (1x1x1 included).  Errors: QG_ERR_NULL, QG_ERR_SHAPE,
+ * sizes are accepted (1x1x1 included).  QG_FP32: A, B and C fp32 with fp32
+ * products and accumulation (the post tunes and validates FP32 in all three
+ * layouts as well), pointers 4-byte aligned; leading dimensions in elements.  Errors: QG_ERR_NULL, QG_ERR_SHAPE,
  * QG_ERR_ALIGN, QG_ERR_DTYPE, QG_ERR_LAYOUT, QG_ERR_HIP.
  */
 int32_t gemm_dense(int32_t layout, int32_t dtype, int64_t M, int64_t N, int64_t K, const void* A,

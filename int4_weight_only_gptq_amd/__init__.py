@@ -21,7 +21,7 @@ _lib = None
 
 PATHS = {"auto": 0, "gemv": 1, "fused": 2, "mfma": 3}
 LAYOUTS = {"NT": 0, "NN": 1, "TN": 2}
-_DTYPES = {"bf16": 0, "fp16": 1}
+_DTYPES = {"bf16": 0, "fp16": 1, "fp32": 2}
 
 
 class QGemmError(RuntimeError):
@@ -185,14 +185,22 @@ def qgemm_int4_dequant(qweight, scales, qzeros, out=None, group_size: int = 128,
     return out
 
 
+def _dtype_of(a, b):
+    import torch
+
+    names = {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}
+    if a.dtype != b.dtype or a.dtype not in names:
+        raise TypeError("A and B must share dtype bf16, fp16 or fp32")
+    return names[a.dtype]
+
+
 def gemm_dense(layout: str, a, b, out=None, stream=None):
-    """C = op(A) . op(B) for layout "NT", "NN" or "TN" (row-major, see qgemm.h)."""
+    """C = op(A) . op(B) for layout "NT", "NN" or "TN" (row-major, see qgemm.h);
+    bf16 / fp16 with fp32 accumulation, or fp32 throughout."""
     import torch
 
     lib = load()
-    if a.dtype != b.dtype or a.dtype not in (torch.bfloat16, torch.float16):
-        raise TypeError("A and B must share dtype bf16 or fp16")
-    dtype = "bf16" if a.dtype == torch.bfloat16 else "fp16"
+    dtype = _dtype_of(a, b)
     if layout == "NT":
         (M, K), N = a.shape, b.shape[0]
     elif layout == "NN":
@@ -215,11 +223,9 @@ def gemm_dense_batched(layout: str, a, b, out=None, stream=None):
     import torch
 
     lib = load()
-    if a.dtype != b.dtype or a.dtype not in (torch.bfloat16, torch.float16):
-        raise TypeError("A and B must share dtype bf16 or fp16")
+    dtype = _dtype_of(a, b)
     if a.dim() != 3 or b.dim() != 3 or a.shape[0] != b.shape[0]:
         raise ValueError("A and B must be [batch][rows][cols] with the same batch")
-    dtype = "bf16" if a.dtype == torch.bfloat16 else "fp16"
     batch = a.shape[0]
     if layout == "NT":
         (M, K), N = a.shape[1:], b.shape[1]

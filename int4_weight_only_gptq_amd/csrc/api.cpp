@@ -154,20 +154,21 @@ static int32_t run_dense(int32_t layout, int32_t dtype, int64_t batch, int64_t M
                          const void* A, int64_t lda, int64_t sa, const void* B, int64_t ldb, int64_t sb,
                          void* C, int64_t ldc, int64_t sc, void* stream) {
   if (layout < QG_NT || layout > QG_TN) return QG_ERR_LAYOUT;
-  if (dtype != QG_BF16 && dtype != QG_FP16) return QG_ERR_DTYPE;
+  if (dtype != QG_BF16 && dtype != QG_FP16 && dtype != QG_FP32) return QG_ERR_DTYPE;
+  const uintptr_t esize = dtype == QG_FP32 ? 4 : 2;
   if (M < 0 || N < 0 || K < 0 || batch < 0 || batch > 65535) return QG_ERR_SHAPE;
   if (sa < 0 || sb < 0 || sc < 0) return QG_ERR_SHAPE;
   if (M == 0 || N == 0 || batch == 0) return QG_OK;
   if (C == nullptr) return QG_ERR_NULL;
   if (ldc < N) return QG_ERR_SHAPE;
   if (batch > 1 && sc < (M - 1) * ldc + N) return QG_ERR_SHAPE;     // outputs must not overlap
-  if (!aligned(C, 2)) return QG_ERR_ALIGN;
+  if (!aligned(C, esize)) return QG_ERR_ALIGN;
   if (K > 0) {
     if (A == nullptr || B == nullptr) return QG_ERR_NULL;
     const int64_t a_row = layout == QG_TN ? M : K;
     const int64_t b_row = layout == QG_NT ? K : N;
     if (lda < a_row || ldb < b_row) return QG_ERR_SHAPE;
-    if (!aligned(A, 2) || !aligned(B, 2)) return QG_ERR_ALIGN;
+    if (!aligned(A, esize) || !aligned(B, esize)) return QG_ERR_ALIGN;
   }
   if (batch == 1) sa = sb = sc = 0;
   const qg::DenseArgs a{layout, dtype, M, N, K, (const uint16_t*)A, lda, (const uint16_t*)B, ldb,

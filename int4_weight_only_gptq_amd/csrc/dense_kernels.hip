@@ -762,6 +762,160 @@ __global__ __launch_bounds__(256) void dense_generic_kernel(const uint16_t* __re
   else C[r * ldc + c] = __builtin_bit_cast(uint16_t, (_Float16)acc);
 }
 
+// ---------------------------------------------------------------------------
+// FP32 products (A, B and C fp32, fp32 accumulation) on the 16x16x4 fp32 MFMA.
+// Tile 128 x 128 per workgroup of 4 waves (2 x 2, 64 x 64 each), k tiles of 32
+// staged through registers into two LDS buffers, one barrier per k tile.
+//
+// One MFMA takes one value per lane per operand (lane l: row or column l % 16,
+// k index l / 16 of its 4).  The k order inside a 16-k group is permuted so
+// that a K-contiguous fragment is one 16-byte read: lane group g holds
+// k = 16q + 4g .. 16q + 4g + 3 and MFMA j (0..3) of the group uses element j,
+// i.e. MFMA j covers k = 16q + 4g + j over the four lane groups g.  Both
+// operands use the same order, so each of the 16 k of the group enters the
+// sum exactly once.  An M/N-contiguous fragment gathers the same four k with
+// four 4-byte reads.  LDS rows are padded by 16 bytes (K-contiguous: 36
+// floats per row; M/N-contiguous: 132 floats per k-row) so that the 16 rows a
+// fragment read touches fall in distinct banks.
+// ---------------------------------------------------------------------------
+constexpr int FBK = 32;                  // k per stage
+constexpr int FKP = FBK + 4;             // floats per LDS row, K-contiguous operand
+constexpr int FMP = 128 + 4;             // floats per LDS k-row, M/N-contiguous operand
+constexpr int F32_REGION = 128 * FKP > FBK * FMP ? 128 * FKP : FBK * FMP;   // floats per operand buffer
+
+__device__ __forceinline__ f32x4 mfma16_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int LAYOUT>
+__global__ __launch_bounds__(256) void dense_f32_kernel(const float* __restrict__ A, int64_t lda,
+                                                        const float* __restrict__ B, int64_t ldb,
+                                                        float* __restrict__ C, int64_t ldc, int M, int N,
+                                                        int K, int tiles_n, int tiles, int tiles_per_xcd,
+                                                        BatchStrides bs) {
+  A += blockIdx.y * bs.a;   // batch blockIdx.y
+  B += blockIdx.y * bs.b;
+  C += blockIdx.y * bs.c;
+  constexpr bool A_MN = (LAYOUT == 2), B_MN = (LAYOUT != 0);
+  constexpr int FM = 4, FN = 4;
+  __shared__ __attribute__((aligned(16))) float fsm[2][2][F32_REGION];   // [buffer][A, B]
+
+  const int t = (blockIdx.x & 7) * tiles_per_xcd + (blockIdx.x >> 3);
+  if (t >= tiles) return;
+  const int tm = t / tiles_n, tn = t - tm * tiles_n;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cl = lane & 15, ks = lane >> 4;
+  const int64_t m0 = (int64_t)tm * 128, n0 = (int64_t)tn * 128;
+  const int wm0 = (wave & 1) * 64, wn0 = (wave >> 1) * 64;
+
+  // 4 float4 per thread per operand and k tile; past the edges: zeros
+  f32x4 ra[4], rb[4];
+  auto load_op = [&](const float* __restrict__ P, int64_t ld, int64_t r0, int64_t rows, bool mn, int64_t k0,
+                     f32x4 (&reg)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      if (mn) {
+        const int64_t gk = k0 + c / 32, gr = r0 + 4 * (c % 32);
+        reg[i] = (gk < K && gr < rows) ? *reinterpret_cast<const f32x4*>(P + gk * ld + gr)
+                                       : f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+        const int64_t gr = r0 + c / 8, gk = k0 + 4 * (c % 8);
+        reg[i] = (gr < rows && gk < K) ? *reinterpret_cast<const f32x4*>(P + gr * ld + gk)
+                                       : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  auto store_op = [&](float* region, bool mn, const f32x4 (&reg)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      if (mn) *reinterpret_cast<f32x4*>(region + (c / 32) * FMP + 4 * (c % 32)) = reg[i];
+      else *reinterpret_cast<f32x4*>(region + (c / 8) * FKP + 4 * (c % 8)) = reg[i];
+    }
+  };
+  auto load = [&](int64_t k0) {
+    load_op(A, lda, m0, M, A_MN, k0, ra);
+    load_op(B, ldb, n0, N, B_MN, k0, rb);
+  };
+  auto store = [&](int buf) {
+    store_op(fsm[buf][0], A_MN, ra);
+    store_op(fsm[buf][1], B_MN, rb);
+  };
+  // the four k (16q + 4 ks + j, j = 0..3) of row or column `r` of a region
+  auto frag = [&](const float* region, bool mn, int r, int q) {
+    if (mn) {
+      const float* p = region + (16 * q + 4 * ks) * FMP + r;
+      return f32x4{p[0], p[FMP], p[2 * FMP], p[3 * FMP]};
+    }
+    return *reinterpret_cast<const f32x4*>(region + r * FKP + 16 * q + 4 * ks);
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int f = 0; f < FM; ++f)
+#pragma unroll
+    for (int c = 0; c < FN; ++c) acc[f][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int ktiles = (K + FBK - 1) / FBK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < ktiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < ktiles) load((int64_t)(kt + 1) * FBK);
+#pragma unroll
+    for (int q = 0; q < FBK / 16; ++q) {
+      f32x4 a[FM], b[FN];
+#pragma unroll
+      for (int f = 0; f < FM; ++f) a[f] = frag(fsm[buf][0], A_MN, wm0 + 16 * f + cl, q);
+#pragma unroll
+      for (int c = 0; c < FN; ++c) b[c] = frag(fsm[buf][1], B_MN, wn0 + 16 * c + cl, q);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+#pragma unroll
+          for (int c = 0; c < FN; ++c) acc[f][c] = mfma16_f32(a[f][j], b[c][j], acc[f][c]);
+    }
+    if (kt + 1 < ktiles) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // lane (cl, ks) holds rows 4 ks + v, column cl of each 16 x 16 block: 16 lanes
+  // store 64 contiguous bytes of a row
+#pragma unroll
+  for (int f = 0; f < FM; ++f)
+#pragma unroll
+    for (int c = 0; c < FN; ++c)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t gr = m0 + wm0 + 16 * f + 4 * ks + v, gc = n0 + wn0 + 16 * c + cl;
+        if (gr < M && gc < N) C[gr * ldc + gc] = acc[f][c][v];
+      }
+}
+
+// Any fp32 shape and alignment: one thread per output element.
+template <int LAYOUT>
+__global__ __launch_bounds__(256) void dense_generic_f32_kernel(const float* __restrict__ A, int64_t lda,
+                                                                const float* __restrict__ B, int64_t ldb,
+                                                                float* __restrict__ C, int64_t ldc, int64_t M,
+                                                                int64_t N, int64_t K, BatchStrides bs) {
+  A += blockIdx.y * bs.a;
+  B += blockIdx.y * bs.b;
+  C += blockIdx.y * bs.c;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= M * N) return;
+  const int64_t r = i / N, c = i - r * N;
+  float acc = 0.f;
+  for (int64_t p = 0; p < K; ++p) {
+    const float a = LAYOUT == 2 ? A[p * lda + r] : A[r * lda + p];
+    const float b = LAYOUT == 0 ? B[c * ldb + p] : B[p * ldb + c];
+    acc = __builtin_fmaf(a, b, acc);
+  }
+  C[r * ldc + c] = acc;
+}
+
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 static BatchStrides strides(const DenseArgs& a) { return BatchStrides{a.sa, a.sb, a.sc}; }
@@ -870,14 +1024,46 @@ static void dense_dispatch(const DenseArgs& a, hipStream_t stream) {
   }
 }
 
+template <int LAYOUT>
+static void dense_dispatch_f32(const DenseArgs& a, hipStream_t stream) {
+  const float* A = reinterpret_cast<const float*>(a.A);
+  const float* B = reinterpret_cast<const float*>(a.B);
+  float* C = reinterpret_cast<float*>(a.C);
+  const int64_t a_contig = LAYOUT == 2 ? a.M : a.K, b_contig = LAYOUT == 0 ? a.K : a.N;
+  const bool vec = aligned16(A) && aligned16(B) && a.lda % 4 == 0 && a.ldb % 4 == 0 && a.sa % 4 == 0 &&
+                   a.sb % 4 == 0 && a_contig % 4 == 0 && b_contig % 4 == 0 && a.M < (1LL << 31) &&
+                   a.N < (1LL << 31) && a.K < (1LL << 31);
+  if (vec) {
+    const int tiles_n = (int)((a.N + 127) / 128);
+    const int tiles = (int)(((a.M + 127) / 128) * tiles_n), per_xcd = (tiles + 7) / 8;
+    dense_f32_kernel<LAYOUT><<<dim3((unsigned)(per_xcd * 8), (unsigned)a.batch), dim3(256), 0, stream>>>(
+        A, a.lda, B, a.ldb, C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, strides(a));
+  } else {
+    const int64_t total = a.M * a.N;
+    dense_generic_f32_kernel<LAYOUT><<<dim3((unsigned)((total + 255) / 256), (unsigned)a.batch), dim3(256), 0,
+                                       stream>>>(A, a.lda, B, a.ldb, C, a.ldc, a.M, a.N, a.K, strides(a));
+  }
+}
+
 hipError_t launch_dense(const DenseArgs& a, hipStream_t stream) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   if (a.K == 0) {
+    // fp32: each element is two zero halves at twice the leading dimension
+    const int w = a.dtype == 2 ? 2 : 1;
     for (int64_t b = 0; b < a.batch; ++b) {
-      const hipError_t e = launch_zero16(a.C + b * a.sc, a.M, a.N, a.ldc, stream);
+      const hipError_t e = launch_zero16(a.C + w * b * a.sc, a.M, w * a.N, w * a.ldc, stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
+  }
+  if (a.dtype == 2) {
+    switch (a.layout) {
+      case 0: dense_dispatch_f32<0>(a, stream); break;
+      case 1: dense_dispatch_f32<1>(a, stream); break;
+      case 2: dense_dispatch_f32<2>(a, stream); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
   }
   switch (a.layout * 2 + a.dtype) {
     case 0: dense_dispatch<0, 0>(a, stream); break;

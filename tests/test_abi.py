@@ -111,7 +111,7 @@ def test_dequant_rejects_invalid_arguments(lib):
 
 @pytest.mark.parametrize("args,code", [
     ((3, 0, 4, 4, 4, A16, 4, A16, 4, A16, 4), LAYOUT),
-    ((0, 2, 4, 4, 4, A16, 4, A16, 4, A16, 4), DTYPE),
+    ((0, 3, 4, 4, 4, A16, 4, A16, 4, A16, 4), DTYPE),
     ((0, 0, -1, 4, 4, A16, 4, A16, 4, A16, 4), SHAPE),
     ((0, 0, 4, 4, 4, 0, 4, A16, 4, A16, 4), NULL),
     ((0, 0, 4, 4, 4, A16, 4, A16, 4, 0, 4), NULL),
@@ -132,7 +132,7 @@ def batched(lib, layout=0, dtype=0, batch=2, M=4, N=4, K=4, A=A16, lda=4, sa=16,
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(layout=3), LAYOUT), (dict(dtype=2), DTYPE), (dict(batch=-1), SHAPE), (dict(batch=65536), SHAPE),
+    (dict(layout=3), LAYOUT), (dict(dtype=3), DTYPE), (dict(batch=-1), SHAPE), (dict(batch=65536), SHAPE),
     (dict(sa=-1), SHAPE), (dict(sb=-16), SHAPE), (dict(sc=-16), SHAPE),
     (dict(sc=15), SHAPE),                       # outputs of consecutive products overlap
     (dict(A=0), NULL), (dict(C=0), NULL), (dict(lda=3), SHAPE), (dict(B=A16 + 1), ALIGN),
@@ -141,6 +141,14 @@ def batched(lib, layout=0, dtype=0, batch=2, M=4, N=4, K=4, A=A16, lda=4, sa=16,
 ])
 def test_dense_batched_rejects_invalid_arguments(lib, kw, code):
     assert batched(lib, **kw) == code
+
+
+def test_dense_fp32_alignment_and_dtype(lib):
+    # fp32 (dtype 2) needs 4-byte aligned pointers; dtype 3 does not exist
+    assert lib.gemm_dense(0, 2, 4, 4, 4, A16 + 2, 4, A16, 4, A16, 4, None) == ALIGN
+    assert lib.gemm_dense(0, 2, 4, 4, 4, A16, 4, A16, 4, A16 + 2, 4, None) == ALIGN
+    assert lib.gemm_dense(0, 3, 4, 4, 4, A16, 4, A16, 4, A16, 4, None) == DTYPE
+    assert lib.gemm_dense(0, 2, 0, 4, 4, 0, 4, 0, 4, 0, 4, None) == OK
 
 
 def test_describe_names_the_dispatch(lib):

@@ -274,3 +274,76 @@ def test_attention_products_sampled(gpu_lib, case):
         cols = sample_indices(N, 24, case["seed"] + q + 1)
         ref = oracle.dense_batched_at(layout, dtype, d["a"], d["b"], q, rows, cols)
         assert_accepted(c[np.ix_(rows, cols)], ref, dtype, (case["role"], q))
+
+
+# ----------------------------------------------------------------------------
+# FP32 products (fp32 in, fp32 products and accumulation, fp32 out): accepted
+# under the dot-product error bound gamma_K * |A||B| (zero rejections), rms
+# error at the fp32 floor
+# ----------------------------------------------------------------------------
+from gpu_helpers import host_u32  # noqa: E402
+
+FP32_RMS_GATE = 2e-5
+FP32_SHAPES = [(1, 1, 1), (13, 17, 19), (128, 128, 64), (130, 264, 200), (256, 136, 520), (1000, 8, 16),
+               (200, 264, 36), (64, 16, 1024)]
+
+
+def assert_fp32_accepted(c_bits, ref, absd, K, what):
+    rep = oracle.compare_fp32(c_bits, ref, absd, K)
+    say(what, rep)
+    assert rep["nonfinite"] == 0, (what, rep)
+    assert rep["rejected"] == 0, (what, rep)
+    if ref.size >= 64:
+        assert rep["rms_rel"] < FP32_RMS_GATE, (what, rep)
+
+
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_fp32_shapes_match_oracle(gpu_lib, layout):
+    import torch
+
+    for i, (M, N, K) in enumerate(FP32_SHAPES):
+        say("fp32", layout, M, N, K)
+        d = dense_inputs(layout, "fp32", M, N, K, seed=1400 + i, std=1.0)
+        c = host_u32(run(gpu_lib, layout, dev(d["a"], torch.float32), dev(d["b"], torch.float32)))
+        ref = oracle.dense(layout, "fp32", d["a"], d["b"], M, N, K)
+        absd = oracle.dense_absdot(layout, "fp32", d["a"], d["b"])
+        assert_fp32_accepted(c, ref, absd, K, ("fp32", layout, M, N, K))
+
+
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_fp32_batched_strided(gpu_lib, layout):
+    import torch
+
+    bt, M, N, K = 3, 136, 132, 72
+    d = dense_batched_inputs(layout, "fp32", bt, M, N, K, seed=1500, std=1.0)
+    ra, ca = d["a"].shape[1:]
+    pa = torch.zeros((bt, ra + 1, ca + 4), dtype=torch.float32, device="cuda")
+    pa[:, :ra, :ca] = dev(d["a"], torch.float32)
+    big = torch.full((bt, M, N + 4), 5.0, dtype=torch.float32, device="cuda")
+    out = big[:, :, 4:]
+    run_batched(gpu_lib, layout, pa[:, :ra, :ca], dev(d["b"], torch.float32), out=out)
+    got = host_u32(out)
+    for q in range(bt):
+        ref = oracle.dense(layout, "fp32", d["a"][q], d["b"][q], M, N, K)
+        absd = oracle.dense_absdot(layout, "fp32", d["a"][q], d["b"][q])
+        assert_fp32_accepted(got[q], ref, absd, K, ("fp32-batched", layout, q))
+    assert torch.all(big[:, :, :4] == 5.0)
+
+
+FP32_FULL = [c for c in dense_cases(3, with_lora=False) if c["dtype"] == "bf16" and c["t"] in (1024, 4096)]
+
+
+@pytest.mark.parametrize("case", FP32_FULL,
+                         ids=["%s-%s-t%d-w%dx%d" % (c["role"], c["layout"], c["t"], *c["w"]) for c in FP32_FULL])
+def test_fp32_training_products_sampled(gpu_lib, case):
+    import torch
+
+    layout, M, N, K = case["layout"], case["M"], case["N"], case["K"]
+    say("fp32-trio", case)
+    d = dense_inputs(layout, "fp32", M, N, K, seed=case["seed"] + 7, std=0.02)
+    c = host_u32(run(gpu_lib, layout, dev(d["a"], torch.float32), dev(d["b"], torch.float32)))
+    rows = sample_indices(M, 48, case["seed"])
+    cols = sample_indices(N, 48, case["seed"] + 1)
+    ref = oracle.dense_at(layout, "fp32", d["a"], d["b"], rows, cols)
+    absd = oracle.dense_absdot(layout, "fp32", d["a"], d["b"], rows, cols)
+    assert_fp32_accepted(c[np.ix_(rows, cols)], ref, absd, K, ("fp32-trio", case["role"]))
