@@ -177,6 +177,36 @@ def copy_peak_gbps(torch, nbytes=2 << 30):
     return 2 * nbytes / us / 1e3
 
 
+def same_size_reference(torch, nbytes, regime, iters):
+    """Plain torch kernels over the same number of bytes, in the same regime (cold:
+    rotating copies), graph-replayed back to back: a reduction that reads the
+    bytes (torch.sum) and a copy that reads and writes them.  Microseconds each."""
+    n = max(1, nbytes // 4)
+    copies = copies_for(4 * n, regime)
+    src = [torch.randn(n, device="cuda") for _ in range(copies)]
+    dst = [torch.empty_like(src[0]) for _ in range(copies)]
+    acc = torch.empty((), device="cuda")
+    st = {"i": 0}
+
+    def read():
+        torch.sum(src[st["i"] % copies], dim=0, out=acc)
+        st["i"] += 1
+
+    def copy():
+        dst[st["i"] % copies].copy_(src[st["i"] % copies])
+        st["i"] += 1
+
+    for _ in range(3):
+        read()
+        copy()
+    r = time_us(torch, read, iters)
+    c = time_us(torch, copy, iters)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes": 4 * n, "read_us": round(r, 3), "copy_us": round(c, 3),
+            "kernels": "torch.sum (reads the bytes), Tensor.copy_ (reads and writes them)"}
+
+
 def cpu_baseline(cases, seconds):
     """The CPU oracle, as it stands, on the same inputs until `seconds` have passed."""
     import oracle
@@ -285,6 +315,12 @@ def main():
         "roofline": roofline,
     }
     roofline["frac_of_copy"] = round(achieved / copy_gbps, 4)
+    # the same bytes through plain torch kernels: context for how far launch and
+    # latency, not bandwidth, bound a launch of this size
+    same = same_size_reference(torch, int(avg_bytes), args.regime, args.steps)
+    out["same_size_reference"] = same
+    roofline["time_vs_same_size_copy"] = round(avg_us / same["copy_us"], 3)
+    roofline["time_vs_same_size_read"] = round(avg_us / same["read_us"], 3)
     if args.suite:
         out["suite_file"] = args.suite
         run_suite(qg, torch, args, args.suite)
