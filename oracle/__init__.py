@@ -16,6 +16,8 @@ from .qgemm_oracle import (  # noqa: F401
     dequant,
     qgemm_int4,
     qgemm_int4_at,
+    qgemm_int4_lora,
+    qgemm_int4_lora_at,
     dense,
     dense_at,
     dense_batched,

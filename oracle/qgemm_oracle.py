@@ -172,6 +172,33 @@ def qgemm_int4_at(x_bits, qweight, scales, qzeros, k: int, n: int, rows, cols,
     return x @ w
 
 
+def qgemm_int4_lora(x_bits, qweight, scales, qzeros, a_bits, b_bits, lora_scale: float, m: int, k: int,
+                    n: int, group_size: int = GROUP_SIZE) -> np.ndarray:
+    """Y64 = X . W + lora_scale * (X . A^T) . B^T, fp64 throughout.
+
+    The int4 linear layer with a LoRA adapter added in its epilogue (the BC-250
+    post's LoRA training, "Where the time went": rank-16 adapters on every
+    linear layer; the mi50grad README, "Key Optimizations": a linear layer's
+    epilogue fused into the same launch).  a_bits bf16 [r][k] (lora_A),
+    b_bits bf16 [n][r] (lora_B); U = X . A^T is kept unrounded.
+    """
+    y = qgemm_int4(x_bits, qweight, scales, qzeros, m, k, n, group_size)
+    if m == 0 or n == 0:
+        return y
+    x = bf16_value(np.asarray(x_bits)[:, :k])
+    u = x @ bf16_value(a_bits).T
+    return y + float(lora_scale) * (u @ bf16_value(b_bits).T)
+
+
+def qgemm_int4_lora_at(x_bits, qweight, scales, qzeros, a_bits, b_bits, lora_scale: float, k: int, n: int,
+                       rows, cols, group_size: int = GROUP_SIZE) -> np.ndarray:
+    """qgemm_int4_lora restricted to the given rows and columns."""
+    y = qgemm_int4_at(x_bits, qweight, scales, qzeros, k, n, rows, cols, group_size)
+    x = bf16_value(np.asarray(x_bits)[np.asarray(rows), :k])
+    u = x @ bf16_value(a_bits).T
+    return y + float(lora_scale) * (u @ bf16_value(np.asarray(b_bits)[np.asarray(cols)]).T)
+
+
 # ----------------------------------------------------------------------------
 # dense products
 # ----------------------------------------------------------------------------

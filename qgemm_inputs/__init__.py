@@ -14,6 +14,7 @@ from .gen import (  # noqa: F401
     int4_inputs,
     dense_inputs,
     dense_batched_inputs,
+    lora_inputs,
 )
 from .configs import (  # noqa: F401
     INT4_CONFIGS, DENSE_CONFIGS, ATTENTION_CONFIG, int4_cases, dense_cases, attention_cases,

@@ -149,3 +149,12 @@ def dense_batched_inputs(layout: str, dtype: str, batch: int, M: int, N: int, K:
     a = normal_bits(rng, (batch,) + tuple(sa), std, dtype)
     b = normal_bits(rng, (batch,) + tuple(sb), std, dtype)
     return {"a": a, "b": b, "layout": layout, "dtype": dtype, "batch": batch, "M": M, "N": N, "K": K}
+
+
+def lora_inputs(k: int, n: int, rank: int, seed: int, std_a: float = 0.02, std_b: float = 0.05) -> dict:
+    """A LoRA adapter for an int4 layer: lora_a bf16 bits [rank][k] ~ N(0, std_a^2),
+    then lora_b bf16 bits [n][rank] ~ N(0, std_b^2)."""
+    rng = SplitMix64(seed)
+    a = normal_bits(rng, (rank, k), std_a, "bf16")
+    b = normal_bits(rng, (n, rank), std_b, "bf16")
+    return {"lora_a": a, "lora_b": b, "rank": rank}

@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 from qgemm_inputs import (SplitMix64, f32_to_bf16_bits, f64_to_fp16_bits, int4_inputs, dense_inputs,
-                          dense_batched_inputs)
+                          dense_batched_inputs, lora_inputs)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -279,6 +279,44 @@ def test_brute_force_small_int4_without_zero_point():
             assert abs(y[r, j] - exact) <= 1e-12 * max(1.0, abs(exact))
     part = oracle.qgemm_int4_at(d["x"], d["qweight"], d["scales"], None, k, n, [1], [2, 7])
     np.testing.assert_allclose(part, y[np.ix_([1], [2, 7])], rtol=1e-14, atol=1e-14)
+
+
+def test_brute_force_small_int4_lora():
+    m, k, n, r = 2, 256, 8, 3
+    d = int4_inputs(m, k, n, seed=18)
+    l = lora_inputs(k, n, r, seed=19, std_a=0.5, std_b=0.5)
+    y = oracle.qgemm_int4_lora(d["x"], d["qweight"], d["scales"], d["qzeros"], l["lora_a"], l["lora_b"],
+                               2.0, m, k, n)
+    for row in range(m):
+        u = [math.fsum(_bf16_py(d["x"][row, i]) * _bf16_py(l["lora_a"][j, i]) for i in range(k))
+             for j in range(r)]
+        for col in range(n):
+            terms = []
+            for i in range(k):
+                q = (int(d["qweight"][i >> 3, col]) >> ((i & 7) << 2)) & 0xF
+                z = (int(d["qzeros"][i >> 7, col >> 3]) >> ((col & 7) << 2)) & 0xF
+                s = _fp16_py(d["scales"][i >> 7, col])
+                terms.append(_bf16_py(d["x"][row, i]) * ((q - z) * s))
+            terms += [2.0 * u[j] * _bf16_py(l["lora_b"][col, j]) for j in range(r)]
+            exact = math.fsum(terms)
+            assert abs(y[row, col] - exact) <= 1e-12 * max(1.0, abs(exact))
+    part = oracle.qgemm_int4_lora_at(d["x"], d["qweight"], d["scales"], d["qzeros"], l["lora_a"],
+                                     l["lora_b"], 2.0, k, n, [1], [0, 5])
+    np.testing.assert_allclose(part, y[np.ix_([1], [0, 5])], rtol=1e-14, atol=1e-14)
+
+
+def test_lora_one_hot_closed_form():
+    # X = e_0 (one-hot), A = e_j rows, B = ones: the LoRA term is scale * sum_j A[j][0]
+    m, k, n, r = 1, 128, 8, 4
+    d = int4_inputs(m, k, n, seed=20)
+    x = np.zeros((m, k), dtype=np.uint16)
+    x[0, 0] = 0x3F80                                   # 1.0
+    a = np.zeros((r, k), dtype=np.uint16)
+    a[:, 0] = [0x3F80, 0x4000, 0x4040, 0x4080]         # 1, 2, 3, 4
+    b = np.full((n, r), 0x3F80, dtype=np.uint16)       # 1.0
+    base = oracle.qgemm_int4(x, d["qweight"], d["scales"], d["qzeros"], m, k, n)
+    y = oracle.qgemm_int4_lora(x, d["qweight"], d["scales"], d["qzeros"], a, b, 0.5, m, k, n)
+    assert np.array_equal(y - base, np.full((m, n), 0.5 * 10.0))
 
 
 def test_sampled_outputs_match_full():
