@@ -377,6 +377,30 @@ def run_suite(qg, torch, args, path):
                      "gbps": dense_bytes(M, N, K) / us / 1e3, "tflops": 2 * M * N * K / us / 1e6,
                      "mfma_frac": 2 * M * N * K / us / 1e6 / MFMA_BF16_PEAK_TFLOPS})
         print("suite dense", rows[-1], file=sys.stderr, flush=True)
+    # a rank-16 LoRA add in the epilogue (U = X A^T launched first) on the same shapes
+    for cfg in (1, 2):
+        for (_, m, k, n, seed) in int4_cases(cfg):
+            c = Int4Case(qg, torch, m, k, n, seed, copies_for(int4_bytes(0, k, n), args.regime))
+            g = torch.Generator(device="cuda")
+            g.manual_seed(seed)
+            la = (torch.randn((16, k), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+            lb = (torch.randn((n, 16), generator=g, device="cuda") * 0.05).to(torch.bfloat16)
+
+            def launch(c=c, la=la, lb=lb):
+                qw, sc, qz = c.w[c.i % len(c.w)]
+                c.i += 1
+                qg.qgemm_int4_lora(c.x, qw, sc, qz, la, lb, 2.0, out=c.y)
+
+            for _ in range(3):
+                launch()
+            us = time_us(torch, launch, iters)
+            nbytes = c.bytes + 2 * 16 * (k + n)
+            rows.append({"kind": "int4_lora", "m": m, "k": k, "n": n, "kernel": c.kernel, "us": us,
+                         "gbps": nbytes / us / 1e3, "tflops": c.flops / us / 1e6,
+                         "mfma_frac": c.flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS})
+            print("suite int4_lora", rows[-1], file=sys.stderr, flush=True)
+            del c, la, lb
+            torch.cuda.empty_cache()
     # the FP32 training trio (fp32 products and accumulation) against the fp32 peak
     for case in dense_cases(3, with_lora=False):
         if case["dtype"] != "bf16":

@@ -115,6 +115,41 @@ int32_t qgemm_int4(const void* x, int64_t ldx, const uint32_t* qweight, const ui
                    int32_t group_size, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * qgemm_int4_lora -- qgemm_int4 with a LoRA adapter added in the product's
+ * epilogue (the BC-250 post trains rank-16 LoRA adapters on every linear layer,
+ * "Where the time went"; the mi50grad README, "Key Optimizations", fuses a
+ * linear layer's epilogue into its kernel launch):
+ *
+ *   Y[r][j] = bf16_rne( sum_i X[r][i] W[i][j]  +  lora_scale * sum_t U[r][t] B[j][t] ),
+ *   U[r][t] = sum_i X[r][i] A[t][i]   (fp32, not rounded to bf16).
+ *
+ *   lora_a   bf16 [rank][lda_a] (A, the adapter's down projection),
+ *            lda_a >= k, lda_a % 8 == 0, 16-byte aligned.
+ *   lora_b   bf16 [n][ldb_b] (B, the up projection), ldb_b >= rank, 2-byte aligned.
+ *   rank     1..16.
+ *   path     as qgemm_int4_path (QG_PATH_AUTO chooses from m).
+ *   workspace, workspace_bytes
+ *            required: the last round_up(64 m, 256) bytes hold U; the front
+ *            part, rounded down to 256 bytes, serves the path as in
+ *            qgemm_int4 (same counter contract).  qgemm_int4_lora_workspace_size
+ *            gives the size that also enables the path's split / preparation.
+ *
+ * U is computed by a small kernel launched first on the same stream; the LoRA
+ * term is added to the fp32 accumulators of the product's own epilogue (once
+ * per output also when k is split).  Other arguments, limits and errors as
+ * qgemm_int4 (plus QG_ERR_SHAPE for a bad rank or a workspace without room
+ * for U).
+ */
+int32_t qgemm_int4_lora(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
+                        const uint32_t* qzeros, const void* lora_a, int64_t lda_a, const void* lora_b,
+                        int64_t ldb_b, int32_t rank, float lora_scale, void* y, int64_t ldy, int64_t m,
+                        int64_t n, int64_t k, int32_t group_size, int32_t path, void* workspace,
+                        int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes for qgemm_int4_lora (U plus what the path can use); < 0: -error. */
+int64_t qgemm_int4_lora_workspace_size(int64_t m, int64_t n, int64_t k, int32_t path);
+
+/*
  * qgemm_int4_path -- qgemm_int4 with the kernel path forced (QG_PATH_* code),
  * for same-process A/B measurement and per-path testing.  A path that cannot
  * take m returns QG_ERR_UNSUPPORTED.  Same arguments and results otherwise.

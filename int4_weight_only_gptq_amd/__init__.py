@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["load", "lib_path", "QGemmError", "qgemm_int4", "qgemm_int4_dequant", "gemm_dense",
+__all__ = ["load", "lib_path", "QGemmError", "qgemm_int4", "qgemm_int4_lora", "qgemm_int4_dequant", "gemm_dense",
            "gemm_dense_batched", "describe_int4",
            "workspace_size",
            "abi_version", "PATHS", "LAYOUTS"]
@@ -66,6 +66,11 @@ def load():
     lib.qgemm_int4_describe.argtypes = [i64, i64, i64, i32, i64, ctypes.c_char_p, i64]
     lib.qgemm_int4_dequant.restype = i32
     lib.qgemm_int4_dequant.argtypes = [vp, vp, vp, vp, i64, i64, i32, vp]
+    lib.qgemm_int4_lora.restype = i32
+    lib.qgemm_int4_lora.argtypes = [vp, i64, vp, vp, vp, vp, i64, vp, i64, i32, ctypes.c_float, vp, i64,
+                                    i64, i64, i64, i32, i32, vp, i64, vp]
+    lib.qgemm_int4_lora_workspace_size.restype = i64
+    lib.qgemm_int4_lora_workspace_size.argtypes = [i64, i64, i64, i32]
     lib.gemm_dense.restype = i32
     lib.gemm_dense.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
     lib.gemm_dense_batched.restype = i32
@@ -153,6 +158,42 @@ def qgemm_int4(x, qweight, scales, qzeros, out=None, group_size: int = 128, path
                              _ptr(qzeros), out.data_ptr(), _ld(out), m, n, k, group_size,
                              PATHS[path], wptr, wbytes, sh)
     _check(st, "qgemm_int4")
+    return out
+
+
+def qgemm_int4_lora(x, qweight, scales, qzeros, lora_a, lora_b, lora_scale: float, out=None,
+                    group_size: int = 128, path: str = "auto", workspace=None, stream=None):
+    """qgemm_int4 plus a LoRA add in the epilogue: Y = X W + lora_scale (X A^T) B^T.
+
+    lora_a bf16 [rank][k], lora_b bf16 [n][rank] (rank <= 16, last dimension
+    contiguous).  ``workspace``: None = a cached buffer of
+    qgemm_int4_lora_workspace_size bytes, or a caller-owned uint8 tensor (it
+    must hold at least the fp32 [m][16] intermediate at its end)."""
+    import torch
+
+    lib = load()
+    m, k = x.shape
+    n = qweight.shape[1]
+    rank = lora_a.shape[0]
+    if x.dtype != torch.bfloat16 or lora_a.dtype != torch.bfloat16 or lora_b.dtype != torch.bfloat16:
+        raise TypeError("x, lora_a and lora_b must be bfloat16")
+    if lora_b.shape[1] < rank:
+        raise ValueError("lora_b must be [n][rank]")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    sh = _stream(x, stream)
+    if workspace is None:
+        size = lib.qgemm_int4_lora_workspace_size(m, n, k, PATHS[path])
+        if size < 0:
+            raise QGemmError(-size, "qgemm_int4_lora_workspace_size")
+        workspace = _workspace(x.device, sh, size)
+    wptr = None if workspace is None else workspace.data_ptr()
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.qgemm_int4_lora(x.data_ptr(), _ld(x), qweight.data_ptr(), scales.data_ptr(), _ptr(qzeros),
+                             lora_a.data_ptr(), _ld(lora_a), lora_b.data_ptr(), _ld(lora_b), rank,
+                             float(lora_scale), out.data_ptr(), _ld(out), m, n, k, group_size, PATHS[path],
+                             wptr, wbytes, sh)
+    _check(st, "qgemm_int4_lora")
     return out
 
 

@@ -53,9 +53,13 @@ int32_t check_path(int64_t m, int32_t path) {
   return QG_OK;
 }
 
+// Bytes of the LoRA intermediate U (fp32 [m][16]) at the end of the workspace.
+int64_t lora_u_bytes(int64_t m) { return (m * 16 * 4 + 255) & ~(int64_t)255; }
+
 int32_t run_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
                  const uint32_t* qzeros, void* y, int64_t ldy, int64_t m, int64_t n, int64_t k,
-                 int32_t group_size, int32_t path, void* ws, int64_t ws_bytes, void* stream) {
+                 int32_t group_size, int32_t path, void* ws, int64_t ws_bytes, void* stream,
+                 const qg::LoraEpi* lora = nullptr, const void* lora_a = nullptr, int64_t lda_a = 0) {
   int32_t st = check_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size);
   if (st != QG_OK) return st;
   st = check_path(m, path);
@@ -65,8 +69,21 @@ int32_t run_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint
   if (m == 0 || n == 0) return QG_OK;
   hipStream_t s = (hipStream_t)stream;
   if (k == 0) return hip_status(qg::launch_zero16((uint16_t*)y, m, n, ldy, s));
-  const qg::Int4Args a{(const uint16_t*)x, ldx, qweight, scales, qzeros, (uint16_t*)y, ldy, m, n, k};
+  qg::Int4Args a{(const uint16_t*)x, ldx, qweight, scales, qzeros, (uint16_t*)y, ldy, m, n, k};
   if (ws == nullptr) ws_bytes = 0;
+  if (lora != nullptr) {
+    // U = X . A^T into the end of the workspace, then the product with the
+    // LoRA add in its epilogue; the path keeps the 256-byte aligned front part
+    const int64_t rest = (ws_bytes - lora_u_bytes(m)) & ~(int64_t)255;
+    float* u = (float*)((char*)ws + rest);
+    st = hip_status(qg::launch_lora_u((const uint16_t*)x, ldx, (const uint16_t*)lora_a, lda_a, lora->rank, m,
+                                      k, u, s));
+    if (st != QG_OK) return st;
+    a.lora = *lora;
+    a.lora.u = u;
+    ws_bytes = rest;
+    if (ws_bytes == 0) ws = nullptr;
+  }
   switch (resolve_path(m, path)) {
     case QG_PATH_GEMV: return hip_status(qg::launch_gemv_int4(a, ws, ws_bytes, s));
     case QG_PATH_FUSED: return hip_status(qg::launch_fused_int4(a, ws, ws_bytes, s));
@@ -109,6 +126,32 @@ int32_t qgemm_int4_path(const void* x, int64_t ldx, const uint32_t* qweight,
                         void* workspace, int64_t workspace_bytes, void* stream) {
   return run_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size, path, workspace,
                   workspace_bytes, stream);
+}
+
+int32_t qgemm_int4_lora(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
+                        const uint32_t* qzeros, const void* lora_a, int64_t lda_a, const void* lora_b,
+                        int64_t ldb_b, int32_t rank, float lora_scale, void* y, int64_t ldy, int64_t m,
+                        int64_t n, int64_t k, int32_t group_size, int32_t path, void* workspace,
+                        int64_t workspace_bytes, void* stream) {
+  if (rank < 1 || rank > 16) return QG_ERR_SHAPE;
+  if (m > 0 && n > 0 && k > 0) {
+    if (lora_a == nullptr || lora_b == nullptr) return QG_ERR_NULL;
+    if (lda_a < k || ldb_b < rank) return QG_ERR_SHAPE;
+    if (!aligned(lora_a, 16) || lda_a % 8 != 0 || !aligned(lora_b, 2)) return QG_ERR_ALIGN;
+    if (workspace == nullptr || workspace_bytes < lora_u_bytes(m)) return QG_ERR_SHAPE;
+  }
+  if (m > 0 && n > 0 && k == 0)      // U = 0: the plain product (zeros)
+    return run_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size, path, workspace,
+                    workspace_bytes, stream);
+  const qg::LoraEpi l{nullptr, (const uint16_t*)lora_b, ldb_b, rank, lora_scale};
+  return run_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size, path, workspace,
+                  workspace_bytes, stream, &l, lora_a, lda_a);
+}
+
+int64_t qgemm_int4_lora_workspace_size(int64_t m, int64_t n, int64_t k, int32_t path) {
+  const int64_t base = qgemm_int4_workspace_size(m, n, k, path);
+  if (base < 0) return base;
+  return ((base + 255) & ~(int64_t)255) + lora_u_bytes(m);
 }
 
 int64_t qgemm_int4_workspace_size(int64_t m, int64_t n, int64_t k, int32_t path) {

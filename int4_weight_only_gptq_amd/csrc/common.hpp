@@ -92,6 +92,11 @@ __device__ __forceinline__ f32x4 mfma16_f16(u32x4 a, u32x4 b, f32x4 c) {
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// fp32 16x16x4 MFMA: lane l gives A[l % 16][l / 16] and B[l / 16][l % 16].
+__device__ __forceinline__ f32x4 mfma16_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // Sum of a value over the four 16-lane rows of the wave (lanes l, l^16, l^32,
 // l^48), using the gfx950 row-swap permutes; every lane gets the total.
 __device__ __forceinline__ float sum_over_rows(float v) {

@@ -783,10 +783,6 @@ constexpr int FKP = FBK + 4;             // floats per LDS row, K-contiguous ope
 constexpr int FMP = 128 + 4;             // floats per LDS k-row, M/N-contiguous operand
 constexpr int F32_REGION = 128 * FKP > FBK * FMP ? 128 * FKP : FBK * FMP;   // floats per operand buffer
 
-__device__ __forceinline__ f32x4 mfma16_f32(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
 template <int LAYOUT>
 __global__ __launch_bounds__(256) void dense_f32_kernel(const float* __restrict__ A, int64_t lda,
                                                         const float* __restrict__ B, int64_t ldb,

@@ -189,12 +189,71 @@ __device__ __forceinline__ void load_group(GroupRegs<M, DOT, CPL>& r, bool gok, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// LoRA add in the epilogue: Y += scale * U . B^T, U = X . A^T (fp32 [m][16]).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __builtin_bit_cast(float, h << 16); }
+
+// The LoRA term of one output (row, col): scale * sum_r U[row][r] B[col][r].
+__device__ __forceinline__ float lora_term(const LoraEpi& L, int64_t row, int64_t col) {
+  const float* u = L.u + row * 16;
+  const uint16_t* b = L.b + col * L.ldb;
+  float s = 0.f;
+  for (int r = 0; r < L.rank; ++r) s = __builtin_fmaf(u[r], bf16_bits_to_float(b[r]), s);
+  return L.scale * s;
+}
+
+// U rows row0 .. row0+15 (one workgroup of 16 waves, which take interleaved
+// 32-k steps): 16x16x32 bf16 MFMA with the activations as A and lora_A's rows
+// as B, fp32 accumulation, the waves' partial tiles summed through LDS.
+__global__ __launch_bounds__(1024) void lora_u_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                      const uint16_t* __restrict__ a, int64_t lda, int rank,
+                                                      int64_t m, int64_t k, float* __restrict__ u) {
+  __shared__ float red[16][16][16];   // [wave][row][r]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cl = lane & 15, ks = lane >> 4;
+  const int64_t row0 = (int64_t)blockIdx.x * 16;
+  const bool xok = row0 + cl < m, aok = cl < rank;
+  const uint16_t* xp = x + (xok ? row0 + cl : 0) * ldx + 8 * ks;
+  const uint16_t* ap = a + (aok ? cl : 0) * lda + 8 * ks;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int kw = (int)k;   // k <= 2^22
+  for (int k0 = 32 * wave; k0 < kw; k0 += 4 * 512) {   // four steps' loads in flight, then the MFMAs
+    u32x4 xv[4], av[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kk = k0 + 512 * j;
+      xv[j] = xok && kk < kw ? *reinterpret_cast<const u32x4*>(xp + kk) : z;
+      av[j] = aok && kk < kw ? *reinterpret_cast<const u32x4*>(ap + kk) : z;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = mfma16_bf16(xv[j], av[j], acc);
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[wave][4 * ks + v][cl] = acc[v];
+  __syncthreads();
+  if (tid < 256) {
+    const int rr = tid >> 4, c = tid & 15;
+    float sum = 0.f;
+    for (int w = 0; w < 16; ++w) sum += red[w][rr][c];
+    if (row0 + rr < m) u[(row0 + rr) * 16 + c] = sum;
+  }
+}
+
+hipError_t launch_lora_u(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t lda, int rank, int64_t m,
+                         int64_t k, float* u, hipStream_t stream) {
+  if (m == 0) return hipSuccess;
+  lora_u_kernel<<<dim3((unsigned)((m + 15) / 16)), dim3(1024), 0, stream>>>(x, ldx, a, lda, rank, m, k, u);
+  return hipGetLastError();
+}
+
 template <int M, bool DOT, int CPL>
 __global__ __launch_bounds__(1024) void skinny_int4_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
     uint16_t* __restrict__ y, int64_t ldy, int n, int k, int nstrips, int ksplit, int gwg,
-    int items_per_xcd, float* __restrict__ partials, uint32_t* __restrict__ tickets) {
+    int items_per_xcd, float* __restrict__ partials, uint32_t* __restrict__ tickets, LoraEpi lora) {
   static_assert(!DOT || M == 1, "the VALU variant computes one token");
   constexpr int SW = 16 * CPL;                 // strip width in columns
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -301,6 +360,7 @@ __global__ __launch_bounds__(1024) void skinny_int4_kernel(
     float v = 0.f;
     for (int w = 0; w < nw; ++w) v += plane[(w * M + token) * SW + cc];
     const int64_t cg = (int64_t)strip * SW + cc;
+    if (lora.u && kslice == 0 && cg < n) v += lora_term(lora, token, cg);   // once per output
     if (ksplit == 1) {
       if (cg < n) y[(int64_t)token * ldy + cg] = (uint16_t)f32_to_bf16_bits(v);
     } else {
@@ -392,7 +452,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
     const float* __restrict__ xsum, uint16_t* __restrict__ y, int64_t ldy, int m, int n, int k,
     int tiles_n, int items, int items_per_xcd, int vec_store, int ksplit, int gps,
-    float* __restrict__ partials, uint32_t* __restrict__ tickets) {
+    float* __restrict__ partials, uint32_t* __restrict__ tickets, LoraEpi lora) {
   using S = PipeShape<NWM, NWN, FM, PREP>;
   constexpr int T = S::T, BM = S::BM, BN = S::BN, XL = S::XL, WL = S::WL, LOADS = S::LOADS;
   static_assert(LOADS * (STAGES - 2) <= 63, "vmcnt range");
@@ -583,6 +643,44 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
       }
     }
   }
+  if (lora.u && kslice == 0) {
+    // LoRA add (once per output: slice 0 of a split tile): total += scale *
+    // U[rows] . B[cols]^T as four 16x16x4 fp32 MFMAs per 16 x 16 block, the
+    // A operand U[row][4 j + k4] and the B operand B[col][4 j + k4] (k4 =
+    // lane / 16) for the block's rows and its fragment's columns 4 l + c, so
+    // the result lands in the layout of total.  U's columns past the rank are
+    // zero; B is read only below the rank.
+    f32x4 lr[FM][4];
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) lr[f][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * j + ks;
+      float ua[FM], bb[4];
+#pragma unroll
+      for (int f = 0; f < FM; ++f) {
+        const int64_t row = m0 + wm0 + 16 * f + cl;
+        ua[f] = row < m ? lora.u[row * 16 + r] : 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int64_t col = n0 + wn0 + 4 * cl + c;
+        bb[c] = (col < n && r < lora.rank) ? bf16_bits_to_float(lora.b[col * lora.ldb + r]) : 0.f;
+      }
+#pragma unroll
+      for (int f = 0; f < FM; ++f)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) lr[f][c] = mfma16_f32(ua[f], bb[c], lr[f][c]);
+    }
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) total[f][c][v] = __builtin_fmaf(lora.scale, lr[f][c][v], total[f][c][v]);
+  }
   if (ksplit > 1) {
     // Split k: every slice stores its fp32 partial tile with agent-coherent
     // stores and takes a ticket; the last slice of the tile to arrive adds the
@@ -727,7 +825,7 @@ static void skinny_launch(const Int4Args& a, const SkinnyPlan& p, void* ws, hipS
   float* partials = ws ? (float*)((char*)ws + kTicketBytes) : nullptr;
   skinny_int4_kernel<M, DOT, CPL><<<dim3((unsigned)p.blocks), dim3(64 * p.waves), p.lds, stream>>>(
       a.x, a.ldx, a.qweight, a.scales, a.qzeros, a.y, a.ldy, (int)a.n, (int)a.k, p.nstrips,
-      p.ksplit, p.gwg, p.items_per_xcd, partials, tickets);
+      p.ksplit, p.gwg, p.items_per_xcd, partials, tickets, a.lora);
 }
 
 template <int M, bool DOT>
@@ -908,7 +1006,7 @@ static void pipe_launch(const Int4Args& a, const MfmaPlan& p, const uint16_t* x,
   const int vec = ((uintptr_t)a.y & 15u) == 0 && a.ldy % 8 == 0;
   int4_pipe_kernel<NWM, NWN, FM, STAGES, PREP><<<dim3((unsigned)(per_xcd * 8)), dim3(c.threads), c.lds, stream>>>(
       x, ldx, a.qweight, a.scales, a.qzeros, xsum, a.y, a.ldy, (int)a.m, (int)a.n, (int)a.k, tiles_n,
-      items, per_xcd, vec, p.ksplit, p.gps, partials, tickets);
+      items, per_xcd, vec, p.ksplit, p.gps, partials, tickets, a.lora);
 }
 
 template <bool PREP>

@@ -7,6 +7,16 @@
 
 namespace qg {
 
+// LoRA add in the epilogue of an int4 product: Y += scale * U . B^T with
+// U = X . A^T (fp32 [m][16], columns >= rank zero) computed beforehand.
+struct LoraEpi {
+  const float* u;         // nullptr: no adapter
+  const uint16_t* b;      // lora_B bf16 [n][ldb], the first `rank` entries of each row used
+  int64_t ldb;
+  int rank;
+  float scale;
+};
+
 struct Int4Args {
   const uint16_t* x;
   int64_t ldx;
@@ -16,7 +26,13 @@ struct Int4Args {
   uint16_t* y;
   int64_t ldy;
   int64_t m, n, k;
+  LoraEpi lora;           // zero-initialised: no adapter
 };
+
+// U[m][16] = X . A^T in fp32 for lora_A bf16 [rank][lda] (rank <= 16; the
+// other columns of U are written as zeros).
+hipError_t launch_lora_u(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t lda, int rank, int64_t m,
+                         int64_t k, float* u, hipStream_t stream);
 
 hipError_t launch_dequant(const uint32_t* qweight, const uint16_t* scales, const uint32_t* qzeros,
                           float* w, int64_t n, int64_t k, hipStream_t stream);

@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "qg_abi_version", "qg_status_str", "qg_last_hip_error", "qgemm_int4", "qgemm_int4_path",
         "qgemm_int4_workspace_size", "qgemm_int4_describe", "qgemm_int4_dequant", "gemm_dense",
-        "gemm_dense_batched"])
+        "gemm_dense_batched", "qgemm_int4_lora", "qgemm_int4_lora_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -90,6 +90,31 @@ def int4(lib, x=A16, ldx=256, qw=A16, sc=A16, qz=A16, y=A16, ldy=64, m=1, n=64, 
 ])
 def test_int4_rejects_invalid_arguments(lib, kw, code):
     assert int4(lib, **kw) == code
+
+
+def lora(lib, x=A16, ldx=256, qw=A16, sc=A16, qz=A16, la=A16, lda=256, lb=A16, ldb=16, rank=16, y=A16,
+         ldy=64, m=1, n=64, k=256, gs=128, path=0, ws=A16, wsb=1 << 20):
+    return lib.qgemm_int4_lora(x, ldx, qw, sc, qz, la, lda, lb, ldb, rank, 1.0, y, ldy, m, n, k, gs, path,
+                               ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rank=0), SHAPE), (dict(rank=17), SHAPE), (dict(la=0), NULL), (dict(lb=0), NULL),
+    (dict(lda=128), SHAPE), (dict(ldb=8), SHAPE), (dict(la=A16 + 8), ALIGN), (dict(lda=260), ALIGN),
+    (dict(lb=A16 + 1), ALIGN), (dict(ws=None, wsb=0), SHAPE), (dict(wsb=32), SHAPE),
+    (dict(x=MIS), ALIGN), (dict(gs=64), UNSUP), (dict(y=0), NULL),
+    (dict(m=0, x=0, qw=0, sc=0, qz=0, la=0, lb=0, y=0, ws=None, wsb=0), OK),
+])
+def test_int4_lora_rejects_invalid_arguments(lib, kw, code):
+    assert lora(lib, **kw) == code
+
+
+def test_int4_lora_workspace_size(lib):
+    for m, n, k in ((1, 4096, 4096), (15, 8192, 2048), (512, 25600, 5120), (33, 1040, 2048)):
+        base = lib.qgemm_int4_workspace_size(m, n, k, 0)
+        up = lambda v: (v + 255) // 256 * 256
+        assert lib.qgemm_int4_lora_workspace_size(m, n, k, 0) == up(base) + up(64 * m)
+    assert lib.qgemm_int4_lora_workspace_size(1, 64, 100, 0) < 0
 
 
 def test_int4_empty_problems_are_noops(lib):

@@ -303,3 +303,62 @@ def test_full_size_without_zero_point_sampled(gpu_lib, m, k, n):
     cols = sample_indices(n, 160, m + 1)
     ref = oracle.qgemm_int4_at(d["x"], d["qweight"], d["scales"], None, k, n, rows, cols)
     assert_accepted(y[np.ix_(rows, cols)], ref, ("nozero-full", m, k, n))
+
+
+# ----------------------------------------------------------------------------
+# LoRA add in the epilogue (qgemm_int4_lora): every path, with and without the
+# k split / preparation, ranks 16 and 5, full sizes sampled
+# ----------------------------------------------------------------------------
+from qgemm_inputs import lora_inputs  # noqa: E402
+
+
+def upload_lora(l):
+    import torch
+
+    return dev(l["lora_a"], torch.bfloat16), dev(l["lora_b"], torch.bfloat16)
+
+
+LORA_CASES = [("gemv", 1, 1152, 776, 16), ("fused", 2, 2048, 1040, 16), ("fused", 8, 1152, 776, 5),
+              ("fused", 15, 2048, 1040, 16), ("fused", 16, 1152, 776, 16), ("mfma", 17, 2048, 1040, 16),
+              ("mfma", 130, 1152, 776, 5), ("mfma", 257, 2048, 1040, 16),
+              ("gemv", 1, 16384, 520, 16), ("fused", 8, 16384, 520, 16), ("mfma", 33, 4096, 520, 16)]
+
+
+@pytest.mark.parametrize("path,m,k,n,rank", LORA_CASES)
+def test_lora_paths_match_oracle(gpu_lib, path, m, k, n, rank):
+    import torch
+
+    say("lora", path, m, k, n, rank, gpu_lib.describe_int4(m, n, k, path))
+    d = int4_inputs(m, k, n, seed=600 + m + k + n)
+    l = lora_inputs(k, n, rank, seed=700 + rank)
+    t = upload_int4(d)
+    la, lb = upload_lora(l)
+    ref = oracle.qgemm_int4_lora(d["x"], d["qweight"], d["scales"], d["qzeros"], l["lora_a"], l["lora_b"],
+                                 2.0, m, k, n)
+    y = gpu_lib.qgemm_int4_lora(t["x"], t["qweight"], t["scales"], t["qzeros"], la, lb, 2.0, path=path)
+    torch.cuda.synchronize()
+    assert_accepted(host_u16(y), ref, ("lora", path, m, k, n, rank))
+    # the smallest workspace (U only): no k split, no preparation pass
+    u_only = torch.zeros(((64 * m + 255) // 256) * 256, dtype=torch.uint8, device="cuda")
+    y2 = gpu_lib.qgemm_int4_lora(t["x"], t["qweight"], t["scales"], t["qzeros"], la, lb, 2.0, path=path,
+                                 workspace=u_only)
+    torch.cuda.synchronize()
+    assert_accepted(host_u16(y2), ref, ("lora-min-ws", path, m, k, n, rank))
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 4096, 4096), (15, 2048, 8192), (512, 5120, 25600)])
+def test_lora_full_size_sampled(gpu_lib, m, k, n):
+    import torch
+
+    say("lora-full", m, k, n)
+    d = int4_inputs(m, k, n, seed=900 + m)
+    l = lora_inputs(k, n, 16, seed=901)
+    t = upload_int4(d)
+    la, lb = upload_lora(l)
+    y = host_u16(gpu_lib.qgemm_int4_lora(t["x"], t["qweight"], t["scales"], t["qzeros"], la, lb, 2.0))
+    torch.cuda.synchronize()
+    rows = sample_indices(m, 24, m)
+    cols = sample_indices(n, 160, m + 1)
+    ref = oracle.qgemm_int4_lora_at(d["x"], d["qweight"], d["scales"], d["qzeros"], l["lora_a"], l["lora_b"],
+                                    2.0, k, n, rows, cols)
+    assert_accepted(y[np.ix_(rows, cols)], ref, ("lora-full", m, k, n))

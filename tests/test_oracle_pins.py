@@ -319,6 +319,18 @@ def test_lora_one_hot_closed_form():
     assert np.array_equal(y - base, np.full((m, n), 0.5 * 10.0))
 
 
+def test_lora_term_exceeds_the_tolerance():
+    # at the adapter scale the tests use, the LoRA term moves most outputs by more
+    # than the acceptance rule allows: a kernel that dropped it would be rejected
+    m, k, n = 8, 1152, 776
+    d = int4_inputs(m, k, n, seed=801)
+    l = lora_inputs(k, n, 16, seed=802)
+    base = oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], m, k, n)
+    with_lora = oracle.qgemm_int4_lora(d["x"], d["qweight"], d["scales"], d["qzeros"], l["lora_a"],
+                                       l["lora_b"], 2.0, m, k, n)
+    assert np.mean(oracle.accept(oracle.round_to_grid(base, "bf16"), with_lora, "bf16")) < 0.2
+
+
 def test_sampled_outputs_match_full():
     m, k, n = 5, 512, 64
     d = int4_inputs(m, k, n, seed=16)
