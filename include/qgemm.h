@@ -129,12 +129,16 @@ int32_t qgemm_int4(const void* x, int64_t ldx, const uint32_t* qweight, const ui
  *   rank     1..16.
  *   path     as qgemm_int4_path (QG_PATH_AUTO chooses from m).
  *   workspace, workspace_bytes
- *            required: the last round_up(64 m, 256) bytes hold U; the front
- *            part, rounded down to 256 bytes, serves the path as in
- *            qgemm_int4 (same counter contract).  qgemm_int4_lora_workspace_size
- *            gives the size that also enables the path's split / preparation.
+ *            required: its end holds U and the partial tiles of U's k
+ *            slices (round_up(64 m, 256) + 1 KiB per 16 rows and slice; the
+ *            minimum is qgemm_int4_lora_workspace_size with path data
+ *            excluded); the front part, rounded down to 256 bytes, serves the
+ *            path as in qgemm_int4 (same counter contract).
+ *            qgemm_int4_lora_workspace_size gives the size that also enables
+ *            the path's split / preparation.
  *
- * U is computed by a small kernel launched first on the same stream; the LoRA
+ * U is computed by two small kernels launched first on the same stream (k
+ * slices of U in parallel, then their sum in slice order); the LoRA
  * term is added to the fp32 accumulators of the product's own epilogue (once
  * per output also when k is split).  Other arguments, limits and errors as
  * qgemm_int4 (plus QG_ERR_SHAPE for a bad rank or a workspace without room

@@ -53,8 +53,9 @@ int32_t check_path(int64_t m, int32_t path) {
   return QG_OK;
 }
 
-// Bytes of the LoRA intermediate U (fp32 [m][16]) at the end of the workspace.
-int64_t lora_u_bytes(int64_t m) { return (m * 16 * 4 + 255) & ~(int64_t)255; }
+// Bytes of the LoRA intermediate U (fp32 [m][16]) and its k-slice partials at
+// the end of the workspace.
+int64_t lora_u_bytes(int64_t m, int64_t k) { return qg::lora_bytes(m, k); }
 
 int32_t run_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
                  const uint32_t* qzeros, void* y, int64_t ldy, int64_t m, int64_t n, int64_t k,
@@ -74,7 +75,7 @@ int32_t run_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint
   if (lora != nullptr) {
     // U = X . A^T into the end of the workspace, then the product with the
     // LoRA add in its epilogue; the path keeps the 256-byte aligned front part
-    const int64_t rest = (ws_bytes - lora_u_bytes(m)) & ~(int64_t)255;
+    const int64_t rest = (ws_bytes - lora_u_bytes(m, k)) & ~(int64_t)255;
     float* u = (float*)((char*)ws + rest);
     st = hip_status(qg::launch_lora_u((const uint16_t*)x, ldx, (const uint16_t*)lora_a, lda_a, lora->rank, m,
                                       k, u, s));
@@ -138,7 +139,7 @@ int32_t qgemm_int4_lora(const void* x, int64_t ldx, const uint32_t* qweight, con
     if (lora_a == nullptr || lora_b == nullptr) return QG_ERR_NULL;
     if (lda_a < k || ldb_b < rank) return QG_ERR_SHAPE;
     if (!aligned(lora_a, 16) || lda_a % 8 != 0 || !aligned(lora_b, 2)) return QG_ERR_ALIGN;
-    if (workspace == nullptr || workspace_bytes < lora_u_bytes(m)) return QG_ERR_SHAPE;
+    if (workspace == nullptr || workspace_bytes < lora_u_bytes(m, k)) return QG_ERR_SHAPE;
   }
   if (m > 0 && n > 0 && k == 0)      // U = 0: the plain product (zeros)
     return run_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size, path, workspace,
@@ -151,7 +152,7 @@ int32_t qgemm_int4_lora(const void* x, int64_t ldx, const uint32_t* qweight, con
 int64_t qgemm_int4_lora_workspace_size(int64_t m, int64_t n, int64_t k, int32_t path) {
   const int64_t base = qgemm_int4_workspace_size(m, n, k, path);
   if (base < 0) return base;
-  return ((base + 255) & ~(int64_t)255) + lora_u_bytes(m);
+  return ((base + 255) & ~(int64_t)255) + lora_u_bytes(m, k);
 }
 
 int64_t qgemm_int4_workspace_size(int64_t m, int64_t n, int64_t k, int32_t path) {

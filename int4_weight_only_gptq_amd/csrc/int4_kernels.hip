@@ -195,37 +195,68 @@ __device__ __forceinline__ void load_group(GroupRegs<M, DOT, CPL>& r, bool gok, 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __builtin_bit_cast(float, h << 16); }
 
 // The LoRA term of one output (row, col): scale * sum_r U[row][r] B[col][r].
+// All loads are issued before the first use (one round trip): the U row as
+// four 16-byte loads, the B row as two when its 16 entries are aligned (else
+// element loads); U's columns past the rank are zero, B is used only below it.
 __device__ __forceinline__ float lora_term(const LoraEpi& L, int64_t row, int64_t col) {
-  const float* u = L.u + row * 16;
+  const f32x4* u = reinterpret_cast<const f32x4*>(L.u + row * 16);
   const uint16_t* b = L.b + col * L.ldb;
+  f32x4 uu[4];
+  float bb[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) uu[i] = u[i];
+  // loads from clamped in-range addresses, the rank applied by a select after
+  // them: no branch between the loads
+  if (L.ldb >= 16 && (L.ldb & 7) == 0 && ((uintptr_t)L.b & 15u) == 0) {
+    const u32x4 w0 = *reinterpret_cast<const u32x4*>(b), w1 = *reinterpret_cast<const u32x4*>(b + 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bb[2 * i] = bf16_bits_to_float(w0[i] & 0xFFFFu);
+      bb[2 * i + 1] = bf16_bits_to_float(w0[i] >> 16);
+      bb[8 + 2 * i] = bf16_bits_to_float(w1[i] & 0xFFFFu);
+      bb[8 + 2 * i + 1] = bf16_bits_to_float(w1[i] >> 16);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bb[r] = r < L.rank ? bb[r] : 0.f;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float v = bf16_bits_to_float(b[r < L.rank ? r : 0]);
+      bb[r] = r < L.rank ? v : 0.f;
+    }
+  }
   float s = 0.f;
-  for (int r = 0; r < L.rank; ++r) s = __builtin_fmaf(u[r], bf16_bits_to_float(b[r]), s);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s = __builtin_fmaf(uu[r >> 2][r & 3], bb[r], s);
   return L.scale * s;
 }
 
-// U rows row0 .. row0+15 (one workgroup of 16 waves, which take interleaved
-// 32-k steps): 16x16x32 bf16 MFMA with the activations as A and lora_A's rows
-// as B, fp32 accumulation, the waves' partial tiles summed through LDS.
-__global__ __launch_bounds__(1024) void lora_u_kernel(const uint16_t* __restrict__ x, int64_t ldx,
-                                                      const uint16_t* __restrict__ a, int64_t lda, int rank,
-                                                      int64_t m, int64_t k, float* __restrict__ u) {
+// U = X . A^T in two small launches: partial 16 x 16 tiles of U over k slices
+// (workgroup (b, s): rows 16 b .. 16 b + 15, k slice s; its 16 waves take
+// interleaved 32-k steps on the 16x16x32 bf16 MFMA with the activations as A
+// and lora_A's rows as B, fp32), then the slices summed in slice order.
+// Slices of `kps` k (a multiple of 512); partials [b][s][16][16] fp32.
+__global__ __launch_bounds__(1024) void lora_u_partial_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                              const uint16_t* __restrict__ a, int64_t lda,
+                                                              int rank, int64_t m, int k, int kps,
+                                                              float* __restrict__ part) {
   __shared__ float red[16][16][16];   // [wave][row][r]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cl = lane & 15, ks = lane >> 4;
   const int64_t row0 = (int64_t)blockIdx.x * 16;
+  const int kbeg = blockIdx.y * kps, kend = min(k, kbeg + kps);
   const bool xok = row0 + cl < m, aok = cl < rank;
   const uint16_t* xp = x + (xok ? row0 + cl : 0) * ldx + 8 * ks;
   const uint16_t* ap = a + (aok ? cl : 0) * lda + 8 * ks;
   const u32x4 z = {0u, 0u, 0u, 0u};
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const int kw = (int)k;   // k <= 2^22
-  for (int k0 = 32 * wave; k0 < kw; k0 += 4 * 512) {   // four steps' loads in flight, then the MFMAs
+  for (int k0 = kbeg + 32 * wave; k0 < kend; k0 += 4 * 512) {   // four steps' loads in flight, then the MFMAs
     u32x4 xv[4], av[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int kk = k0 + 512 * j;
-      xv[j] = xok && kk < kw ? *reinterpret_cast<const u32x4*>(xp + kk) : z;
-      av[j] = aok && kk < kw ? *reinterpret_cast<const u32x4*>(ap + kk) : z;
+      xv[j] = xok && kk < kend ? *reinterpret_cast<const u32x4*>(xp + kk) : z;
+      av[j] = aok && kk < kend ? *reinterpret_cast<const u32x4*>(ap + kk) : z;
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc = mfma16_bf16(xv[j], av[j], acc);
@@ -237,14 +268,59 @@ __global__ __launch_bounds__(1024) void lora_u_kernel(const uint16_t* __restrict
     const int rr = tid >> 4, c = tid & 15;
     float sum = 0.f;
     for (int w = 0; w < 16; ++w) sum += red[w][rr][c];
-    if (row0 + rr < m) u[(row0 + rr) * 16 + c] = sum;
+    part[((int64_t)blockIdx.x * gridDim.y + blockIdx.y) * 256 + tid] = sum;
   }
+}
+
+__global__ __launch_bounds__(256) void lora_u_reduce_kernel(const float* __restrict__ part, int slices, int64_t m,
+                                                            float* __restrict__ u) {
+  const int tid = threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (tid >> 4);
+  const float* p = part + (int64_t)blockIdx.x * slices * 256 + tid;
+  float sum = 0.f;
+  for (int s0 = 0; s0 < slices; s0 += 8) {      // eight loads in flight, added in slice order
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float w = p[(int64_t)(s0 + j < slices ? s0 + j : slices - 1) * 256];
+      v[j] = s0 + j < slices ? w : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sum += v[j];
+  }
+  if (row < m) u[row * 16 + (tid & 15)] = sum;
+}
+
+// k slices of the U product: about 512 workgroups over the row blocks, each
+// slice a multiple of 512 k.
+void lora_u_split(int64_t m, int64_t k, int* slices, int* kps) {
+  const int64_t blocks = (m + 15) / 16, steps = (k + 511) / 512;
+  int64_t s = (512 + blocks - 1) / blocks;
+  if (s > steps) s = steps;
+  if (s < 1) s = 1;
+  const int64_t per = (steps + s - 1) / s;
+  *kps = (int)(per * 512);
+  *slices = (int)((k + *kps - 1) / *kps);
+  if (*slices < 1) *slices = 1;
+}
+
+int64_t lora_bytes(int64_t m, int64_t k) {
+  int slices, kps;
+  lora_u_split(m, k, &slices, &kps);
+  const int64_t blocks = (m + 15) / 16;
+  return ((m * 64 + 255) & ~(int64_t)255) + blocks * slices * 1024;
 }
 
 hipError_t launch_lora_u(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t lda, int rank, int64_t m,
                          int64_t k, float* u, hipStream_t stream) {
   if (m == 0) return hipSuccess;
-  lora_u_kernel<<<dim3((unsigned)((m + 15) / 16)), dim3(1024), 0, stream>>>(x, ldx, a, lda, rank, m, k, u);
+  int slices, kps;
+  lora_u_split(m, k, &slices, &kps);
+  const int64_t blocks = (m + 15) / 16;
+  float* part = u + ((m * 16 + 63) & ~(int64_t)63);      // after U, 256-byte aligned
+  lora_u_partial_kernel<<<dim3((unsigned)blocks, (unsigned)slices), dim3(1024), 0, stream>>>(
+      x, ldx, a, lda, rank, m, (int)k, kps, part);
+  lora_u_reduce_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(part, slices, m, u);
   return hipGetLastError();
 }
 
@@ -282,6 +358,20 @@ __global__ __launch_bounds__(1024) void skinny_int4_kernel(
   GroupRegs<M, DOT, CPL> cur, nxt;
   int g = gbeg + wave;
   load_group<M, DOT, CPL>(cur, g < gend, live, xrow, qp, xp, scales, qzeros, n, g, col, ks);
+
+  // the LoRA terms of this thread's outputs in the final reduction (output
+  // o = tid + j * blockDim), computed now so that their loads overlap the
+  // k loop; added once per output (slice 0 of a split strip)
+  float lora_pre[4] = {0.f, 0.f, 0.f, 0.f};
+  if (lora.u && kslice == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int o = tid + j * blockDim.x;
+      const int token = o / SW, cc = o - token * SW;
+      const int64_t cg = (int64_t)strip * SW + cc;
+      if (o < M * SW && cg < n) lora_pre[j] = lora_term(lora, token, cg);
+    }
+  }
 
   f32x4 total[CPL];
 #pragma unroll
@@ -355,12 +445,19 @@ __global__ __launch_bounds__(1024) void skinny_int4_kernel(
   __syncthreads();
 
   float* mine = ksplit > 1 ? partials + ((int64_t)strip * ksplit + kslice) * (M * SW) : nullptr;
-  for (int o = tid; o < M * SW; o += blockDim.x) {
+  int jo = 0;                              // index of the output within this thread's
+  for (int o = tid; o < M * SW; o += blockDim.x, ++jo) {
     const int token = o / SW, cc = o - token * SW;
     float v = 0.f;
     for (int w = 0; w < nw; ++w) v += plane[(w * M + token) * SW + cc];
     const int64_t cg = (int64_t)strip * SW + cc;
-    if (lora.u && kslice == 0 && cg < n) v += lora_term(lora, token, cg);   // once per output
+    if (lora.u && kslice == 0 && cg < n) {
+      // precomputed for the first four outputs (selects, no indexed registers)
+      float pre = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pre = jo == i ? lora_pre[i] : pre;
+      v += jo < 4 ? pre : lora_term(lora, token, cg);
+    }
     if (ksplit == 1) {
       if (cg < n) y[(int64_t)token * ldy + cg] = (uint16_t)f32_to_bf16_bits(v);
     } else {
@@ -546,6 +643,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
   for (int f = 0; f < FM; ++f)
 #pragma unroll
     for (int c = 0; c < 4; ++c) total[f][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
   const u32x4 ones = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
 
   const int ktiles = 2 * (gend - gbeg);   // stages of this slice
@@ -559,6 +657,44 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
     fw = *reinterpret_cast<const u32x4*>(st + S::X_DW + (4 * s + ks) * BN + wn0 + 4 * cl);
   };
 
+  // LoRA add (once per output: slice 0 of a split tile): total starts at
+  // scale * U[rows] . B[cols]^T, four 16x16x4 fp32 MFMAs per 16 x 16 block
+  // with the block's rows of U as A and its fragment's columns 4 l + c of B
+  // as B; MFMA j takes rank index r = 4 k4 + j (k4 = lane / 16) from both, so
+  // a lane's operands are four consecutive entries of a U row (one 16-byte
+  // load) and of a B row (one 8-byte load when B's rows hold 16 aligned
+  // entries; else element loads).  The result lands in the layout of total.
+  // The operands are loaded before the prologue's stage loads and multiplied
+  // once the first stage has landed.  U's columns past the rank are zero; B
+  // is used only below the rank (clamped addresses, selects after the loads).
+  const bool lora_on = lora.u && kslice == 0;
+  f32x4 ua[FM];
+  float bb[4][4];
+  if (lora_on) {
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+      const int64_t row = m0 + wm0 + 16 * f + cl;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(lora.u + (row < m ? row : m - 1) * 16 + 4 * ks);
+      ua[f] = row < m ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const bool bvec = lora.ldb >= 16 && (lora.ldb & 3) == 0 && ((uintptr_t)lora.b & 7u) == 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int64_t col = n0 + wn0 + 4 * cl + c;
+      const uint16_t* brow = lora.b + (col < n ? col : n - 1) * lora.ldb;
+      uint32_t h[4];
+      if (bvec) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(brow + 4 * ks);
+        h[0] = w[0] & 0xFFFFu; h[1] = w[0] >> 16; h[2] = w[1] & 0xFFFFu; h[3] = w[1] >> 16;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[j] = brow[4 * ks + j < lora.rank ? 4 * ks + j : 0];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bb[j][c] = (col < n && 4 * ks + j < lora.rank) ? bf16_bits_to_float(h[j]) : 0.f;
+    }
+  }
+
   // all STAGES buffers start filling; stage 0 must land before the first read
 #pragma unroll
   for (int st = 0; st < STAGES; ++st)
@@ -570,6 +706,20 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
   }
   lds_barrier();
   read_step(0, 0);
+  if (lora_on) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int f = 0; f < FM; ++f)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) total[f][c] = mfma16_f32(ua[f][j], bb[j][c], total[f][c]);
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) total[f][c][v] *= lora.scale;
+  }
 
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   for (int g = 0; g < (ktiles >> 1); ++g) {
@@ -642,44 +792,6 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
                                               total[f][c][v]);
       }
     }
-  }
-  if (lora.u && kslice == 0) {
-    // LoRA add (once per output: slice 0 of a split tile): total += scale *
-    // U[rows] . B[cols]^T as four 16x16x4 fp32 MFMAs per 16 x 16 block, the
-    // A operand U[row][4 j + k4] and the B operand B[col][4 j + k4] (k4 =
-    // lane / 16) for the block's rows and its fragment's columns 4 l + c, so
-    // the result lands in the layout of total.  U's columns past the rank are
-    // zero; B is read only below the rank.
-    f32x4 lr[FM][4];
-#pragma unroll
-    for (int f = 0; f < FM; ++f)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) lr[f][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * j + ks;
-      float ua[FM], bb[4];
-#pragma unroll
-      for (int f = 0; f < FM; ++f) {
-        const int64_t row = m0 + wm0 + 16 * f + cl;
-        ua[f] = row < m ? lora.u[row * 16 + r] : 0.f;
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int64_t col = n0 + wn0 + 4 * cl + c;
-        bb[c] = (col < n && r < lora.rank) ? bf16_bits_to_float(lora.b[col * lora.ldb + r]) : 0.f;
-      }
-#pragma unroll
-      for (int f = 0; f < FM; ++f)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) lr[f][c] = mfma16_f32(ua[f], bb[c], lr[f][c]);
-    }
-#pragma unroll
-    for (int f = 0; f < FM; ++f)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) total[f][c][v] = __builtin_fmaf(lora.scale, lr[f][c][v], total[f][c][v]);
   }
   if (ksplit > 1) {
     // Split k: every slice stores its fp32 partial tile with agent-coherent

@@ -30,9 +30,11 @@ struct Int4Args {
 };
 
 // U[m][16] = X . A^T in fp32 for lora_A bf16 [rank][lda] (rank <= 16; the
-// other columns of U are written as zeros).
+// other columns of U are written as zeros).  u points at lora_bytes(m, k)
+// bytes: U, then (256-byte aligned) the partial tiles of its k slices.
 hipError_t launch_lora_u(const uint16_t* x, int64_t ldx, const uint16_t* a, int64_t lda, int rank, int64_t m,
                          int64_t k, float* u, hipStream_t stream);
+int64_t lora_bytes(int64_t m, int64_t k);
 
 hipError_t launch_dequant(const uint32_t* qweight, const uint16_t* scales, const uint32_t* qzeros,
                           float* w, int64_t n, int64_t k, hipStream_t stream);

@@ -338,8 +338,12 @@ def test_lora_paths_match_oracle(gpu_lib, path, m, k, n, rank):
     y = gpu_lib.qgemm_int4_lora(t["x"], t["qweight"], t["scales"], t["qzeros"], la, lb, 2.0, path=path)
     torch.cuda.synchronize()
     assert_accepted(host_u16(y), ref, ("lora", path, m, k, n, rank))
-    # the smallest workspace (U only): no k split, no preparation pass
-    u_only = torch.zeros(((64 * m + 255) // 256) * 256, dtype=torch.uint8, device="cuda")
+    # the smallest workspace (U and its slices only): no k split, no preparation pass
+    lib = gpu_lib.load()
+    up = lambda v: (v + 255) // 256 * 256
+    u_bytes = (lib.qgemm_int4_lora_workspace_size(m, n, k, gpu_lib.PATHS[path])
+               - up(gpu_lib.workspace_size(m, n, k, path)))
+    u_only = torch.zeros(u_bytes, dtype=torch.uint8, device="cuda")
     y2 = gpu_lib.qgemm_int4_lora(t["x"], t["qweight"], t["scales"], t["qzeros"], la, lb, 2.0, path=path,
                                  workspace=u_only)
     torch.cuda.synchronize()
