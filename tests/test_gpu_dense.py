@@ -347,3 +347,16 @@ def test_fp32_training_products_sampled(gpu_lib, case):
     ref = oracle.dense_at(layout, "fp32", d["a"], d["b"], rows, cols)
     absd = oracle.dense_absdot(layout, "fp32", d["a"], d["b"], rows, cols)
     assert_fp32_accepted(c[np.ix_(rows, cols)], ref, absd, K, ("fp32-trio", case["role"]))
+
+
+# long reductions: the 16 x 16 split-k kernel over 2^19 k and the pipeline over
+# 2^16 k (fp32 accumulation over long k stays inside the bound)
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+@pytest.mark.parametrize("M,N,K", [(32, 16, 1 << 19), (256, 256, 1 << 16)])
+def test_long_k(gpu_lib, layout, M, N, K):
+    say("long-k", layout, M, N, K)
+    d = dense_inputs(layout, "bf16", M, N, K, seed=1600 + M, std=0.02)
+    c = host_u16(run(gpu_lib, layout, dev(d["a"], tdtype("bf16")), dev(d["b"], tdtype("bf16"))))
+    rows, cols = sample_indices(M, 16, 1), sample_indices(N, 16, 2)
+    ref = oracle.dense_at(layout, "bf16", d["a"], d["b"], rows, cols)
+    assert_accepted(c[np.ix_(rows, cols)], ref, "bf16", ("long-k", layout, M, N, K))

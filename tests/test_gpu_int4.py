@@ -366,3 +366,57 @@ def test_lora_full_size_sampled(gpu_lib, m, k, n):
     ref = oracle.qgemm_int4_lora_at(d["x"], d["qweight"], d["scales"], d["qzeros"], l["lora_a"], l["lora_b"],
                                     2.0, k, n, rows, cols)
     assert_accepted(y[np.ix_(rows, cols)], ref, ("lora-full", m, k, n))
+
+
+# ----------------------------------------------------------------------------
+# maximum sizes of the ABI: k = 2^22 (the 32-bit stage offsets' limit) on every
+# path, and n = 2^26 columns (4 GiB of codes) on the GEMV and fused paths,
+# checked on sampled columns
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("path,m", [("gemv", 1), ("fused", 8), ("mfma", 17), ("mfma_nows", 17)])
+def test_max_k(gpu_lib, path, m):
+    k, n = 1 << 22, 64
+    p, ws = ("mfma", False) if path == "mfma_nows" else (path, None)
+    say("max-k", path, m, k, n, gpu_lib.describe_int4(m, n, k, p, None if ws is None else 0))
+    d = int4_inputs(m, k, n, seed=1100 + m)
+    y = host_u16(run(gpu_lib, upload_int4(d), p, workspace=ws))
+    cols = np.array([0, 1, 9, 31, 40, 63])
+    ref = oracle.qgemm_int4_at(d["x"], d["qweight"], d["scales"], d["qzeros"], k, n, np.arange(m), cols)
+    assert_accepted(y[:, cols], ref, ("max-k", path, m))
+
+
+@pytest.mark.parametrize("path,m", [("gemv", 1), ("fused", 2)])
+def test_max_n(gpu_lib, path, m):
+    # 2^26 columns: operands drawn on the device from a seeded torch generator
+    # (raw words and scale bit patterns of the same distributions), the sampled
+    # columns copied back for the oracle
+    import torch
+
+    k, n = 128, 1 << 26
+    say("max-n", path, m, k, n)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1200 + m)
+    x = (torch.randn((m, k), generator=g, device="cuda")).to(torch.bfloat16)
+    qw = torch.randint(-2 ** 31, 2 ** 31 - 1, (k // 8, n), generator=g, device="cuda", dtype=torch.int32)
+    sc = (0.005 + (torch.randn((1, n), generator=g, device="cuda") * 0.01).abs()).to(torch.float16)
+    qz = torch.randint(-2 ** 31, 2 ** 31 - 1, (1, n // 8), generator=g, device="cuda", dtype=torch.int32)
+    y = gpu_lib.qgemm_int4(x, qw, sc, qz, path=path)
+    torch.cuda.synchronize()
+    cols = np.array([0, 7, 8, 12345, (1 << 25) + 3, n - 9, n - 1])
+    ct = torch.from_numpy(cols).cuda()
+    xb = host_u16(x)
+    qwb = host_u32(qw[:, ct])
+    scb = host_u16(sc[:, ct])
+    # zero words of the sampled columns, re-packed so that column j sits in nibble j % 8
+    zw = host_u32(qz[:, ct // 8])
+    zsel = ((zw >> (4 * (cols % 8)).astype(np.uint32)) & 0xF).astype(np.uint32) << (4 * (np.arange(len(cols)) % 8)).astype(np.uint32)
+    # the oracle's zero layout packs 8 columns per word: rebuild words for the sample
+    nq = (len(cols) + 7) // 8
+    qzs = np.zeros((1, nq), dtype=np.uint32)
+    for i in range(len(cols)):
+        qzs[0, i // 8] |= np.uint32(zsel[0, i])
+    pad = nq * 8 - len(cols)
+    qwp = np.concatenate([qwb, np.zeros((k // 8, pad), dtype=np.uint32)], axis=1)
+    scp = np.concatenate([scb, np.zeros((1, pad), dtype=np.uint16)], axis=1)
+    ref = oracle.qgemm_int4(xb, qwp, scp, qzs, m, k, nq * 8)[:, :len(cols)]
+    assert_accepted(host_u16(y[:, ct]), ref, ("max-n", path, m))
