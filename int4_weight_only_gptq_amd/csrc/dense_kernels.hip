@@ -975,18 +975,61 @@ static void pipe_launch(const DenseArgs& a, hipStream_t stream) {
 #ifndef QG_DENSE_T64X128
 #define QG_DENSE_T64X128 0.4
 #endif
+// rounds-model cost of tile t (2: 256 x 256, 1: 256 x 128, 0: 128 x 128,
+// -1: 64 x 128) over an M x N output (batch products)
+static double pipe_cost(int t, int64_t M, int64_t N, int64_t batch) {
+  auto rounds = [batch](int64_t tiles) { return (double)((tiles * batch + 255) / 256); };
+  switch (t) {
+    case 2: return rounds(((M + 255) / 256) * ((N + 255) / 256)) * QG_DENSE_T256X256;
+    case 1: return rounds(((M + 255) / 256) * ((N + 127) / 128));
+    case 0: return rounds(((M + 127) / 128) * ((N + 127) / 128)) * QG_DENSE_T128X128;
+    default: return rounds(((M + 63) / 64) * ((N + 127) / 128)) * QG_DENSE_T64X128;
+  }
+}
+
 static int pick_pipe_tile(int64_t M, int64_t N, int64_t batch) {
 #ifdef QG_DENSE_FORCE_TILE
   return QG_DENSE_FORCE_TILE;       // tile sweeps
 #endif
-  auto rounds = [batch](int64_t tiles) { return (double)((tiles * batch + 255) / 256); };
-  const double c2 = rounds(((M + 255) / 256) * ((N + 255) / 256)) * QG_DENSE_T256X256;
-  const double c1 = rounds(((M + 255) / 256) * ((N + 127) / 128));
-  const double c0 = rounds(((M + 127) / 128) * ((N + 127) / 128)) * QG_DENSE_T128X128;
-  const double cm = rounds(((M + 63) / 64) * ((N + 127) / 128)) * QG_DENSE_T64X128;
+  const double c2 = pipe_cost(2, M, N, batch), c1 = pipe_cost(1, M, N, batch);
+  const double c0 = pipe_cost(0, M, N, batch), cm = pipe_cost(-1, M, N, batch);
   if (c2 <= c1 && c2 < c0 && c2 < cm) return 2;     // ties: 256 x 256 measured 3-4% ahead
   if (c1 <= c0 && c1 <= cm) return 1;
   return c0 <= cm ? 0 : -1;
+}
+
+// Two row bands when a tile size leaves its last round mostly empty: the first
+// band is whole rounds of 256-row tiles (256 x 256 or 256 x 128), the rest gets
+// its own tile choice, each band one launch on the stream.  Returns the first
+// band's rows (a multiple of 256) or 0 when one launch is cheaper; a second
+// launch is charged QG_DENSE_BAND_GAP of a 256 x 128 round.
+#ifndef QG_DENSE_BAND_GAP
+#define QG_DENSE_BAND_GAP 0.1
+#endif
+static int64_t pick_row_bands(int64_t M, int64_t N, int64_t batch, int* t1, int* t2) {
+#ifdef QG_DENSE_FORCE_TILE
+  return 0;
+#endif
+  if (batch != 1) return 0;
+  const int one = pick_pipe_tile(M, N, 1);
+  double best = pipe_cost(one, M, N, 1);
+  int64_t m1_best = 0;
+  for (int t = 1; t <= 2; ++t) {
+    const int64_t tn = t == 2 ? (N + 255) / 256 : (N + 127) / 128;
+    for (int64_t r = 1; r <= 8; ++r) {
+      const int64_t m1 = (256 * r / tn) * 256;
+      if (m1 <= 0 || m1 >= M) break;
+      const int other = pick_pipe_tile(M - m1, N, 1);
+      const double c = pipe_cost(t, m1, N, 1) + pipe_cost(other, M - m1, N, 1) + QG_DENSE_BAND_GAP;
+      if (c < best - 1e-9) {
+        best = c;
+        m1_best = m1;
+        *t1 = t;
+        *t2 = other;
+      }
+    }
+  }
+  return m1_best;
 }
 
 template <int LAYOUT, int DTYPE>
@@ -1003,11 +1046,27 @@ static void dense_dispatch(const DenseArgs& a, hipStream_t stream) {
     dense_smallk_kernel<LAYOUT, DTYPE><<<dim3((unsigned)(per_xcd * 8), (unsigned)a.batch), dim3(256), 0, stream>>>(
         a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, vec, strides(a));
   } else if (mfma_fits(a) && a.K % DBK == 0 && a.M >= 128 && a.N >= 128) {
-    switch (pick_pipe_tile(a.M, a.N, a.batch)) {
-      case 2: pipe_launch<LAYOUT, DTYPE, 256, 256, 2>(a, stream); break;
-      case 1: pipe_launch<LAYOUT, DTYPE, 256, 128, QG_DENSE_PIPE_STAGES>(a, stream); break;
-      case 0: pipe_launch<LAYOUT, DTYPE, 128, 128, 4>(a, stream); break;
-      default: pipe_launch<LAYOUT, DTYPE, 64, 128, 4>(a, stream); break;
+    auto launch_tile = [&](int t, const DenseArgs& b) {
+      switch (t) {
+        case 2: pipe_launch<LAYOUT, DTYPE, 256, 256, 2>(b, stream); break;
+        case 1: pipe_launch<LAYOUT, DTYPE, 256, 128, QG_DENSE_PIPE_STAGES>(b, stream); break;
+        case 0: pipe_launch<LAYOUT, DTYPE, 128, 128, 4>(b, stream); break;
+        default: pipe_launch<LAYOUT, DTYPE, 64, 128, 4>(b, stream); break;
+      }
+    };
+    int t1 = 0, t2 = 0;
+    const int64_t m1 = pick_row_bands(a.M, a.N, a.batch, &t1, &t2);
+    if (m1 > 0) {
+      // rows [0, m1) and [m1, M): A's rows (its columns for TN) and C's rows
+      DenseArgs lo = a, hi = a;
+      lo.M = m1;
+      hi.M = a.M - m1;
+      hi.A = a.A + (LAYOUT == 2 ? m1 : m1 * a.lda);
+      hi.C = a.C + m1 * a.ldc;
+      launch_tile(t1, lo);
+      launch_tile(t2, hi);
+    } else {
+      launch_tile(pick_pipe_tile(a.M, a.N, a.batch), a);
     }
   } else if (mfma_fits(a)) {
     const int64_t big = ((a.M + 255) / 256) * ((a.N + 127) / 128);

@@ -58,9 +58,9 @@ def test_shapes_match_oracle(gpu_lib, layout, dtype):
 
 # shapes for the pipelined kernel (K % 64 == 0): ragged M and N edges, all four tile
 # sizes (2050 x 5624 takes 256 x 256 tiles: one round of 198 against two of 396;
-# 1000 x 2000 takes 64 x 128 tiles: one round of 256)
+# 1000 x 2000 takes 64 x 128 tiles: one round of 256), and two row bands
 PIPE_SHAPES = [(128, 128, 64), (200, 264, 128), (1000, 136, 192), (2000, 2600, 64), (2050, 5624, 192),
-               (1000, 2000, 128)]
+               (1000, 2000, 128), (3000, 5632, 128)]   # the last in two row bands (2816 + 184 rows)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
