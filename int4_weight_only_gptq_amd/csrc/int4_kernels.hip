@@ -888,6 +888,9 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
 #ifndef QG_SKINNY_MAX_GPW
 #define QG_SKINNY_MAX_GPW 6        // groups per wave above which k is split
 #endif
+#ifndef QG_SKINNY_WIDE_M
+#define QG_SKINNY_WIDE_M 8         // tokens from which wide strips pay for a k split
+#endif
 
 int64_t split_workspace_bytes(int64_t nstrips, int64_t ksplit, int64_t m, int cpl) {
   return kTicketBytes + nstrips * ksplit * m * 16 * cpl * 4;
@@ -912,6 +915,28 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes,
     ks = (per_wave + 3) / 4;
     if (ks > SK_MAX_SPLIT) ks = SK_MAX_SPLIT;
   }
+  // Several tokens: every workgroup reads X over its k range, so the X traffic
+  // is (strips) x m x k x 2 bytes, 4m / (16 CPL) times the codes' traffic.
+  // When k is long enough to be split anyway, take the widest strip whose
+  // count, times a split of at most SK_MAX_SPLIT, still fills the CUs.
+  if (!dot && m >= QG_SKINNY_WIDE_M && ks > 1 && p.cpl < 4) {
+    for (int c = 4; c > p.cpl; c /= 2) {
+      const int64_t strips = (n + 16 * c - 1) / (16 * c);
+      const int64_t wc = strips >= 384 ? (QG_SKINNY_WAVES < 8 ? QG_SKINNY_WAVES : 8) : QG_SKINNY_WAVES;
+      const int64_t wv = G < 2 ? 1 : (G / 2 < wc ? G / 2 : wc);
+      const int64_t pw = (G + wv - 1) / wv;
+      int64_t kc = (pw + 3) / 4;
+      const int64_t fill = (QG_SKINNY_MIN_STRIPS + strips - 1) / strips;
+      if (kc < fill) kc = fill;
+      if (kc > SK_MAX_SPLIT || kc > G || strips * 4 > kTicketBytes) continue;
+      p.cpl = c;
+      p.nstrips = (int)strips;
+      p.waves = (int)wv;
+      ks = kc;
+      break;
+    }
+  }
+  const int sw2 = 16 * p.cpl;
   int64_t gwg = (G + ks - 1) / ks;
   ks = G > 0 ? (G + gwg - 1) / gwg : 1;
   int64_t need = ks > 1 ? split_workspace_bytes(p.nstrips, ks, m, p.cpl) : 0;
@@ -926,7 +951,7 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes,
   const int64_t items = (int64_t)p.nstrips * p.ksplit;
   p.items_per_xcd = (int)((items + 7) / 8);
   p.blocks = (int64_t)p.items_per_xcd * 8;
-  p.lds = (size_t)p.waves * m * sw * 4;   // the wave partial plane
+  p.lds = (size_t)p.waves * m * sw2 * 4;   // the wave partial plane
   (void)dot;
   return p;
 }
