@@ -889,7 +889,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
 #define QG_SKINNY_MAX_GPW 6        // groups per wave above which k is split
 #endif
 #ifndef QG_SKINNY_WIDE_M
-#define QG_SKINNY_WIDE_M 8         // tokens from which wide strips pay for a k split
+#define QG_SKINNY_WIDE_M 1         // tokens from which wide strips pay for a k split
 #endif
 
 int64_t split_workspace_bytes(int64_t nstrips, int64_t ksplit, int64_t m, int cpl) {
@@ -915,11 +915,13 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes,
     ks = (per_wave + 3) / 4;
     if (ks > SK_MAX_SPLIT) ks = SK_MAX_SPLIT;
   }
-  // Several tokens: every workgroup reads X over its k range, so the X traffic
-  // is (strips) x m x k x 2 bytes, 4m / (16 CPL) times the codes' traffic.
   // When k is long enough to be split anyway, take the widest strip whose
-  // count, times a split of at most SK_MAX_SPLIT, still fills the CUs.
-  if (!dot && m >= QG_SKINNY_WIDE_M && ks > 1 && p.cpl < 4) {
+  // count, times a split of at most SK_MAX_SPLIT, still fills the CUs: every
+  // workgroup reads X over its k range (X traffic = strips x m x k x 2 bytes,
+  // 4m / (16 CPL) times the codes' traffic) and wider strips load more code
+  // bytes per instruction.  Measured at k = 25600, n = 5120: m = 1 40 -> 29 µs,
+  // m = 2 39 -> 27 µs, m = 16 57 -> 35 µs.
+  if ((dot || m >= QG_SKINNY_WIDE_M) && ks > 1 && p.cpl < 4) {
     for (int c = 4; c > p.cpl; c /= 2) {
       const int64_t strips = (n + 16 * c - 1) / (16 * c);
       const int64_t wc = strips >= 384 ? (QG_SKINNY_WAVES < 8 ? QG_SKINNY_WAVES : 8) : QG_SKINNY_WAVES;
