@@ -65,6 +65,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="wall time budget of the CPU oracle sample (0 disables)")
     p.add_argument("--suite", default=None, help="also time all workload shapes into this JSON file")
+    p.add_argument("--suite-kinds", default="int4,int4_nozero,dense,int4_lora,dense_fp32,attention",
+                   help="comma-separated row kinds the suite times")
     return p.parse_args()
 
 
@@ -208,17 +210,21 @@ def same_size_reference(torch, nbytes, regime, iters):
 
 
 def cpu_baseline(cases, seconds):
-    """The CPU oracle, as it stands, on the same inputs until `seconds` have passed."""
-    import oracle
-    from threadpoolctl import threadpool_info
+    """The C++ CPU oracle, as it stands, on the same inputs until `seconds` have passed.
 
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    It runs on std::threads over output columns; the thread count is the
+    host's CPU share (OMP_NUM_THREADS when set, else the hardware threads, at
+    most 16).
+    """
+    from oracle import cpu
+
+    threads = cpu.default_threads()
     t0 = time.perf_counter()
     done_bytes, calls = 0, 0
     while True:
         for c in cases:
             d = c.host
-            oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], c.m, c.k, c.n)
+            cpu.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], c.m, c.k, c.n, threads=threads)
             done_bytes += c.bytes
             calls += 1
         if time.perf_counter() - t0 >= seconds:
@@ -226,8 +232,9 @@ def cpu_baseline(cases, seconds):
     el = time.perf_counter() - t0
     return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": "%d oracle calls cycling over the six small-M products (%.1f s, numpy with "
-                      "a %d-thread BLAS)" % (calls, el, threads)}
+            "sample": "%d calls of the C++ oracle (dequantise to fp32, accumulate in fp64, %d std::threads "
+                      "over output columns) cycling over the six small-M products, %.1f s"
+                      % (calls, threads, el)}
 
 
 def main():
@@ -338,7 +345,8 @@ def run_suite(qg, torch, args, path):
 
     rows = []
     iters = max(10, args.steps // 4)
-    for cfg in (0, 1, 2, 4):
+    kinds = set(args.suite_kinds.split(","))
+    for cfg in ((0, 1, 2, 4) if "int4" in kinds else ()):
         for (_, m, k, n, seed) in int4_cases(cfg):
             c = Int4Case(qg, torch, m, k, n, seed, copies_for(int4_bytes(0, k, n), args.regime))
             for _ in range(3):
@@ -351,7 +359,7 @@ def run_suite(qg, torch, args, path):
             del c
             torch.cuda.empty_cache()
     # weights without a zero point (qzeros NULL) on the small-M and prefill shapes
-    for cfg in (1, 2):
+    for cfg in ((1, 2) if "int4_nozero" in kinds else ()):
         for (_, m, k, n, seed) in int4_cases(cfg):
             c = Int4Case(qg, torch, m, k, n, seed, copies_for(int4_bytes(0, k, n, False), args.regime),
                          zeros=False)
@@ -364,7 +372,7 @@ def run_suite(qg, torch, args, path):
             print("suite int4_nozero", rows[-1], file=sys.stderr, flush=True)
             del c
             torch.cuda.empty_cache()
-    for case in dense_cases(3):
+    for case in (dense_cases(3) if "dense" in kinds else ()):
         d = dense_inputs(case["layout"], case["dtype"], case["M"], case["N"], case["K"], case["seed"])
         dt = torch.bfloat16 if case["dtype"] == "bf16" else torch.float16
         a = torch.from_numpy(d["a"].view(np.int16)).cuda().view(dt)
@@ -378,7 +386,7 @@ def run_suite(qg, torch, args, path):
                      "mfma_frac": 2 * M * N * K / us / 1e6 / MFMA_BF16_PEAK_TFLOPS})
         print("suite dense", rows[-1], file=sys.stderr, flush=True)
     # a rank-16 LoRA add in the epilogue (U = X A^T launched first) on the same shapes
-    for cfg in (1, 2):
+    for cfg in ((1, 2) if "int4_lora" in kinds else ()):
         for (_, m, k, n, seed) in int4_cases(cfg):
             c = Int4Case(qg, torch, m, k, n, seed, copies_for(int4_bytes(0, k, n), args.regime))
             g = torch.Generator(device="cuda")
@@ -402,7 +410,7 @@ def run_suite(qg, torch, args, path):
             del c, la, lb
             torch.cuda.empty_cache()
     # the FP32 training trio (fp32 products and accumulation) against the fp32 peak
-    for case in dense_cases(3, with_lora=False):
+    for case in (dense_cases(3, with_lora=False) if "dense_fp32" in kinds else ()):
         if case["dtype"] != "bf16":
             continue
         M, N, K, layout = case["M"], case["N"], case["K"], case["layout"]
@@ -423,7 +431,7 @@ def run_suite(qg, torch, args, path):
     # batched attention products; operands drawn on the device from a seeded
     # generator (timing only: the parity tests use the host generator)
     from qgemm_inputs import attention_cases
-    for case in attention_cases():
+    for case in (attention_cases() if "attention" in kinds else ()):
         dt = torch.bfloat16 if case["dtype"] == "bf16" else torch.float16
         bt, M, N, K, layout = case["batch"], case["M"], case["N"], case["K"], case["layout"]
         sa = (bt, M, K) if layout != "TN" else (bt, K, M)

@@ -52,7 +52,7 @@ def test_shapes_match_oracle(gpu_lib, layout, dtype):
         d = dense_inputs(layout, dtype, M, N, K, seed=500 + i)
         a, b = dev(d["a"], tdtype(dtype)), dev(d["b"], tdtype(dtype))
         c = host_u16(run(gpu_lib, layout, a, b))
-        ref = oracle.dense(layout, dtype, d["a"], d["b"], M, N, K)
+        ref = cpp_oracle.dense(layout, dtype, d["a"], d["b"], M, N, K)
         assert_accepted(c, ref, dtype, (layout, dtype, M, N, K))
 
 
