@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
+from oracle import cpu as cpp_oracle
 from qgemm_inputs import dense_cases, dense_inputs, f32_to_bf16_bits, f64_to_fp16_bits
 
 from gpu_helpers import dev, host_u16, sample_indices, say
