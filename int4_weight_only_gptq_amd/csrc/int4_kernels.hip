@@ -891,6 +891,12 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
 #ifndef QG_SKINNY_WIDE_M
 #define QG_SKINNY_WIDE_M 1         // tokens from which wide strips pay for a k split
 #endif
+#ifndef QG_SKINNY_GPW_MIN
+#define QG_SKINNY_GPW_MIN 1        // groups per wave the wave count aims at (at least)
+#endif
+#ifndef QG_SKINNY_LONG_G
+#define QG_SKINNY_LONG_G 48        // groups from which MFMA strips (m >= 8) use 8-wave workgroups
+#endif
 
 int64_t split_workspace_bytes(int64_t nstrips, int64_t ksplit, int64_t m, int cpl) {
   return kTicketBytes + nstrips * ksplit * m * 16 * cpl * 4;
@@ -905,9 +911,17 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes,
   else if ((n + 31) / 32 >= QG_SKINNY_MIN_STRIPS) p.cpl = 2;
   const int sw = 16 * p.cpl;
   p.nstrips = (int)((n + sw - 1) / sw);
-  // many strips: 8-wave workgroups so that two fit on a CU; few: 16 waves
-  const int64_t wcap = p.nstrips >= 384 ? (QG_SKINNY_WAVES < 8 ? QG_SKINNY_WAVES : 8) : QG_SKINNY_WAVES;
-  p.waves = (int)(G < 2 ? 1 : (G / 2 < wcap ? G / 2 : wcap));
+  // many strips: 8-wave workgroups so that two fit on a CU; few: 16 waves.
+  // One group per wave: every wave's loads go out at once (a wave waits for
+  // all of its loads in flight at each group, so a chain of groups costs a
+  // memory latency per link).  Long k with m >= 8: 8 waves (longer chains,
+  // and a k split chosen for them) measured faster than 16: 25600 x 5120
+  // m = 16 33.3 -> 28.7 µs, 8192 x 8192 m = 8 / 16 14.2 / 17.0 -> 13.5 / 15.2 µs;
+  // at 4096 x 4096 and for the GEMV they were slower.
+  const bool long_k = !dot && m >= 8 && G >= QG_SKINNY_LONG_G;
+  const int64_t wcap = (p.nstrips >= 384 || long_k) ? (QG_SKINNY_WAVES < 8 ? QG_SKINNY_WAVES : 8)
+                                                     : QG_SKINNY_WAVES;
+  p.waves = (int)(G < QG_SKINNY_GPW_MIN ? 1 : (G / QG_SKINNY_GPW_MIN < wcap ? G / QG_SKINNY_GPW_MIN : wcap));
   // k split only when each wave would otherwise walk a long chain of groups
   int64_t ks = 1;
   const int64_t per_wave = (G + p.waves - 1) / p.waves;
@@ -924,8 +938,9 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes,
   if ((dot || m >= QG_SKINNY_WIDE_M) && ks > 1 && p.cpl < 4) {
     for (int c = 4; c > p.cpl; c /= 2) {
       const int64_t strips = (n + 16 * c - 1) / (16 * c);
-      const int64_t wc = strips >= 384 ? (QG_SKINNY_WAVES < 8 ? QG_SKINNY_WAVES : 8) : QG_SKINNY_WAVES;
-      const int64_t wv = G < 2 ? 1 : (G / 2 < wc ? G / 2 : wc);
+      const int64_t wc = (strips >= 384 || long_k) ? (QG_SKINNY_WAVES < 8 ? QG_SKINNY_WAVES : 8)
+                                                   : QG_SKINNY_WAVES;
+      const int64_t wv = G < QG_SKINNY_GPW_MIN ? 1 : (G / QG_SKINNY_GPW_MIN < wc ? G / QG_SKINNY_GPW_MIN : wc);
       const int64_t pw = (G + wv - 1) / wv;
       int64_t kc = (pw + 3) / 4;
       const int64_t fill = (QG_SKINNY_MIN_STRIPS + strips - 1) / strips;
@@ -938,6 +953,14 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes,
       break;
     }
   }
+#ifdef QG_SKINNY_FORCE_CPL   // launch-shape sweeps: strip width, k split and waves fixed from m on
+  if (m >= QG_SKINNY_FORCE_MINM) {
+    p.cpl = QG_SKINNY_FORCE_CPL;
+    p.nstrips = (int)((n + 16 * p.cpl - 1) / (16 * p.cpl));
+    ks = QG_SKINNY_FORCE_KS < G ? QG_SKINNY_FORCE_KS : (G > 0 ? G : 1);
+    p.waves = QG_SKINNY_FORCE_WAVES;
+  }
+#endif
   const int sw2 = 16 * p.cpl;
   int64_t gwg = (G + ks - 1) / ks;
   ks = G > 0 ? (G + gwg - 1) / gwg : 1;

@@ -183,10 +183,13 @@ def test_describe_names_the_dispatch(lib):
     # 4096 columns: 256 strips of 16, 16 waves splitting 32 groups, no k split
     assert qg.describe_int4(1, 4096, 4096) == (
         "skinny_int4_kernel<1,dot,1> grid=256 block=1024 lds=%d ksplit=1 groups=32" % (16 * 64))
-    assert qg.describe_int4(8, 8192, 2048).startswith("skinny_int4_kernel<8,mfma,2> grid=256 block=512")
+    # 8192 columns: 256 strips of 32, one wave per group (16 groups)
+    assert qg.describe_int4(8, 8192, 2048).startswith("skinny_int4_kernel<8,mfma,2> grid=256 block=1024")
     assert qg.describe_int4(16, 28672, 4096).startswith("skinny_int4_kernel<16,mfma,4> grid=448 block=512")
-    # a long k with few strips is split: 200 groups over 16 waves -> 4 slices of 50
-    assert "ksplit=4 groups=50" in qg.describe_int4(16, 5120, 25600)
+    # a long k with few strips is split: m >= 8 and 200 groups take 8-wave workgroups,
+    # 25 groups per wave -> 7 slices of 29 over 80 strips of 64 columns
+    assert qg.describe_int4(16, 5120, 25600).startswith("skinny_int4_kernel<16,mfma,4> grid=560 block=512")
+    assert "ksplit=7 groups=29" in qg.describe_int4(16, 5120, 25600)
     assert "ksplit=1 groups=200" in qg.describe_int4(16, 5120, 25600, workspace_bytes=0)
     # pipelined MFMA kernel: 64-token tiles for small m, 256 x 128 once there are enough of them
     # (lds = 4 stages x (activations + words + metadata) dwords x 4 bytes)
@@ -213,8 +216,8 @@ def test_describe_names_the_dispatch(lib):
 
 
 def test_workspace_size(lib):
-    # 64 KiB of counters, then 320 strips x 4 slices x 16 tokens x 16 columns x 4 bytes
-    assert qg.workspace_size(16, 5120, 25600) == 65536 + 320 * 4 * 16 * 16 * 4
+    # 64 KiB of counters, then 80 strips x 7 slices x 16 tokens x 64 columns x 4 bytes
+    assert qg.workspace_size(16, 5120, 25600) == 65536 + 80 * 7 * 16 * 64 * 4
     assert qg.workspace_size(8, 4096, 4096) == 0           # no split needed
     # MFMA tiles: 64 KiB of counters, prepared activations, group sums, then the k split's
     # partial tiles (tiles x slices x BM x 128 fp32)
