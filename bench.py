@@ -209,6 +209,37 @@ def same_size_reference(torch, nbytes, regime, iters):
             "kernels": "torch.sum (reads the bytes), Tensor.copy_ (reads and writes them)"}
 
 
+def mfma_probe(qg, torch, blocks=1024, iters=4000):
+    """Sustained bf16 MFMA rate of a register-only loop and the shader clock under it.
+
+    1024 workgroups of 4 waves (4 per CU: one per SIMD) each run 8 independent
+    16x16x32 bf16 MFMA chains; the clock is the median over workgroups of 100 MHz x
+    shader cycles / constant-counter ticks between the loop's start and end.
+    """
+    flops = blocks * 4 * iters * 8 * 16384
+    clocks = qg.probe_mfma_bf16(blocks, iters)          # warm-up launch
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(5):
+        e0.record(stream)
+        qg.probe_mfma_bf16(blocks, iters, clocks=clocks)
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    c = clocks.cpu().numpy().astype("float64")
+    import numpy as np
+
+    ticks = c[:, 3] - c[:, 1]
+    mhz = float(np.median(100.0 * (c[:, 2] - c[:, 0]) / np.where(ticks > 0, ticks, np.nan)))
+    tflops = flops / (best * 1e-3) / 1e12
+    return {"tflops": round(tflops, 1), "frac_of_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "sclk_mhz": round(mhz, 1), "ms": round(best, 4), "blocks": blocks, "iters": iters,
+            "kernel": "mfma_probe_kernel (register-only 16x16x32 bf16 MFMA chains)"}
+
+
 def cpu_baseline(cases, seconds):
     """The C++ CPU oracle, as it stands, on the same inputs until `seconds` have passed.
 
@@ -328,6 +359,9 @@ def main():
     out["same_size_reference"] = same
     roofline["time_vs_same_size_copy"] = round(avg_us / same["copy_us"], 3)
     roofline["time_vs_same_size_read"] = round(avg_us / same["read_us"], 3)
+    # the MFMA-bound denominators beside the datasheet peak: a register-only
+    # bf16 MFMA loop and the shader clock it runs at
+    out["mfma_probe"] = mfma_probe(qg, torch)
     if args.suite:
         out["suite_file"] = args.suite
         run_suite(qg, torch, args, args.suite)
@@ -449,8 +483,12 @@ def run_suite(qg, torch, args, path):
         print("suite attention", rows[-1], file=sys.stderr, flush=True)
         del a, b, out
         torch.cuda.empty_cache()
+    probe = mfma_probe(qg, torch)
+    for r in rows:
+        if "tflops" in r and r.get("kind") != "dense_fp32":
+            r["frac_of_mfma_probe"] = r["tflops"] / probe["tflops"]
     with open(path, "w") as f:
-        json.dump({"regime": args.regime, "rows": rows}, f, indent=1)
+        json.dump({"regime": args.regime, "mfma_probe": probe, "rows": rows}, f, indent=1)
 
 
 if __name__ == "__main__":

@@ -232,6 +232,26 @@ int32_t gemm_dense_batched(int32_t layout, int32_t dtype, int64_t batch, int64_t
                            const void* A, int64_t lda, int64_t stride_a, const void* B, int64_t ldb,
                            int64_t stride_b, void* C, int64_t ldc, int64_t stride_c, void* stream);
 
+/*
+ * Measurement probe (not a product): the sustained bf16 MFMA rate and the
+ * shader clock under that load, the two denominators the BC-250 tuned-GEMM
+ * post ("Checking the hardware first") establishes before tuning -- a
+ * register-only matrix loop, and a cycle counter compared with a
+ * constant-rate counter.
+ *
+ * Launches `blocks` workgroups of 4 waves; every wave runs `iters` rounds of 8
+ * independent 16x16x32 bf16 MFMAs on register operands, i.e.
+ *   flops = blocks * 4 * iters * 8 * 16384.
+ * clocks: device buffer of blocks * 4 uint64_t (8-byte aligned), written as
+ * {shader cycles at start, constant counter at start, shader cycles at end,
+ * constant counter at end} per workgroup (s_memtime / s_memrealtime; the
+ * constant counter runs at 100 MHz on this GPU family, so the clock in MHz is
+ * 100 * cycles / constant ticks).
+ * 1 <= blocks <= 65536, iters >= 1; errors: QG_ERR_NULL, QG_ERR_SHAPE,
+ * QG_ERR_ALIGN, QG_ERR_HIP.
+ */
+int32_t qg_probe_mfma_bf16(int64_t blocks, int32_t iters, uint64_t* clocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

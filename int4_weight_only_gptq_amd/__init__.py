@@ -76,6 +76,8 @@ def load():
     lib.gemm_dense_batched.restype = i32
     lib.gemm_dense_batched.argtypes = [i32, i32, i64, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64,
                                        i64, vp]
+    lib.qg_probe_mfma_bf16.restype = i32
+    lib.qg_probe_mfma_bf16.argtypes = [i64, i32, vp, vp]
     _lib = lib
     return lib
 
@@ -287,3 +289,18 @@ def gemm_dense_batched(layout: str, a, b, out=None, stream=None):
                                 _stream(a, stream))
     _check(st, "gemm_dense_batched")
     return out
+
+
+def probe_mfma_bf16(blocks: int, iters: int, clocks=None, stream=None):
+    """Launch the register-resident bf16 MFMA probe (4 waves per workgroup, 8
+    independent 16x16x32 MFMAs per wave per iteration: blocks * 4 * iters * 8 *
+    16384 flops).  Returns the int64 [blocks][4] device tensor of clock stamps
+    {shader cycles, constant counter} at start and end per workgroup."""
+    import torch
+
+    lib = load()
+    if clocks is None:
+        clocks = torch.zeros((blocks, 4), dtype=torch.int64, device="cuda")
+    st = lib.qg_probe_mfma_bf16(blocks, iters, clocks.data_ptr(), _stream(clocks, stream))
+    _check(st, "qg_probe_mfma_bf16")
+    return clocks

@@ -19,7 +19,11 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqgemm_gfx950.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "int4_kernels.hip", "dense_kernels.hip"]
+SOURCES = ["api.cpp", "int4_kernels.hip", "dense_kernels.hip", "probes.hip"]
+# per-source flags: the MFMA probe keeps its accumulator chains in VGPRs (with
+# AGPR accumulators this compiler shuffled them between iterations); the
+# product kernels keep the default form, whose k loops carry no such moves
+EXTRA = {"probes.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -41,7 +45,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd = [HIPCC, "-x", "hip"] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
         err = _run(cmd)

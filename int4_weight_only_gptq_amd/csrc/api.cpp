@@ -232,4 +232,11 @@ int32_t gemm_dense_batched(int32_t layout, int32_t dtype, int64_t batch, int64_t
                    stream);
 }
 
+int32_t qg_probe_mfma_bf16(int64_t blocks, int32_t iters, uint64_t* clocks, void* stream) {
+  if (!clocks) return QG_ERR_NULL;
+  if (blocks < 1 || blocks > 65536 || iters < 1) return QG_ERR_SHAPE;
+  if (((uintptr_t)clocks & 7u) != 0) return QG_ERR_ALIGN;
+  return hip_status(qg::launch_mfma_probe(blocks, iters, clocks, (hipStream_t)stream));
+}
+
 }  // extern "C"

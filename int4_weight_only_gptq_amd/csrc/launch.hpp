@@ -84,4 +84,7 @@ struct BatchStrides {
 
 hipError_t launch_dense(const DenseArgs& a, hipStream_t stream);
 
+// register-resident bf16 MFMA loop with clock stamps (measurement probe)
+hipError_t launch_mfma_probe(int64_t blocks, int iters, uint64_t* clocks, hipStream_t stream);
+
 }  // namespace qg

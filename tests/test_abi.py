@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "qg_abi_version", "qg_status_str", "qg_last_hip_error", "qgemm_int4", "qgemm_int4_path",
         "qgemm_int4_workspace_size", "qgemm_int4_describe", "qgemm_int4_dequant", "gemm_dense",
-        "gemm_dense_batched", "qgemm_int4_lora", "qgemm_int4_lora_workspace_size"])
+        "gemm_dense_batched", "qgemm_int4_lora", "qgemm_int4_lora_workspace_size", "qg_probe_mfma_bf16"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -124,6 +124,15 @@ def test_int4_empty_problems_are_noops(lib):
     # m == 0 or n == 0: nothing is launched, NULL pointers allowed
     assert int4(lib, m=0, x=0, qw=0, sc=0, qz=0, y=0) == OK
     assert int4(lib, n=0, x=0, qw=0, sc=0, qz=0, y=0) == OK
+
+
+def test_probe_rejects_invalid_arguments(lib):
+    buf = ctypes.c_void_p(0x100000)
+    assert lib.qg_probe_mfma_bf16(4, 10, None, None) == 1                     # NULL clocks
+    assert lib.qg_probe_mfma_bf16(0, 10, buf, None) == 2                      # no workgroups
+    assert lib.qg_probe_mfma_bf16(65537, 10, buf, None) == 2                  # too many
+    assert lib.qg_probe_mfma_bf16(4, 0, buf, None) == 2                       # no iterations
+    assert lib.qg_probe_mfma_bf16(4, 10, ctypes.c_void_p(0x100004), None) == 3  # misaligned
 
 
 def test_dequant_rejects_invalid_arguments(lib):
