@@ -106,14 +106,20 @@ def copies_for(bytes_per_copy, regime):
     return max(2, -(-2 * LLC_BYTES // bytes_per_copy))
 
 
-def time_us(torch, fn, iters, graph=True):
-    """Average microseconds per call of fn() over iters back-to-back calls.
+def time_us(torch, fn, iters, graph=True, reps=7):
+    """Microseconds per call of fn() over iters back-to-back calls: the median of
+    `reps` timed repetitions.
 
     With graph=True the iters calls are captured once into a HIP graph on the
-    launch stream and the timed region is one replay of it, so host launch cost
-    (Python, ctypes) is not on the clock; HIP events bracket the replay on the
+    launch stream and each repetition is one replay of it, so host launch cost
+    (Python, ctypes) is not on the clock; HIP events bracket each replay on the
     same stream.  graph=False times eager launches from Python.
     """
+    import statistics
+
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
     if graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -121,22 +127,22 @@ def time_us(torch, fn, iters, graph=True):
                 fn()
         g.replay()                       # warm replay
         torch.cuda.synchronize()
-        s = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(reps):
+            e0.record(s)
+            g.replay()
+            e1.record(s)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3 / iters)
+        del g
+        return statistics.median(times)
+    for _ in range(reps):
         e0.record(s)
-        g.replay()
+        for _ in range(iters):
+            fn()
         e1.record(s)
         e1.synchronize()
-        del g
-        return e0.elapsed_time(e1) * 1e3 / iters
-    s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    for _ in range(iters):
-        fn()
-    e1.record(s)
-    e1.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / iters
+        times.append(e0.elapsed_time(e1) * 1e3 / iters)
+    return statistics.median(times)
 
 
 def kernel_source_sha256():
@@ -316,7 +322,8 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    step_us = time_us(torch, step, args.steps)
+    # the step: exactly K steps in one timed region (one graph replay between events)
+    step_us = time_us(torch, step, args.steps, reps=1)
     step_bytes = sum(c.bytes for c in cases)
     value = step_bytes / step_us / 1e3
 
@@ -347,7 +354,8 @@ def main():
                    "regime": args.regime, "calls_per_step": len(cases),
                    "parallelism": "none (1 GPU)"},
         "cases": per_case,
-        "timing": "HIP graph replay of back-to-back launches, HIP events on the launch stream",
+        "timing": "HIP graph replay of back-to-back launches, HIP events on the launch stream; the step: one "
+                  "replay of exactly K steps; per-case, floor and suite figures: median of 7 replays",
         "floor_us": round(floor_us, 3),
         "copy_gbps": round(copy_gbps, 1),
         "roofline": roofline,
