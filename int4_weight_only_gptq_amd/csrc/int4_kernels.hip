@@ -520,6 +520,10 @@ __global__ __launch_bounds__(1024) void skinny_int4_kernel(
 // fragments gives the per-token group sums in the accumulator layout.  After
 // both stages of a group: total += s * (acc - (128 + z) * sum_x), fp32.
 // ---------------------------------------------------------------------------
+#ifndef QG_PIPE_INTERLEAVE
+#define QG_PIPE_INTERLEAVE 1   // interleave the second k step's decode with the first step's MFMAs
+#endif
+
 template <int NWM, int NWN, int FM, bool PREP>
 struct PipeShape {
   static constexpr int T = 64 * NWM * NWN;               // threads
@@ -726,6 +730,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int kt = 2 * g + h;
+      u32x4 bn[4];   // the second k step's decoded words, decoded under the first step's MFMAs
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         // reorder / decode this step's fragments (their LDS reads were issued
@@ -735,7 +740,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int f = 0; f < FM; ++f) ap[f] = PREP ? fa[f] : x_pairs_permuted(fa[f]);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) b[c] = codes_as_bf16_pairs(fw[c]);
+        for (int c = 0; c < 4; ++c) b[c] = s == 0 ? codes_as_bf16_pairs(fw[c]) : bn[c];
         if (s == 0) read_step(kt, 1);
         const bool first = h == 0 && s == 0;   // first k step of the group
         // the ones-MFMA sums the reordered activations; a sum's order does not matter
@@ -744,6 +749,26 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
           if constexpr (!PREP) xs[f] = mfma16_bf16(ap[f], ones, first ? zero : xs[f]);
 #pragma unroll
           for (int c = 0; c < 4; ++c) acc[f][c] = mfma16_bf16(ap[f], b[c], first ? zero : acc[f][c]);
+        }
+        if (s == 0) {
+          // the second step's words (fw now holds them once the reads above
+          // land) are decoded while the first step's MFMAs run: the matrix
+          // core and the vector ALU then work side by side.  Scheduling
+          // order of this step: its own decode, the next step's LDS reads,
+          // four MFMAs (covering the read latency), then one MFMA per three
+          // decode instructions.
+#pragma unroll
+          for (int c = 0; c < 4; ++c) bn[c] = codes_as_bf16_pairs(fw[c]);
+          if constexpr (PREP && QG_PIPE_INTERLEAVE) {
+            __builtin_amdgcn_sched_group_barrier(0x002, 28, 0);   // VALU: this step's decode
+            __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);    // DS reads of the next step
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);    // MFMA
+#pragma unroll
+            for (int i = 0; i < 12; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+              __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU: next step's decode
+            }
+          }
         }
       }
       // the group's scales, zeros (and prepared group sums), read while stage
@@ -826,23 +851,34 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
     __syncthreads();
     if (!last_slice) return;
     const uint64_t* base = reinterpret_cast<const uint64_t*>(partials) + (int64_t)t * ksplit * (BM * BN / 2);
+    // slice by slice: the 8 FM pairs of a slice are loaded together (one round
+    // trip per slice, not per element), then added; each element still sums
+    // the slices in slice order
 #pragma unroll
     for (int f = 0; f < FM; ++f)
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+      for (int c = 0; c < 4; ++c) total[f][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < ksplit; ++p) {
+      const uint64_t* sl = base + (int64_t)p * (BM * BN / 2);
+      uint64_t pr[FM][4][2];
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int o = ((f * 4 + v) * 2 + h2) * T + tid;
-          float s0 = 0.f, s1 = 0.f;
-          for (int p = 0; p < ksplit; ++p) {
-            const uint64_t pair = __hip_atomic_load(&base[(int64_t)p * (BM * BN / 2) + o], __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-            s0 += __builtin_bit_cast(float, (uint32_t)pair);
-            s1 += __builtin_bit_cast(float, (uint32_t)(pair >> 32));
+      for (int f = 0; f < FM; ++f)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2)
+            pr[f][v][h2] = __hip_atomic_load(&sl[((f * 4 + v) * 2 + h2) * T + tid], __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int f = 0; f < FM; ++f)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            total[f][2 * h2][v] += __builtin_bit_cast(float, (uint32_t)pr[f][v][h2]);
+            total[f][2 * h2 + 1][v] += __builtin_bit_cast(float, (uint32_t)(pr[f][v][h2] >> 32));
           }
-          total[f][2 * h2][v] = s0;
-          total[f][2 * h2 + 1][v] = s1;
-        }
+    }
     if (tid == 0) __hip_atomic_store(&tickets[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
@@ -1159,12 +1195,19 @@ static MfmaPlan plan_mfma(int64_t m, int64_t n, int64_t k, int64_t ws_bytes) {
   return best;
 }
 
+#ifndef QG_PIPE_S128
+#define QG_PIPE_S128 4     // LDS stages of the 128 x 128 tile
+#endif
+#ifndef QG_PIPE_S64
+#define QG_PIPE_S64 4      // LDS stages of the 64 x 128 tile
+#endif
+
 template <bool PREP>
 static PipeCfg pipe_cfg_of(int which) {
   switch (which) {
     case 2: return pipe_cfg<4, 2, 4, 4, PREP>();
-    case 1: return pipe_cfg<2, 2, 4, 4, PREP>();
-    default: return pipe_cfg<1, 2, 4, 4, PREP>();
+    case 1: return pipe_cfg<2, 2, 4, QG_PIPE_S128, PREP>();
+    default: return pipe_cfg<1, 2, 4, QG_PIPE_S64, PREP>();
   }
 }
 
@@ -1185,8 +1228,8 @@ static void pipe_dispatch(const Int4Args& a, const MfmaPlan& p, const uint16_t* 
                           const float* xsum, float* partials, uint32_t* tickets, hipStream_t stream) {
   switch (p.cfg) {
     case 2: pipe_launch<4, 2, 4, 4, PREP>(a, p, x, ldx, xsum, partials, tickets, stream); break;
-    case 1: pipe_launch<2, 2, 4, 4, PREP>(a, p, x, ldx, xsum, partials, tickets, stream); break;
-    default: pipe_launch<1, 2, 4, 4, PREP>(a, p, x, ldx, xsum, partials, tickets, stream); break;
+    case 1: pipe_launch<2, 2, 4, QG_PIPE_S128, PREP>(a, p, x, ldx, xsum, partials, tickets, stream); break;
+    default: pipe_launch<1, 2, 4, QG_PIPE_S64, PREP>(a, p, x, ldx, xsum, partials, tickets, stream); break;
   }
 }
 
