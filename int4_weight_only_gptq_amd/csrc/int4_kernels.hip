@@ -1048,6 +1048,19 @@ hipError_t launch_gemv_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipSt
 }
 
 hipError_t launch_fused_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream) {
+  if (a.m > 16) {
+    // 16-row passes, in order on the stream (they share the workspace): the
+    // first 16 tokens, then the rest (the LoRA intermediate U moves with them)
+    Int4Args lo = a, hi = a;
+    lo.m = 16;
+    hi.m = a.m - 16;
+    hi.x = a.x + 16 * a.ldx;
+    hi.y = a.y + 16 * a.ldy;
+    if (a.lora.u) hi.lora.u = a.lora.u + 16 * 16;
+    const hipError_t e = launch_fused_int4(lo, ws, ws_bytes, stream);
+    if (e != hipSuccess) return e;
+    return launch_fused_int4(hi, ws, ws_bytes, stream);
+  }
   const SkinnyPlan p = plan_skinny(a.m, a.n, a.k, ws ? ws_bytes : 0, false);
   switch (a.m) {
     case 1: skinny_launch_c<1, false>(a, p, ws, stream); break;
@@ -1128,7 +1141,7 @@ static PipeCfg pipe_cfg() {
 #define QG_PIPE_T64 0.85
 #endif
 #ifndef QG_PIPE_MIN_GPS
-#define QG_PIPE_MIN_GPS 8
+#define QG_PIPE_MIN_GPS 4
 #endif
 // Costs in rounds of a full-k 256 x 128 tile (≈ 0.0192 us per k row on this
 // chip): a slice pays QG_PIPE_FILL stages of pipeline fill and drain, and a
@@ -1253,17 +1266,18 @@ hipError_t launch_mfma_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipSt
 int64_t workspace_int4(int64_t m, int64_t n, int64_t k, int path) {
   if (m == 0 || n == 0 || k == 0) return 0;
   if (path == 3) return plan_mfma(m, n, k, INT64_MAX).ws_bytes;
-  return plan_skinny(m, n, k, INT64_MAX, path == 1).ws_bytes;
+  return plan_skinny(m < 16 ? m : 16, n, k, INT64_MAX, path == 1).ws_bytes;   // 16-row passes above 16
 }
 
 void describe_int4(int64_t m, int64_t n, int64_t k, int path, int64_t ws_bytes, char* buf,
                    size_t len) {
   if (path == 1 || path == 2) {
-    const SkinnyPlan p = plan_skinny(path == 1 ? 1 : m, n, k, ws_bytes, path == 1);
+    const int64_t mp = path == 1 ? 1 : (m < 16 ? m : 16);   // above 16: the first 16-row pass
+    const SkinnyPlan p = plan_skinny(mp, n, k, ws_bytes, path == 1);
     const bool dot = path == 1;
-    snprintf(buf, len, "skinny_int4_kernel<%lld,%s,%d> grid=%lld block=%d lds=%lld ksplit=%d groups=%d",
-             path == 1 ? 1LL : (long long)m, dot ? "dot" : "mfma", p.cpl, (long long)p.blocks,
-             64 * p.waves, (long long)p.lds, p.ksplit, p.gwg);
+    snprintf(buf, len, "skinny_int4_kernel<%lld,%s,%d> grid=%lld block=%d lds=%lld ksplit=%d groups=%d%s",
+             (long long)mp, dot ? "dot" : "mfma", p.cpl, (long long)p.blocks, 64 * p.waves, (long long)p.lds,
+             p.ksplit, p.gwg, m > 16 && !dot ? " passes=2" : "");
   } else {
     const MfmaPlan p = plan_mfma(m, n, k, ws_bytes);
     const PipeCfg c = p.prep ? pipe_cfg_of<true>(p.cfg) : pipe_cfg_of<false>(p.cfg);

@@ -205,10 +205,10 @@ def test_describe_names_the_dispatch(lib):
     # pipelined MFMA kernel: tile and k split by rounds on 256 CUs (64 x 128 fits three to a
     # CU); with the workspace the activations are prepared and the group sums ride in the
     # metadata slots, without it a ones-MFMA per fragment and no split
-    assert qg.describe_int4(17, 5120, 25600) == (
+    assert qg.describe_int4(17, 5120, 25600, path="mfma") == (
         "int4_pipe_kernel<64,128,4,prep> grid=320 block=128 lds=%d ksplit=8 groups=25"
         % (4 * (2048 + 1024 + 256) * 4))
-    assert qg.describe_int4(17, 5120, 25600, workspace_bytes=0) == (
+    assert qg.describe_int4(17, 5120, 25600, path="mfma", workspace_bytes=0) == (
         "int4_pipe_kernel<128,128,4,ones> grid=40 block=256 lds=%d ksplit=1 groups=200"
         % (4 * (4096 + 1024 + 256) * 4))
     assert qg.describe_int4(2048, 25600, 5120) == (
@@ -217,7 +217,9 @@ def test_describe_names_the_dispatch(lib):
     assert qg.describe_int4(512, 5120, 25600).startswith("int4_pipe_kernel<256,128,4,prep> grid=240 block=512")
     assert qg.describe_int4(2048, 5120, 25600, workspace_bytes=0).startswith(
         "int4_pipe_kernel<64,128,4,ones> grid=1280 block=128 lds=%d ksplit=1" % (4 * (2048 + 1024 + 128) * 4))
-    assert qg.describe_int4(1, 4096, 4096, "mfma").startswith("int4_pipe_kernel<128,128,4,prep> grid=128 ")
+    # few tiles and a short k: 32 tiles of 64 x 128, k split into 8 slices of 4 groups
+    assert qg.describe_int4(1, 4096, 4096, "mfma") == (
+        "int4_pipe_kernel<64,128,4,prep> grid=256 block=128 lds=%d ksplit=8 groups=4" % (4 * (2048 + 1024 + 256) * 4))
     assert qg.describe_int4(0, 64, 128) == "none"
     assert qg.describe_int4(3, 64, 0) == "zero16_kernel"
     with pytest.raises(qg.QGemmError):
@@ -232,12 +234,19 @@ def test_workspace_size(lib):
     # partial tiles (tiles x slices x BM x 128 fp32)
     up = lambda b: (b + 255) // 256 * 256
     assert qg.workspace_size(2048, 25600, 5120) == up(65536 + 2048 * 5120 * 2 + 40 * 2048 * 4)  # no split
-    desc = qg.describe_int4(17, 4096, 4096)
+    desc = qg.describe_int4(17, 4096, 4096, path="mfma")
     bm = int(desc.split("<")[1].split(",")[0])
     ks = int(desc.split("ksplit=")[1].split()[0])
     tiles = ((17 + bm - 1) // bm) * (4096 // 128)
     assert ks > 1
-    assert qg.workspace_size(17, 4096, 4096) == up(65536 + 17 * 4096 * 2 + 32 * 17 * 4) + tiles * ks * bm * 128 * 4
+    assert qg.workspace_size(17, 4096, 4096, path="mfma") == (
+        up(65536 + 17 * 4096 * 2 + 32 * 17 * 4) + tiles * ks * bm * 128 * 4)
+    # auto path, 16 < m <= 32 and n < 20480: the small-M kernel in 16-row passes
+    assert qg.describe_int4(17, 4096, 4096).startswith("skinny_int4_kernel<16,mfma,1>")
+    assert qg.describe_int4(17, 4096, 4096).endswith("passes=2")
+    assert qg.workspace_size(24, 5120, 25600) == qg.workspace_size(16, 5120, 25600)
+    assert qg.describe_int4(33, 4096, 4096).startswith("int4_pipe_kernel")
+    assert qg.describe_int4(17, 25600, 5120).startswith("int4_pipe_kernel")
     assert lib.qgemm_int4_workspace_size(8, 60, 4096, 0) == -SHAPE
     assert lib.qgemm_int4_workspace_size(8, 64, 4096, 1) == -UNSUP
 
