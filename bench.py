@@ -267,8 +267,24 @@ def cpu_baseline(cases, seconds):
         if time.perf_counter() - t0 >= seconds:
             break
     el = time.perf_counter() - t0
+    # the same oracle on one thread, on the GEMV workload (m = 1, k = 896, n = 4864)
+    from qgemm_inputs import int4_inputs
+
+    g = int4_inputs(1, 896, 4864, seed=1000 * 65536)
+    t1, n1 = time.perf_counter(), 0
+    while time.perf_counter() - t1 < 1.0:
+        cpu.qgemm_int4(g["x"], g["qweight"], g["scales"], g["qzeros"], 1, 896, 4864, threads=1)
+        n1 += 1
+    el1 = time.perf_counter() - t1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "hardware_threads": cpu.hardware_threads(),
+            "single_thread_gemv_us": round(el1 / n1 * 1e6, 1),
             "sample": "%d calls of the C++ oracle (dequantise to fp32, accumulate in fp64, %d std::threads "
                       "over output columns) cycling over the six small-M products, %.1f s"
                       % (calls, threads, el)}
