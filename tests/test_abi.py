@@ -6,6 +6,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import int4_weight_only_gptq_amd as qg
@@ -257,3 +258,38 @@ def test_library_has_no_undefined_kernel_symbols(lib):
                          text=True, check=True).stdout
     bad = [ln for ln in out.splitlines() if "qg" in ln or "device_stub" in ln]
     assert not bad, bad
+
+
+def _parse_plan(desc):
+    kv = dict(p.split("=") for p in desc.split()[1:] if "=" in p)
+    return desc.split()[0], {k: int(v) for k, v in kv.items()}
+
+
+def test_planned_launches_fit_the_hardware():
+    # every plan the int4 dispatch can choose, over seeded random shapes and all paths:
+    # a grid of at least one workgroup, at most 1024 threads, LDS within the 160 KiB of
+    # a CU, k slices within the kernels' limits, and the workspace the plan was made
+    # for is the size the library asks for
+    rng = np.random.default_rng(20261203)
+    shapes = [(1, 8, 128), (16, 8, 128), (17, 8, 128), (32, 20472, 128), (17, 20480, 128), (33, 20480, 25600)]   # (m, n, k)
+    for _ in range(300):
+        m = int(rng.choice([1, 2, 5, 8, 15, 16, 17, 24, 31, 32, 33, 64, 100, 257, 512, 2048, 4097]))
+        n = 8 * int(rng.integers(1, 4096))
+        k = 128 * int(rng.integers(1, 256))
+        shapes.append((m, n, k))
+    for (m, n, k) in shapes:
+        for path in ("auto", "gemv", "fused", "mfma"):
+            if (path == "gemv" and m != 1) or (path == "fused" and m > 16):
+                continue
+            for ws in (None, 0):
+                desc = qg.describe_int4(m, n, k, path, workspace_bytes=ws)
+                name, p = _parse_plan(desc)
+                what = (m, n, k, path, ws, desc)
+                assert p["grid"] >= 1 and 64 <= p["block"] <= 1024 and p["block"] % 64 == 0, what
+                assert 0 < p["lds"] <= 160 * 1024, what
+                assert 1 <= p["ksplit"] <= 16 and p["groups"] >= 1, what
+                assert p["ksplit"] * p["groups"] >= k // 128 > (p["ksplit"] - 1) * p["groups"], what
+                if ws == 0:
+                    assert p["ksplit"] == 1, what           # no workspace: no k split
+                if name.startswith("skinny"):
+                    assert p["grid"] % 8 == 0, what          # whole XCD rounds
