@@ -276,6 +276,12 @@ def cpu_baseline(cases, seconds):
         cpu.qgemm_int4(g["x"], g["qweight"], g["scales"], g["qzeros"], 1, 896, 4864, threads=1)
         n1 += 1
     el1 = time.perf_counter() - t1
+    # one pass over the six small-M products on one thread
+    t2 = time.perf_counter()
+    for c in cases:
+        d = c.host
+        cpu.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], c.m, c.k, c.n, threads=1)
+    el2 = time.perf_counter() - t2
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -285,6 +291,7 @@ def cpu_baseline(cases, seconds):
     return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "cpu_model": model, "hardware_threads": cpu.hardware_threads(),
             "single_thread_gemv_us": round(el1 / n1 * 1e6, 1),
+            "single_thread_step_s": round(el2, 3),
             "sample": "%d calls of the C++ oracle (dequantise to fp32, accumulate in fp64, %d std::threads "
                       "over output columns) cycling over the six small-M products, %.1f s"
                       % (calls, threads, el)}
@@ -386,6 +393,14 @@ def main():
     # the MFMA-bound denominators beside the datasheet peak: a register-only
     # bf16 MFMA loop and the shader clock it runs at
     out["mfma_probe"] = mfma_probe(qg, torch)
+    # context only (another codec on another GPU, so no vs_baseline): the fused
+    # small-M kernel times the GPTQModel NF12 pull request reports on an R9700
+    # (gfx1201) for the same shapes, beside this path's per-call times
+    pages = {(1, 4096, 4096): 20.45, (8, 4096, 4096): 24.15, (1, 2048, 8192): 18.49, (8, 2048, 8192): 23.87}
+    out["pages_context"] = [
+        {"m": c["m"], "k": c["k"], "n": c["n"], "us": c["us"], "pages_us_r9700_nf12": pages[(c["m"], c["k"], c["n"])],
+         "ratio": round(pages[(c["m"], c["k"], c["n"])] / c["us"], 2)}
+        for c in per_case if (c["m"], c["k"], c["n"]) in pages]
     if args.suite:
         out["suite_file"] = args.suite
         run_suite(qg, torch, args, args.suite)
