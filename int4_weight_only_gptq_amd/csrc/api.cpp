@@ -41,17 +41,22 @@ int32_t check_int4(const void* x, int64_t ldx, const uint32_t* qweight, const ui
   return QG_OK;
 }
 
-// Automatic choice: m = 1 the GEMV, m <= 16 the small-M kernel, 16 < m <= 32
-// with n < kRowPassMaxN the small-M kernel in two 16-row passes (each streams
-// the weights; measured faster than the MFMA tiles, whose few column tiles
-// leave the CUs idle: 4096 x 4096 m = 17 21.0 -> 14.6 µs, 25600 x 5120
-// 61.8 -> 55.5 µs; from n = 25600 the tiles win), else the MFMA tiles.
-constexpr int64_t kRowPassMaxN = 20480;
+// Automatic choice: m = 1 the GEMV; m <= 16 the small-M kernel (one MFMA row
+// tile); 16 < m <= 32 the small-M kernel with two row tiles when n is below
+// kRowTileMaxN or m <= 24, else the MFMA tiles.  Measured (cold weights): the
+// tiles pad every wave to 64 rows and at small n leave CUs idle (4096 x 4096
+// m = 17 21.0 -> 9.7 µs, 2048 x 8192 m = 17 17.6 -> 7.7 µs, 4096 x 14336 m = 20
+// 28.8 -> 14.7 µs); at n >= 20480 the row tiles still win to m = 24
+// (5120 x 25600 m = 17 38.9 -> 31.0 µs) and lose at m = 32 (39.4 vs 42.5 µs).
+#ifndef QG_ROWTILE_MAX_N
+#define QG_ROWTILE_MAX_N 20480
+#endif
+constexpr int64_t kRowTileMaxN = QG_ROWTILE_MAX_N;
 
 int32_t resolve_path(int64_t m, int64_t n, int32_t path) {
   if (path != QG_PATH_AUTO) return path;
   if (m == 1) return QG_PATH_GEMV;
-  if (m <= 16 || (m <= 32 && n < kRowPassMaxN)) return QG_PATH_FUSED;
+  if (m <= 16 || (m <= 32 && (n < kRowTileMaxN || m <= 24))) return QG_PATH_FUSED;
   return QG_PATH_MFMA;
 }
 

@@ -149,20 +149,25 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 constexpr int64_t kTicketBytes = 64 << 10;   // counters of up to 16384 strips
 constexpr int SK_MAX_SPLIT = 16;              // k-slices per strip at most
 
+// MFMA row tiles of 16 tokens: one up to 16 tokens, two up to 32
+template <int M, bool DOT>
+constexpr int kRowTiles = DOT ? 1 : (M + 15) / 16;
+
 template <int M, bool DOT, int CPL>
 struct GroupRegs {
   uint32_t w[4][CPL];                  // codes of the 4 k-steps
-  u32x4 xa[4];                         // activations of the 4 k-steps (MFMA: the A slices)
+  u32x4 xa[kRowTiles<M, DOT>][4];      // activations of the 4 k-steps per row tile (MFMA: the A slices)
   Meta<CPL> meta;
 };
 
-// gok: the group is in range; live: this lane's columns are in range; xrow:
-// this lane supplies activation row (token) cl.  The activation row does not
-// depend on the lane's columns.
+// gok: the group is in range; live: this lane's columns are in range.  The
+// activation rows do not depend on the lane's columns: GEMV: every lane reads
+// the one token (xp = x); MFMA: in row tile t the lane supplies token 16 t + cl
+// (xp = x + cl * ldx; zeros past M).
 template <int M, bool DOT, int CPL>
-__device__ __forceinline__ void load_group(GroupRegs<M, DOT, CPL>& r, bool gok, bool live, bool xrow,
+__device__ __forceinline__ void load_group(GroupRegs<M, DOT, CPL>& r, bool gok, bool live, int cl,
                                            const uint32_t* __restrict__ qp,
-                                           const uint16_t* __restrict__ xp,
+                                           const uint16_t* __restrict__ xp, int64_t ldx,
                                            const uint16_t* __restrict__ scales,
                                            const uint32_t* __restrict__ qzeros, int64_t n,
                                            int64_t g, int64_t col, int ks) {
@@ -176,9 +181,14 @@ __device__ __forceinline__ void load_group(GroupRegs<M, DOT, CPL>& r, bool gok, 
 #pragma unroll
       for (int c = 0; c < CPL; ++c) r.w[s][c] = 0u;
     }
-    // MFMA: token cl's 8 k of this lane's word-row; GEMV: the one token's 8 k
-    // (the same address for the 16 lanes of a row: one broadcast load)
-    r.xa[s] = (gok && xrow) ? *reinterpret_cast<const u32x4*>(xp + 8 * (g * 16 + 4 * s + ks)) : zero4;
+    // MFMA: token 16 t + cl's 8 k of this lane's word-row; GEMV: the one
+    // token's 8 k (the same address for the 16 lanes of a row: one broadcast load)
+#pragma unroll
+    for (int t = 0; t < kRowTiles<M, DOT>; ++t) {
+      const bool xrow = DOT || 16 * t + cl < M;
+      r.xa[t][s] = (gok && xrow) ? *reinterpret_cast<const u32x4*>(xp + 16 * t * ldx + 8 * (g * 16 + 4 * s + ks))
+                                 : zero4;
+    }
   }
   if (ok) {
     r.meta = load_meta<CPL>(scales, qzeros, n, g, col);
@@ -325,7 +335,7 @@ hipError_t launch_lora_u(const uint16_t* x, int64_t ldx, const uint16_t* a, int6
 }
 
 template <int M, bool DOT, int CPL>
-__global__ __launch_bounds__(1024) void skinny_int4_kernel(
+__global__ __launch_bounds__(M > 16 ? 512 : 1024) void skinny_int4_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
     uint16_t* __restrict__ y, int64_t ldy, int n, int k, int nstrips, int ksplit, int gwg,
@@ -347,17 +357,18 @@ __global__ __launch_bounds__(1024) void skinny_int4_kernel(
   const int gbeg = kslice * gwg, gend = min(G, gbeg + gwg);
   const int64_t col = (int64_t)strip * SW + CPL * cl;
   const bool live = col < n;
-  // MFMA: the lane supplies token cl (zeros past M); GEMV: every lane the one token
-  const bool xrow = DOT || cl < M;
+  // MFMA: the lane supplies token 16 t + cl of row tile t (zeros past M); GEMV:
+  // every lane the one token
+  constexpr int MT = kRowTiles<M, DOT>;
   const uint32_t* qp = qweight + (live ? col : 0);
-  const uint16_t* xp = x + (!DOT && xrow ? (int64_t)cl * ldx : 0);
+  const uint16_t* xp = x + (!DOT && cl < M ? (int64_t)cl * ldx : 0);
   const int zshift = (int)(col & 7) * 4;
   const u32x4 ones = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
 
   // first group's loads go out before anything waits
   GroupRegs<M, DOT, CPL> cur, nxt;
   int g = gbeg + wave;
-  load_group<M, DOT, CPL>(cur, g < gend, live, xrow, qp, xp, scales, qzeros, n, g, col, ks);
+  load_group<M, DOT, CPL>(cur, g < gend, live, cl, qp, xp, ldx, scales, qzeros, n, g, col, ks);
 
   // the LoRA terms of this thread's outputs in the final reduction (output
   // o = tid + j * blockDim), computed now so that their loads overlap the
@@ -373,13 +384,15 @@ __global__ __launch_bounds__(1024) void skinny_int4_kernel(
     }
   }
 
-  f32x4 total[CPL];
+  f32x4 total[MT][CPL];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) total[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) total[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (; g < gend; g += nw) {
     const int gn = g + nw;
-    load_group<M, DOT, CPL>(nxt, gn < gend, live, xrow, qp, xp, scales, qzeros, n, gn, col, ks);
+    load_group<M, DOT, CPL>(nxt, gn < gend, live, cl, qp, xp, ldx, scales, qzeros, n, gn, col, ks);
     float sc[CPL], bz[CPL];
     if constexpr (DOT) {
       float d[CPL];
@@ -388,7 +401,7 @@ __global__ __launch_bounds__(1024) void skinny_int4_kernel(
       float xs = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const u32x4 a = x_pairs_permuted(cur.xa[s]);
+        const u32x4 a = x_pairs_permuted(cur.xa[0][s]);
 #pragma unroll
         for (int t = 0; t < 4; ++t) xs = dot2_bf16(a[t], kOnesBf16x2, xs);
 #pragma unroll
@@ -400,25 +413,43 @@ __global__ __launch_bounds__(1024) void skinny_int4_kernel(
       }
       decode_meta<CPL>(cur.meta, zshift, sc, bz);
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) total[c][0] += sc[c] * (d[c] - bz[c] * xs);
+      for (int c = 0; c < CPL; ++c) total[0][c][0] += sc[c] * (d[c] - bz[c] * xs);
     } else {
       constexpr int VMAX = M < 4 ? M : 4;
-      f32x4 acc[CPL];
+      f32x4 acc[MT][CPL], xsum[MT];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-      f32x4 xsum = {0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < MT; ++t) {
+        xsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const u32x4 a = x_pairs_permuted(cur.xa[s]);
-        xsum = mfma16_bf16(a, ones, xsum);
+        if constexpr (MT == 1) {
+          const u32x4 a = x_pairs_permuted(cur.xa[0][s]);
+          xsum[0] = mfma16_bf16(a, ones, xsum[0]);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[c] = mfma16_bf16(a, codes_as_bf16_pairs(cur.w[s][c]), acc[c]);
+          for (int c = 0; c < CPL; ++c) acc[0][c] = mfma16_bf16(a, codes_as_bf16_pairs(cur.w[s][c]), acc[0][c]);
+        } else {
+          u32x4 b[CPL];   // one decode of the step's words serves both row tiles
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) b[c] = codes_as_bf16_pairs(cur.w[s][c]);
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            const u32x4 a = x_pairs_permuted(cur.xa[t][s]);
+            xsum[t] = mfma16_bf16(a, ones, xsum[t]);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[t][c] = mfma16_bf16(a, b[c], acc[t][c]);
+          }
+        }
       }
       decode_meta<CPL>(cur.meta, zshift, sc, bz);
 #pragma unroll
-      for (int c = 0; c < CPL; ++c)
+      for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int v = 0; v < VMAX; ++v) total[c][v] += sc[c] * (acc[c][v] - bz[c] * xsum[v]);
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+          for (int v = 0; v < VMAX; ++v) total[t][c][v] += sc[c] * (acc[t][c][v] - bz[c] * xsum[t][v]);
     }
     cur = nxt;
   }
@@ -426,21 +457,23 @@ __global__ __launch_bounds__(1024) void skinny_int4_kernel(
   // wave partials [M][SW] -> LDS plane -> sum over the waves
   if constexpr (DOT) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) total[c][0] = sum_over_rows(total[c][0]);
+    for (int c = 0; c < CPL; ++c) total[0][c][0] = sum_over_rows(total[0][c][0]);
     if (ks == 0) {
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) plane[wave * SW + CPL * cl + c] = total[c][0];
+      for (int c = 0; c < CPL; ++c) plane[wave * SW + CPL * cl + c] = total[0][c][0];
     }
   } else {
     constexpr int VMAX = M < 4 ? M : 4;
 #pragma unroll
-    for (int v = 0; v < VMAX; ++v) {
-      const int token = 4 * ks + v;
-      if (token < M) {
+    for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) plane[(wave * M + token) * SW + CPL * cl + c] = total[c][v];
+      for (int v = 0; v < VMAX; ++v) {
+        const int token = 16 * t + 4 * ks + v;
+        if (token < M) {
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) plane[(wave * M + token) * SW + CPL * cl + c] = total[t][c][v];
+        }
       }
-    }
   }
   __syncthreads();
 
@@ -964,8 +997,9 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes,
   // m = 16 33.3 -> 28.7 µs, 8192 x 8192 m = 8 / 16 14.2 / 17.0 -> 13.5 / 15.2 µs;
   // at 4096 x 4096 and for the GEMV they were slower.
   const bool long_k = !dot && m >= 8 && G >= QG_SKINNY_LONG_G;
-  const int64_t wcap = (p.nstrips >= 384 || long_k) ? (QG_SKINNY_WAVES < 8 ? QG_SKINNY_WAVES : 8)
-                                                     : QG_SKINNY_WAVES;
+  // above 16 tokens (two row tiles) the kernel is bounded to 512 threads
+  const int64_t wcap = (p.nstrips >= 384 || long_k || m > 16) ? (QG_SKINNY_WAVES < 8 ? QG_SKINNY_WAVES : 8)
+                                                               : QG_SKINNY_WAVES;
   p.waves = (int)(G < QG_SKINNY_GPW_MIN ? 1 : (G / QG_SKINNY_GPW_MIN < wcap ? G / QG_SKINNY_GPW_MIN : wcap));
   // k split only when each wave would otherwise walk a long chain of groups
   int64_t ks = 1;
@@ -983,8 +1017,8 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes,
   if ((dot || m >= QG_SKINNY_WIDE_M) && ks > 1 && p.cpl < 4) {
     for (int c = 4; c > p.cpl; c /= 2) {
       const int64_t strips = (n + 16 * c - 1) / (16 * c);
-      const int64_t wc = (strips >= 384 || long_k) ? (QG_SKINNY_WAVES < 8 ? QG_SKINNY_WAVES : 8)
-                                                   : QG_SKINNY_WAVES;
+      const int64_t wc = (strips >= 384 || long_k || m > 16) ? (QG_SKINNY_WAVES < 8 ? QG_SKINNY_WAVES : 8)
+                                                             : QG_SKINNY_WAVES;
       const int64_t wv = G < QG_SKINNY_GPW_MIN ? 1 : (G / QG_SKINNY_GPW_MIN < wc ? G / QG_SKINNY_GPW_MIN : wc);
       const int64_t pw = (G + wv - 1) / wv;
       int64_t kc = (pw + 3) / 4;
@@ -1048,19 +1082,6 @@ hipError_t launch_gemv_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipSt
 }
 
 hipError_t launch_fused_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream) {
-  if (a.m > 16) {
-    // 16-row passes, in order on the stream (they share the workspace): the
-    // first 16 tokens, then the rest (the LoRA intermediate U moves with them)
-    Int4Args lo = a, hi = a;
-    lo.m = 16;
-    hi.m = a.m - 16;
-    hi.x = a.x + 16 * a.ldx;
-    hi.y = a.y + 16 * a.ldy;
-    if (a.lora.u) hi.lora.u = a.lora.u + 16 * 16;
-    const hipError_t e = launch_fused_int4(lo, ws, ws_bytes, stream);
-    if (e != hipSuccess) return e;
-    return launch_fused_int4(hi, ws, ws_bytes, stream);
-  }
   const SkinnyPlan p = plan_skinny(a.m, a.n, a.k, ws ? ws_bytes : 0, false);
   switch (a.m) {
     case 1: skinny_launch_c<1, false>(a, p, ws, stream); break;
@@ -1079,6 +1100,23 @@ hipError_t launch_fused_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipS
     case 14: skinny_launch_c<14, false>(a, p, ws, stream); break;
     case 15: skinny_launch_c<15, false>(a, p, ws, stream); break;
     case 16: skinny_launch_c<16, false>(a, p, ws, stream); break;
+    // two MFMA row tiles (the automatic path sends 16 < m <= 32 here when n is small)
+    case 17: skinny_launch_c<17, false>(a, p, ws, stream); break;
+    case 18: skinny_launch_c<18, false>(a, p, ws, stream); break;
+    case 19: skinny_launch_c<19, false>(a, p, ws, stream); break;
+    case 20: skinny_launch_c<20, false>(a, p, ws, stream); break;
+    case 21: skinny_launch_c<21, false>(a, p, ws, stream); break;
+    case 22: skinny_launch_c<22, false>(a, p, ws, stream); break;
+    case 23: skinny_launch_c<23, false>(a, p, ws, stream); break;
+    case 24: skinny_launch_c<24, false>(a, p, ws, stream); break;
+    case 25: skinny_launch_c<25, false>(a, p, ws, stream); break;
+    case 26: skinny_launch_c<26, false>(a, p, ws, stream); break;
+    case 27: skinny_launch_c<27, false>(a, p, ws, stream); break;
+    case 28: skinny_launch_c<28, false>(a, p, ws, stream); break;
+    case 29: skinny_launch_c<29, false>(a, p, ws, stream); break;
+    case 30: skinny_launch_c<30, false>(a, p, ws, stream); break;
+    case 31: skinny_launch_c<31, false>(a, p, ws, stream); break;
+    case 32: skinny_launch_c<32, false>(a, p, ws, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1266,18 +1304,18 @@ hipError_t launch_mfma_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipSt
 int64_t workspace_int4(int64_t m, int64_t n, int64_t k, int path) {
   if (m == 0 || n == 0 || k == 0) return 0;
   if (path == 3) return plan_mfma(m, n, k, INT64_MAX).ws_bytes;
-  return plan_skinny(m < 16 ? m : 16, n, k, INT64_MAX, path == 1).ws_bytes;   // 16-row passes above 16
+  return plan_skinny(m, n, k, INT64_MAX, path == 1).ws_bytes;
 }
 
 void describe_int4(int64_t m, int64_t n, int64_t k, int path, int64_t ws_bytes, char* buf,
                    size_t len) {
   if (path == 1 || path == 2) {
-    const int64_t mp = path == 1 ? 1 : (m < 16 ? m : 16);   // above 16: the first 16-row pass
+    const int64_t mp = path == 1 ? 1 : m;
     const SkinnyPlan p = plan_skinny(mp, n, k, ws_bytes, path == 1);
     const bool dot = path == 1;
-    snprintf(buf, len, "skinny_int4_kernel<%lld,%s,%d> grid=%lld block=%d lds=%lld ksplit=%d groups=%d%s",
+    snprintf(buf, len, "skinny_int4_kernel<%lld,%s,%d> grid=%lld block=%d lds=%lld ksplit=%d groups=%d",
              (long long)mp, dot ? "dot" : "mfma", p.cpl, (long long)p.blocks, 64 * p.waves, (long long)p.lds,
-             p.ksplit, p.gwg, m > 16 && !dot ? " passes=2" : "");
+             p.ksplit, p.gwg);
   } else {
     const MfmaPlan p = plan_mfma(m, n, k, ws_bytes);
     const PipeCfg c = p.prep ? pipe_cfg_of<true>(p.cfg) : pipe_cfg_of<false>(p.cfg);

@@ -242,12 +242,15 @@ def test_workspace_size(lib):
     assert ks > 1
     assert qg.workspace_size(17, 4096, 4096, path="mfma") == (
         up(65536 + 17 * 4096 * 2 + 32 * 17 * 4) + tiles * ks * bm * 128 * 4)
-    # auto path, 16 < m <= 32 and n < 20480: the small-M kernel in 16-row passes
-    assert qg.describe_int4(17, 4096, 4096).startswith("skinny_int4_kernel<16,mfma,1>")
-    assert qg.describe_int4(17, 4096, 4096).endswith("passes=2")
-    assert qg.workspace_size(24, 5120, 25600) == qg.workspace_size(16, 5120, 25600)
+    # auto path, 16 < m <= 32 and n < 20480: the small-M kernel with two MFMA row tiles,
+    # at most 8 waves (512 threads)
+    assert qg.describe_int4(17, 4096, 4096).startswith("skinny_int4_kernel<17,mfma,1>")
+    assert "block=512" in qg.describe_int4(32, 4096, 4096)
+    assert qg.workspace_size(24, 5120, 25600) > 0
     assert qg.describe_int4(33, 4096, 4096).startswith("int4_pipe_kernel")
-    assert qg.describe_int4(17, 25600, 5120).startswith("int4_pipe_kernel")
+    assert qg.describe_int4(17, 25600, 5120).startswith("skinny_int4_kernel<17,mfma,4>")   # m <= 24
+    assert qg.describe_int4(32, 25600, 5120).startswith("int4_pipe_kernel")
+    assert qg.describe_int4(32, 20472, 5120).startswith("skinny_int4_kernel<32,mfma,")
     assert lib.qgemm_int4_workspace_size(8, 60, 4096, 0) == -SHAPE
     assert lib.qgemm_int4_workspace_size(8, 64, 4096, 1) == -UNSUP
 

@@ -63,7 +63,7 @@ PATH_MS = {
     "fused": [1, 2, 3, 4, 5, 7, 8, 9, 12, 15, 16],
     "mfma": [1, 16, 17, 33, 130, 257],
     "mfma_nows": [17, 33, 130, 257],     # no workspace: the MFMA tiles without the preparation pass
-    "auto": [1, 6, 16, 17, 24, 32, 33, 200],   # 17..32 at n < 20480: two 16-row passes
+    "auto": [1, 6, 16, 17, 24, 32, 33, 200],   # 17..32 at n < 20480: two MFMA row tiles
 }
 
 
@@ -327,7 +327,7 @@ LORA_CASES = [("gemv", 1, 1152, 776, 16), ("fused", 2, 2048, 1040, 16), ("fused"
               ("fused", 15, 2048, 1040, 16), ("fused", 16, 1152, 776, 16), ("mfma", 17, 2048, 1040, 16),
               ("mfma", 130, 1152, 776, 5), ("mfma", 257, 2048, 1040, 16),
               ("gemv", 1, 16384, 520, 16), ("fused", 8, 16384, 520, 16), ("mfma", 33, 4096, 520, 16),
-              ("auto", 24, 2048, 1040, 16), ("auto", 32, 16384, 520, 5)]   # 16-row passes
+              ("auto", 24, 2048, 1040, 16), ("auto", 32, 16384, 520, 5)]   # two row tiles
 
 
 @pytest.mark.parametrize("path,m,k,n,rank", LORA_CASES)
