@@ -255,6 +255,10 @@ def test_deterministic(gpu_lib):
 # checked on sampled outputs the oracle computes one by one
 # ----------------------------------------------------------------------------
 FULL = [(c, case) for c in (0, 1, 2, 4) for case in int4_cases(c)]
+# 17..32 tokens at workload sizes: two row tiles with a k split (25600 x 5120), at n >= 20480 (m <= 24),
+# and the MFMA tiles above that (m = 32, n = 25600)
+FULL += [(2, ("row-tiles", 20, 25600, 5120, 2020)), (2, ("row-tiles", 24, 5120, 25600, 2024)),
+         (2, ("row-tiles", 32, 5120, 25600, 2032)), (1, ("row-tiles", 17, 4096, 4096, 1017))]
 
 
 @pytest.mark.parametrize("cfg,case", FULL, ids=["c%d-m%d-k%d-n%d" % (c, x[1], x[2], x[3]) for c, x in FULL])
@@ -285,7 +289,8 @@ def test_dequant_without_zero_point_bit_exact(gpu_lib, k, n):
 NOZERO_CASES = [("gemv", 1, 1152, 776), ("fused", 2, 2048, 1040), ("fused", 8, 1152, 776),
                 ("fused", 15, 2048, 1040), ("fused", 16, 1152, 776), ("mfma", 17, 2048, 1040),
                 ("mfma", 130, 1152, 776), ("mfma_nows", 33, 2048, 1040),
-                ("gemv", 1, 16384, 520), ("fused", 8, 16384, 520), ("mfma", 33, 4096, 520)]
+                ("gemv", 1, 16384, 520), ("fused", 8, 16384, 520), ("mfma", 33, 4096, 520),
+                ("auto", 24, 16384, 520), ("auto", 31, 2048, 1040)]   # two row tiles (k split / none)
 
 
 @pytest.mark.parametrize("path,m,k,n", NOZERO_CASES)
