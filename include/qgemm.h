@@ -58,7 +58,8 @@ extern "C" {
 #define QG_TN 2
 
 /* path codes of qgemm_int4_path */
-#define QG_PATH_AUTO 0  /* m == 1: GEMV; 2 <= m <= 16: fused small-M; m > 16: MFMA tiles */
+#define QG_PATH_AUTO 0  /* m == 1: GEMV; 2 <= m <= 16: fused small-M; 16 < m <= 32: fused small-M
+                           with two row tiles when n < 20480 or m <= 24; otherwise MFMA tiles */
 #define QG_PATH_GEMV 1  /* m must be 1                                                   */
 #define QG_PATH_FUSED 2 /* 1 <= m <= 16                                                   */
 #define QG_PATH_MFMA 3  /* any m >= 1                                                    */
@@ -94,7 +95,7 @@ int32_t qg_last_hip_error(void);
  *   m >= 0 tokens, 0 <= n <= 2^26 output columns (n % 8 == 0), 0 <= k <= 2^22
  *   input rows (k % 128 == 0), group_size must be 128.
  *   workspace, workspace_bytes
- *            optional device scratch (16-byte aligned).  The m <= 16 paths
+ *            optional device scratch (16-byte aligned).  The small-M paths
  *            use it to split k over several workgroups; the MFMA path (m > 16)
  *            to hold the activations in the decode's pair order and their
  *            per-group sums (a preparation pass before the tiles run).
