@@ -154,6 +154,29 @@ def test_strided_x_and_y_with_guard_bands(gpu_lib):
         assert np.all(b == -384.0), "write outside the output view"
 
 
+@pytest.mark.parametrize("m,k,n", [(24, 1024, 520), (32, 16384, 264), (17, 128, 8), (32, 128, 8)])
+def test_row_tiles_strided_guarded_and_tiny(gpu_lib, m, k, n):
+    # the two-row-tile small-M kernel (automatic path): strided X and Y inside
+    # guard bands, a k split (k = 16384), and the smallest k and n
+    import torch
+
+    d = int4_inputs(m, k, n, seed=35 + m + k)
+    t = upload_int4(d)
+    xs = torch.zeros((m, k + 64), dtype=torch.bfloat16, device="cuda")
+    xs[:, :k] = t["x"]
+    t["x"] = xs[:, :k]
+    big = torch.full((m + 2, n + 24), -384.0, dtype=torch.bfloat16, device="cuda")
+    out = big[1:m + 1, 8:8 + n]
+    say("row tiles strided", m, k, n, gpu_lib.describe_int4(m, n, k))
+    assert gpu_lib.describe_int4(m, n, k).startswith("skinny_int4_kernel<%d,mfma," % m)
+    run(gpu_lib, t, "auto", out=out)
+    ref = cpp_oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], m, k, n)
+    assert_accepted(host_u16(out), ref, ("row tiles strided", m, k, n))
+    b = big.float().cpu().numpy()
+    b[1:m + 1, 8:8 + n] = -384.0
+    assert np.all(b == -384.0), "write outside the output view"
+
+
 def test_k_zero_writes_zeros_and_m_zero_is_noop(gpu_lib):
     import torch
 
@@ -332,7 +355,7 @@ LORA_CASES = [("gemv", 1, 1152, 776, 16), ("fused", 2, 2048, 1040, 16), ("fused"
               ("fused", 15, 2048, 1040, 16), ("fused", 16, 1152, 776, 16), ("mfma", 17, 2048, 1040, 16),
               ("mfma", 130, 1152, 776, 5), ("mfma", 257, 2048, 1040, 16),
               ("gemv", 1, 16384, 520, 16), ("fused", 8, 16384, 520, 16), ("mfma", 33, 4096, 520, 16),
-              ("auto", 24, 2048, 1040, 16), ("auto", 32, 16384, 520, 5)]   # two row tiles
+              ("auto", 24, 2048, 1040, 16), ("auto", 32, 16384, 520, 5), ("auto", 31, 1152, 776, 1)]   # two row tiles
 
 
 @pytest.mark.parametrize("path,m,k,n,rank", LORA_CASES)
