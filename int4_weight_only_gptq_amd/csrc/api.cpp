@@ -43,20 +43,29 @@ int32_t check_int4(const void* x, int64_t ldx, const uint32_t* qweight, const ui
 
 // Automatic choice: m = 1 the GEMV; m <= 16 the small-M kernel (one MFMA row
 // tile); 16 < m <= 32 the small-M kernel with two row tiles when n is below
-// kRowTileMaxN or m <= 24, else the MFMA tiles.  Measured (cold weights): the
-// tiles pad every wave to 64 rows and at small n leave CUs idle (4096 x 4096
-// m = 17 21.0 -> 9.7 µs, 2048 x 8192 m = 17 17.6 -> 7.7 µs, 4096 x 14336 m = 20
-// 28.8 -> 14.7 µs); at n >= 20480 the row tiles still win to m = 24
-// (5120 x 25600 m = 17 38.9 -> 31.0 µs) and lose at m = 32 (39.4 vs 42.5 µs).
+// kRowTileMaxN or m <= 24; 32 < m <= 64 the small-M kernel with three or four
+// row tiles when its planned workgroups take a single pass over the 256 CUs;
+// else the MFMA tiles.  Measured (cold weights): the tiles pad every wave to 64
+// rows and at small n leave CUs idle (4096 x 4096 m = 17 21.0 -> 9.7 µs,
+// 2048 x 8192 m = 17 17.6 -> 7.7 µs, 4096 x 14336 m = 20 28.8 -> 14.7 µs); at
+// n >= 20480 the row tiles still win to m = 24 (5120 x 25600 m = 17
+// 38.9 -> 31.0 µs) and lose at m = 32 (39.4 vs 42.5 µs).  Above 32 tokens the
+// small-M time grows with m and with every further pass over the CUs: in one
+// pass 4096 x 4096 m = 33 / 48 / 56 21.2 / 21.4 / 21.5 -> 14.9 / 17.8 / 21.0 µs,
+// 2048 x 8192 m = 48 17.9 -> 11.8 µs, 8192 x 4096 m = 48 31.9 -> 23.1 µs,
+// 1024 x 4096 m = 64 16.0 -> 7.9 µs; in two 8192 x 8192 m = 33 32.1 vs 39.0 µs,
+// 4096 x 14336 m = 48 30.2 vs 39.0 µs.
 #ifndef QG_ROWTILE_MAX_N
 #define QG_ROWTILE_MAX_N 20480
 #endif
 constexpr int64_t kRowTileMaxN = QG_ROWTILE_MAX_N;
+constexpr int64_t kOnePassBlocks = 256;   // one workgroup per CU
 
-int32_t resolve_path(int64_t m, int64_t n, int32_t path) {
+int32_t resolve_path(int64_t m, int64_t n, int64_t k, int32_t path) {
   if (path != QG_PATH_AUTO) return path;
   if (m == 1) return QG_PATH_GEMV;
   if (m <= 16 || (m <= 32 && (n < kRowTileMaxN || m <= 24))) return QG_PATH_FUSED;
+  if (m <= 64 && qg::plan_skinny(m, n, k, INT64_MAX, false).blocks <= kOnePassBlocks) return QG_PATH_FUSED;
   return QG_PATH_MFMA;
 }
 
@@ -99,7 +108,7 @@ int32_t run_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint
     ws_bytes = rest;
     if (ws_bytes == 0) ws = nullptr;
   }
-  switch (resolve_path(m, n, path)) {
+  switch (resolve_path(m, n, k, path)) {
     case QG_PATH_GEMV: return hip_status(qg::launch_gemv_int4(a, ws, ws_bytes, s));
     case QG_PATH_FUSED: return hip_status(qg::launch_fused_int4(a, ws, ws_bytes, s));
     default: return hip_status(qg::launch_mfma_int4(a, ws, ws_bytes, s));
@@ -173,7 +182,7 @@ int64_t qgemm_int4_workspace_size(int64_t m, int64_t n, int64_t k, int32_t path)
   if (m < 0 || n < 0 || k < 0 || k % 128 != 0 || n % 8 != 0) return -QG_ERR_SHAPE;
   if (n > (int64_t)1 << 30 || k > (int64_t)1 << 30) return -QG_ERR_SHAPE;
   if (check_path(m, path) != QG_OK) return -QG_ERR_UNSUPPORTED;
-  return qg::workspace_int4(m, n, k, resolve_path(m, n, path));
+  return qg::workspace_int4(m, n, k, resolve_path(m, n, k, path));
 }
 
 int32_t qgemm_int4_describe(int64_t m, int64_t n, int64_t k, int32_t path, int64_t workspace_bytes,
@@ -190,7 +199,7 @@ int32_t qgemm_int4_describe(int64_t m, int64_t n, int64_t k, int32_t path, int64
     snprintf(buf, (size_t)len, "zero16_kernel");
     return QG_OK;
   }
-  qg::describe_int4(m, n, k, resolve_path(m, n, path), workspace_bytes < 0 ? 0 : workspace_bytes, buf,
+  qg::describe_int4(m, n, k, resolve_path(m, n, k, path), workspace_bytes < 0 ? 0 : workspace_bytes, buf,
                     (size_t)len);
   return QG_OK;
 }

@@ -149,7 +149,7 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 constexpr int64_t kTicketBytes = 64 << 10;   // counters of up to 16384 strips
 constexpr int SK_MAX_SPLIT = 16;              // k-slices per strip at most
 
-// MFMA row tiles of 16 tokens: one up to 16 tokens, two up to 32
+// MFMA row tiles of 16 tokens: one up to 16 tokens, two up to 32, ... four up to 64
 template <int M, bool DOT>
 constexpr int kRowTiles = DOT ? 1 : (M + 15) / 16;
 
@@ -974,6 +974,9 @@ int64_t split_workspace_bytes(int64_t nstrips, int64_t ksplit, int64_t m, int cp
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes, bool dot) {
   SkinnyPlan p{};
   const int64_t G = k / 128;
+  // widest strip the registers allow: 64 columns up to 32 tokens, 32 up to 48,
+  // 16 above (each row tile adds accumulators and double-buffered activations)
+  const int cplmax = dot || m <= 32 ? 4 : (m <= 48 ? 2 : 1);
   // widest strip that still leaves enough strips for the CUs
   p.cpl = 1;
   if ((n + 63) / 64 >= QG_SKINNY_MIN_STRIPS) p.cpl = 4;
@@ -987,6 +990,7 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes,
     const int64_t s4 = (n + 63) / 64;
     if (s4 >= 192 && s4 <= 256) p.cpl = 4;
   }
+  if (p.cpl > cplmax) p.cpl = cplmax;
   const int sw = 16 * p.cpl;
   p.nstrips = (int)((n + sw - 1) / sw);
   // many strips: 8-wave workgroups so that two fit on a CU; few: 16 waves.
@@ -1015,7 +1019,7 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes,
   // bytes per instruction.  Measured at k = 25600, n = 5120: m = 1 40 -> 29 µs,
   // m = 2 39 -> 27 µs, m = 16 57 -> 35 µs.
   if ((dot || m >= QG_SKINNY_WIDE_M) && ks > 1 && p.cpl < 4) {
-    for (int c = 4; c > p.cpl; c /= 2) {
+    for (int c = cplmax; c > p.cpl; c /= 2) {
       const int64_t strips = (n + 16 * c - 1) / (16 * c);
       const int64_t wc = (strips >= 384 || long_k || m > 16) ? (QG_SKINNY_WAVES < 8 ? QG_SKINNY_WAVES : 8)
                                                              : QG_SKINNY_WAVES;
@@ -1071,9 +1075,16 @@ static void skinny_launch(const Int4Args& a, const SkinnyPlan& p, void* ws, hipS
 
 template <int M, bool DOT>
 static void skinny_launch_c(const Int4Args& a, const SkinnyPlan& p, void* ws, hipStream_t stream) {
-  if (p.cpl == 4) skinny_launch<M, DOT, 4>(a, p, ws, stream);
-  else if (p.cpl == 2) skinny_launch<M, DOT, 2>(a, p, ws, stream);
-  else skinny_launch<M, DOT, 1>(a, p, ws, stream);
+  if constexpr (M <= 32) {
+    if (p.cpl == 4) skinny_launch<M, DOT, 4>(a, p, ws, stream);
+    else if (p.cpl == 2) skinny_launch<M, DOT, 2>(a, p, ws, stream);
+    else skinny_launch<M, DOT, 1>(a, p, ws, stream);
+  } else if constexpr (M <= 48) {   // the planner caps the strip width by the token count
+    if (p.cpl >= 2) skinny_launch<M, DOT, 2>(a, p, ws, stream);
+    else skinny_launch<M, DOT, 1>(a, p, ws, stream);
+  } else {
+    skinny_launch<M, DOT, 1>(a, p, ws, stream);
+  }
 }
 
 hipError_t launch_gemv_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream) {
@@ -1117,6 +1128,40 @@ hipError_t launch_fused_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipS
     case 30: skinny_launch_c<30, false>(a, p, ws, stream); break;
     case 31: skinny_launch_c<31, false>(a, p, ws, stream); break;
     case 32: skinny_launch_c<32, false>(a, p, ws, stream); break;
+    // three and four row tiles (the automatic path sends 32 < m <= 64 here when
+    // the planned workgroups take a single pass over the CUs)
+    case 33: skinny_launch_c<33, false>(a, p, ws, stream); break;
+    case 34: skinny_launch_c<34, false>(a, p, ws, stream); break;
+    case 35: skinny_launch_c<35, false>(a, p, ws, stream); break;
+    case 36: skinny_launch_c<36, false>(a, p, ws, stream); break;
+    case 37: skinny_launch_c<37, false>(a, p, ws, stream); break;
+    case 38: skinny_launch_c<38, false>(a, p, ws, stream); break;
+    case 39: skinny_launch_c<39, false>(a, p, ws, stream); break;
+    case 40: skinny_launch_c<40, false>(a, p, ws, stream); break;
+    case 41: skinny_launch_c<41, false>(a, p, ws, stream); break;
+    case 42: skinny_launch_c<42, false>(a, p, ws, stream); break;
+    case 43: skinny_launch_c<43, false>(a, p, ws, stream); break;
+    case 44: skinny_launch_c<44, false>(a, p, ws, stream); break;
+    case 45: skinny_launch_c<45, false>(a, p, ws, stream); break;
+    case 46: skinny_launch_c<46, false>(a, p, ws, stream); break;
+    case 47: skinny_launch_c<47, false>(a, p, ws, stream); break;
+    case 48: skinny_launch_c<48, false>(a, p, ws, stream); break;
+    case 49: skinny_launch_c<49, false>(a, p, ws, stream); break;
+    case 50: skinny_launch_c<50, false>(a, p, ws, stream); break;
+    case 51: skinny_launch_c<51, false>(a, p, ws, stream); break;
+    case 52: skinny_launch_c<52, false>(a, p, ws, stream); break;
+    case 53: skinny_launch_c<53, false>(a, p, ws, stream); break;
+    case 54: skinny_launch_c<54, false>(a, p, ws, stream); break;
+    case 55: skinny_launch_c<55, false>(a, p, ws, stream); break;
+    case 56: skinny_launch_c<56, false>(a, p, ws, stream); break;
+    case 57: skinny_launch_c<57, false>(a, p, ws, stream); break;
+    case 58: skinny_launch_c<58, false>(a, p, ws, stream); break;
+    case 59: skinny_launch_c<59, false>(a, p, ws, stream); break;
+    case 60: skinny_launch_c<60, false>(a, p, ws, stream); break;
+    case 61: skinny_launch_c<61, false>(a, p, ws, stream); break;
+    case 62: skinny_launch_c<62, false>(a, p, ws, stream); break;
+    case 63: skinny_launch_c<63, false>(a, p, ws, stream); break;
+    case 64: skinny_launch_c<64, false>(a, p, ws, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

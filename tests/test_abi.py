@@ -247,7 +247,14 @@ def test_workspace_size(lib):
     assert qg.describe_int4(17, 4096, 4096).startswith("skinny_int4_kernel<17,mfma,1>")
     assert "block=512" in qg.describe_int4(32, 4096, 4096)
     assert qg.workspace_size(24, 5120, 25600) > 0
-    assert qg.describe_int4(33, 4096, 4096).startswith("int4_pipe_kernel")
+    # 32 < m <= 64: three or four row tiles when the workgroups fit one pass over the
+    # 256 CUs (strips 32 columns wide up to 48 tokens, 16 above), else the MFMA tiles
+    assert qg.describe_int4(33, 4096, 4096).startswith("skinny_int4_kernel<33,mfma,1> grid=256 ")
+    assert qg.describe_int4(48, 8192, 2048).startswith("skinny_int4_kernel<48,mfma,2> grid=256 ")
+    assert qg.describe_int4(64, 4096, 4096).startswith("skinny_int4_kernel<64,mfma,1> grid=256 ")
+    assert qg.describe_int4(48, 14336, 4096).startswith("int4_pipe_kernel")   # 448 workgroups
+    assert qg.describe_int4(64, 8192, 2048).startswith("int4_pipe_kernel")    # 512 workgroups
+    assert qg.describe_int4(65, 1024, 1024).startswith("int4_pipe_kernel")
     assert qg.describe_int4(17, 25600, 5120).startswith("skinny_int4_kernel<17,mfma,4>")   # m <= 24
     assert qg.describe_int4(32, 25600, 5120).startswith("int4_pipe_kernel")
     assert qg.describe_int4(32, 20472, 5120).startswith("skinny_int4_kernel<32,mfma,")
@@ -276,7 +283,8 @@ def test_planned_launches_fit_the_hardware():
     rng = np.random.default_rng(20261203)
     shapes = [(1, 8, 128), (16, 8, 128), (17, 8, 128), (32, 20472, 128), (17, 20480, 128), (33, 20480, 25600)]   # (m, n, k)
     for _ in range(300):
-        m = int(rng.choice([1, 2, 5, 8, 15, 16, 17, 24, 31, 32, 33, 64, 100, 257, 512, 2048, 4097]))
+        m = int(rng.choice([1, 2, 5, 8, 15, 16, 17, 24, 31, 32, 33, 40, 48, 49, 56, 64, 65, 100, 257, 512,
+                            2048, 4097]))
         n = 8 * int(rng.integers(1, 4096))
         k = 128 * int(rng.integers(1, 256))
         shapes.append((m, n, k))
@@ -296,3 +304,5 @@ def test_planned_launches_fit_the_hardware():
                     assert p["ksplit"] == 1, what           # no workspace: no k split
                 if name.startswith("skinny"):
                     assert p["grid"] % 8 == 0, what          # whole XCD rounds
+                    if m > 32:
+                        assert m <= 64 and p["grid"] <= 256, what   # row tiles only in one pass

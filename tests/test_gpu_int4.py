@@ -63,7 +63,7 @@ PATH_MS = {
     "fused": [1, 2, 3, 4, 5, 7, 8, 9, 12, 15, 16],
     "mfma": [1, 16, 17, 33, 130, 257],
     "mfma_nows": [17, 33, 130, 257],     # no workspace: the MFMA tiles without the preparation pass
-    "auto": [1, 6, 16, 17, 24, 32, 33, 200],   # 17..32 at n < 20480: two MFMA row tiles
+    "auto": [1, 6, 16, 17, 24, 32, 33, 40, 48, 64, 200],   # 17..64: two to four MFMA row tiles
 }
 
 
@@ -154,10 +154,12 @@ def test_strided_x_and_y_with_guard_bands(gpu_lib):
         assert np.all(b == -384.0), "write outside the output view"
 
 
-@pytest.mark.parametrize("m,k,n", [(24, 1024, 520), (32, 16384, 264), (17, 128, 8), (32, 128, 8)])
+@pytest.mark.parametrize("m,k,n", [(24, 1024, 520), (32, 16384, 264), (17, 128, 8), (32, 128, 8),
+                                   (40, 2048, 1040), (48, 16384, 264), (56, 1024, 520), (64, 16384, 264),
+                                   (33, 128, 8), (64, 128, 8)])
 def test_row_tiles_strided_guarded_and_tiny(gpu_lib, m, k, n):
-    # the two-row-tile small-M kernel (automatic path): strided X and Y inside
-    # guard bands, a k split (k = 16384), and the smallest k and n
+    # the small-M kernel with two to four MFMA row tiles (automatic path): strided
+    # X and Y inside guard bands, a k split (k = 16384), and the smallest k and n
     import torch
 
     d = int4_inputs(m, k, n, seed=35 + m + k)
@@ -282,6 +284,9 @@ FULL = [(c, case) for c in (0, 1, 2, 4) for case in int4_cases(c)]
 # and the MFMA tiles above that (m = 32, n = 25600)
 FULL += [(2, ("row-tiles", 20, 25600, 5120, 2020)), (2, ("row-tiles", 24, 5120, 25600, 2024)),
          (2, ("row-tiles", 32, 5120, 25600, 2032)), (1, ("row-tiles", 17, 4096, 4096, 1017))]
+# 33..64 tokens: three and four row tiles in one pass over the CUs (4096 x 4096, 2048 x 8192)
+FULL += [(1, ("row-tiles", 33, 4096, 4096, 1033)), (1, ("row-tiles", 64, 4096, 4096, 1064)),
+         (1, ("row-tiles", 48, 2048, 8192, 1048))]
 
 
 @pytest.mark.parametrize("cfg,case", FULL, ids=["c%d-m%d-k%d-n%d" % (c, x[1], x[2], x[3]) for c, x in FULL])
@@ -313,7 +318,8 @@ NOZERO_CASES = [("gemv", 1, 1152, 776), ("fused", 2, 2048, 1040), ("fused", 8, 1
                 ("fused", 15, 2048, 1040), ("fused", 16, 1152, 776), ("mfma", 17, 2048, 1040),
                 ("mfma", 130, 1152, 776), ("mfma_nows", 33, 2048, 1040),
                 ("gemv", 1, 16384, 520), ("fused", 8, 16384, 520), ("mfma", 33, 4096, 520),
-                ("auto", 24, 16384, 520), ("auto", 31, 2048, 1040)]   # two row tiles (k split / none)
+                ("auto", 24, 16384, 520), ("auto", 31, 2048, 1040),   # two row tiles (k split / none)
+                ("auto", 48, 2048, 1040), ("auto", 64, 16384, 264)]   # three / four row tiles
 
 
 @pytest.mark.parametrize("path,m,k,n", NOZERO_CASES)
@@ -355,7 +361,8 @@ LORA_CASES = [("gemv", 1, 1152, 776, 16), ("fused", 2, 2048, 1040, 16), ("fused"
               ("fused", 15, 2048, 1040, 16), ("fused", 16, 1152, 776, 16), ("mfma", 17, 2048, 1040, 16),
               ("mfma", 130, 1152, 776, 5), ("mfma", 257, 2048, 1040, 16),
               ("gemv", 1, 16384, 520, 16), ("fused", 8, 16384, 520, 16), ("mfma", 33, 4096, 520, 16),
-              ("auto", 24, 2048, 1040, 16), ("auto", 32, 16384, 520, 5), ("auto", 31, 1152, 776, 1)]   # two row tiles
+              ("auto", 24, 2048, 1040, 16), ("auto", 32, 16384, 520, 5), ("auto", 31, 1152, 776, 1),   # two row tiles
+              ("auto", 40, 2048, 1040, 16), ("auto", 64, 16384, 264, 3)]   # three / four row tiles
 
 
 @pytest.mark.parametrize("path,m,k,n,rank", LORA_CASES)
