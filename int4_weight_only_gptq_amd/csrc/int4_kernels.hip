@@ -85,11 +85,8 @@ struct Meta {
 };
 
 template <int CPL>
-__device__ __forceinline__ Meta<CPL> load_meta(const uint16_t* __restrict__ scales,
-                                               const uint32_t* __restrict__ qzeros, int64_t n,
-                                               int64_t g, int64_t col) {
+__device__ __forceinline__ Meta<CPL> load_meta(const uint16_t* __restrict__ sp, const uint32_t* __restrict__ zp) {
   Meta<CPL> r;
-  const uint16_t* sp = scales + g * n + col;
   if constexpr (CPL == 4) {
     const u32x2 v = *reinterpret_cast<const u32x2*>(sp);
     r.s[0] = v[0];
@@ -99,18 +96,19 @@ __device__ __forceinline__ Meta<CPL> load_meta(const uint16_t* __restrict__ scal
   } else {
     r.s[0] = *sp;
   }
-  r.z = qzeros ? qzeros[g * (n >> 3) + (col >> 3)] : 0u;   // no zero point: z = 0
+  r.z = *zp;
   return r;
 }
 
-// zshift = 4 * (col % 8): the nibble of the first of the CPL columns.
+// zshift = 4 * (col % 8): the nibble of the first of the CPL columns; zmask = 0
+// without a zero point (z = 0).
 template <int CPL>
-__device__ __forceinline__ void decode_meta(const Meta<CPL>& mt, int zshift, float (&s)[CPL],
+__device__ __forceinline__ void decode_meta(const Meta<CPL>& mt, int zshift, uint32_t zmask, float (&s)[CPL],
                                             float (&bz)[CPL]) {
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     s[c] = half_bits_to_float((mt.s[c >> 1] >> (16 * (c & 1))) & 0xFFFFu);
-    bz[c] = (float)(128u + ((mt.z >> (zshift + 4 * c)) & 15u));
+    bz[c] = (float)(128u + (((mt.z & zmask) >> (zshift + 4 * c)) & 15u));
   }
 }
 
@@ -160,43 +158,30 @@ struct GroupRegs {
   Meta<CPL> meta;
 };
 
-// gok: the group is in range; live: this lane's columns are in range.  The
-// activation rows do not depend on the lane's columns: GEMV: every lane reads
-// the one token (xp = x); MFMA: in row tile t the lane supplies token 16 t + cl
-// (xp = x + cl * ldx; zeros past M).
+// One group's loads.  Every address is in range, so no load carries a
+// condition: a load inside an exec-masked branch makes the number of loads in
+// flight depend on the path, and the compiler then waits for all of them
+// before the current group's arithmetic instead of only for that group's.  The
+// caller clamps the pointers: lanes whose columns are past n read column 0 and
+// MFMA lanes whose token is past M read token 0 (xr[t] is the lane's row of row
+// tile t; GEMV: the one token for every lane); those values reach only outputs
+// that are never stored, since MFMA rows and columns are independent.  Without
+// a zero point zp is any readable word (zstride 0) and the caller masks z.
 template <int M, bool DOT, int CPL>
-__device__ __forceinline__ void load_group(GroupRegs<M, DOT, CPL>& r, bool gok, bool live, int cl,
-                                           const uint32_t* __restrict__ qp,
-                                           const uint16_t* __restrict__ xp, int64_t ldx,
-                                           const uint16_t* __restrict__ scales,
-                                           const uint32_t* __restrict__ qzeros, int64_t n,
-                                           int64_t g, int64_t col, int ks) {
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  const bool ok = gok && live;
+__device__ __forceinline__ void load_group(GroupRegs<M, DOT, CPL>& r, const uint32_t* __restrict__ qp,
+                                           const uint16_t* const (&xr)[kRowTiles<M, DOT>],
+                                           const uint16_t* __restrict__ sp, const uint32_t* __restrict__ zp,
+                                           int64_t n, int64_t zstride, int64_t g, int ks) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    if (ok) {
-      load_words<CPL>(qp + (g * 16 + 4 * s + ks) * n, r.w[s]);
-    } else {
+    load_words<CPL>(qp + (g * 16 + 4 * s + ks) * n, r.w[s]);
+    // MFMA: the lane's token's 8 k of this word-row; GEMV: the one token's 8 k
+    // (the same address for the 16 lanes of a row: one broadcast load)
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) r.w[s][c] = 0u;
-    }
-    // MFMA: token 16 t + cl's 8 k of this lane's word-row; GEMV: the one
-    // token's 8 k (the same address for the 16 lanes of a row: one broadcast load)
-#pragma unroll
-    for (int t = 0; t < kRowTiles<M, DOT>; ++t) {
-      const bool xrow = DOT || 16 * t + cl < M;
-      r.xa[t][s] = (gok && xrow) ? *reinterpret_cast<const u32x4*>(xp + 16 * t * ldx + 8 * (g * 16 + 4 * s + ks))
-                                 : zero4;
-    }
+    for (int t = 0; t < kRowTiles<M, DOT>; ++t)
+      r.xa[t][s] = *reinterpret_cast<const u32x4*>(xr[t] + 8 * (g * 16 + 4 * s + ks));
   }
-  if (ok) {
-    r.meta = load_meta<CPL>(scales, qzeros, n, g, col);
-  } else {
-    r.meta.z = 0u;
-#pragma unroll
-    for (int i = 0; i < (CPL == 4 ? 2 : 1); ++i) r.meta.s[i] = 0u;
-  }
+  r.meta = load_meta<CPL>(sp + g * n, zp + g * zstride);
 }
 
 // ---------------------------------------------------------------------------
@@ -357,18 +342,29 @@ __global__ __launch_bounds__(M > 16 ? 512 : 1024) void skinny_int4_kernel(
   const int gbeg = kslice * gwg, gend = min(G, gbeg + gwg);
   const int64_t col = (int64_t)strip * SW + CPL * cl;
   const bool live = col < n;
-  // MFMA: the lane supplies token 16 t + cl of row tile t (zeros past M); GEMV:
-  // every lane the one token
+  // clamped pointers (see load_group): columns past n read column 0; MFMA: the
+  // lane supplies token 16 t + cl of row tile t (token 0 past M); GEMV: every
+  // lane the one token
   constexpr int MT = kRowTiles<M, DOT>;
-  const uint32_t* qp = qweight + (live ? col : 0);
-  const uint16_t* xp = x + (!DOT && cl < M ? (int64_t)cl * ldx : 0);
+  const int64_t colc = live ? col : 0;
+  const uint32_t* qp = qweight + colc;
+  const uint16_t* xr[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) xr[t] = x + (!DOT && 16 * t + cl < M ? (int64_t)(16 * t + cl) * ldx : 0);
+  const uint16_t* sp = scales + colc;
+  const uint32_t* zp = qzeros ? qzeros + (colc >> 3) : reinterpret_cast<const uint32_t*>(scales);
+  const int64_t zstride = qzeros ? (int64_t)(n >> 3) : 0;
+  const uint32_t zmask = qzeros ? ~0u : 0u;
   const int zshift = (int)(col & 7) * 4;
   const u32x4 ones = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
 
-  // first group's loads go out before anything waits
-  GroupRegs<M, DOT, CPL> cur, nxt;
-  int g = gbeg + wave;
-  load_group<M, DOT, CPL>(cur, g < gend, live, cl, qp, xp, ldx, scales, qzeros, n, g, col, ks);
+  // first group's loads go out before anything waits (a wave without a group
+  // loads the slice's first one and skips the arithmetic); the wave index is
+  // made scalar so that the group loop's branches are uniform
+  GroupRegs<M, DOT, CPL> ra, rb;
+  int g = gbeg + __builtin_amdgcn_readfirstlane(wave);
+  const bool busy = g < gend;
+  load_group<M, DOT, CPL>(ra, qp, xr, sp, zp, n, zstride, busy ? g : gbeg, ks);
 
   // the LoRA terms of this thread's outputs in the final reduction (output
   // o = tid + j * blockDim), computed now so that their loads overlap the
@@ -390,9 +386,8 @@ __global__ __launch_bounds__(M > 16 ? 512 : 1024) void skinny_int4_kernel(
 #pragma unroll
     for (int c = 0; c < CPL; ++c) total[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (; g < gend; g += nw) {
-    const int gn = g + nw;
-    load_group<M, DOT, CPL>(nxt, gn < gend, live, cl, qp, xp, ldx, scales, qzeros, n, gn, col, ks);
+  // the group's arithmetic, accumulated into total
+  auto compute = [&](const GroupRegs<M, DOT, CPL>& cur) {
     float sc[CPL], bz[CPL];
     if constexpr (DOT) {
       float d[CPL];
@@ -411,7 +406,7 @@ __global__ __launch_bounds__(M > 16 ? 512 : 1024) void skinny_int4_kernel(
           for (int t = 0; t < 4; ++t) d[c] = dot2_bf16(bq[t], a[t], d[c]);
         }
       }
-      decode_meta<CPL>(cur.meta, zshift, sc, bz);
+      decode_meta<CPL>(cur.meta, zshift, zmask, sc, bz);
 #pragma unroll
       for (int c = 0; c < CPL; ++c) total[0][c][0] += sc[c] * (d[c] - bz[c] * xs);
     } else {
@@ -443,7 +438,7 @@ __global__ __launch_bounds__(M > 16 ? 512 : 1024) void skinny_int4_kernel(
           }
         }
       }
-      decode_meta<CPL>(cur.meta, zshift, sc, bz);
+      decode_meta<CPL>(cur.meta, zshift, zmask, sc, bz);
 #pragma unroll
       for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -451,7 +446,41 @@ __global__ __launch_bounds__(M > 16 ? 512 : 1024) void skinny_int4_kernel(
 #pragma unroll
           for (int v = 0; v < VMAX; ++v) total[t][c][v] += sc[c] * (acc[t][c][v] - bz[c] * xsum[t][v]);
     }
-    cur = nxt;
+  };
+  // Two register sets in turn, no copy between them (a copy of registers whose
+  // loads are in flight would wait for them): the next group's loads are issued
+  // before the current group's arithmetic, which waits for its own loads only.
+  // The 64-column MFMA strips of 1024-thread workgroups (128 registers) would
+  // spill with both sets live across the arithmetic; they keep one set and a
+  // copy, and wait for both groups' loads.  Measured against conditional loads
+  // and one set (cold weights): 4096 x 4096 m = 1 / 15 6.17 / 8.23 -> 5.73 /
+  // 8.12 µs, m = 33 14.9 -> 13.0 µs, 4096 x 14336 m = 1 10.1 -> 9.0 µs,
+  // 5120 x 25600 m = 24 38.0 -> 31.3 µs; the 64-column m = 16 strips, one set
+  // with unconditional loads: 5120 x 25600 26.2 -> 23.6 µs (11-15% slower than
+  // that with both sets).
+  constexpr bool kTwoSets = DOT || M > 16 || CPL < 4;
+  if (busy) {
+    if constexpr (kTwoSets) {
+      for (;;) {
+        if (g + nw >= gend) { compute(ra); break; }
+        load_group<M, DOT, CPL>(rb, qp, xr, sp, zp, n, zstride, g + nw, ks);
+        compute(ra);
+        g += nw;
+        if (g + nw >= gend) { compute(rb); break; }
+        load_group<M, DOT, CPL>(ra, qp, xr, sp, zp, n, zstride, g + nw, ks);
+        compute(rb);
+        g += nw;
+      }
+    } else {
+      for (;;) {
+        const bool more = g + nw < gend;
+        if (more) load_group<M, DOT, CPL>(rb, qp, xr, sp, zp, n, zstride, g + nw, ks);
+        compute(ra);
+        if (!more) break;
+        ra = rb;
+        g += nw;
+      }
+    }
   }
 
   // wave partials [M][SW] -> LDS plane -> sum over the waves
