@@ -453,28 +453,49 @@ __global__ __launch_bounds__(M > 16 ? 512 : 1024) void skinny_int4_kernel(
   // The 64-column MFMA strips of 1024-thread workgroups (128 registers) would
   // spill with both sets live across the arithmetic; they keep one set and a
   // copy, and wait for both groups' loads.  Measured against conditional loads
-  // and one set (cold weights): 4096 x 4096 m = 1 / 15 6.17 / 8.23 -> 5.73 /
-  // 8.12 µs, m = 33 14.9 -> 13.0 µs, 4096 x 14336 m = 1 10.1 -> 9.0 µs,
-  // 5120 x 25600 m = 24 38.0 -> 31.3 µs; the 64-column m = 16 strips, one set
-  // with unconditional loads: 5120 x 25600 26.2 -> 23.6 µs (11-15% slower than
-  // that with both sets).
+  // and one set (cold weights): 4096 x 4096 m = 1 / 8 / 15 6.18 / 6.99 / 8.33
+  // -> 5.49 / 6.63 / 7.99 µs, m = 33 14.9 -> 12.7 µs, 4096 x 14336 m = 1
+  // 10.2 -> 8.7 µs, 5120 x 25600 m = 24 38.0 -> 32.2 µs; the 64-column m = 16
+  // strips, one set with unconditional loads: 5120 x 25600 26.1 -> 23.7 µs
+  // (11-15% slower than that with both sets).
   constexpr bool kTwoSets = DOT || M > 16 || CPL < 4;
   if (busy) {
+    // (the scheduling barriers keep the next group's loads ahead of the current
+    // group's first use: scheduled after it, they would go out only once the
+    // current group had arrived)
+    // Waves with one or two groups run straight-line code: at a loop head the
+    // compiler merges the entry and back-edge states and waited there for most
+    // of the current group's loads before issuing the next group's.
     if constexpr (kTwoSets) {
-      for (;;) {
-        if (g + nw >= gend) { compute(ra); break; }
+      if (g + nw >= gend) {
+        compute(ra);
+      } else {
         load_group<M, DOT, CPL>(rb, qp, xr, sp, zp, n, zstride, g + nw, ks);
+        __builtin_amdgcn_sched_barrier(0);
         compute(ra);
         g += nw;
-        if (g + nw >= gend) { compute(rb); break; }
-        load_group<M, DOT, CPL>(ra, qp, xr, sp, zp, n, zstride, g + nw, ks);
-        compute(rb);
-        g += nw;
+        if (g + nw >= gend) {
+          compute(rb);
+        } else {
+          for (;;) {
+            load_group<M, DOT, CPL>(ra, qp, xr, sp, zp, n, zstride, g + nw, ks);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(rb);
+            g += nw;
+            if (g + nw >= gend) { compute(ra); break; }
+            load_group<M, DOT, CPL>(rb, qp, xr, sp, zp, n, zstride, g + nw, ks);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(ra);
+            g += nw;
+            if (g + nw >= gend) { compute(rb); break; }
+          }
+        }
       }
     } else {
       for (;;) {
         const bool more = g + nw < gend;
         if (more) load_group<M, DOT, CPL>(rb, qp, xr, sp, zp, n, zstride, g + nw, ks);
+        __builtin_amdgcn_sched_barrier(0);
         compute(ra);
         if (!more) break;
         ra = rb;
