@@ -61,7 +61,8 @@ extern "C" {
 #define QG_PATH_AUTO 0  /* m == 1: GEMV; 2 <= m <= 16: fused small-M; 16 < m <= 32: fused small-M
                            with two row tiles when n < 20480 or m <= 24; 32 < m <= 64: fused
                            small-M with three or four row tiles when its workgroups fit one
-                           pass over the 256 CUs; otherwise MFMA tiles */
+                           pass over the 256 CUs (two passes at k > 8192 and m <= 48);
+                           otherwise MFMA tiles */
 #define QG_PATH_GEMV 1  /* m must be 1                                                   */
 #define QG_PATH_FUSED 2 /* 1 <= m <= 16                                                   */
 #define QG_PATH_MFMA 3  /* any m >= 1                                                    */

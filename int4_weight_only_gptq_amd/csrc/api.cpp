@@ -44,8 +44,8 @@ int32_t check_int4(const void* x, int64_t ldx, const uint32_t* qweight, const ui
 // Automatic choice: m = 1 the GEMV; m <= 16 the small-M kernel (one MFMA row
 // tile); 16 < m <= 32 the small-M kernel with two row tiles when n is below
 // kRowTileMaxN or m <= 24; 32 < m <= 64 the small-M kernel with three or four
-// row tiles when its planned workgroups take a single pass over the 256 CUs;
-// else the MFMA tiles.  Measured (cold weights): the tiles pad every wave to 64
+// row tiles when its planned workgroups take a single pass over the 256 CUs,
+// or two passes at k > 8192 and m <= 48; else the MFMA tiles.  Measured (cold weights): the tiles pad every wave to 64
 // rows and at small n leave CUs idle (4096 x 4096 m = 17 21.0 -> 9.7 µs,
 // 2048 x 8192 m = 17 17.6 -> 7.7 µs, 4096 x 14336 m = 20 28.8 -> 14.7 µs); at
 // n >= 20480 the row tiles still win to m = 24 (5120 x 25600 m = 17
@@ -53,19 +53,30 @@ int32_t check_int4(const void* x, int64_t ldx, const uint32_t* qweight, const ui
 // small-M time grows with m and with every further pass over the CUs: in one
 // pass 4096 x 4096 m = 33 / 48 / 56 21.2 / 21.4 / 21.5 -> 14.9 / 17.8 / 21.0 µs,
 // 2048 x 8192 m = 48 17.9 -> 11.8 µs, 8192 x 4096 m = 48 31.9 -> 23.1 µs,
-// 1024 x 4096 m = 64 16.0 -> 7.9 µs; in two 8192 x 8192 m = 33 32.1 vs 39.0 µs,
-// 4096 x 14336 m = 48 30.2 vs 39.0 µs.
+// 1024 x 4096 m = 64 16.0 -> 7.9 µs.  In two passes the row tiles win at long
+// k (14336 x 4096 m = 33 / 40 / 48 40.1 / 40.3 / 40.3 -> 30.8 / 33.8 / 36.8 µs,
+// 11008 x 4096 m = 33 / 40 35.5 / 35.5 -> 30.1 / 32.7 µs, m = 48 even) and not
+// at k <= 8192 (8192 x 8192 m = 33 / 40 32.0 / 32.2 vs 32.9 / 35.5 µs,
+// 4096 x 11008 m = 48 29.7 vs 31.9 µs).
 #ifndef QG_ROWTILE_MAX_N
 #define QG_ROWTILE_MAX_N 20480
 #endif
 constexpr int64_t kRowTileMaxN = QG_ROWTILE_MAX_N;
-constexpr int64_t kOnePassBlocks = 256;   // one workgroup per CU
+#ifndef QG_ROWTILE_MAX_BLOCKS
+#define QG_ROWTILE_MAX_BLOCKS 256   // one workgroup per CU
+#endif
+constexpr int64_t kOnePassBlocks = QG_ROWTILE_MAX_BLOCKS;
+constexpr int64_t kTwoPassMinK = 8192;    // two passes only above this k (and m <= 48)
 
 int32_t resolve_path(int64_t m, int64_t n, int64_t k, int32_t path) {
   if (path != QG_PATH_AUTO) return path;
   if (m == 1) return QG_PATH_GEMV;
   if (m <= 16 || (m <= 32 && (n < kRowTileMaxN || m <= 24))) return QG_PATH_FUSED;
-  if (m <= 64 && qg::plan_skinny(m, n, k, INT64_MAX, false).blocks <= kOnePassBlocks) return QG_PATH_FUSED;
+  if (m <= 64) {
+    const int64_t blocks = qg::plan_skinny(m, n, k, INT64_MAX, false).blocks;
+    if (blocks <= kOnePassBlocks || (m <= 48 && k > kTwoPassMinK && blocks <= 2 * kOnePassBlocks))
+      return QG_PATH_FUSED;
+  }
   return QG_PATH_MFMA;
 }
 

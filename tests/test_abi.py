@@ -253,6 +253,10 @@ def test_workspace_size(lib):
     assert qg.describe_int4(48, 8192, 2048).startswith("skinny_int4_kernel<48,mfma,2> grid=256 ")
     assert qg.describe_int4(64, 4096, 4096).startswith("skinny_int4_kernel<64,mfma,1> grid=256 ")
     assert qg.describe_int4(48, 14336, 4096).startswith("int4_pipe_kernel")   # 448 workgroups
+    # two passes (at most 512 workgroups) only at k > 8192 and m <= 48
+    assert qg.describe_int4(48, 4096, 14336).startswith("skinny_int4_kernel<48,mfma,2> grid=512 ")
+    assert qg.describe_int4(33, 8192, 8192).startswith("int4_pipe_kernel")    # k = 8192: 512 workgroups
+    assert qg.describe_int4(56, 4096, 14336).startswith("int4_pipe_kernel")
     assert qg.describe_int4(64, 8192, 2048).startswith("int4_pipe_kernel")    # 512 workgroups
     assert qg.describe_int4(65, 1024, 1024).startswith("int4_pipe_kernel")
     assert qg.describe_int4(17, 25600, 5120).startswith("skinny_int4_kernel<17,mfma,4>")   # m <= 24
@@ -304,5 +308,5 @@ def test_planned_launches_fit_the_hardware():
                     assert p["ksplit"] == 1, what           # no workspace: no k split
                 if name.startswith("skinny"):
                     assert p["grid"] % 8 == 0, what          # whole XCD rounds
-                    if m > 32:
-                        assert m <= 64 and p["grid"] <= 256, what   # row tiles only in one pass
+                    if m > 32:   # row tiles in one pass, or two at long k
+                        assert m <= 64 and (p["grid"] <= 256 or (m <= 48 and k > 8192 and p["grid"] <= 512)), what

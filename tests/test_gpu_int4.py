@@ -286,7 +286,7 @@ FULL += [(2, ("row-tiles", 20, 25600, 5120, 2020)), (2, ("row-tiles", 24, 5120, 
          (2, ("row-tiles", 32, 5120, 25600, 2032)), (1, ("row-tiles", 17, 4096, 4096, 1017))]
 # 33..64 tokens: three and four row tiles in one pass over the CUs (4096 x 4096, 2048 x 8192)
 FULL += [(1, ("row-tiles", 33, 4096, 4096, 1033)), (1, ("row-tiles", 64, 4096, 4096, 1064)),
-         (1, ("row-tiles", 48, 2048, 8192, 1048))]
+         (1, ("row-tiles", 48, 2048, 8192, 1048)), (2, ("row-tiles", 40, 14336, 4096, 2040))]   # two passes, k split
 
 
 @pytest.mark.parametrize("cfg,case", FULL, ids=["c%d-m%d-k%d-n%d" % (c, x[1], x[2], x[3]) for c, x in FULL])
