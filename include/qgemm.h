@@ -59,7 +59,8 @@ extern "C" {
 
 /* path codes of qgemm_int4_path */
 #define QG_PATH_AUTO 0  /* m == 1: GEMV; 2 <= m <= 16: fused small-M; 16 < m <= 32: fused small-M
-                           with two row tiles when n < 20480 or m <= 24; 32 < m <= 64: fused
+                           with two row tiles when n < 20480, m <= 24 or its workgroups fit two
+                           passes over the 256 CUs; 32 < m <= 64: fused
                            small-M with three or four row tiles when its workgroups fit one
                            pass over the 256 CUs (two passes at k > 8192 and m <= 48);
                            otherwise MFMA tiles */

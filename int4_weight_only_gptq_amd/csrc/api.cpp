@@ -43,13 +43,15 @@ int32_t check_int4(const void* x, int64_t ldx, const uint32_t* qweight, const ui
 
 // Automatic choice: m = 1 the GEMV; m <= 16 the small-M kernel (one MFMA row
 // tile); 16 < m <= 32 the small-M kernel with two row tiles when n is below
-// kRowTileMaxN or m <= 24; 32 < m <= 64 the small-M kernel with three or four
+// kRowTileMaxN, m <= 24 or its workgroups take at most two passes; 32 < m <= 64 the small-M kernel with three or four
 // row tiles when its planned workgroups take a single pass over the 256 CUs,
 // or two passes at k > 8192 and m <= 48; else the MFMA tiles.  Measured (cold weights): the tiles pad every wave to 64
 // rows and at small n leave CUs idle (4096 x 4096 m = 17 21.0 -> 9.7 µs,
 // 2048 x 8192 m = 17 17.6 -> 7.7 µs, 4096 x 14336 m = 20 28.8 -> 14.7 µs); at
 // n >= 20480 the row tiles still win to m = 24 (5120 x 25600 m = 17
-// 38.9 -> 31.0 µs) and lose at m = 32 (39.4 vs 42.5 µs).  Above 32 tokens the
+// 38.9 -> 31.0 µs); above that, in at most two passes (5120 x 25600 m = 28 / 32
+// 39.5 / 39.5 -> 34.4 / 37.3 µs, 4096 x 28672 m = 32 35.3 -> 29.4 µs), not in
+// more (8192 x 28672 m = 32, 896 workgroups: 55.1 vs 68.0 µs).  Above 32 tokens the
 // small-M time grows with m and with every further pass over the CUs: in one
 // pass 4096 x 4096 m = 33 / 48 / 56 21.2 / 21.4 / 21.5 -> 14.9 / 17.8 / 21.0 µs,
 // 2048 x 8192 m = 48 17.9 -> 11.8 µs, 8192 x 4096 m = 48 31.9 -> 23.1 µs,
@@ -71,9 +73,10 @@ constexpr int64_t kTwoPassMinK = 8192;    // two passes only above this k (and m
 int32_t resolve_path(int64_t m, int64_t n, int64_t k, int32_t path) {
   if (path != QG_PATH_AUTO) return path;
   if (m == 1) return QG_PATH_GEMV;
-  if (m <= 16 || (m <= 32 && (n < kRowTileMaxN || m <= 24))) return QG_PATH_FUSED;
+  if (m <= 16) return QG_PATH_FUSED;
   if (m <= 64) {
     const int64_t blocks = qg::plan_skinny(m, n, k, INT64_MAX, false).blocks;
+    if (m <= 32 && (n < kRowTileMaxN || m <= 24 || blocks <= 2 * kOnePassBlocks)) return QG_PATH_FUSED;
     if (blocks <= kOnePassBlocks || (m <= 48 && k > kTwoPassMinK && blocks <= 2 * kOnePassBlocks))
       return QG_PATH_FUSED;
   }

@@ -260,7 +260,8 @@ def test_workspace_size(lib):
     assert qg.describe_int4(64, 8192, 2048).startswith("int4_pipe_kernel")    # 512 workgroups
     assert qg.describe_int4(65, 1024, 1024).startswith("int4_pipe_kernel")
     assert qg.describe_int4(17, 25600, 5120).startswith("skinny_int4_kernel<17,mfma,4>")   # m <= 24
-    assert qg.describe_int4(32, 25600, 5120).startswith("int4_pipe_kernel")
+    assert qg.describe_int4(32, 25600, 5120).startswith("skinny_int4_kernel<32,mfma,4> grid=400 ")  # 2 passes
+    assert qg.describe_int4(32, 28672, 8192).startswith("int4_pipe_kernel")   # n >= 20480, 896 workgroups
     assert qg.describe_int4(32, 20472, 5120).startswith("skinny_int4_kernel<32,mfma,")
     assert lib.qgemm_int4_workspace_size(8, 60, 4096, 0) == -SHAPE
     assert lib.qgemm_int4_workspace_size(8, 64, 4096, 1) == -UNSUP

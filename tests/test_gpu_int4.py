@@ -280,10 +280,11 @@ def test_deterministic(gpu_lib):
 # checked on sampled outputs the oracle computes one by one
 # ----------------------------------------------------------------------------
 FULL = [(c, case) for c in (0, 1, 2, 4) for case in int4_cases(c)]
-# 17..32 tokens at workload sizes: two row tiles with a k split (25600 x 5120), at n >= 20480 (m <= 24),
-# and the MFMA tiles above that (m = 32, n = 25600)
+# 17..32 tokens at workload sizes: two row tiles with a k split (25600 x 5120), at n >= 20480 (m <= 24,
+# and m = 32 in two passes), and the MFMA tiles beyond two passes (m = 32, 8192 x 28672)
 FULL += [(2, ("row-tiles", 20, 25600, 5120, 2020)), (2, ("row-tiles", 24, 5120, 25600, 2024)),
-         (2, ("row-tiles", 32, 5120, 25600, 2032)), (1, ("row-tiles", 17, 4096, 4096, 1017))]
+         (2, ("row-tiles", 32, 5120, 25600, 2032)), (1, ("row-tiles", 17, 4096, 4096, 1017)),
+         (3, ("row-tiles", 32, 8192, 28672, 3032))]
 # 33..64 tokens: three and four row tiles in one pass over the CUs (4096 x 4096, 2048 x 8192)
 FULL += [(1, ("row-tiles", 33, 4096, 4096, 1033)), (1, ("row-tiles", 64, 4096, 4096, 1064)),
          (1, ("row-tiles", 48, 2048, 8192, 1048)), (2, ("row-tiles", 40, 14336, 4096, 2040))]   # two passes, k split
