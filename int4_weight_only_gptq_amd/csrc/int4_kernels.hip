@@ -1013,6 +1013,13 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
 #ifndef QG_SKINNY_GPW_MIN
 #define QG_SKINNY_GPW_MIN 1        // groups per wave the wave count aims at (at least)
 #endif
+// More strips than CUs: 8-wave workgroups, so that two fit on a CU and the
+// strips take one pass instead of two (257-383 strips with 16 waves took two):
+// 2048 x 5632 m = 1 / 8 / 15 6.38 / 7.49 / 8.83 -> 5.45 / 6.61 / 7.90 µs,
+// 4096 x 11008 m = 8 12.6 -> 11.6 µs, 2048 x 9216 m = 8 8.50 -> 7.11 µs.
+#ifndef QG_SKINNY_MANY_STRIPS
+#define QG_SKINNY_MANY_STRIPS 257  // strips from which workgroups have 8 waves (two per CU)
+#endif
 #ifndef QG_SKINNY_LONG_G
 #define QG_SKINNY_LONG_G 48        // groups from which MFMA strips (m >= 8) use 8-wave workgroups
 #endif
@@ -1043,7 +1050,7 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes,
   if (p.cpl > cplmax) p.cpl = cplmax;
   const int sw = 16 * p.cpl;
   p.nstrips = (int)((n + sw - 1) / sw);
-  // many strips: 8-wave workgroups so that two fit on a CU; few: 16 waves.
+  // more strips than CUs: 8-wave workgroups so that two fit on a CU; few: 16 waves.
   // One group per wave: every wave's loads go out at once (a wave waits for
   // all of its loads in flight at each group, so a chain of groups costs a
   // memory latency per link).  Long k with m >= 8: 8 waves (longer chains,
@@ -1052,7 +1059,7 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes,
   // at 4096 x 4096 and for the GEMV they were slower.
   const bool long_k = !dot && m >= 8 && G >= QG_SKINNY_LONG_G;
   // above 16 tokens (two row tiles) the kernel is bounded to 512 threads
-  const int64_t wcap = (p.nstrips >= 384 || long_k || m > 16) ? (QG_SKINNY_WAVES < 8 ? QG_SKINNY_WAVES : 8)
+  const int64_t wcap = (p.nstrips >= QG_SKINNY_MANY_STRIPS || long_k || m > 16) ? (QG_SKINNY_WAVES < 8 ? QG_SKINNY_WAVES : 8)
                                                                : QG_SKINNY_WAVES;
   p.waves = (int)(G < QG_SKINNY_GPW_MIN ? 1 : (G / QG_SKINNY_GPW_MIN < wcap ? G / QG_SKINNY_GPW_MIN : wcap));
   // k split only when each wave would otherwise walk a long chain of groups
@@ -1071,7 +1078,7 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes,
   if ((dot || m >= QG_SKINNY_WIDE_M) && ks > 1 && p.cpl < 4) {
     for (int c = cplmax; c > p.cpl; c /= 2) {
       const int64_t strips = (n + 16 * c - 1) / (16 * c);
-      const int64_t wc = (strips >= 384 || long_k || m > 16) ? (QG_SKINNY_WAVES < 8 ? QG_SKINNY_WAVES : 8)
+      const int64_t wc = (strips >= QG_SKINNY_MANY_STRIPS || long_k || m > 16) ? (QG_SKINNY_WAVES < 8 ? QG_SKINNY_WAVES : 8)
                                                              : QG_SKINNY_WAVES;
       const int64_t wv = G < QG_SKINNY_GPW_MIN ? 1 : (G / QG_SKINNY_GPW_MIN < wc ? G / QG_SKINNY_GPW_MIN : wc);
       const int64_t pw = (G + wv - 1) / wv;

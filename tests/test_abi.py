@@ -245,6 +245,9 @@ def test_workspace_size(lib):
     # auto path, 16 < m <= 32 and n < 20480: the small-M kernel with two MFMA row tiles,
     # at most 8 waves (512 threads)
     assert qg.describe_int4(17, 4096, 4096).startswith("skinny_int4_kernel<17,mfma,1>")
+    # more strips than CUs (352 here): 8-wave workgroups, two per CU; 256 strips: 16 waves
+    assert qg.describe_int4(8, 5632, 2048).startswith("skinny_int4_kernel<8,mfma,1> grid=352 block=512 ")
+    assert qg.describe_int4(8, 4096, 2048).startswith("skinny_int4_kernel<8,mfma,1> grid=256 block=1024 ")
     assert "block=512" in qg.describe_int4(32, 4096, 4096)
     assert qg.workspace_size(24, 5120, 25600) > 0
     # 32 < m <= 64: three or four row tiles when the workgroups fit one pass over the

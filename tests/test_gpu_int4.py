@@ -285,6 +285,8 @@ FULL = [(c, case) for c in (0, 1, 2, 4) for case in int4_cases(c)]
 FULL += [(2, ("row-tiles", 20, 25600, 5120, 2020)), (2, ("row-tiles", 24, 5120, 25600, 2024)),
          (2, ("row-tiles", 32, 5120, 25600, 2032)), (1, ("row-tiles", 17, 4096, 4096, 1017)),
          (3, ("row-tiles", 32, 8192, 28672, 3032))]
+# 257..383 strips: 8-wave workgroups, two per CU (2048 x 5632: 352 strips)
+FULL += [(1, ("strips", 8, 2048, 5632, 1108)), (1, ("strips", 1, 2048, 5632, 1101))]
 # 33..64 tokens: three and four row tiles in one pass over the CUs (4096 x 4096, 2048 x 8192)
 FULL += [(1, ("row-tiles", 33, 4096, 4096, 1033)), (1, ("row-tiles", 64, 4096, 4096, 1064)),
          (1, ("row-tiles", 48, 2048, 8192, 1048)), (2, ("row-tiles", 40, 14336, 4096, 2040))]   # two passes, k split
