@@ -322,7 +322,8 @@ NOZERO_CASES = [("gemv", 1, 1152, 776), ("fused", 2, 2048, 1040), ("fused", 8, 1
                 ("mfma", 130, 1152, 776), ("mfma_nows", 33, 2048, 1040),
                 ("gemv", 1, 16384, 520), ("fused", 8, 16384, 520), ("mfma", 33, 4096, 520),
                 ("auto", 24, 16384, 520), ("auto", 31, 2048, 1040),   # two row tiles (k split / none)
-                ("auto", 48, 2048, 1040), ("auto", 64, 16384, 264)]   # three / four row tiles
+                ("auto", 48, 2048, 1040), ("auto", 64, 16384, 264),   # three / four row tiles
+                ("fused", 4, 16384, 520)]   # MFMA strips with idle waves (16 waves, 8 groups per k slice)
 
 
 @pytest.mark.parametrize("path,m,k,n", NOZERO_CASES)
@@ -365,7 +366,8 @@ LORA_CASES = [("gemv", 1, 1152, 776, 16), ("fused", 2, 2048, 1040, 16), ("fused"
               ("mfma", 130, 1152, 776, 5), ("mfma", 257, 2048, 1040, 16),
               ("gemv", 1, 16384, 520, 16), ("fused", 8, 16384, 520, 16), ("mfma", 33, 4096, 520, 16),
               ("auto", 24, 2048, 1040, 16), ("auto", 32, 16384, 520, 5), ("auto", 31, 1152, 776, 1),   # two row tiles
-              ("auto", 40, 2048, 1040, 16), ("auto", 64, 16384, 264, 3)]   # three / four row tiles
+              ("auto", 40, 2048, 1040, 16), ("auto", 64, 16384, 264, 3),   # three / four row tiles
+              ("fused", 4, 16384, 520, 16)]   # idle waves
 
 
 @pytest.mark.parametrize("path,m,k,n,rank", LORA_CASES)
