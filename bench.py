@@ -106,24 +106,27 @@ def copies_for(bytes_per_copy, regime):
     return max(2, -(-2 * LLC_BYTES // bytes_per_copy))
 
 
-def time_us(torch, fn, iters, graph=True, reps=7):
-    """Microseconds per call of fn() over iters back-to-back calls: the median of
-    `reps` timed repetitions.
+def time_us(torch, fn, iters, graph=True, reps=7, min_calls=1):
+    """Microseconds per call of fn() over n = max(iters, min_calls) back-to-back
+    calls: the median of `reps` timed repetitions.
 
-    With graph=True the iters calls are captured once into a HIP graph on the
+    With graph=True the n calls are captured once into a HIP graph on the
     launch stream and each repetition is one replay of it, so host launch cost
     (Python, ctypes) is not on the clock; HIP events bracket each replay on the
-    same stream.  graph=False times eager launches from Python.
+    same stream.  graph=False times eager launches from Python.  A caller that
+    rotates over R buffer copies passes min_calls=R, so every replay touches all
+    of them (the cold regime: R copies span at least twice the LLC).
     """
     import statistics
 
+    n = max(iters, min_calls)
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     times = []
     if graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for _ in range(iters):
+            for _ in range(n):
                 fn()
         g.replay()                       # warm replay
         torch.cuda.synchronize()
@@ -132,16 +135,16 @@ def time_us(torch, fn, iters, graph=True, reps=7):
             g.replay()
             e1.record(s)
             e1.synchronize()
-            times.append(e0.elapsed_time(e1) * 1e3 / iters)
+            times.append(e0.elapsed_time(e1) * 1e3 / n)
         del g
         return statistics.median(times)
     for _ in range(reps):
         e0.record(s)
-        for _ in range(iters):
+        for _ in range(n):
             fn()
         e1.record(s)
         e1.synchronize()
-        times.append(e0.elapsed_time(e1) * 1e3 / iters)
+        times.append(e0.elapsed_time(e1) * 1e3 / n)
     return statistics.median(times)
 
 
@@ -173,46 +176,99 @@ def measured_traffic(kernel):
     return None if k is None else int(k["fetch_bytes"] + k["write_bytes"])
 
 
-def copy_peak_gbps(torch, nbytes=2 << 30):
-    """Measured device copy bandwidth (read + write bytes / time), torch's copy kernel."""
-    a = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
-    b = torch.empty_like(a)
-    for _ in range(3):
-        b.copy_(a)
-    us = time_us(torch, lambda: b.copy_(a), 10, graph=False)
-    del a, b
+def bandwidth_peaks(qg, torch, nbytes=4 << 30):
+    """Measured HBM bandwidth with the library's 16-byte lane probes over nbytes
+    (4 GiB, sixteen times the LLC): a copy (read + write bytes / time) and a
+    read-only stream.  Best of 5 launches, HIP events on the launch stream."""
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    src.fill_(0x5A5A5A5A)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(5):
+            e0.record(s)
+            fn()
+            e1.record(s)
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return min(ms)
+
+    copy_ms = best(lambda: qg.probe_copy(src, dst))
+    read_ms = best(lambda: qg.probe_read(src, sink))
+    del src, dst
     torch.cuda.empty_cache()
-    return 2 * nbytes / us / 1e3
+    return {"copy_gbps": round(2 * nbytes / copy_ms / 1e6, 1), "read_gbps": round(nbytes / read_ms / 1e6, 1),
+            "bytes": nbytes, "kernels": "copy16_kernel, read16_kernel (16-byte lane loads/stores, grid-stride)"}
 
 
-def same_size_reference(torch, nbytes, regime, iters):
-    """Plain torch kernels over the same number of bytes, in the same regime (cold:
-    rotating copies), graph-replayed back to back: a reduction that reads the
-    bytes (torch.sum) and a copy that reads and writes them.  Microseconds each."""
-    n = max(1, nbytes // 4)
-    copies = copies_for(4 * n, regime)
-    src = [torch.randn(n, device="cuda") for _ in range(copies)]
+def same_size_reference(qg, torch, nbytes, regime, iters):
+    """The library's read and copy probes over the same number of bytes as one
+    launch of the dominant kernel, in the same regime (cold: rotating copies
+    spanning twice the LLC, every copy touched in each replay), graph-replayed
+    back to back.  Microseconds per launch each."""
+    nbytes = max(16, nbytes // 16 * 16)
+    copies = copies_for(nbytes, regime)
+    src = [torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(i) for i in range(copies)]
     dst = [torch.empty_like(src[0]) for _ in range(copies)]
-    acc = torch.empty((), device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     st = {"i": 0}
 
     def read():
-        torch.sum(src[st["i"] % copies], dim=0, out=acc)
+        qg.probe_read(src[st["i"] % copies], sink)
         st["i"] += 1
 
     def copy():
-        dst[st["i"] % copies].copy_(src[st["i"] % copies])
+        qg.probe_copy(src[st["i"] % copies], dst[st["i"] % copies])
         st["i"] += 1
 
     for _ in range(3):
         read()
         copy()
-    r = time_us(torch, read, iters)
-    c = time_us(torch, copy, iters)
+    r = time_us(torch, read, iters, min_calls=copies)
+    c = time_us(torch, copy, iters, min_calls=copies)
     del src, dst
     torch.cuda.empty_cache()
-    return {"bytes": 4 * n, "read_us": round(r, 3), "copy_us": round(c, 3),
-            "kernels": "torch.sum (reads the bytes), Tensor.copy_ (reads and writes them)"}
+    return {"bytes": nbytes, "read_us": round(r, 3), "copy_us": round(c, 3), "copies": copies,
+            "kernels": "read16_kernel (reads the bytes), copy16_kernel (reads and writes them)"}
+
+
+def gpu_state(qg, torch):
+    """Shader clock under a short MFMA load (cycle counter against the 100 MHz
+    constant counter) and the temperatures rocm-smi reports, logged per config
+    (the BC-250 post found sysfs clocks wrong and benchmarked from a known
+    thermal state)."""
+    import subprocess
+
+    import numpy as np
+
+    clocks = qg.probe_mfma_bf16(256, 400)
+    torch.cuda.synchronize()
+    c = clocks.cpu().numpy().astype("float64")
+    ticks = c[:, 3] - c[:, 1]
+    mhz = float(np.median(100.0 * (c[:, 2] - c[:, 0]) / np.where(ticks > 0, ticks, np.nan)))
+    out = {"sclk_mhz": round(mhz, 1)}
+    try:
+        res = subprocess.run(["rocm-smi", "--showtemp", "--json"], capture_output=True, text=True, timeout=15)
+        data = json.loads(res.stdout)
+        temps = {}
+        for card, vals in data.items():
+            for key, v in vals.items():
+                if "emperature" in key:
+                    try:
+                        temps[key.replace("Temperature (Sensor ", "").rstrip(")").replace(") (C", "")] = float(v)
+                    except (TypeError, ValueError):
+                        pass
+            break
+        out["temp_c"] = temps or None
+    except Exception:       # no rocm-smi or no JSON: the clock alone
+        out["temp_c"] = None
+    return out
 
 
 def mfma_probe(qg, torch, blocks=1024, iters=4000):
@@ -297,6 +353,78 @@ def cpu_baseline(cases, seconds):
                       % (calls, threads, el)}
 
 
+class DeviceWeights:
+    """`copies` resident copies of one (k, n) int4 weight set drawn on the device
+    from a seeded torch generator (timing only: the parity tests draw the same
+    distributions from the host generator).  q and z uniform 0..15 (random
+    words), s = fp16(0.005 + |N(0, 0.01)|)."""
+
+    def __init__(self, torch, k, n, seed, copies):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        self.k, self.n = k, n
+        self.w = []
+        for _ in range(copies):
+            qw = torch.randint(-2 ** 31, 2 ** 31 - 1, (k // 8, n), generator=g, dtype=torch.int32, device="cuda")
+            sc = (0.005 + (torch.randn((k // 128, n), generator=g, device="cuda") * 0.01).abs()).to(torch.float16)
+            qz = torch.randint(-2 ** 31, 2 ** 31 - 1, (k // 128, n // 8), generator=g, dtype=torch.int32,
+                               device="cuda")
+            self.w.append((qw, sc, qz))
+        self.i = 0
+
+    def next(self):
+        w = self.w[self.i % len(self.w)]
+        self.i += 1
+        return w
+
+
+def time_configs(qg, torch, args, bw):
+    """The rest of the metric, per call in the cold regime: the prefill shapes
+    (25600 x 5120, 5120 x 25600) at m = 16, 512, 2048 and the large-weight shapes
+    (4096 x 28672, 4096 x 14336, 8192 x 8192) at m = 1, 8, 16; each row with its
+    kernel, µs, GB/s of algorithmic bytes, TFLOP/s and the fraction of its
+    roofline (MFMA-bound rows: of the 2.5 PFLOP/s bf16 peak; the others: of the
+    measured copy), plus the shader clock and temperatures after each shape."""
+    from qgemm_inputs.configs import seed_for
+
+    rows, states = [], []
+    for cfg, shapes, tokens in ((2, [(25600, 5120), (5120, 25600)], [16, 512, 2048]),
+                                (4, [(4096, 28672), (4096, 14336), (8192, 8192)], [1, 8, 16])):
+        for si, (k, n) in enumerate(shapes):
+            w = DeviceWeights(torch, k, n, seed_for(cfg, 100 + si), copies_for(int4_bytes(0, k, n), args.regime))
+            g = torch.Generator(device="cuda")
+            g.manual_seed(seed_for(cfg, 200 + si))
+            for m in tokens:
+                x = torch.randn((m, k), generator=g, device="cuda").to(torch.bfloat16)
+                y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+
+                def launch(x=x, y=y):
+                    qw, sc, qz = w.next()
+                    qg.qgemm_int4(x, qw, sc, qz, out=y)
+
+                for _ in range(3):
+                    launch()
+                us = time_us(torch, launch, args.steps, min_calls=len(w.w))
+                nb, fl = int4_bytes(m, k, n), 2 * m * n * k
+                row = {"config": cfg, "m": m, "k": k, "n": n, "kernel": qg.describe_int4(m, n, k).split(" ")[0],
+                       "us": round(us, 3), "gbps": round(nb / us / 1e3, 1), "tflops": round(fl / us / 1e6, 1),
+                       "bytes": nb}
+                ridge = bw["copy_gbps"] * 1e-3 * fl / nb           # TFLOP/s the copy bandwidth allows
+                if ridge >= MFMA_BF16_PEAK_TFLOPS:
+                    row.update(bound="mfma", frac_of_mfma_peak=round(row["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4))
+                else:
+                    row.update(bound="hbm", frac_of_copy=round(row["gbps"] / bw["copy_gbps"], 4))
+                rows.append(row)
+                print("config", row, file=sys.stderr, flush=True)
+                del x, y
+            del w
+            torch.cuda.empty_cache()
+            st = gpu_state(qg, torch)
+            st.update(config=cfg, k=k, n=n)
+            states.append(st)
+    return rows, states
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -317,18 +445,22 @@ def main():
             cases.append(Int4Case(qg, torch, m, k, n, seed=(1001 * 65536) + 3 * si + mi,
                                   copies=copies_for(nb, args.regime)))
     torch.cuda.synchronize()
+    state0 = gpu_state(qg, torch)
 
-    # per-call timing (each case back to back), then the whole step
+    # per-call timing (each case back to back, every weight copy touched in each
+    # replay), then the whole step
     for c in cases:
         for _ in range(args.warmup):
             c.launch()
     per_case = []
     for c in cases:
-        us = time_us(torch, c.launch, args.steps)
-        eager = time_us(torch, c.launch, args.steps, graph=False)
+        us = time_us(torch, c.launch, args.steps, min_calls=len(c.w))
         per_case.append({"m": c.m, "k": c.k, "n": c.n, "kernel": c.kernel, "us": round(us, 3),
                          "gbps": round(c.bytes / us / 1e3, 1), "bytes": c.bytes,
-                         "eager_us": round(eager, 3)})
+                         "calls_per_replay": max(args.steps, len(c.w)),
+                         "bytes_per_replay": max(args.steps, len(c.w)) * c.bytes})
+        print("case", per_case[-1], file=sys.stderr, flush=True)
+    state1 = gpu_state(qg, torch)
     # floor: the smallest kernel the same entry point launches (k = 0 -> a zero fill of 1 x 8)
     fx = torch.empty((1, 0), dtype=torch.bfloat16, device="cuda")
     fw = torch.empty((0, 8), dtype=torch.int32, device="cuda")
@@ -336,7 +468,6 @@ def main():
     fz = torch.empty((0, 1), dtype=torch.int32, device="cuda")
     fy = torch.empty((1, 8), dtype=torch.bfloat16, device="cuda")
     floor_us = time_us(torch, lambda: qg.qgemm_int4(fx, fw, fs, fz, out=fy), args.steps)
-    copy_gbps = copy_peak_gbps(torch)
 
     def step():
         for c in cases:
@@ -349,6 +480,9 @@ def main():
     step_us = time_us(torch, step, args.steps, reps=1)
     step_bytes = sum(c.bytes for c in cases)
     value = step_bytes / step_us / 1e3
+    print("step", {"us": step_us, "gbps": value}, file=sys.stderr, flush=True)
+    bw = bandwidth_peaks(qg, torch)
+    print("bandwidth", bw, file=sys.stderr, flush=True)
 
     # dominant kernel: largest share of the step; its average launch duration is
     # the event-timed average over its calls in the per-call runs above
@@ -378,21 +512,29 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "cases": per_case,
         "timing": "HIP graph replay of back-to-back launches, HIP events on the launch stream; the step: one "
-                  "replay of exactly K steps; per-case, floor and suite figures: median of 7 replays",
+                  "replay of exactly K steps; per-case, floor, reference and config figures: median of 7 "
+                  "replays, each touching every weight copy (>= 2x the LLC per replay in the cold regime)",
         "floor_us": round(floor_us, 3),
-        "copy_gbps": round(copy_gbps, 1),
+        "copy_gbps": bw["copy_gbps"],
+        "read_gbps": bw["read_gbps"],
+        "bandwidth_probe": bw,
         "roofline": roofline,
     }
-    roofline["frac_of_copy"] = round(achieved / copy_gbps, 4)
-    # the same bytes through plain torch kernels: context for how far launch and
-    # latency, not bandwidth, bound a launch of this size
-    same = same_size_reference(torch, int(avg_bytes), args.regime, args.steps)
+    roofline["frac_of_copy"] = round(achieved / bw["copy_gbps"], 4)
+    roofline["frac_of_read"] = round(achieved / bw["read_gbps"], 4)
+    # the same bytes through the library's read and copy probes: how far launch
+    # and latency, not bandwidth, bound a launch of this size
+    same = same_size_reference(qg, torch, int(avg_bytes), args.regime, args.steps)
     out["same_size_reference"] = same
     roofline["time_vs_same_size_copy"] = round(avg_us / same["copy_us"], 3)
     roofline["time_vs_same_size_read"] = round(avg_us / same["read_us"], 3)
     # the MFMA-bound denominators beside the datasheet peak: a register-only
     # bf16 MFMA loop and the shader clock it runs at
     out["mfma_probe"] = mfma_probe(qg, torch)
+    # the m >= 512 TFLOP/s and the large-weight GB/s halves of the metric
+    rows, states = time_configs(qg, torch, args, bw)
+    out["configs"] = rows
+    out["gpu_state"] = [dict(state0, at="start"), dict(state1, at="after the small-M cases")] + states
     # context only (another codec on another GPU, so no vs_baseline): the fused
     # small-M kernel times the GPTQModel NF12 pull request reports on an R9700
     # (gfx1201) for the same shapes, beside this path's per-call times
@@ -424,7 +566,7 @@ def run_suite(qg, torch, args, path):
             c = Int4Case(qg, torch, m, k, n, seed, copies_for(int4_bytes(0, k, n), args.regime))
             for _ in range(3):
                 c.launch()
-            us = time_us(torch, c.launch, iters)
+            us = time_us(torch, c.launch, iters, min_calls=len(c.w))
             rows.append({"kind": "int4", "m": m, "k": k, "n": n, "kernel": c.kernel, "us": us,
                          "gbps": c.bytes / us / 1e3, "tflops": c.flops / us / 1e6,
                          "mfma_frac": c.flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS})
@@ -438,7 +580,7 @@ def run_suite(qg, torch, args, path):
                          zeros=False)
             for _ in range(3):
                 c.launch()
-            us = time_us(torch, c.launch, iters)
+            us = time_us(torch, c.launch, iters, min_calls=len(c.w))
             rows.append({"kind": "int4_nozero", "m": m, "k": k, "n": n, "kernel": c.kernel, "us": us,
                          "gbps": c.bytes / us / 1e3, "tflops": c.flops / us / 1e6,
                          "mfma_frac": c.flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS})
@@ -474,7 +616,7 @@ def run_suite(qg, torch, args, path):
 
             for _ in range(3):
                 launch()
-            us = time_us(torch, launch, iters)
+            us = time_us(torch, launch, iters, min_calls=len(c.w))
             nbytes = c.bytes + 2 * 16 * (k + n)
             rows.append({"kind": "int4_lora", "m": m, "k": k, "n": n, "kernel": c.kernel, "us": us,
                          "gbps": nbytes / us / 1e3, "tflops": c.flops / us / 1e6,

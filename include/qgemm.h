@@ -188,7 +188,12 @@ int32_t qgemm_int4_describe(int64_t m, int64_t n, int64_t k, int32_t path, int64
 
 /*
  * qgemm_int4_dequant -- the dequantised weights themselves, for a bit-exact
- * check of the decode every int4 path shares (same storage as qgemm_int4):
+ * check of the decode every int4 path shares (same storage as qgemm_int4).
+ * GPTQModel #3645, "What changed" and "Accuracy": the codec decodes to exact
+ * values that the matmul then accumulates in FP32; for GPTQ int4 with fp16
+ * scales (mi50grad README, "Model": GPTQ-Int4, group size 128) the exact
+ * decoded value is the fp32 product below (4-bit difference times an 11-bit
+ * significand: at most 15 significant bits, so no rounding):
  *
  *   w[i][j] = (float)(q[i][j] - z[i/128][j]) * s[i/128][j],  fp32 [k][n], n-contiguous.
  *
@@ -256,6 +261,28 @@ int32_t gemm_dense_batched(int32_t layout, int32_t dtype, int64_t batch, int64_t
  * QG_ERR_ALIGN, QG_ERR_HIP.
  */
 int32_t qg_probe_mfma_bf16(int64_t blocks, int32_t iters, uint64_t* clocks, void* stream);
+
+/*
+ * Measurement probes (not products): the bandwidth denominators.  The BC-250
+ * tuned-GEMM post ("Checking the hardware first") measures a large copy and a
+ * multi-stream add before tuning; the int4 paths at m <= 16 are judged against
+ * a measured copy of this kind, and against a read-only stream because they
+ * mostly read.
+ *
+ * qg_probe_copy: dst[0 .. bytes) = src[0 .. bytes) with 16-byte lane loads and
+ *   stores (device buffers, 16-byte aligned, must not overlap).
+ * qg_probe_read: reads src[0 .. bytes) with 16-byte lane loads and folds it by
+ *   XOR; the device word *sink (4-byte aligned) is written only when a
+ *   thread's fold equals `key`, so the caller chooses a key and treats *sink
+ *   as scratch.
+ * bytes % 16 == 0, 0 <= bytes; blocks: workgroups of 256 threads, 1..65536,
+ * or 0 for one loop trip of four 16-byte chunks per thread (at most 4096
+ * workgroups; larger sizes loop over the grid).  Errors: QG_ERR_NULL,
+ * QG_ERR_SHAPE, QG_ERR_ALIGN, QG_ERR_HIP.
+ */
+int32_t qg_probe_copy(const void* src, void* dst, int64_t bytes, int64_t blocks, void* stream);
+int32_t qg_probe_read(const void* src, int64_t bytes, int64_t blocks, uint32_t key, uint32_t* sink,
+                      void* stream);
 
 #ifdef __cplusplus
 }

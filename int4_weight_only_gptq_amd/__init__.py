@@ -13,7 +13,7 @@ import os
 
 __all__ = ["load", "lib_path", "QGemmError", "qgemm_int4", "qgemm_int4_lora", "qgemm_int4_dequant", "gemm_dense",
            "gemm_dense_batched", "describe_int4",
-           "workspace_size",
+           "workspace_size", "probe_mfma_bf16", "probe_copy", "probe_read",
            "abi_version", "PATHS", "LAYOUTS"]
 
 _LIB_NAME = "libqgemm_gfx950.so"
@@ -78,6 +78,10 @@ def load():
                                        i64, vp]
     lib.qg_probe_mfma_bf16.restype = i32
     lib.qg_probe_mfma_bf16.argtypes = [i64, i32, vp, vp]
+    lib.qg_probe_copy.restype = i32
+    lib.qg_probe_copy.argtypes = [vp, vp, i64, i64, vp]
+    lib.qg_probe_read.restype = i32
+    lib.qg_probe_read.argtypes = [vp, i64, i64, ctypes.c_uint32, vp, vp]
     _lib = lib
     return lib
 
@@ -92,6 +96,18 @@ def _stream(t, stream):
     if stream is not None:
         return stream if isinstance(stream, int) else stream.cuda_stream
     return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _torch_stream(device, stream):
+    """The launch stream as a torch stream object (the caller's, torch's current
+    one, or a wrapper of a raw hipStream_t handle)."""
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream, device=device)
+    return stream
 
 
 def _ld(t) -> int:
@@ -116,16 +132,23 @@ def workspace_size(m: int, n: int, k: int, path: str = "auto") -> int:
     return size
 
 
-def _workspace(device, stream_handle, nbytes):
-    """A zero-filled scratch tensor per (device, stream), grown on demand."""
+def _workspace(device, stream, nbytes):
+    """A zero-filled scratch tensor per (device, launch stream), grown on demand.
+
+    It is allocated and zero-filled on the launch stream itself, so the fill is
+    ordered before the kernels that read its counters, and the caching allocator
+    hands a replaced buffer to later allocations on that stream only, after the
+    kernels already queued there."""
     import torch
 
     if nbytes <= 0:
         return None
-    key = (device.index, stream_handle)
+    ts = _torch_stream(device, stream)
+    key = (device.index, ts.cuda_stream)
     t = _workspaces.get(key)
     if t is None or t.numel() < nbytes:
-        t = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(ts):
+            t = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _workspaces[key] = t
     return t
 
@@ -151,7 +174,7 @@ def qgemm_int4(x, qweight, scales, qzeros, out=None, group_size: int = 128, path
         out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
     sh = _stream(x, stream)
     if workspace is None:
-        workspace = _workspace(x.device, sh, workspace_size(m, n, k, path))
+        workspace = _workspace(x.device, stream, workspace_size(m, n, k, path))
     if workspace is None or workspace is False:
         wptr, wbytes = None, 0
     else:
@@ -188,7 +211,7 @@ def qgemm_int4_lora(x, qweight, scales, qzeros, lora_a, lora_b, lora_scale: floa
         size = lib.qgemm_int4_lora_workspace_size(m, n, k, PATHS[path])
         if size < 0:
             raise QGemmError(-size, "qgemm_int4_lora_workspace_size")
-        workspace = _workspace(x.device, sh, size)
+        workspace = _workspace(x.device, stream, size)
     wptr = None if workspace is None else workspace.data_ptr()
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.qgemm_int4_lora(x.data_ptr(), _ld(x), qweight.data_ptr(), scales.data_ptr(), _ptr(qzeros),
@@ -304,3 +327,28 @@ def probe_mfma_bf16(blocks: int, iters: int, clocks=None, stream=None):
     st = lib.qg_probe_mfma_bf16(blocks, iters, clocks.data_ptr(), _stream(clocks, stream))
     _check(st, "qg_probe_mfma_bf16")
     return clocks
+
+
+def probe_copy(src, dst, nbytes=None, blocks: int = 0, stream=None):
+    """16-byte lane copy of the first nbytes (default: all) of src into dst
+    (measurement probe; both device tensors, 16-byte aligned)."""
+    lib = load()
+    if nbytes is None:
+        nbytes = src.numel() * src.element_size()
+    if nbytes > min(src.numel() * src.element_size(), dst.numel() * dst.element_size()):
+        raise ValueError("nbytes exceeds a buffer")
+    _check(lib.qg_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, blocks, _stream(src, stream)),
+           "qg_probe_copy")
+
+
+def probe_read(src, sink, nbytes=None, blocks: int = 0, key: int = 0x9E3779B9, stream=None):
+    """16-byte lane read-only stream over the first nbytes (default: all) of src
+    (measurement probe); sink is a device int32 tensor written only when a
+    thread's XOR fold equals key."""
+    lib = load()
+    if nbytes is None:
+        nbytes = src.numel() * src.element_size()
+    if nbytes > src.numel() * src.element_size():
+        raise ValueError("nbytes exceeds the buffer")
+    _check(lib.qg_probe_read(src.data_ptr(), nbytes, blocks, key, sink.data_ptr(), _stream(src, stream)),
+           "qg_probe_read")

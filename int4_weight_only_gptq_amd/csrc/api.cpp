@@ -269,6 +269,23 @@ int32_t gemm_dense_batched(int32_t layout, int32_t dtype, int64_t batch, int64_t
                    stream);
 }
 
+int32_t qg_probe_copy(const void* src, void* dst, int64_t bytes, int64_t blocks, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0 || blocks < 0 || blocks > 65536) return QG_ERR_SHAPE;
+  if (bytes == 0) return QG_OK;
+  if (!src || !dst) return QG_ERR_NULL;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return QG_ERR_ALIGN;
+  return hip_status(qg::launch_copy_probe(src, dst, bytes, blocks, (hipStream_t)stream));
+}
+
+int32_t qg_probe_read(const void* src, int64_t bytes, int64_t blocks, uint32_t key, uint32_t* sink,
+                      void* stream) {
+  if (bytes < 0 || bytes % 16 != 0 || blocks < 0 || blocks > 65536) return QG_ERR_SHAPE;
+  if (bytes == 0) return QG_OK;
+  if (!src || !sink) return QG_ERR_NULL;
+  if (!aligned(src, 16) || !aligned(sink, 4)) return QG_ERR_ALIGN;
+  return hip_status(qg::launch_read_probe(src, bytes, blocks, key, sink, (hipStream_t)stream));
+}
+
 int32_t qg_probe_mfma_bf16(int64_t blocks, int32_t iters, uint64_t* clocks, void* stream) {
   if (!clocks) return QG_ERR_NULL;
   if (blocks < 1 || blocks > 65536 || iters < 1) return QG_ERR_SHAPE;

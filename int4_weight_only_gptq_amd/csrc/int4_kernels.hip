@@ -1113,6 +1113,9 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes,
   p.ksplit = (int)ks;
   p.gwg = (int)gwg;
   p.ws_bytes = need;
+  // no more waves than groups in a slice: a wave without a group would still
+  // load one and widen the partial plane
+  if (gwg >= 1 && p.waves > gwg) p.waves = (int)gwg;
   const int64_t items = (int64_t)p.nstrips * p.ksplit;
   p.items_per_xcd = (int)((items + 7) / 8);
   p.blocks = (int64_t)p.items_per_xcd * 8;

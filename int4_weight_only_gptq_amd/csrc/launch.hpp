@@ -86,5 +86,9 @@ hipError_t launch_dense(const DenseArgs& a, hipStream_t stream);
 
 // register-resident bf16 MFMA loop with clock stamps (measurement probe)
 hipError_t launch_mfma_probe(int64_t blocks, int iters, uint64_t* clocks, hipStream_t stream);
+// 16-byte copy and read-only streams over `bytes` (measurement probes); blocks 0 = automatic
+hipError_t launch_copy_probe(const void* src, void* dst, int64_t bytes, int64_t blocks, hipStream_t stream);
+hipError_t launch_read_probe(const void* src, int64_t bytes, int64_t blocks, uint32_t key, uint32_t* sink,
+                             hipStream_t stream);
 
 }  // namespace qg

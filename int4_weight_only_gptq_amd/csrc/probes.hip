@@ -1,5 +1,5 @@
 // Measurement probes: the sustained bf16 MFMA rate and the shader clock under
-// that load.  The BC-250 tuned-GEMM post ("Checking the hardware first") checks
+// that load, and the HBM copy and read bandwidth.  The BC-250 tuned-GEMM post ("Checking the hardware first") checks
 // the machine before tuning: it measures the real clock by comparing a cycle
 // counter with a constant-rate counter, and the peak against a register-only
 // loop.  These probes give the same two denominators on gfx950; the library's
@@ -62,6 +62,65 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, uint64_t* __
 
 hipError_t launch_mfma_probe(int64_t blocks, int iters, uint64_t* clocks, hipStream_t stream) {
   mfma_probe_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(iters, clocks);
+  return hipGetLastError();
+}
+
+// Bandwidth denominators (the same post measures a large copy and a
+// multi-stream add before tuning): a copy and a read-only stream of 16-byte
+// lane accesses.  Thread t of a grid of T threads handles the 16-byte chunks
+// t, t + T, t + 2T, ...; four of them per loop trip, all loads issued before
+// the first use.  The read folds its chunks with XOR and stores only when the
+// result equals `key` (never, in practice), which keeps every load live.
+__global__ __launch_bounds__(256) void copy16_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                     int64_t chunks) {
+  const int64_t T = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * T < chunks; i += 4 * T) {
+    const u32x4 a = src[i], b = src[i + T], c = src[i + 2 * T], d = src[i + 3 * T];
+    dst[i] = a;
+    dst[i + T] = b;
+    dst[i + 2 * T] = c;
+    dst[i + 3 * T] = d;
+  }
+  for (; i < chunks; i += T) dst[i] = src[i];
+}
+
+__global__ __launch_bounds__(256) void read16_kernel(const u32x4* __restrict__ src, int64_t chunks, uint32_t key,
+                                                     uint32_t* __restrict__ sink) {
+  const int64_t T = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (; i + 3 * T < chunks; i += 4 * T) {
+    const u32x4 a = src[i], b = src[i + T], c = src[i + 2 * T], d = src[i + 3 * T];
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < chunks; i += T) acc ^= src[i];
+  const uint32_t v = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  if (v == key) sink[0] = v;
+}
+
+// Workgroups of a probe launch: one loop trip (4 chunks per thread) over the
+// bytes, at most 16 workgroups per CU (the rest by the grid stride).
+static int64_t stream_blocks(int64_t chunks, int64_t blocks) {
+  if (blocks > 0) return blocks;
+  int64_t b = (chunks + 1023) / 1024;
+  return b < 1 ? 1 : (b > 4096 ? 4096 : b);
+}
+
+hipError_t launch_copy_probe(const void* src, void* dst, int64_t bytes, int64_t blocks, hipStream_t stream) {
+  const int64_t chunks = bytes / 16;
+  if (chunks == 0) return hipSuccess;
+  copy16_kernel<<<dim3((unsigned)stream_blocks(chunks, blocks)), dim3(256), 0, stream>>>(
+      (const u32x4*)src, (u32x4*)dst, chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const void* src, int64_t bytes, int64_t blocks, uint32_t key, uint32_t* sink,
+                             hipStream_t stream) {
+  const int64_t chunks = bytes / 16;
+  if (chunks == 0) return hipSuccess;
+  read16_kernel<<<dim3((unsigned)stream_blocks(chunks, blocks)), dim3(256), 0, stream>>>((const u32x4*)src,
+                                                                                          chunks, key, sink);
   return hipGetLastError();
 }
 

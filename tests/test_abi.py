@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "qg_abi_version", "qg_status_str", "qg_last_hip_error", "qgemm_int4", "qgemm_int4_path",
         "qgemm_int4_workspace_size", "qgemm_int4_describe", "qgemm_int4_dequant", "gemm_dense",
-        "gemm_dense_batched", "qgemm_int4_lora", "qgemm_int4_lora_workspace_size", "qg_probe_mfma_bf16"])
+        "gemm_dense_batched", "qgemm_int4_lora", "qgemm_int4_lora_workspace_size", "qg_probe_mfma_bf16",
+        "qg_probe_copy", "qg_probe_read"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -134,6 +135,19 @@ def test_probe_rejects_invalid_arguments(lib):
     assert lib.qg_probe_mfma_bf16(65537, 10, buf, None) == 2                  # too many
     assert lib.qg_probe_mfma_bf16(4, 0, buf, None) == 2                       # no iterations
     assert lib.qg_probe_mfma_bf16(4, 10, ctypes.c_void_p(0x100004), None) == 3  # misaligned
+
+
+def test_bandwidth_probes_reject_invalid_arguments(lib):
+    buf = 0x100000
+    assert lib.qg_probe_copy(buf, buf + 4096, 100, 0, None) == SHAPE           # bytes % 16
+    assert lib.qg_probe_copy(buf, buf + 4096, -16, 0, None) == SHAPE
+    assert lib.qg_probe_copy(buf, buf + 4096, 64, 65537, None) == SHAPE        # too many workgroups
+    assert lib.qg_probe_copy(None, buf, 64, 0, None) == NULL
+    assert lib.qg_probe_copy(buf + 8, buf + 4096, 64, 0, None) == ALIGN
+    assert lib.qg_probe_copy(None, None, 0, 0, None) == OK                     # nothing to do
+    assert lib.qg_probe_read(buf, 64, 0, 1, None, None) == NULL                # NULL sink
+    assert lib.qg_probe_read(buf, 64, -1, 1, buf + 4096, None) == SHAPE
+    assert lib.qg_probe_read(buf, 64, 0, 1, buf + 4098, None) == ALIGN
 
 
 def test_dequant_rejects_invalid_arguments(lib):
@@ -312,5 +326,8 @@ def test_planned_launches_fit_the_hardware():
                     assert p["ksplit"] == 1, what           # no workspace: no k split
                 if name.startswith("skinny"):
                     assert p["grid"] % 8 == 0, what          # whole XCD rounds
+                    if int(name.split("<")[1].split(",")[0]) > 16:
+                        assert p["block"] <= 512, what       # __launch_bounds__(512) above 16 tokens
+                    assert p["block"] // 64 <= p["groups"], what   # every wave has a group
                     if m > 32:   # row tiles in one pass, or two at long k
                         assert m <= 64 and (p["grid"] <= 256 or (m <= 48 and k > 8192 and p["grid"] <= 512)), what

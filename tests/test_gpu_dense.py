@@ -59,9 +59,12 @@ def test_shapes_match_oracle(gpu_lib, layout, dtype):
 
 # shapes for the pipelined kernel (K % 64 == 0): ragged M and N edges, all four tile
 # sizes (2050 x 5624 takes 256 x 256 tiles: one round of 198 against two of 396;
-# 1000 x 2000 takes 64 x 128 tiles: one round of 256), and two row bands
+# 1000 x 2000 takes 64 x 128 tiles: one round of 256), two row bands, and the
+# 128 x 128 tile over a long k (2048 x 2048 x 5632, the 2048-token forward and
+# input-gradient products: 256 tiles in one round)
 PIPE_SHAPES = [(128, 128, 64), (200, 264, 128), (1000, 136, 192), (2000, 2600, 64), (2050, 5624, 192),
-               (1000, 2000, 128), (3000, 5632, 128)]   # the last in two row bands (2816 + 184 rows)
+               (1000, 2000, 128), (3000, 5632, 128),   # the last in two row bands (2816 + 184 rows)
+               (2048, 2048, 5632)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
@@ -179,9 +182,9 @@ def test_k_zero_writes_zeros(gpu_lib):
 
 
 # ----------------------------------------------------------------------------
-# the training trio at full size (t = 1024 and 4096), sampled outputs
+# the training trio at full size (t = 1024, 2048 and 4096), sampled outputs
 # ----------------------------------------------------------------------------
-FULL = [c for c in dense_cases(3) if c["t"] in (1024, 4096)]
+FULL = [c for c in dense_cases(3) if c["t"] in (1024, 2048, 4096)]
 
 
 @pytest.mark.parametrize("case", FULL, ids=["%s-%s-%s-t%d-w%dx%d" % (c["role"], c["layout"], c["dtype"], c["t"], *c["w"]) for c in FULL])
@@ -331,7 +334,7 @@ def test_fp32_batched_strided(gpu_lib, layout):
     assert torch.all(big[:, :, :4] == 5.0)
 
 
-FP32_FULL = [c for c in dense_cases(3, with_lora=False) if c["dtype"] == "bf16" and c["t"] in (1024, 4096)]
+FP32_FULL = [c for c in dense_cases(3, with_lora=False) if c["dtype"] == "bf16" and c["t"] in (1024, 2048, 4096)]
 
 
 @pytest.mark.parametrize("case", FP32_FULL,

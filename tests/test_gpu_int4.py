@@ -258,6 +258,33 @@ def test_shared_workspace_across_shapes_and_counters_reset(gpu_lib):
         assert int(torch.count_nonzero(ws[:65536])) == 0
 
 
+def test_first_split_call_on_a_side_stream(gpu_lib):
+    # the binding's cached workspace for a stream it has not seen is created and
+    # zero-filled on that stream, ordered before the kernels that read its
+    # counters; the first call on a fresh, non-current stream takes the k split
+    import torch
+
+    m, k, n = 8, 16384, 520
+    assert "ksplit=1 " not in gpu_lib.describe_int4(m, n, k) + " "
+    d = int4_inputs(m, k, n, seed=34)
+    t = upload_int4(d)
+    ref = oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], m, k, n)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    assert side.cuda_stream != torch.cuda.current_stream().cuda_stream
+    outs = [torch.empty((m, n), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    for o in outs:
+        gpu_lib.qgemm_int4(t["x"], t["qweight"], t["scales"], t["qzeros"], out=o, stream=side)
+    side.synchronize()
+    for o in outs:
+        assert_accepted(host_u16(o), ref, ("side-stream", m, k, n))
+    # also through a raw stream handle (the workspace of that stream is reused)
+    o = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    gpu_lib.qgemm_int4(t["x"], t["qweight"], t["scales"], t["qzeros"], out=o, stream=side.cuda_stream)
+    side.synchronize()
+    assert np.array_equal(host_u16(o), host_u16(outs[0]))
+
+
 def test_deterministic(gpu_lib):
     m, k, n = 8, 2048, 1040
     d = int4_inputs(m, k, n, seed=35)

@@ -27,3 +27,25 @@ def test_mfma_probe_stamps_and_rate(gpu_lib):
     say("probe", {"sclk_mhz": float(mhz), "tflops": tflops})
     assert 300.0 < mhz < 3500.0                 # a shader clock, in MHz
     assert 0.0 < tflops < 2.6e3                 # never above the datasheet bf16 peak (2.5 PFLOP/s) + 4%
+
+
+def test_copy_and_read_probes(gpu_lib):
+    import torch
+
+    for nbytes, blocks in ((16, 0), (4096 + 48, 0), (3 << 20, 0), (3 << 20, 7), (64 << 20, 0)):
+        say("bandwidth probe", nbytes, blocks)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(nbytes + blocks)
+        src = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4 + 8,), generator=g, dtype=torch.int32,
+                            device="cuda")
+        dst = torch.full_like(src, 7)
+        gpu_lib.probe_copy(src, dst, nbytes, blocks)
+        torch.cuda.synchronize()
+        q = nbytes // 4
+        assert torch.equal(dst[:q], src[:q])
+        assert torch.all(dst[q:] == 7)                      # nothing past the bytes
+        sink = torch.full((4,), 5, dtype=torch.int32, device="cuda")
+        gpu_lib.probe_read(src, sink, nbytes, blocks, key=0x12345677)
+        torch.cuda.synchronize()
+        got = sink.cpu().numpy().view(np.uint32)
+        assert got[0] in (5, 0x12345677) and np.all(got[1:] == 5)
