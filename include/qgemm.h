@@ -46,6 +46,8 @@ extern "C" {
 #define QG_ERR_LAYOUT 5      /* unknown layout code                                */
 #define QG_ERR_UNSUPPORTED 6 /* group size != 128, or a forced path that cannot take m */
 #define QG_ERR_HIP 7         /* the HIP runtime rejected a launch                  */
+#define QG_ERR_SCRATCH 8     /* qgemm_int4_noalloc: the problem needs more scratch
+                                than QG_NOALLOC_SCRATCH_BYTES                        */
 
 /* dtype codes of gemm_dense */
 #define QG_BF16 0
@@ -157,6 +159,29 @@ int32_t qgemm_int4_lora(const void* x, int64_t ldx, const uint32_t* qweight, con
 
 /* Workspace bytes for qgemm_int4_lora (U plus what the path can use); < 0: -error. */
 int64_t qgemm_int4_lora_workspace_size(int64_t m, int64_t n, int64_t k, int32_t path);
+
+/*
+ * qgemm_int4_noalloc -- qgemm_int4 for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and path choice as qgemm_int4
+ * called with a workspace of qgemm_int4_workspace_size(m, n, k, QG_PATH_AUTO)
+ * bytes, but the workspace is a static device buffer of the library
+ * (QG_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends): the call
+ * allocates and frees nothing.
+ *
+ * The first call on a device looks the buffer up and clears its split
+ * counters with a small fill kernel on `stream`; every call leaves them zero
+ * again.  All calls on one GPU share the buffer: calls that overlap on one
+ * GPU (other streams or host threads) race and must be serialised by the
+ * caller.  A problem whose workspace would exceed the buffer (for the MFMA
+ * path, roughly m * k * 2 bytes of prepared activations: e.g. m = 2048,
+ * k = 25600) returns QG_ERR_SCRATCH and launches nothing.  Other errors as
+ * qgemm_int4.
+ */
+#define QG_NOALLOC_SCRATCH_BYTES 33554432 /* 32 MiB */
+int32_t qgemm_int4_noalloc(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
+                           const uint32_t* qzeros, void* y, int64_t ldy, int64_t m, int64_t n, int64_t k,
+                           int32_t group_size, void* stream);
 
 /*
  * qgemm_int4_path -- qgemm_int4 with the kernel path forced (QG_PATH_* code),

@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["load", "lib_path", "QGemmError", "qgemm_int4", "qgemm_int4_lora", "qgemm_int4_dequant", "gemm_dense",
+__all__ = ["load", "lib_path", "QGemmError", "qgemm_int4", "qgemm_int4_noalloc", "qgemm_int4_lora", "qgemm_int4_dequant", "gemm_dense",
            "gemm_dense_batched", "describe_int4",
            "workspace_size", "probe_mfma_bf16", "probe_copy", "probe_read",
            "abi_version", "PATHS", "LAYOUTS"]
@@ -58,6 +58,8 @@ def load():
     int4_args = [vp, i64, vp, vp, vp, vp, i64, i64, i64, i64, i32]
     lib.qgemm_int4.restype = i32
     lib.qgemm_int4.argtypes = int4_args + [vp, i64, vp]
+    lib.qgemm_int4_noalloc.restype = i32
+    lib.qgemm_int4_noalloc.argtypes = int4_args + [vp]
     lib.qgemm_int4_path.restype = i32
     lib.qgemm_int4_path.argtypes = int4_args + [i32, vp, i64, vp]
     lib.qgemm_int4_workspace_size.restype = i64
@@ -183,6 +185,23 @@ def qgemm_int4(x, qweight, scales, qzeros, out=None, group_size: int = 128, path
                              _ptr(qzeros), out.data_ptr(), _ld(out), m, n, k, group_size,
                              PATHS[path], wptr, wbytes, sh)
     _check(st, "qgemm_int4")
+    return out
+
+
+def qgemm_int4_noalloc(x, qweight, scales, qzeros, out, group_size: int = 128, stream=None):
+    """qgemm_int4 through the entry point that allocates nothing: its workspace
+    is the library's static per-GPU scratch (calls on one GPU must not overlap).
+    ``out`` (bf16 [m][n]) is required, so this wrapper allocates nothing either."""
+    import torch
+
+    lib = load()
+    m, k = x.shape
+    n = qweight.shape[1]
+    if x.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise TypeError("x and out must be bfloat16")
+    st = lib.qgemm_int4_noalloc(x.data_ptr(), _ld(x), qweight.data_ptr(), scales.data_ptr(), _ptr(qzeros),
+                                out.data_ptr(), _ld(out), m, n, k, group_size, _stream(x, stream))
+    _check(st, "qgemm_int4_noalloc")
     return out
 
 

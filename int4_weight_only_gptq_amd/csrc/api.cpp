@@ -5,7 +5,15 @@
 #include <hip/hip_runtime.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "launch.hpp"
+
+// Scratch of qgemm_int4_noalloc: one copy per GPU the library runs on, held
+// until the process ends.  Host code never passes this name to a kernel: on
+// the host it is a stand-in, not a device address; the device address comes
+// from hipGetSymbolAddress (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[QG_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -129,6 +137,33 @@ int32_t run_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint
   }
 }
 
+// Device address of `scratch` on the current device, looked up once per device
+// with that device current; the split counters (its first 64 KiB) are cleared
+// then with a fill kernel on `stream`, ordered before the first product.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int32_t noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return QG_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (p == nullptr || !aligned(p, 256)) return QG_ERR_HIP;
+    const int64_t halves = qg::kSplitCounterBytes / 2;
+    e = qg::launch_zero16((uint16_t*)p, 1, halves, halves, stream);
+    if (e != hipSuccess) return hip_status(e);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -145,6 +180,7 @@ const char* qg_status_str(int32_t status) {
     case QG_ERR_LAYOUT: return "unknown layout";
     case QG_ERR_UNSUPPORTED: return "unsupported group size or path for this m";
     case QG_ERR_HIP: return "HIP launch error";
+    case QG_ERR_SCRATCH: return "the problem needs more scratch than the static buffer holds";
     default: return "unknown status";
   }
 }
@@ -156,6 +192,22 @@ int32_t qgemm_int4(const void* x, int64_t ldx, const uint32_t* qweight, const ui
                    int32_t group_size, void* workspace, int64_t workspace_bytes, void* stream) {
   return run_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size, QG_PATH_AUTO,
                   workspace, workspace_bytes, stream);
+}
+
+int32_t qgemm_int4_noalloc(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
+                           const uint32_t* qzeros, void* y, int64_t ldy, int64_t m, int64_t n, int64_t k,
+                           int32_t group_size, void* stream) {
+  int32_t st = check_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size);
+  if (st != QG_OK) return st;
+  if (m == 0 || n == 0 || k == 0) return run_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size,
+                                                  QG_PATH_AUTO, nullptr, 0, stream);
+  const int64_t need = qg::workspace_int4(m, n, k, resolve_path(m, n, k, QG_PATH_AUTO));
+  if (need > (int64_t)QG_NOALLOC_SCRATCH_BYTES) return QG_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = noalloc_scratch((hipStream_t)stream, &ws);
+  if (st != QG_OK) return st;
+  return run_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size, QG_PATH_AUTO, ws, need,
+                  stream);
 }
 
 int32_t qgemm_int4_path(const void* x, int64_t ldx, const uint32_t* qweight,

@@ -144,7 +144,7 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // Blocks are numbered so that consecutive strips, and all k-slices of a
 // strip, land on the same XCD (block b runs on XCD b % 8).
 // ---------------------------------------------------------------------------
-constexpr int64_t kTicketBytes = 64 << 10;   // counters of up to 16384 strips
+constexpr int64_t kTicketBytes = kSplitCounterBytes;   // counters of up to 16384 strips
 constexpr int SK_MAX_SPLIT = 16;              // k-slices per strip at most
 
 // MFMA row tiles of 16 tokens: one up to 16 tokens, two up to 32, ... four up to 64

@@ -49,6 +49,10 @@ struct SkinnyPlan {
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes, bool dot);
 int64_t split_workspace_bytes(int64_t nstrips, int64_t ksplit, int64_t m, int cpl);
 
+// Bytes at the front of an int4 workspace that hold the split counters (zero
+// between calls).
+constexpr int64_t kSplitCounterBytes = 64 << 10;
+
 // ws may be NULL (then no k split); ws_bytes is its size.
 hipError_t launch_gemv_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream);
 hipError_t launch_fused_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream);

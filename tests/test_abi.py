@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
         "qg_abi_version", "qg_status_str", "qg_last_hip_error", "qgemm_int4", "qgemm_int4_path",
         "qgemm_int4_workspace_size", "qgemm_int4_describe", "qgemm_int4_dequant", "gemm_dense",
         "gemm_dense_batched", "qgemm_int4_lora", "qgemm_int4_lora_workspace_size", "qg_probe_mfma_bf16",
-        "qg_probe_copy", "qg_probe_read"])
+        "qg_probe_copy", "qg_probe_read", "qgemm_int4_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -59,8 +59,8 @@ def test_header_codes_match_binding():
 
 def test_version_and_status_strings(lib):
     assert lib.qg_abi_version() == defines("QG_ABI")["QG_ABI_VERSION"]
-    for code in range(8):
-        assert lib.qg_status_str(code)
+    for code in range(9):
+        assert lib.qg_status_str(code) and lib.qg_status_str(code) != b"unknown status"
     assert lib.qg_status_str(99) == b"unknown status"
 
 
@@ -120,6 +120,20 @@ def test_int4_lora_workspace_size(lib):
         blocks = (m + 15) // 16
         assert up(base) + up(64 * m) + 1024 * blocks <= got <= up(base) + up(64 * m) + 1024 * blocks * (k // 512)
     assert lib.qgemm_int4_lora_workspace_size(1, 64, 100, 0) < 0
+
+
+def test_noalloc_validates_before_touching_the_device(lib):
+    # the same argument checks as qgemm_int4, and problems whose workspace exceeds
+    # the static scratch are rejected -- all before any HIP call
+    f = lib.qgemm_int4_noalloc
+    assert f(A16, 256, A16, A16, A16, A16, 64, 1, 64, 200, 128, None) == SHAPE
+    assert f(0, 256, A16, A16, A16, A16, 64, 1, 64, 256, 128, None) == NULL
+    assert f(MIS, 256, A16, A16, A16, A16, 64, 1, 64, 256, 128, None) == ALIGN
+    assert f(A16, 256, A16, A16, A16, A16, 64, 1, 64, 256, 64, None) == UNSUP
+    need = lib.qgemm_int4_workspace_size(2048, 5120, 25600, 0)
+    assert need > defines("QG_NOALLOC")["QG_NOALLOC_SCRATCH_BYTES"] == 32 << 20
+    assert f(A16, 25600, A16, A16, A16, A16, 5120, 2048, 5120, 25600, 128, None) == 8   # QG_ERR_SCRATCH
+    assert f(0, 0, 0, 0, 0, 0, 0, 0, 64, 256, 128, None) == OK                          # m == 0: no-op
 
 
 def test_int4_empty_problems_are_noops(lib):
