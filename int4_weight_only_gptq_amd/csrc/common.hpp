@@ -39,6 +39,16 @@ __device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
   return v;
 }
 
+// With the mask and bias already in VGPRs (see codes_as_bf16_pairs below).
+__device__ __forceinline__ u32x4 codes_as_bf16_pairs_mb(uint32_t w, uint32_t mask, uint32_t bias) {
+  u32x4 r;
+  r[0] = (w & mask) | bias;
+  r[1] = ((w >> 4) & mask) | bias;
+  r[2] = ((w >> 8) & mask) | bias;
+  r[3] = ((w >> 12) & mask) | bias;
+  return r;
+}
+
 __device__ __forceinline__ u32x4 codes_as_bf16_pairs(uint32_t w) {
   const uint32_t mask = in_vgpr(0x000F000Fu), bias = in_vgpr(kBias128x2);
   u32x4 r;
@@ -113,6 +123,78 @@ __device__ __forceinline__ float sum_over_rows(float v) {
 // 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
+// s_waitcnt vmcnt(n) for an n that is a constant only after unrolling (the
+// builtin wants a literal): the switch folds to the one wait.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(1)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6)); break;
+    case 7: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); break;
+    case 9: __builtin_amdgcn_s_waitcnt(vmcnt_imm(9)); break;
+    case 10: __builtin_amdgcn_s_waitcnt(vmcnt_imm(10)); break;
+    case 11: __builtin_amdgcn_s_waitcnt(vmcnt_imm(11)); break;
+    case 12: __builtin_amdgcn_s_waitcnt(vmcnt_imm(12)); break;
+    case 13: __builtin_amdgcn_s_waitcnt(vmcnt_imm(13)); break;
+    case 14: __builtin_amdgcn_s_waitcnt(vmcnt_imm(14)); break;
+    case 15: __builtin_amdgcn_s_waitcnt(vmcnt_imm(15)); break;
+    case 16: __builtin_amdgcn_s_waitcnt(vmcnt_imm(16)); break;
+    case 17: __builtin_amdgcn_s_waitcnt(vmcnt_imm(17)); break;
+    case 18: __builtin_amdgcn_s_waitcnt(vmcnt_imm(18)); break;
+    case 19: __builtin_amdgcn_s_waitcnt(vmcnt_imm(19)); break;
+    case 20: __builtin_amdgcn_s_waitcnt(vmcnt_imm(20)); break;
+    case 21: __builtin_amdgcn_s_waitcnt(vmcnt_imm(21)); break;
+    case 22: __builtin_amdgcn_s_waitcnt(vmcnt_imm(22)); break;
+    case 23: __builtin_amdgcn_s_waitcnt(vmcnt_imm(23)); break;
+    case 24: __builtin_amdgcn_s_waitcnt(vmcnt_imm(24)); break;
+    case 25: __builtin_amdgcn_s_waitcnt(vmcnt_imm(25)); break;
+    case 26: __builtin_amdgcn_s_waitcnt(vmcnt_imm(26)); break;
+    case 27: __builtin_amdgcn_s_waitcnt(vmcnt_imm(27)); break;
+    case 28: __builtin_amdgcn_s_waitcnt(vmcnt_imm(28)); break;
+    case 29: __builtin_amdgcn_s_waitcnt(vmcnt_imm(29)); break;
+    case 30: __builtin_amdgcn_s_waitcnt(vmcnt_imm(30)); break;
+    case 31: __builtin_amdgcn_s_waitcnt(vmcnt_imm(31)); break;
+    case 32: __builtin_amdgcn_s_waitcnt(vmcnt_imm(32)); break;
+    case 33: __builtin_amdgcn_s_waitcnt(vmcnt_imm(33)); break;
+    case 34: __builtin_amdgcn_s_waitcnt(vmcnt_imm(34)); break;
+    case 35: __builtin_amdgcn_s_waitcnt(vmcnt_imm(35)); break;
+    case 36: __builtin_amdgcn_s_waitcnt(vmcnt_imm(36)); break;
+    case 37: __builtin_amdgcn_s_waitcnt(vmcnt_imm(37)); break;
+    case 38: __builtin_amdgcn_s_waitcnt(vmcnt_imm(38)); break;
+    case 39: __builtin_amdgcn_s_waitcnt(vmcnt_imm(39)); break;
+    case 40: __builtin_amdgcn_s_waitcnt(vmcnt_imm(40)); break;
+    case 41: __builtin_amdgcn_s_waitcnt(vmcnt_imm(41)); break;
+    case 42: __builtin_amdgcn_s_waitcnt(vmcnt_imm(42)); break;
+    case 43: __builtin_amdgcn_s_waitcnt(vmcnt_imm(43)); break;
+    case 44: __builtin_amdgcn_s_waitcnt(vmcnt_imm(44)); break;
+    case 45: __builtin_amdgcn_s_waitcnt(vmcnt_imm(45)); break;
+    case 46: __builtin_amdgcn_s_waitcnt(vmcnt_imm(46)); break;
+    case 47: __builtin_amdgcn_s_waitcnt(vmcnt_imm(47)); break;
+    case 48: __builtin_amdgcn_s_waitcnt(vmcnt_imm(48)); break;
+    case 49: __builtin_amdgcn_s_waitcnt(vmcnt_imm(49)); break;
+    case 50: __builtin_amdgcn_s_waitcnt(vmcnt_imm(50)); break;
+    case 51: __builtin_amdgcn_s_waitcnt(vmcnt_imm(51)); break;
+    case 52: __builtin_amdgcn_s_waitcnt(vmcnt_imm(52)); break;
+    case 53: __builtin_amdgcn_s_waitcnt(vmcnt_imm(53)); break;
+    case 54: __builtin_amdgcn_s_waitcnt(vmcnt_imm(54)); break;
+    case 55: __builtin_amdgcn_s_waitcnt(vmcnt_imm(55)); break;
+    case 56: __builtin_amdgcn_s_waitcnt(vmcnt_imm(56)); break;
+    case 57: __builtin_amdgcn_s_waitcnt(vmcnt_imm(57)); break;
+    case 58: __builtin_amdgcn_s_waitcnt(vmcnt_imm(58)); break;
+    case 59: __builtin_amdgcn_s_waitcnt(vmcnt_imm(59)); break;
+    case 60: __builtin_amdgcn_s_waitcnt(vmcnt_imm(60)); break;
+    case 61: __builtin_amdgcn_s_waitcnt(vmcnt_imm(61)); break;
+    case 62: __builtin_amdgcn_s_waitcnt(vmcnt_imm(62)); break;
+    case 63: __builtin_amdgcn_s_waitcnt(vmcnt_imm(63)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(63)); break;
+  }
+}
+
 // Slot of 16-byte chunk c (8 bf16 of k) of row r in a K-contiguous LDS tile of
 // 8 chunks per row: the XOR spreads the 16 rows one MFMA operand read touches
 // over distinct banks.
@@ -147,6 +229,45 @@ __device__ __forceinline__ void buffer_to_lds4(const void* base, uint32_t voff, 
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, -1, 0x00020000),
                                            (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
+#endif
+}
+
+// Loads through a raw buffer resource on a wave-uniform base (SGPRs) with a
+// 32-bit per-lane byte offset (below 4 GiB): the lane offset register can
+// serve many loads whose bases differ only in the uniform part.
+__device__ __forceinline__ u32x4 buffer_load16(const void* base, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_raw_buffer_load_b128(__builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, -1, 0x00020000),
+                                               voff, 0, 0);
+#else
+  return u32x4{0u, 0u, 0u, 0u};
+#endif
+}
+
+__device__ __forceinline__ u32x2 buffer_load8(const void* base, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_raw_buffer_load_b64(__builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, -1, 0x00020000),
+                                              voff, 0, 0);
+#else
+  return u32x2{0u, 0u};
+#endif
+}
+
+__device__ __forceinline__ uint32_t buffer_load4(const void* base, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_raw_buffer_load_b32(__builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, -1, 0x00020000),
+                                              voff, 0, 0);
+#else
+  return 0u;
+#endif
+}
+
+__device__ __forceinline__ uint32_t buffer_load2(const void* base, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_raw_buffer_load_b16(__builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, -1, 0x00020000),
+                                              voff, 0, 0);
+#else
+  return 0u;
 #endif
 }
 

@@ -580,6 +580,221 @@ __global__ __launch_bounds__(M > 16 ? 512 : 1024) void skinny_int4_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Small-M kernel with the codes staged in LDS (m <= 16, whole k per
+// workgroup).  Same work split as skinny_int4_kernel (a strip of 16 * CPL
+// columns per workgroup, wave w takes groups w, w + W, ...), but every group a
+// wave owns has its loads issued before any arithmetic: the codes go straight
+// to LDS with 16-byte lane loads (buffer_load ... lds: no registers held while
+// in flight; one instruction moves 1 KiB of a group's 16 word rows), the
+// activations and raw metadata to registers through buffer resources on
+// wave-uniform group bases (one lane-offset register serves every group).
+// Groups are then computed in issue order, each after an explicit wait for its
+// own loads (a wave's vector memory operations complete in order), so the
+// arithmetic of group j runs while groups j + 1 .. are still arriving; the
+// scheduling barriers keep the compiler from hoisting a later group's decode
+// above its wait.  A wave owns NGW = NG or NG - 1 groups (NG at compile time:
+// the activation registers and the wait counts depend on it).
+//
+// Measured (cold weights, HIP-graph replay) against skinny_int4_kernel:
+// 4096 x 4096 m = 1 / 8 / 15 5.53 / 6.66 / 8.01 -> 5.03 / 6.12 / 7.21 µs,
+// 2048 x 8192 4.98 / 5.38 / 6.27 -> 4.34 / 4.84 / 5.47 µs.  Timing copies
+// with parts switched off (4096 x 4096): without arithmetic the time hardly
+// changes (4.85 / 6.16 / 6.96 µs), without loads it is 2.9-3.1 µs, so the
+// arithmetic is hidden and the loads bound the kernel; the activation loads
+// (every strip reads all of X) add 0.3 / 1.2 / 2.3 µs over the codes alone.
+// ---------------------------------------------------------------------------
+template <int M, bool DOT, int CPL, int NGW>
+__device__ __forceinline__ void lds_strip_groups(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qweight,
+                                                 const uint16_t* __restrict__ scales, const uint32_t* zbase,
+                                                 int64_t zstride, uint32_t* codes, int n, int wave, int nw, int lane,
+                                                 uint32_t xoff, uint32_t soff, uint32_t zoff, const uint32_t (&coff)[CPL],
+                                                 int zshift, uint32_t zmask, f32x4 (&total)[CPL]) {
+  constexpr int SW = 16 * CPL;                 // strip width in columns
+  constexpr int GDW = 16 * SW;                 // dwords of codes per group
+  constexpr int LPG = CPL + 4 + 2;             // vector memory operations per group
+  static_assert(NGW * LPG <= 63, "vmcnt range");
+  const int cl = lane & 15, ks = lane >> 4;
+  const u32x4 ones = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
+  u32x4 xa[NGW][4];
+  Meta<CPL> meta[NGW];
+#pragma unroll
+  for (int j = 0; j < NGW; ++j) {
+    const int g = wave + nw * j;
+    const uint32_t* gbase = qweight + (int64_t)g * 16 * n;
+    uint32_t* lds = codes + (size_t)g * GDW;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) buffer_to_lds16(gbase, coff[i], lds + 256 * i);
+    const uint16_t* xg = x + (int64_t)g * 128;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) xa[j][s] = buffer_load16(xg, xoff + 64 * s);
+    const uint16_t* sg = scales + (int64_t)g * n;
+    if constexpr (CPL == 4) {
+      const u32x2 v = buffer_load8(sg, soff);
+      meta[j].s[0] = v[0];
+      meta[j].s[CPL == 4 ? 1 : 0] = v[1];
+    } else if constexpr (CPL == 2) {
+      meta[j].s[0] = buffer_load4(sg, soff);
+    } else {
+      meta[j].s[0] = buffer_load2(sg, soff);
+    }
+    meta[j].z = buffer_load4(zbase + (int64_t)g * zstride, zoff);
+    __builtin_amdgcn_sched_barrier(0);   // groups' loads stay in issue order
+  }
+  const uint32_t mask = in_vgpr(0x000F000Fu), bias = in_vgpr(kBias128x2);   // VGPR operands of v_and_or_b32
+#pragma unroll
+  for (int j = 0; j < NGW; ++j) {
+    // this group's loads have landed once at most the later groups' are outstanding
+    wait_vmcnt((NGW - 1 - j) * LPG);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t* lds = codes + (size_t)(wave + nw * j) * GDW;
+    uint32_t w[4][CPL];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t* p = lds + (4 * s + ks) * SW + CPL * cl;
+      if constexpr (CPL == 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        w[s][0] = v[0]; w[s][1] = v[1]; w[s][2] = v[2]; w[s][3] = v[3];
+      } else if constexpr (CPL == 2) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+        w[s][0] = v[0]; w[s][1] = v[1];
+      } else {
+        w[s][0] = *p;
+      }
+    }
+    float sc[CPL], bz[CPL];
+    decode_meta<CPL>(meta[j], zshift, zmask, sc, bz);
+    if constexpr (DOT) {
+      float d[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) d[c] = 0.f;
+      float xs = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 a = x_pairs_permuted(xa[j][s]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) xs = dot2_bf16(a[t], kOnesBf16x2, xs);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const u32x4 bq = codes_as_bf16_pairs_mb(w[s][c], mask, bias);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) d[c] = dot2_bf16(bq[t], a[t], d[c]);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) total[c][0] += sc[c] * (d[c] - bz[c] * xs);
+    } else {
+      constexpr int VMAX = M < 4 ? M : 4;
+      f32x4 acc[CPL], xsum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 a = x_pairs_permuted(xa[j][s]);
+        xsum = mfma16_bf16(a, ones, xsum);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[c] = mfma16_bf16(a, codes_as_bf16_pairs_mb(w[s][c], mask, bias), acc[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int v = 0; v < VMAX; ++v) total[c][v] += sc[c] * (acc[c][v] - bz[c] * xsum[v]);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // nothing of the next group moves above its wait
+  }
+}
+
+template <int M, bool DOT, int CPL, int NG>
+__global__ __launch_bounds__(1024) void skinny_lds_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint32_t* __restrict__ qweight,
+    const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
+    uint16_t* __restrict__ y, int64_t ldy, int n, int k, int nstrips, int items_per_xcd, int plane_off,
+    LoraEpi lora) {
+  static_assert(!DOT || M == 1, "the VALU variant computes one token");
+  static_assert(M <= 16, "one MFMA row tile");
+  constexpr int SW = 16 * CPL;                 // strip width in columns
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int nw = blockDim.x >> 6;
+  // codes [G][16][SW], and the wave partial plane [nw][M][SW] behind them or,
+  // when LDS is short (plane_off 0), over them once every wave is done
+  uint32_t* codes = reinterpret_cast<uint32_t*>(smem);
+  float* plane = reinterpret_cast<float*>(smem + plane_off);
+
+  const int strip = (blockIdx.x & 7) * items_per_xcd + (blockIdx.x >> 3);
+  if (strip >= nstrips) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cl = lane & 15, ks = lane >> 4;
+  const int G = k >> 7;
+  const int64_t col0 = (int64_t)strip * SW;
+  const int64_t col = col0 + CPL * cl;
+  const int64_t colc = col < n ? col : 0;
+  // lane parts of the addresses as 32-bit byte offsets from wave-uniform bases
+  // (columns past n read column 0; MFMA lanes past M read token 0; GEMV: the
+  // one token for every lane)
+  const uint32_t xoff = (uint32_t)(((!DOT && cl < M ? (int64_t)cl * ldx : 0) + 8 * ks) * 2);
+  const uint32_t soff = (uint32_t)(colc * 2);
+  const uint32_t zoff = qzeros ? (uint32_t)((colc >> 3) * 4) : 0u;
+  const uint32_t* zbase = qzeros ? qzeros : reinterpret_cast<const uint32_t*>(scales);
+  const int64_t zstride = qzeros ? (int64_t)(n >> 3) : 0;
+  const uint32_t zmask = qzeros ? ~0u : 0u;
+  const int zshift = (int)(col & 7) * 4;
+  // direct-load lane offsets of the codes: instruction i, lane l -> 16-byte
+  // chunk c = 64 i + l of the group, word row c / (SW / 4), columns
+  // 4 (c % (SW / 4)) .. + 3 (chunks past n read column 0 of their row);
+  // byte offsets from the group's first word row stay below 16 n * 4 <= 2^32
+  uint32_t coff[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = 64 * i + lane, row = c / (SW / 4), cc = 4 * (c % (SW / 4));
+    coff[i] = (uint32_t)(((int64_t)row * n + (col0 + cc < n ? col0 + cc : 0)) * 4);
+  }
+
+  f32x4 total[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) total[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // NG groups for the first G - nw (NG - 1) waves, NG - 1 for the rest (uniform branch)
+  if (wave + nw * (NG - 1) < G) {
+    lds_strip_groups<M, DOT, CPL, NG>(x, qweight, scales, zbase, zstride, codes, n, wave, nw, lane, xoff, soff, zoff,
+                                      coff, zshift, zmask, total);
+  } else if constexpr (NG > 1) {
+    lds_strip_groups<M, DOT, CPL, NG - 1>(x, qweight, scales, zbase, zstride, codes, n, wave, nw, lane, xoff, soff,
+                                          zoff, coff, zshift, zmask, total);
+  }
+
+  // wave partials [M][SW] -> LDS plane -> sum over the waves
+  if (plane_off == 0) __syncthreads();
+  if constexpr (DOT) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) total[c][0] = sum_over_rows(total[c][0]);
+    if (ks == 0) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) plane[wave * SW + CPL * cl + c] = total[c][0];
+    }
+  } else {
+    constexpr int VMAX = M < 4 ? M : 4;
+#pragma unroll
+    for (int v = 0; v < VMAX; ++v) {
+      const int token = 4 * ks + v;
+      if (token < M) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) plane[(wave * M + token) * SW + CPL * cl + c] = total[c][v];
+      }
+    }
+  }
+  __syncthreads();
+  for (int o = tid; o < M * SW; o += blockDim.x) {
+    const int token = o / SW, cc = o - token * SW;
+    float v = 0.f;
+    for (int w = 0; w < nw; ++w) v += plane[(w * M + token) * SW + cc];
+    const int64_t cg = col0 + cc;
+    if (cg < n) {
+      if (lora.u) v += lora_term(lora, token, cg);
+      y[(int64_t)token * ldy + cg] = (uint16_t)f32_to_bf16_bits(v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Pipelined MFMA kernel for m > 16.
 //
 // Workgroup tile BM x BN = (NWM * 16 * FM) tokens x (NWN * 64) columns; wave
@@ -1147,30 +1362,102 @@ static void skinny_launch_c(const Int4Args& a, const SkinnyPlan& p, void* ws, hi
   }
 }
 
+// Launch shape of skinny_lds_kernel for a small-M plan, or ng = 0 where it does
+// not apply: a k split, m > 16, more than 64 groups, or more strips than one
+// pass over the CUs takes (its LDS holds all of a strip's codes).  NG groups
+// per wave: 1 up to 16 groups, 2 up to 32, 4 up to 64; waves = ceil(G / NG).
+struct LdsPlan {
+  int ng, waves, plane_off;
+  size_t lds;
+};
+
+// More strips than CUs: at least two groups per wave (half the waves), so two
+// workgroups share a CU at 16 waves: 2048 x 5632 (352 strips) m = 1 / 8 / 15
+// 5.76 / 6.91 / 8.17 -> 5.05 / 6.11 / 7.16 µs (the register-staged kernel:
+// 5.48 / 6.62 / 7.91).  Padding the LDS to one workgroup per CU for 256
+// strips changed nothing (within 1%).
+#ifndef QG_LDS_MANY_NG
+#define QG_LDS_MANY_NG 2
+#endif
+
+static LdsPlan plan_lds(int64_t m, const SkinnyPlan& p, int64_t k) {
+  LdsPlan r{0, 0, 0, 0};
+  const int64_t G = k / 128;
+  if (m > 16 || p.ksplit != 1 || G < 1) return r;
+  int ng = G <= 16 ? 1 : (G <= 32 ? 2 : (G <= 64 ? 4 : 0));
+  if (p.nstrips > 256 && ng > 0 && ng < QG_LDS_MANY_NG && G > 8) ng = G <= 32 ? 2 : 4;
+  if (ng == 0 || ng * (p.cpl + 6) > 63) return r;
+  const int waves = (int)((G + ng - 1) / ng);
+  const size_t codes = (size_t)G * 16 * 16 * p.cpl * 4, plane = (size_t)waves * m * 16 * p.cpl * 4;
+  size_t lds = codes + plane;
+  r.plane_off = (int)codes;
+  if (lds > 160 * 1024) {
+    lds = codes > plane ? codes : plane;
+    r.plane_off = 0;
+  }
+  const int64_t by_lds = (int64_t)(160 * 1024 / lds), by_waves = 32 / waves;
+  const int64_t per_cu = by_lds < by_waves ? by_lds : by_waves;
+  if (lds > 160 * 1024 || per_cu < 1 || p.nstrips > 256 * per_cu) return r;
+  r.ng = ng;
+  r.waves = waves;
+  r.lds = lds;
+  return r;
+}
+
+template <int M, bool DOT, int CPL, int NG>
+static void lds_launch(const Int4Args& a, const SkinnyPlan& p, const LdsPlan& l, hipStream_t stream) {
+  skinny_lds_kernel<M, DOT, CPL, NG><<<dim3((unsigned)p.blocks), dim3(64 * l.waves), l.lds, stream>>>(
+      a.x, a.ldx, a.qweight, a.scales, a.qzeros, a.y, a.ldy, (int)a.n, (int)a.k, p.nstrips, p.items_per_xcd,
+      l.plane_off, a.lora);
+}
+
+template <int M, bool DOT, int CPL>
+static void lds_launch_n(const Int4Args& a, const SkinnyPlan& p, const LdsPlan& l, hipStream_t stream) {
+  if (l.ng == 4) lds_launch<M, DOT, CPL, 4>(a, p, l, stream);
+  else if (l.ng == 2) lds_launch<M, DOT, CPL, 2>(a, p, l, stream);
+  else lds_launch<M, DOT, CPL, 1>(a, p, l, stream);
+}
+
+// Launches the LDS-staged kernel when it applies (returns false otherwise).
+template <int M, bool DOT>
+static bool lds_launch_c(const Int4Args& a, const SkinnyPlan& p, hipStream_t stream) {
+  if constexpr (M > 16) {
+    return false;
+  } else {
+    const LdsPlan l = plan_lds(M, p, a.k);
+    if (l.ng == 0) return false;
+    if (p.cpl == 4) lds_launch_n<M, DOT, 4>(a, p, l, stream);
+    else if (p.cpl == 2) lds_launch_n<M, DOT, 2>(a, p, l, stream);
+    else lds_launch_n<M, DOT, 1>(a, p, l, stream);
+    return true;
+  }
+}
+
 hipError_t launch_gemv_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream) {
-  skinny_launch_c<1, true>(a, plan_skinny(1, a.n, a.k, ws ? ws_bytes : 0, true), ws, stream);
+  const SkinnyPlan p = plan_skinny(1, a.n, a.k, ws ? ws_bytes : 0, true);
+  if (!lds_launch_c<1, true>(a, p, stream)) skinny_launch_c<1, true>(a, p, ws, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_fused_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream) {
   const SkinnyPlan p = plan_skinny(a.m, a.n, a.k, ws ? ws_bytes : 0, false);
   switch (a.m) {
-    case 1: skinny_launch_c<1, false>(a, p, ws, stream); break;
-    case 2: skinny_launch_c<2, false>(a, p, ws, stream); break;
-    case 3: skinny_launch_c<3, false>(a, p, ws, stream); break;
-    case 4: skinny_launch_c<4, false>(a, p, ws, stream); break;
-    case 5: skinny_launch_c<5, false>(a, p, ws, stream); break;
-    case 6: skinny_launch_c<6, false>(a, p, ws, stream); break;
-    case 7: skinny_launch_c<7, false>(a, p, ws, stream); break;
-    case 8: skinny_launch_c<8, false>(a, p, ws, stream); break;
-    case 9: skinny_launch_c<9, false>(a, p, ws, stream); break;
-    case 10: skinny_launch_c<10, false>(a, p, ws, stream); break;
-    case 11: skinny_launch_c<11, false>(a, p, ws, stream); break;
-    case 12: skinny_launch_c<12, false>(a, p, ws, stream); break;
-    case 13: skinny_launch_c<13, false>(a, p, ws, stream); break;
-    case 14: skinny_launch_c<14, false>(a, p, ws, stream); break;
-    case 15: skinny_launch_c<15, false>(a, p, ws, stream); break;
-    case 16: skinny_launch_c<16, false>(a, p, ws, stream); break;
+    case 1: if (!lds_launch_c<1, false>(a, p, stream)) skinny_launch_c<1, false>(a, p, ws, stream); break;
+    case 2: if (!lds_launch_c<2, false>(a, p, stream)) skinny_launch_c<2, false>(a, p, ws, stream); break;
+    case 3: if (!lds_launch_c<3, false>(a, p, stream)) skinny_launch_c<3, false>(a, p, ws, stream); break;
+    case 4: if (!lds_launch_c<4, false>(a, p, stream)) skinny_launch_c<4, false>(a, p, ws, stream); break;
+    case 5: if (!lds_launch_c<5, false>(a, p, stream)) skinny_launch_c<5, false>(a, p, ws, stream); break;
+    case 6: if (!lds_launch_c<6, false>(a, p, stream)) skinny_launch_c<6, false>(a, p, ws, stream); break;
+    case 7: if (!lds_launch_c<7, false>(a, p, stream)) skinny_launch_c<7, false>(a, p, ws, stream); break;
+    case 8: if (!lds_launch_c<8, false>(a, p, stream)) skinny_launch_c<8, false>(a, p, ws, stream); break;
+    case 9: if (!lds_launch_c<9, false>(a, p, stream)) skinny_launch_c<9, false>(a, p, ws, stream); break;
+    case 10: if (!lds_launch_c<10, false>(a, p, stream)) skinny_launch_c<10, false>(a, p, ws, stream); break;
+    case 11: if (!lds_launch_c<11, false>(a, p, stream)) skinny_launch_c<11, false>(a, p, ws, stream); break;
+    case 12: if (!lds_launch_c<12, false>(a, p, stream)) skinny_launch_c<12, false>(a, p, ws, stream); break;
+    case 13: if (!lds_launch_c<13, false>(a, p, stream)) skinny_launch_c<13, false>(a, p, ws, stream); break;
+    case 14: if (!lds_launch_c<14, false>(a, p, stream)) skinny_launch_c<14, false>(a, p, ws, stream); break;
+    case 15: if (!lds_launch_c<15, false>(a, p, stream)) skinny_launch_c<15, false>(a, p, ws, stream); break;
+    case 16: if (!lds_launch_c<16, false>(a, p, stream)) skinny_launch_c<16, false>(a, p, ws, stream); break;
     // two MFMA row tiles (the automatic path sends 16 < m <= 32 here when n is small)
     case 17: skinny_launch_c<17, false>(a, p, ws, stream); break;
     case 18: skinny_launch_c<18, false>(a, p, ws, stream); break;
@@ -1418,9 +1705,16 @@ void describe_int4(int64_t m, int64_t n, int64_t k, int path, int64_t ws_bytes, 
     const int64_t mp = path == 1 ? 1 : m;
     const SkinnyPlan p = plan_skinny(mp, n, k, ws_bytes, path == 1);
     const bool dot = path == 1;
-    snprintf(buf, len, "skinny_int4_kernel<%lld,%s,%d> grid=%lld block=%d lds=%lld ksplit=%d groups=%d",
-             (long long)mp, dot ? "dot" : "mfma", p.cpl, (long long)p.blocks, 64 * p.waves, (long long)p.lds,
-             p.ksplit, p.gwg);
+    const LdsPlan l = plan_lds(mp, p, k);
+    if (l.ng > 0) {
+      snprintf(buf, len, "skinny_lds_kernel<%lld,%s,%d,%d> grid=%lld block=%d lds=%lld ksplit=1 groups=%d",
+               (long long)mp, dot ? "dot" : "mfma", p.cpl, l.ng, (long long)p.blocks, 64 * l.waves,
+               (long long)l.lds, p.gwg);
+    } else {
+      snprintf(buf, len, "skinny_int4_kernel<%lld,%s,%d> grid=%lld block=%d lds=%lld ksplit=%d groups=%d",
+               (long long)mp, dot ? "dot" : "mfma", p.cpl, (long long)p.blocks, 64 * p.waves, (long long)p.lds,
+               p.ksplit, p.gwg);
+    }
   } else {
     const MfmaPlan p = plan_mfma(m, n, k, ws_bytes);
     const PipeCfg c = p.prep ? pipe_cfg_of<true>(p.cfg) : pipe_cfg_of<false>(p.cfg);
