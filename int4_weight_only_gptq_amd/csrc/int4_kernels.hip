@@ -603,19 +603,33 @@ __global__ __launch_bounds__(M > 16 ? 512 : 1024) void skinny_int4_kernel(
 // arithmetic is hidden and the loads bound the kernel; the activation loads
 // (every strip reads all of X) add 0.3 / 1.2 / 2.3 µs over the codes alone.
 // ---------------------------------------------------------------------------
-template <int M, bool DOT, int CPL, int NGW>
+// Activations staged in LDS too (XL): per group the wave copies its M tokens x
+// 128 k with direct loads, 1 KiB = 4 tokens x 256 contiguous bytes per
+// instruction (MFMA; the GEMV copies its one token's 256 bytes with 4-byte
+// lanes), instead of four 16-byte register loads per lane whose 16 tokens each
+// touch half a cache line: 4096 x 4096 m = 8 / 15 6.16 / 7.21 -> 5.53 / 6.25
+// µs in a timing copy.  The 16-byte chunk c of token t's row sits in slot
+// c ^ t, so the 16 lanes of an MFMA operand read (16 tokens, one chunk) hit
+// distinct banks.
+template <int M, bool DOT, bool XL>
+constexpr int kXLoads = XL ? (DOT ? 1 : (M + 3) / 4) : 4;   // activation loads per group and lane
+
+template <int M, bool DOT, int CPL, int NGW, bool XL>
 __device__ __forceinline__ void lds_strip_groups(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qweight,
                                                  const uint16_t* __restrict__ scales, const uint32_t* zbase,
-                                                 int64_t zstride, uint32_t* codes, int n, int wave, int nw, int lane,
-                                                 uint32_t xoff, uint32_t soff, uint32_t zoff, const uint32_t (&coff)[CPL],
-                                                 int zshift, uint32_t zmask, f32x4 (&total)[CPL]) {
+                                                 int64_t zstride, uint32_t* codes, uint32_t* xlds, int n, int wave,
+                                                 int nw, int lane, const uint32_t (&xo)[4], uint32_t soff, uint32_t zoff,
+                                                 const uint32_t (&coff)[CPL], int zshift, uint32_t zmask,
+                                                 f32x4 (&total)[CPL]) {
   constexpr int SW = 16 * CPL;                 // strip width in columns
   constexpr int GDW = 16 * SW;                 // dwords of codes per group
-  constexpr int LPG = CPL + 4 + 2;             // vector memory operations per group
+  constexpr int XI = kXLoads<M, DOT, XL>;
+  constexpr int XDW = DOT ? 64 : 256 * XI;     // dwords of activations per group (XL)
+  constexpr int LPG = CPL + XI + 2;            // vector memory operations per group
   static_assert(NGW * LPG <= 63, "vmcnt range");
   const int cl = lane & 15, ks = lane >> 4;
   const u32x4 ones = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
-  u32x4 xa[NGW][4];
+  u32x4 xa[XL ? 1 : NGW][4];
   Meta<CPL> meta[NGW];
 #pragma unroll
   for (int j = 0; j < NGW; ++j) {
@@ -625,8 +639,18 @@ __device__ __forceinline__ void lds_strip_groups(const uint16_t* __restrict__ x,
 #pragma unroll
     for (int i = 0; i < CPL; ++i) buffer_to_lds16(gbase, coff[i], lds + 256 * i);
     const uint16_t* xg = x + (int64_t)g * 128;
+    if constexpr (XL) {
+      uint32_t* xl = xlds + (size_t)g * XDW;
+      if constexpr (DOT) {
+        buffer_to_lds4(xg, xo[0], xl);
+      } else {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) xa[j][s] = buffer_load16(xg, xoff + 64 * s);
+        for (int i = 0; i < XI; ++i) buffer_to_lds16(xg, xo[i], xl + 256 * i);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) xa[j][s] = buffer_load16(xg, xo[0] + 64 * s);
+    }
     const uint16_t* sg = scales + (int64_t)g * n;
     if constexpr (CPL == 4) {
       const u32x2 v = buffer_load8(sg, soff);
@@ -641,6 +665,19 @@ __device__ __forceinline__ void lds_strip_groups(const uint16_t* __restrict__ x,
     __builtin_amdgcn_sched_barrier(0);   // groups' loads stay in issue order
   }
   const uint32_t mask = in_vgpr(0x000F000Fu), bias = in_vgpr(kBias128x2);   // VGPR operands of v_and_or_b32
+  // the lane's 8 activations of k step s of group j (MFMA: token cl, GEMV: the
+  // one token), from registers or from the LDS copy (row cl, chunk 4 s + ks in
+  // slot (4 s + ks) ^ cl; rows past the copied ones read row 0)
+  const int xrow = cl < 4 * XI ? cl : 0;
+  auto xfrag = [&](int j, int s) -> u32x4 {
+    if constexpr (!XL) {
+      return xa[j][s];
+    } else {
+      const uint32_t* xl = xlds + (size_t)(wave + nw * j) * XDW;
+      if constexpr (DOT) return *reinterpret_cast<const u32x4*>(xl + 4 * (4 * s + ks));
+      else return *reinterpret_cast<const u32x4*>(xl + 64 * xrow + 4 * ((4 * s + ks) ^ xrow));
+    }
+  };
 #pragma unroll
   for (int j = 0; j < NGW; ++j) {
     // this group's loads have landed once at most the later groups' are outstanding
@@ -670,7 +707,7 @@ __device__ __forceinline__ void lds_strip_groups(const uint16_t* __restrict__ x,
       float xs = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const u32x4 a = x_pairs_permuted(xa[j][s]);
+        const u32x4 a = x_pairs_permuted(xfrag(j, s));
 #pragma unroll
         for (int t = 0; t < 4; ++t) xs = dot2_bf16(a[t], kOnesBf16x2, xs);
 #pragma unroll
@@ -689,7 +726,7 @@ __device__ __forceinline__ void lds_strip_groups(const uint16_t* __restrict__ x,
       for (int c = 0; c < CPL; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const u32x4 a = x_pairs_permuted(xa[j][s]);
+        const u32x4 a = x_pairs_permuted(xfrag(j, s));
         xsum = mfma16_bf16(a, ones, xsum);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) acc[c] = mfma16_bf16(a, codes_as_bf16_pairs_mb(w[s][c], mask, bias), acc[c]);
@@ -703,7 +740,7 @@ __device__ __forceinline__ void lds_strip_groups(const uint16_t* __restrict__ x,
   }
 }
 
-template <int M, bool DOT, int CPL, int NG>
+template <int M, bool DOT, int CPL, int NG, bool XL>
 __global__ __launch_bounds__(1024) void skinny_lds_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
@@ -714,8 +751,9 @@ __global__ __launch_bounds__(1024) void skinny_lds_kernel(
   constexpr int SW = 16 * CPL;                 // strip width in columns
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int nw = blockDim.x >> 6;
-  // codes [G][16][SW], and the wave partial plane [nw][M][SW] behind them or,
-  // when LDS is short (plane_off 0), over them once every wave is done
+  // codes [G][16][SW], with XL the activations [G][rows][128] behind them, and
+  // the wave partial plane [nw][M][SW] behind those or, when LDS is short
+  // (plane_off 0), over them once every wave is done
   uint32_t* codes = reinterpret_cast<uint32_t*>(smem);
   float* plane = reinterpret_cast<float*>(smem + plane_off);
 
@@ -731,7 +769,22 @@ __global__ __launch_bounds__(1024) void skinny_lds_kernel(
   // lane parts of the addresses as 32-bit byte offsets from wave-uniform bases
   // (columns past n read column 0; MFMA lanes past M read token 0; GEMV: the
   // one token for every lane)
-  const uint32_t xoff = (uint32_t)(((!DOT && cl < M ? (int64_t)cl * ldx : 0) + 8 * ks) * 2);
+  // activation offsets: registers -- the lane's token row and k chunk ks;
+  // LDS copy -- instruction i, lane l: token t = 4 i + l / 16 (token 0 past M),
+  // source chunk (l % 16) ^ t; the GEMV copy: dword l of the row
+  uint32_t xo[4] = {0u, 0u, 0u, 0u};
+  if constexpr (!XL) {
+    xo[0] = (uint32_t)(((!DOT && cl < M ? (int64_t)cl * ldx : 0) + 8 * ks) * 2);
+  } else if constexpr (DOT) {
+    xo[0] = (uint32_t)(4 * lane);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * i + ks;
+      xo[i] = (uint32_t)(((t < M ? (int64_t)t * ldx : 0) + 8 * (cl ^ t)) * 2);
+    }
+  }
+  uint32_t* xlds = codes + (size_t)G * 16 * SW;
   const uint32_t soff = (uint32_t)(colc * 2);
   const uint32_t zoff = qzeros ? (uint32_t)((colc >> 3) * 4) : 0u;
   const uint32_t* zbase = qzeros ? qzeros : reinterpret_cast<const uint32_t*>(scales);
@@ -754,11 +807,11 @@ __global__ __launch_bounds__(1024) void skinny_lds_kernel(
   for (int c = 0; c < CPL; ++c) total[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   // NG groups for the first G - nw (NG - 1) waves, NG - 1 for the rest (uniform branch)
   if (wave + nw * (NG - 1) < G) {
-    lds_strip_groups<M, DOT, CPL, NG>(x, qweight, scales, zbase, zstride, codes, n, wave, nw, lane, xoff, soff, zoff,
-                                      coff, zshift, zmask, total);
+    lds_strip_groups<M, DOT, CPL, NG, XL>(x, qweight, scales, zbase, zstride, codes, xlds, n, wave, nw, lane, xo,
+                                          soff, zoff, coff, zshift, zmask, total);
   } else if constexpr (NG > 1) {
-    lds_strip_groups<M, DOT, CPL, NG - 1>(x, qweight, scales, zbase, zstride, codes, n, wave, nw, lane, xoff, soff,
-                                          zoff, coff, zshift, zmask, total);
+    lds_strip_groups<M, DOT, CPL, NG - 1, XL>(x, qweight, scales, zbase, zstride, codes, xlds, n, wave, nw, lane, xo,
+                                              soff, zoff, coff, zshift, zmask, total);
   }
 
   // wave partials [M][SW] -> LDS plane -> sum over the waves
@@ -1368,6 +1421,7 @@ static void skinny_launch_c(const Int4Args& a, const SkinnyPlan& p, void* ws, hi
 // per wave: 1 up to 16 groups, 2 up to 32, 4 up to 64; waves = ceil(G / NG).
 struct LdsPlan {
   int ng, waves, plane_off;
+  bool xl;   // activations staged in LDS as well
   size_t lds;
 };
 
@@ -1380,33 +1434,52 @@ struct LdsPlan {
 #define QG_LDS_MANY_NG 2
 #endif
 
-static LdsPlan plan_lds(int64_t m, const SkinnyPlan& p, int64_t k) {
-  LdsPlan r{0, 0, 0, 0};
+static LdsPlan plan_lds(int64_t m, const SkinnyPlan& p, int64_t k, bool dot) {
+  LdsPlan r{0, 0, 0, false, 0};
   const int64_t G = k / 128;
   if (m > 16 || p.ksplit != 1 || G < 1) return r;
   int ng = G <= 16 ? 1 : (G <= 32 ? 2 : (G <= 64 ? 4 : 0));
   if (p.nstrips > 256 && ng > 0 && ng < QG_LDS_MANY_NG && G > 8) ng = G <= 32 ? 2 : 4;
   if (ng == 0 || ng * (p.cpl + 6) > 63) return r;
   const int waves = (int)((G + ng - 1) / ng);
-  const size_t codes = (size_t)G * 16 * 16 * p.cpl * 4, plane = (size_t)waves * m * 16 * p.cpl * 4;
-  size_t lds = codes + plane;
-  r.plane_off = (int)codes;
-  if (lds > 160 * 1024) {
-    lds = codes > plane ? codes : plane;
-    r.plane_off = 0;
+  const size_t plane = (size_t)waves * m * 16 * p.cpl * 4;
+  const int xi = dot ? 1 : (int)((m + 3) / 4);                 // activation loads per group
+  // the activations join the codes in LDS when both fit (strips of 16 and 32
+  // columns) and the workgroups still take one pass; else they go to registers
+  for (int xl = 1; xl >= 0; --xl) {
+    if (xl && (p.cpl > 2 || ng * (p.cpl + xi + 2) > 63)) continue;
+    const size_t codes = (size_t)G * 16 * 16 * p.cpl * 4 + (xl ? (size_t)G * (dot ? 256 : 1024 * xi) : 0);
+    size_t lds = codes + plane;
+    int plane_off = (int)codes;
+    if (lds > 160 * 1024) {
+      lds = codes > plane ? codes : plane;
+      plane_off = 0;
+    }
+    if (lds > 160 * 1024) continue;
+    const int64_t by_lds = (int64_t)(160 * 1024 / lds), by_waves = 32 / waves;
+    const int64_t per_cu = by_lds < by_waves ? by_lds : by_waves;
+    if (per_cu < 1 || p.nstrips > 256 * per_cu) continue;
+    r.ng = ng;
+    r.waves = waves;
+    r.plane_off = plane_off;
+    r.xl = xl != 0;
+    r.lds = lds;
+    return r;
   }
-  const int64_t by_lds = (int64_t)(160 * 1024 / lds), by_waves = 32 / waves;
-  const int64_t per_cu = by_lds < by_waves ? by_lds : by_waves;
-  if (lds > 160 * 1024 || per_cu < 1 || p.nstrips > 256 * per_cu) return r;
-  r.ng = ng;
-  r.waves = waves;
-  r.lds = lds;
   return r;
 }
 
 template <int M, bool DOT, int CPL, int NG>
 static void lds_launch(const Int4Args& a, const SkinnyPlan& p, const LdsPlan& l, hipStream_t stream) {
-  skinny_lds_kernel<M, DOT, CPL, NG><<<dim3((unsigned)p.blocks), dim3(64 * l.waves), l.lds, stream>>>(
+  if constexpr (CPL <= 2) {
+    if (l.xl) {
+      skinny_lds_kernel<M, DOT, CPL, NG, true><<<dim3((unsigned)p.blocks), dim3(64 * l.waves), l.lds, stream>>>(
+          a.x, a.ldx, a.qweight, a.scales, a.qzeros, a.y, a.ldy, (int)a.n, (int)a.k, p.nstrips, p.items_per_xcd,
+          l.plane_off, a.lora);
+      return;
+    }
+  }
+  skinny_lds_kernel<M, DOT, CPL, NG, false><<<dim3((unsigned)p.blocks), dim3(64 * l.waves), l.lds, stream>>>(
       a.x, a.ldx, a.qweight, a.scales, a.qzeros, a.y, a.ldy, (int)a.n, (int)a.k, p.nstrips, p.items_per_xcd,
       l.plane_off, a.lora);
 }
@@ -1424,7 +1497,7 @@ static bool lds_launch_c(const Int4Args& a, const SkinnyPlan& p, hipStream_t str
   if constexpr (M > 16) {
     return false;
   } else {
-    const LdsPlan l = plan_lds(M, p, a.k);
+    const LdsPlan l = plan_lds(M, p, a.k, DOT);
     if (l.ng == 0) return false;
     if (p.cpl == 4) lds_launch_n<M, DOT, 4>(a, p, l, stream);
     else if (p.cpl == 2) lds_launch_n<M, DOT, 2>(a, p, l, stream);
@@ -1705,11 +1778,11 @@ void describe_int4(int64_t m, int64_t n, int64_t k, int path, int64_t ws_bytes, 
     const int64_t mp = path == 1 ? 1 : m;
     const SkinnyPlan p = plan_skinny(mp, n, k, ws_bytes, path == 1);
     const bool dot = path == 1;
-    const LdsPlan l = plan_lds(mp, p, k);
+    const LdsPlan l = plan_lds(mp, p, k, dot);
     if (l.ng > 0) {
-      snprintf(buf, len, "skinny_lds_kernel<%lld,%s,%d,%d> grid=%lld block=%d lds=%lld ksplit=1 groups=%d",
-               (long long)mp, dot ? "dot" : "mfma", p.cpl, l.ng, (long long)p.blocks, 64 * l.waves,
-               (long long)l.lds, p.gwg);
+      snprintf(buf, len, "skinny_lds_kernel<%lld,%s,%d,%d,%s> grid=%lld block=%d lds=%lld ksplit=1 groups=%d",
+               (long long)mp, dot ? "dot" : "mfma", p.cpl, l.ng, l.xl ? "xlds" : "xreg", (long long)p.blocks,
+               64 * l.waves, (long long)l.lds, p.gwg);
     } else {
       snprintf(buf, len, "skinny_int4_kernel<%lld,%s,%d> grid=%lld block=%d lds=%lld ksplit=%d groups=%d",
                (long long)mp, dot ? "dot" : "mfma", p.cpl, (long long)p.blocks, 64 * p.waves, (long long)p.lds,

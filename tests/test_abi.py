@@ -219,12 +219,18 @@ def test_dense_fp32_alignment_and_dtype(lib):
 
 def test_describe_names_the_dispatch(lib):
     # 4096 columns: 256 strips of 16, the LDS-staged kernel with 2 groups per wave
-    # (16 waves over 32 groups); its LDS holds the strip's codes (32 groups x 1 KiB)
-    # and the wave partial plane behind them (16 waves x 1 token x 16 columns x 4 bytes)
+    # (16 waves over 32 groups); its LDS holds the strip's codes (32 groups x 1 KiB),
+    # the activations (32 groups x 256 bytes) and the wave partial plane behind them
+    # (16 waves x 1 token x 16 columns x 4 bytes)
     assert qg.describe_int4(1, 4096, 4096) == (
-        "skinny_lds_kernel<1,dot,1,2> grid=256 block=1024 lds=%d ksplit=1 groups=32" % (32 * 1024 + 16 * 64))
+        "skinny_lds_kernel<1,dot,1,2,xlds> grid=256 block=1024 lds=%d ksplit=1 groups=32"
+        % (32 * 1024 + 32 * 256 + 16 * 64))
+    # 15 tokens: 4 KiB of activations per group (4 copies of 4 tokens x 256 bytes): 160 KiB
+    # with the codes, so the partial plane reuses the codes' space
+    assert qg.describe_int4(15, 4096, 4096) == (
+        "skinny_lds_kernel<15,mfma,1,2,xlds> grid=256 block=1024 lds=%d ksplit=1 groups=32" % (160 * 1024))
     # 8192 columns: 256 strips of 32, one group per wave (16 groups)
-    assert qg.describe_int4(8, 8192, 2048).startswith("skinny_lds_kernel<8,mfma,2,1> grid=256 block=1024")
+    assert qg.describe_int4(8, 8192, 2048).startswith("skinny_lds_kernel<8,mfma,2,1,xlds> grid=256 block=1024")
     # more strips than one pass holds with all their codes in LDS: the register-staged kernel
     assert qg.describe_int4(8, 28672, 4096).startswith("skinny_int4_kernel<8,mfma,4> grid=448")
     assert qg.describe_int4(16, 28672, 4096).startswith("skinny_int4_kernel<16,mfma,4> grid=448 block=512")
@@ -280,8 +286,10 @@ def test_workspace_size(lib):
     # more strips than CUs (352 here): the LDS-staged kernel with two groups per wave, so
     # that two 8-wave workgroups share a CU; 256 strips: one group per wave, 16 waves;
     # without the LDS-staged kernel (k split forced by a long k) the register-staged one
-    assert qg.describe_int4(8, 5632, 2048).startswith("skinny_lds_kernel<8,mfma,1,2> grid=352 block=512 ")
-    assert qg.describe_int4(8, 4096, 2048).startswith("skinny_lds_kernel<8,mfma,1,1> grid=256 block=1024 ")
+    assert qg.describe_int4(8, 5632, 2048).startswith("skinny_lds_kernel<8,mfma,1,2,xlds> grid=352 block=512 ")
+    assert qg.describe_int4(8, 4096, 2048).startswith("skinny_lds_kernel<8,mfma,1,1,xlds> grid=256 block=1024 ")
+    # two workgroups per CU leave no room for 15 tokens' activations: they stay in registers
+    assert qg.describe_int4(15, 5632, 2048).startswith("skinny_lds_kernel<15,mfma,1,2,xreg> grid=352 block=512 ")
     assert qg.describe_int4(8, 5632, 20480).startswith("skinny_int4_kernel<8,mfma,")
     assert "block=512" in qg.describe_int4(32, 4096, 4096)
     assert qg.workspace_size(24, 5120, 25600) > 0

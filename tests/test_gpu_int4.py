@@ -133,16 +133,17 @@ def test_codes_equal_zeros_give_zero(gpu_lib, path):
     assert np.max(np.abs(y)) < 1e-4
 
 
-def test_strided_x_and_y_with_guard_bands(gpu_lib):
+@pytest.mark.parametrize("m,paths", [(5, ["fused", "mfma"]), (1, ["gemv", "fused"]), (16, ["fused"])])
+def test_strided_x_and_y_with_guard_bands(gpu_lib, m, paths):
     import torch
 
-    m, k, n = 5, 1024, 520
-    d = int4_inputs(m, k, n, seed=34)
+    k, n = 1024, 520
+    d = int4_inputs(m, k, n, seed=34 + m)
     t = upload_int4(d)
     xs = torch.zeros((m, k + 64), dtype=torch.bfloat16, device="cuda")
     xs[:, :k] = t["x"]
     t["x"] = xs[:, :k]
-    for path in ["fused", "mfma"]:
+    for path in paths:
         big = torch.full((m + 2, n + 24), -384.0, dtype=torch.bfloat16, device="cuda")
         out = big[1:m + 1, 8:8 + n]
         say("strided", path)
