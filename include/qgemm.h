@@ -131,7 +131,7 @@ int32_t qgemm_int4(const void* x, int64_t ldx, const uint32_t* qweight, const ui
  *   U[r][t] = sum_i X[r][i] A[t][i]   (fp32, not rounded to bf16).
  *
  *   lora_a   bf16 [rank][lda_a] (A, the adapter's down projection),
- *            lda_a >= k, lda_a % 8 == 0, 16-byte aligned.
+ *            k <= lda_a <= 2^22, lda_a % 8 == 0, 16-byte aligned.
  *   lora_b   bf16 [n][ldb_b] (B, the up projection), ldb_b >= rank, 2-byte aligned.
  *   rank     1..16.
  *   path     as qgemm_int4_path (QG_PATH_AUTO chooses from m).
@@ -144,12 +144,17 @@ int32_t qgemm_int4(const void* x, int64_t ldx, const uint32_t* qweight, const ui
  *            qgemm_int4_lora_workspace_size gives the size that also enables
  *            the path's split / preparation.
  *
- * U is computed by two small kernels launched first on the same stream (k
- * slices of U in parallel, then their sum in slice order); the LoRA
- * term is added to the fp32 accumulators of the product's own epilogue (once
- * per output also when k is split).  Other arguments, limits and errors as
- * qgemm_int4 (plus QG_ERR_SHAPE for a bad rank or a workspace without room
- * for U).
+ * One launch where it pays: the LDS-staged small-M kernel (m <= 16, k up to
+ * 64 groups, strips in one pass) and the MFMA tiles of products up to 2^34
+ * flops accumulate U from the activations they already hold, in fp32, and add
+ * the LoRA term to the product's fp32 accumulators in the same kernel (each k
+ * slice adds its own share of U when k is split).  Otherwise (the
+ * register-staged small-M kernel: long-k splits and 17..64 tokens; larger
+ * MFMA products) U is computed first by two small kernels on the same stream
+ * into the end of the workspace (k slices in parallel, then their sum in slice
+ * order), and the product adds the term in its epilogue (once per output).
+ * Other arguments, limits and errors as qgemm_int4 (plus QG_ERR_SHAPE for a
+ * bad rank or a workspace without room for U).
  */
 int32_t qgemm_int4_lora(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
                         const uint32_t* qzeros, const void* lora_a, int64_t lda_a, const void* lora_b,

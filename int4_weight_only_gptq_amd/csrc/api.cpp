@@ -117,20 +117,28 @@ int32_t run_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint
   if (k == 0) return hip_status(qg::launch_zero16((uint16_t*)y, m, n, ldy, s));
   qg::Int4Args a{(const uint16_t*)x, ldx, qweight, scales, qzeros, (uint16_t*)y, ldy, m, n, k};
   if (ws == nullptr) ws_bytes = 0;
+  const int32_t rp = resolve_path(m, n, k, path);
   if (lora != nullptr) {
-    // U = X . A^T into the end of the workspace, then the product with the
-    // LoRA add in its epilogue; the path keeps the 256-byte aligned front part
+    // the path keeps the 256-byte aligned front part of the workspace; the
+    // product's kernel accumulates U = X . A^T itself where it can (one
+    // launch), else U goes to the end of the workspace first (two small
+    // launches) and the product adds the LoRA term in its epilogue
     const int64_t rest = (ws_bytes - lora_u_bytes(m, k)) & ~(int64_t)255;
-    float* u = (float*)((char*)ws + rest);
-    st = hip_status(qg::launch_lora_u((const uint16_t*)x, ldx, (const uint16_t*)lora_a, lda_a, lora->rank, m,
-                                      k, u, s));
-    if (st != QG_OK) return st;
     a.lora = *lora;
-    a.lora.u = u;
+    a.lora.a = (const uint16_t*)lora_a;
+    a.lora.lda = lda_a;
+    if (!qg::lora_in_launch(a, rp, rest)) {
+      float* u = (float*)((char*)ws + rest);
+      st = hip_status(qg::launch_lora_u((const uint16_t*)x, ldx, (const uint16_t*)lora_a, lda_a, lora->rank, m,
+                                        k, u, s));
+      if (st != QG_OK) return st;
+      a.lora.u = u;
+      a.lora.a = nullptr;
+    }
     ws_bytes = rest;
     if (ws_bytes == 0) ws = nullptr;
   }
-  switch (resolve_path(m, n, k, path)) {
+  switch (rp) {
     case QG_PATH_GEMV: return hip_status(qg::launch_gemv_int4(a, ws, ws_bytes, s));
     case QG_PATH_FUSED: return hip_status(qg::launch_fused_int4(a, ws, ws_bytes, s));
     default: return hip_status(qg::launch_mfma_int4(a, ws, ws_bytes, s));
@@ -226,14 +234,14 @@ int32_t qgemm_int4_lora(const void* x, int64_t ldx, const uint32_t* qweight, con
   if (rank < 1 || rank > 16) return QG_ERR_SHAPE;
   if (m > 0 && n > 0 && k > 0) {
     if (lora_a == nullptr || lora_b == nullptr) return QG_ERR_NULL;
-    if (lda_a < k || ldb_b < rank) return QG_ERR_SHAPE;
+    if (lda_a < k || lda_a > (int64_t)1 << 22 || ldb_b < rank) return QG_ERR_SHAPE;
     if (!aligned(lora_a, 16) || lda_a % 8 != 0 || !aligned(lora_b, 2)) return QG_ERR_ALIGN;
     if (workspace == nullptr || workspace_bytes < lora_u_bytes(m, k)) return QG_ERR_SHAPE;
   }
   if (m > 0 && n > 0 && k == 0)      // U = 0: the plain product (zeros)
     return run_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size, path, workspace,
                     workspace_bytes, stream);
-  const qg::LoraEpi l{nullptr, (const uint16_t*)lora_b, ldb_b, rank, lora_scale};
+  const qg::LoraEpi l{nullptr, (const uint16_t*)lora_b, ldb_b, rank, lora_scale, nullptr, 0};
   return run_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size, path, workspace,
                   workspace_bytes, stream, &l, lora_a, lda_a);
 }

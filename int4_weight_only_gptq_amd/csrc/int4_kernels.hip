@@ -226,6 +226,35 @@ __device__ __forceinline__ float lora_term(const LoraEpi& L, int64_t row, int64_
   return L.scale * s;
 }
 
+// The LoRA term of one output with the U row already at hand (16 fp32 values,
+// columns past the rank zero): the B row loaded as in lora_term.
+__device__ __forceinline__ float lora_term_u(const LoraEpi& L, const float* urow, int64_t col) {
+  const uint16_t* b = L.b + col * L.ldb;
+  float bb[16];
+  if (L.ldb >= 16 && (L.ldb & 7) == 0 && ((uintptr_t)L.b & 15u) == 0) {
+    const u32x4 w0 = *reinterpret_cast<const u32x4*>(b), w1 = *reinterpret_cast<const u32x4*>(b + 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bb[2 * i] = bf16_bits_to_float(w0[i] & 0xFFFFu);
+      bb[2 * i + 1] = bf16_bits_to_float(w0[i] >> 16);
+      bb[8 + 2 * i] = bf16_bits_to_float(w1[i] & 0xFFFFu);
+      bb[8 + 2 * i + 1] = bf16_bits_to_float(w1[i] >> 16);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bb[r] = r < L.rank ? bb[r] : 0.f;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float v = bf16_bits_to_float(b[r < L.rank ? r : 0]);
+      bb[r] = r < L.rank ? v : 0.f;
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s = __builtin_fmaf(urow[r], bb[r], s);
+  return L.scale * s;
+}
+
 // U = X . A^T in two small launches: partial 16 x 16 tiles of U over k slices
 // (workgroup (b, s): rows 16 b .. 16 b + 15, k slice s; its 16 waves take
 // interleaved 32-k steps on the 16x16x32 bf16 MFMA with the activations as A
@@ -614,22 +643,24 @@ __global__ __launch_bounds__(M > 16 ? 512 : 1024) void skinny_int4_kernel(
 template <int M, bool DOT, bool XL>
 constexpr int kXLoads = XL ? (DOT ? 1 : (M + 3) / 4) : 4;   // activation loads per group and lane
 
-template <int M, bool DOT, int CPL, int NGW, bool XL>
+template <int M, bool DOT, int CPL, int NGW, bool XL, bool LORA>
 __device__ __forceinline__ void lds_strip_groups(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qweight,
                                                  const uint16_t* __restrict__ scales, const uint32_t* zbase,
                                                  int64_t zstride, uint32_t* codes, uint32_t* xlds, int n, int wave,
                                                  int nw, int lane, const uint32_t (&xo)[4], uint32_t soff, uint32_t zoff,
                                                  const uint32_t (&coff)[CPL], int zshift, uint32_t zmask,
-                                                 f32x4 (&total)[CPL]) {
+                                                 f32x4 (&total)[CPL], const uint16_t* __restrict__ la_base,
+                                                 uint32_t aoff, bool arank, f32x4& uacc) {
   constexpr int SW = 16 * CPL;                 // strip width in columns
   constexpr int GDW = 16 * SW;                 // dwords of codes per group
   constexpr int XI = kXLoads<M, DOT, XL>;
   constexpr int XDW = DOT ? 64 : 256 * XI;     // dwords of activations per group (XL)
-  constexpr int LPG = CPL + XI + 2;            // vector memory operations per group
+  constexpr int LPG = CPL + XI + 2 + (LORA ? 4 : 0);   // vector memory operations per group
   static_assert(NGW * LPG <= 63, "vmcnt range");
   const int cl = lane & 15, ks = lane >> 4;
   const u32x4 ones = {kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
   u32x4 xa[XL ? 1 : NGW][4];
+  u32x4 la[LORA ? NGW : 1][4];   // LoRA: lane (rank cl, chunk ks) of lora_A per k step
   Meta<CPL> meta[NGW];
 #pragma unroll
   for (int j = 0; j < NGW; ++j) {
@@ -662,6 +693,11 @@ __device__ __forceinline__ void lds_strip_groups(const uint16_t* __restrict__ x,
       meta[j].s[0] = buffer_load2(sg, soff);
     }
     meta[j].z = buffer_load4(zbase + (int64_t)g * zstride, zoff);
+    if constexpr (LORA) {
+      const uint16_t* ag = la_base + (int64_t)g * 128;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) la[j][s] = buffer_load16(ag, aoff + 64 * s);
+    }
     __builtin_amdgcn_sched_barrier(0);   // groups' loads stay in issue order
   }
   const uint32_t mask = in_vgpr(0x000F000Fu), bias = in_vgpr(kBias128x2);   // VGPR operands of v_and_or_b32
@@ -707,7 +743,14 @@ __device__ __forceinline__ void lds_strip_groups(const uint16_t* __restrict__ x,
       float xs = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const u32x4 a = x_pairs_permuted(xfrag(j, s));
+        const u32x4 xr = xfrag(j, s);
+        if constexpr (LORA) {
+          // U[rank cl] += x . lora_A[cl] over this lane's chunk (both in natural order)
+          const u32x4 av = arank ? la[j][s] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) uacc[0] = dot2_bf16(xr[t], av[t], uacc[0]);
+        }
+        const u32x4 a = x_pairs_permuted(xr);
 #pragma unroll
         for (int t = 0; t < 4; ++t) xs = dot2_bf16(a[t], kOnesBf16x2, xs);
 #pragma unroll
@@ -726,7 +769,12 @@ __device__ __forceinline__ void lds_strip_groups(const uint16_t* __restrict__ x,
       for (int c = 0; c < CPL; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const u32x4 a = x_pairs_permuted(xfrag(j, s));
+        const u32x4 xr = xfrag(j, s);
+        if constexpr (LORA) {
+          // U[token][rank] += x . lora_A^T: tokens as A, ranks as B (natural k order)
+          uacc = mfma16_bf16(xr, arank ? la[j][s] : u32x4{0u, 0u, 0u, 0u}, uacc);
+        }
+        const u32x4 a = x_pairs_permuted(xr);
         xsum = mfma16_bf16(a, ones, xsum);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) acc[c] = mfma16_bf16(a, codes_as_bf16_pairs_mb(w[s][c], mask, bias), acc[c]);
@@ -740,7 +788,7 @@ __device__ __forceinline__ void lds_strip_groups(const uint16_t* __restrict__ x,
   }
 }
 
-template <int M, bool DOT, int CPL, int NG, bool XL>
+template <int M, bool DOT, int CPL, int NG, bool XL, bool LORA>
 __global__ __launch_bounds__(1024) void skinny_lds_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
@@ -806,16 +854,36 @@ __global__ __launch_bounds__(1024) void skinny_lds_kernel(
 #pragma unroll
   for (int c = 0; c < CPL; ++c) total[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   // NG groups for the first G - nw (NG - 1) waves, NG - 1 for the rest (uniform branch)
+  // LoRA with U accumulated here: lane (rank cl, chunk ks) reads lora_A row cl
+  // (row 0 past the rank; its contribution is zeroed)
+  const bool arank = LORA && cl < lora.rank;
+  const uint32_t aoff = LORA ? (uint32_t)(((arank ? (int64_t)cl * lora.lda : 0) + 8 * ks) * 2) : 0u;
+  f32x4 uacc = {0.f, 0.f, 0.f, 0.f};
   if (wave + nw * (NG - 1) < G) {
-    lds_strip_groups<M, DOT, CPL, NG, XL>(x, qweight, scales, zbase, zstride, codes, xlds, n, wave, nw, lane, xo,
-                                          soff, zoff, coff, zshift, zmask, total);
+    lds_strip_groups<M, DOT, CPL, NG, XL, LORA>(x, qweight, scales, zbase, zstride, codes, xlds, n, wave, nw, lane,
+                                                xo, soff, zoff, coff, zshift, zmask, total, lora.a, aoff, arank, uacc);
   } else if constexpr (NG > 1) {
-    lds_strip_groups<M, DOT, CPL, NG - 1, XL>(x, qweight, scales, zbase, zstride, codes, xlds, n, wave, nw, lane, xo,
-                                              soff, zoff, coff, zshift, zmask, total);
+    lds_strip_groups<M, DOT, CPL, NG - 1, XL, LORA>(x, qweight, scales, zbase, zstride, codes, xlds, n, wave, nw,
+                                                    lane, xo, soff, zoff, coff, zshift, zmask, total, lora.a, aoff,
+                                                    arank, uacc);
   }
 
-  // wave partials [M][SW] -> LDS plane -> sum over the waves
+  // wave partials [M][SW] -> LDS plane -> sum over the waves (LoRA: the wave
+  // partials of U [M][16] behind the plane, summed into U [M][16] after them)
   if (plane_off == 0) __syncthreads();
+  float* uplane = plane + nw * M * SW;
+  float* utot = uplane + nw * M * 16;
+  if constexpr (LORA) {
+    if constexpr (DOT) {
+      const float u = sum_over_rows(uacc[0]);
+      if (ks == 0) uplane[wave * 16 + cl] = u;
+    } else {
+      constexpr int VMAX = M < 4 ? M : 4;
+#pragma unroll
+      for (int v = 0; v < VMAX; ++v)
+        if (4 * ks + v < M) uplane[(wave * M + 4 * ks + v) * 16 + cl] = uacc[v];
+    }
+  }
   if constexpr (DOT) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) total[c][0] = sum_over_rows(total[c][0]);
@@ -835,13 +903,22 @@ __global__ __launch_bounds__(1024) void skinny_lds_kernel(
     }
   }
   __syncthreads();
+  if constexpr (LORA) {
+    for (int o = tid; o < M * 16; o += blockDim.x) {   // U summed over the waves in wave order
+      float u = 0.f;
+      for (int w = 0; w < nw; ++w) u += uplane[w * M * 16 + o];
+      utot[o] = u;
+    }
+    __syncthreads();
+  }
   for (int o = tid; o < M * SW; o += blockDim.x) {
     const int token = o / SW, cc = o - token * SW;
     float v = 0.f;
     for (int w = 0; w < nw; ++w) v += plane[(w * M + token) * SW + cc];
     const int64_t cg = col0 + cc;
     if (cg < n) {
-      if (lora.u) v += lora_term(lora, token, cg);
+      if constexpr (LORA) v += lora_term_u(lora, utot + token * 16, cg);
+      else if (lora.u) v += lora_term(lora, token, cg);
       y[(int64_t)token * ldy + cg] = (uint16_t)f32_to_bf16_bits(v);
     }
   }
@@ -875,7 +952,7 @@ __global__ __launch_bounds__(1024) void skinny_lds_kernel(
 #define QG_PIPE_INTERLEAVE 1   // interleave the second k step's decode with the first step's MFMAs
 #endif
 
-template <int NWM, int NWN, int FM, bool PREP>
+template <int NWM, int NWN, int FM, bool PREP, bool LORA = false>
 struct PipeShape {
   static constexpr int T = 64 * NWM * NWN;               // threads
   static constexpr int NW = NWM * NWN;                   // waves
@@ -889,27 +966,29 @@ struct PipeShape {
   // sums of the BM tokens (slots 2 .. 2 + BM / 64 - 1); other slots are filler
   static constexpr int MSLOTS = 2 + (PREP ? BM / 64 : 0);
   static constexpr int ML = (MSLOTS + NW - 1) / NW;      // metadata loads per thread
-  static constexpr int LOADS = XL + WL + ML;             // direct loads per thread per stage
-  static constexpr int X_DW = 4 * X_SLOTS, W_DW = 8 * BN, M_DW = 64 * NW * ML;
-  static constexpr int STAGE_DW = X_DW + W_DW + M_DW;    // dwords of LDS per stage
+  // LoRA: the stage's 16 x 64 block of lora_A (512 dwords, 4-byte loads)
+  static constexpr int AL = LORA ? 512 / T : 0;
+  static constexpr int LOADS = XL + WL + ML + AL;        // direct loads per thread per stage
+  static constexpr int X_DW = 4 * X_SLOTS, W_DW = 8 * BN, M_DW = 64 * NW * ML, A_DW = LORA ? 512 : 0;
+  static constexpr int STAGE_DW = X_DW + W_DW + M_DW + A_DW;   // dwords of LDS per stage
   static constexpr int OP = BN + 8;                      // output tile row pitch (bf16)
   static_assert(X_SLOTS % T == 0, "activation chunks per thread");
   static_assert((8 * BN) % T == 0, "word loads per thread");
   static_assert(BN == 128 && BM % 64 == 0, "metadata slots");
+  static_assert(!LORA || (512 % T == 0 && NWN == 2), "lora_A block loads; two column waves share U");
 };
 
-template <int NWM, int NWN, int FM, int STAGES, bool PREP>
+template <int NWM, int NWN, int FM, int STAGES, bool PREP, bool LORA>
 __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(2))) void int4_pipe_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
     const float* __restrict__ xsum, uint16_t* __restrict__ y, int64_t ldy, int m, int n, int k,
     int tiles_n, int items, int items_per_xcd, int vec_store, int ksplit, int gps,
     float* __restrict__ partials, uint32_t* __restrict__ tickets, LoraEpi lora) {
-  using S = PipeShape<NWM, NWN, FM, PREP>;
+  using S = PipeShape<NWM, NWN, FM, PREP, LORA>;
   constexpr int T = S::T, BM = S::BM, BN = S::BN, XL = S::XL, WL = S::WL, LOADS = S::LOADS;
   static_assert(LOADS * (STAGES - 2) <= 63, "vmcnt range");
   extern __shared__ __attribute__((aligned(16))) uint32_t psm_i4[];
-  __shared__ int last_slice;
 
   // item = tile * ksplit + k-slice; the slices of a tile are consecutive items,
   // so they run on one XCD
@@ -967,6 +1046,16 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
       moff[i] = (uint32_t)(zlane * 4);
     }
   }
+  // LoRA: dword d = T i + 64 wave + lane of the stage's lora_A block holds
+  // rank r = d / 32, 16-byte slot c = (d % 32) / 4, dword d % 4, where slot c of
+  // row r carries the row's chunk c ^ (r & 7) (8 k each): the 16 ranks of an
+  // operand read then spread over the banks.  Ranks past the rank read row 0.
+  uint32_t aoff[S::AL > 0 ? S::AL : 1];
+#pragma unroll
+  for (int i = 0; i < S::AL; ++i) {
+    const int d = T * i + 64 * wave + lane, r = d >> 5, c = (d & 31) >> 2;
+    aoff[i] = (uint32_t)(((r < lora.rank ? (int64_t)r * lora.lda : 0) + 8 * (c ^ (r & 7)) + 2 * (d & 3)) * 2);
+  }
   const uint16_t* xbase = x + (int64_t)m0 * ldx;
   const uint32_t* wbase0 = qweight + n0;
 
@@ -991,9 +1080,19 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
       else if (j >= 2 && j < S::MSLOTS) buffer_to_lds4(xsum + g * m + m0, moff[i], wl + S::W_DW + 64 * j);
       else if (qzeros) buffer_to_lds4(qzeros + g * (n >> 3) + (n0 >> 3), moff[i], wl + S::W_DW + 64 * j);
     }
+    if constexpr (LORA) {
+      uint32_t* al = wl + S::W_DW + S::M_DW;
+      const uint16_t* abase = lora.a + 64 * (int64_t)(kt0 + st);
+#pragma unroll
+      for (int i = 0; i < S::AL; ++i) buffer_to_lds4(abase, aoff[i], al + T * i + 64 * wave);
+    }
   };
 
   f32x4 total[FM][4], acc[FM][4], xs[PREP ? 1 : FM];
+  f32x4 uacc[LORA ? FM : 1];   // LoRA: this wave's share of U for its rows (rank = lane % 16)
+#pragma unroll
+  for (int f = 0; f < (LORA ? FM : 1); ++f) uacc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int wn = wave / NWM;     // column wave: takes U for k step wn of each stage
 #pragma unroll
   for (int f = 0; f < FM; ++f)
 #pragma unroll
@@ -1101,6 +1200,19 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
           for (int c = 0; c < 4; ++c) acc[f][c] = mfma16_bf16(ap[f], b[c], first ? zero : acc[f][c]);
         }
+        if constexpr (LORA) {
+          // U[rows][rank] += x . lora_A^T for this k step, by one of the two column
+          // waves (the other takes the stage's other step): lora_A row cl, chunk
+          // 4 s + ks, in the activations' pair order
+          if (wn == s) {
+            const uint32_t* al = psm_i4 + (size_t)(kt % STAGES) * S::STAGE_DW + S::X_DW + S::W_DW + S::M_DW;
+            const int q = 4 * s + ks;
+            const u32x4 raw = *reinterpret_cast<const u32x4*>(al + 32 * cl + 4 * (q ^ (cl & 7)));
+            const u32x4 av = cl < lora.rank ? x_pairs_permuted(raw) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int f = 0; f < FM; ++f) uacc[f] = mfma16_bf16(ap[f], av, uacc[f]);
+          }
+        }
         if (s == 0) {
           // the second step's words (fw now holds them once the reads above
           // land) are decoded while the first step's MFMAs run: the matrix
@@ -1169,6 +1281,55 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
       }
     }
   }
+  if constexpr (LORA) {
+    // total += scale * U . B^T for this slice's U (the sum over slices is linear,
+    // so every slice adds its own).  The two column waves' shares of U meet in
+    // LDS (the stages are done); then four 16x16x4 fp32 MFMAs per 16 x 16 block
+    // with a block's U rows as A and its columns of B as B, as for a precomputed U.
+    __syncthreads();
+    float* ul = reinterpret_cast<float*>(psm_i4);   // [NWN][BM][16]
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) ul[(wn * BM + wm0 + 16 * f + 4 * ks + v) * 16 + cl] = uacc[f][v];
+    __syncthreads();
+    f32x4 ua[FM];
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+      const int row = wm0 + 16 * f + cl;
+      const f32x4 u0 = *reinterpret_cast<const f32x4*>(ul + row * 16 + 4 * ks);
+      const f32x4 u1 = *reinterpret_cast<const f32x4*>(ul + (BM + row) * 16 + 4 * ks);
+      ua[f] = u0 + u1;
+    }
+    float bb[4][4];
+    const bool bvec = lora.ldb >= 16 && (lora.ldb & 3) == 0 && ((uintptr_t)lora.b & 7u) == 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int64_t col = n0 + wn0 + 4 * cl + c;
+      const uint16_t* brow = lora.b + (col < n ? col : n - 1) * lora.ldb;
+      uint32_t hh[4];
+      if (bvec) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(brow + 4 * ks);
+        hh[0] = w[0] & 0xFFFFu; hh[1] = w[0] >> 16; hh[2] = w[1] & 0xFFFFu; hh[3] = w[1] >> 16;
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) hh[jj] = brow[4 * ks + jj < lora.rank ? 4 * ks + jj : 0];
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        bb[jj][c] = (col < n && 4 * ks + jj < lora.rank) ? bf16_bits_to_float(hh[jj]) : 0.f;
+    }
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        f32x4 lt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) lt = mfma16_f32(ua[f][jj], bb[jj][c], lt);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) total[f][c][v] = __builtin_fmaf(lora.scale, lt[v], total[f][c][v]);
+      }
+  }
   if (ksplit > 1) {
     // Split k: every slice stores its fp32 partial tile with agent-coherent
     // stores and takes a ticket; the last slice of the tile to arrive adds the
@@ -1197,10 +1358,10 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
     if (tid == 0)
-      last_slice = __hip_atomic_fetch_add(&tickets[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+      psm_i4[0] = __hip_atomic_fetch_add(&tickets[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                    (uint32_t)(ksplit - 1);
     __syncthreads();
-    if (!last_slice) return;
+    if (!psm_i4[0]) return;
     const uint64_t* base = reinterpret_cast<const uint64_t*>(partials) + (int64_t)t * ksplit * (BM * BN / 2);
     // slice by slice: the 8 FM pairs of a slice are loaded together (one round
     // trip per slice, not per element), then added; each element still sums
@@ -1434,20 +1595,22 @@ struct LdsPlan {
 #define QG_LDS_MANY_NG 2
 #endif
 
-static LdsPlan plan_lds(int64_t m, const SkinnyPlan& p, int64_t k, bool dot) {
+static LdsPlan plan_lds(int64_t m, const SkinnyPlan& p, int64_t k, bool dot, bool lora = false) {
   LdsPlan r{0, 0, 0, false, 0};
   const int64_t G = k / 128;
   if (m > 16 || p.ksplit != 1 || G < 1) return r;
   int ng = G <= 16 ? 1 : (G <= 32 ? 2 : (G <= 64 ? 4 : 0));
   if (p.nstrips > 256 && ng > 0 && ng < QG_LDS_MANY_NG && G > 8) ng = G <= 32 ? 2 : 4;
-  if (ng == 0 || ng * (p.cpl + 6) > 63) return r;
+  const int la = lora ? 4 : 0;                                 // lora_A loads per group
+  if (ng == 0 || ng * (p.cpl + 6 + la) > 63) return r;
   const int waves = (int)((G + ng - 1) / ng);
-  const size_t plane = (size_t)waves * m * 16 * p.cpl * 4;
+  // epilogue: the wave partial plane, and with LoRA the wave partials of U and U
+  const size_t plane = (size_t)waves * m * 16 * p.cpl * 4 + (lora ? (size_t)(waves + 1) * m * 16 * 4 : 0);
   const int xi = dot ? 1 : (int)((m + 3) / 4);                 // activation loads per group
   // the activations join the codes in LDS when both fit (strips of 16 and 32
   // columns) and the workgroups still take one pass; else they go to registers
   for (int xl = 1; xl >= 0; --xl) {
-    if (xl && (p.cpl > 2 || ng * (p.cpl + xi + 2) > 63)) continue;
+    if (xl && (p.cpl > 2 || ng * (p.cpl + xi + 2 + la) > 63)) continue;
     const size_t codes = (size_t)G * 16 * 16 * p.cpl * 4 + (xl ? (size_t)G * (dot ? 256 : 1024 * xi) : 0);
     size_t lds = codes + plane;
     int plane_off = (int)codes;
@@ -1469,19 +1632,25 @@ static LdsPlan plan_lds(int64_t m, const SkinnyPlan& p, int64_t k, bool dot) {
   return r;
 }
 
+template <int M, bool DOT, int CPL, int NG, bool XL, bool LORA>
+static void lds_launch_k(const Int4Args& a, const SkinnyPlan& p, const LdsPlan& l, hipStream_t stream) {
+  skinny_lds_kernel<M, DOT, CPL, NG, XL, LORA><<<dim3((unsigned)p.blocks), dim3(64 * l.waves), l.lds, stream>>>(
+      a.x, a.ldx, a.qweight, a.scales, a.qzeros, a.y, a.ldy, (int)a.n, (int)a.k, p.nstrips, p.items_per_xcd,
+      l.plane_off, a.lora);
+}
+
 template <int M, bool DOT, int CPL, int NG>
 static void lds_launch(const Int4Args& a, const SkinnyPlan& p, const LdsPlan& l, hipStream_t stream) {
+  const bool lora = a.lora.a != nullptr;
   if constexpr (CPL <= 2) {
     if (l.xl) {
-      skinny_lds_kernel<M, DOT, CPL, NG, true><<<dim3((unsigned)p.blocks), dim3(64 * l.waves), l.lds, stream>>>(
-          a.x, a.ldx, a.qweight, a.scales, a.qzeros, a.y, a.ldy, (int)a.n, (int)a.k, p.nstrips, p.items_per_xcd,
-          l.plane_off, a.lora);
+      if (lora) lds_launch_k<M, DOT, CPL, NG, true, true>(a, p, l, stream);
+      else lds_launch_k<M, DOT, CPL, NG, true, false>(a, p, l, stream);
       return;
     }
   }
-  skinny_lds_kernel<M, DOT, CPL, NG, false><<<dim3((unsigned)p.blocks), dim3(64 * l.waves), l.lds, stream>>>(
-      a.x, a.ldx, a.qweight, a.scales, a.qzeros, a.y, a.ldy, (int)a.n, (int)a.k, p.nstrips, p.items_per_xcd,
-      l.plane_off, a.lora);
+  if (lora) lds_launch_k<M, DOT, CPL, NG, false, true>(a, p, l, stream);
+  else lds_launch_k<M, DOT, CPL, NG, false, false>(a, p, l, stream);
 }
 
 template <int M, bool DOT, int CPL>
@@ -1497,13 +1666,34 @@ static bool lds_launch_c(const Int4Args& a, const SkinnyPlan& p, hipStream_t str
   if constexpr (M > 16) {
     return false;
   } else {
-    const LdsPlan l = plan_lds(M, p, a.k, DOT);
+    const LdsPlan l = plan_lds(M, p, a.k, DOT, a.lora.a != nullptr);
     if (l.ng == 0) return false;
     if (p.cpl == 4) lds_launch_n<M, DOT, 4>(a, p, l, stream);
     else if (p.cpl == 2) lds_launch_n<M, DOT, 2>(a, p, l, stream);
     else lds_launch_n<M, DOT, 1>(a, p, l, stream);
     return true;
   }
+}
+
+// Where U goes (measured, cold weights, rank 16; ratio to the plain product):
+// the LDS-staged small-M kernel accumulates it from the activations it already
+// holds -- 4096 x 4096 m = 1 / 8 / 15 1.52 / 1.49 / 1.51 (two extra launches
+// first: 1.97 / 1.82 / 1.72), 2048 x 8192 1.30 / 1.35 / 1.32 (2.05 / 1.99 /
+// 1.89).  The MFMA tiles recompute U in every column tile (an extra 16-column
+// MFMA per k step and row fragment, +12.5%), which beats two launches only
+// for short products: 4096 x 4096 m = 130 1.13 (1.20), but 25600 x 5120
+// m = 512 1.16 (1.08) and 5120 x 25600 m = 2048 1.20 (1.05); so the tiles
+// take U in the launch up to 2^34 flops.  The register-staged small-M kernel
+// (k splits, 17..64 tokens) has no registers to spare for it.
+#ifndef QG_LORA_TILE_MAX_FLOPS
+#define QG_LORA_TILE_MAX_FLOPS 17179869184.0
+#endif
+bool lora_in_launch(const Int4Args& a, int path, int64_t ws_bytes) {
+  if (path == 3) return 2.0 * (double)a.m * (double)a.n * (double)a.k <= QG_LORA_TILE_MAX_FLOPS;
+  if (a.m > 16) return false;
+  const bool dot = path == 1;
+  const SkinnyPlan p = plan_skinny(dot ? 1 : a.m, a.n, a.k, ws_bytes, dot);
+  return plan_lds(dot ? 1 : a.m, p, a.k, dot, true).ng > 0;
 }
 
 hipError_t launch_gemv_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream) {
@@ -1621,9 +1811,9 @@ struct PipeCfg {
   size_t lds;
 };
 
-template <int NWM, int NWN, int FM, int STAGES, bool PREP>
+template <int NWM, int NWN, int FM, int STAGES, bool PREP, bool LORA = false>
 static PipeCfg pipe_cfg() {
-  using S = PipeShape<NWM, NWN, FM, PREP>;
+  using S = PipeShape<NWM, NWN, FM, PREP, LORA>;
   size_t lds = (size_t)STAGES * S::STAGE_DW * 4;
   const size_t out = (size_t)S::BM * S::OP * 2;
   return PipeCfg{S::BM, S::BN, STAGES, S::T, lds > out ? lds : out};
@@ -1727,16 +1917,36 @@ static PipeCfg pipe_cfg_of(int which) {
   }
 }
 
+// LDS of a workgroup must fit the 160 KiB of a CU (the kernel has no static
+// LDS: the k split's ticket flag lives in the dynamic area once the stages
+// are done).  With LoRA the stages also carry a block of lora_A; where four
+// such stages would not fit, three are used.
+constexpr size_t kLdsBytes = 160 * 1024;
+constexpr size_t kPipeStaticLds = 0;
+
 template <int NWM, int NWN, int FM, int STAGES, bool PREP>
 static void pipe_launch(const Int4Args& a, const MfmaPlan& p, const uint16_t* x, int64_t ldx,
                         const float* xsum, float* partials, uint32_t* tickets, hipStream_t stream) {
-  const PipeCfg c = pipe_cfg<NWM, NWN, FM, STAGES, PREP>();
+  using SL = PipeShape<NWM, NWN, FM, PREP, true>;
+  constexpr int LSTAGES = (size_t)STAGES * SL::STAGE_DW * 4 + kPipeStaticLds <= kLdsBytes ? STAGES : STAGES - 1;
+  static_assert((size_t)STAGES * PipeShape<NWM, NWN, FM, PREP>::STAGE_DW * 4 + kPipeStaticLds <= kLdsBytes,
+                "LDS budget");
+  static_assert((size_t)LSTAGES * SL::STAGE_DW * 4 + kPipeStaticLds <= kLdsBytes && LSTAGES >= 3, "LDS budget");
+  const bool lora = a.lora.a != nullptr;
+  const PipeCfg c = lora ? pipe_cfg<NWM, NWN, FM, LSTAGES, PREP, true>() : pipe_cfg<NWM, NWN, FM, STAGES, PREP>();
   const int tiles_n = (int)((a.n + c.bn - 1) / c.bn);
   const int items = (int)(p.tiles * p.ksplit), per_xcd = (items + 7) / 8;
   const int vec = ((uintptr_t)a.y & 15u) == 0 && a.ldy % 8 == 0;
-  int4_pipe_kernel<NWM, NWN, FM, STAGES, PREP><<<dim3((unsigned)(per_xcd * 8)), dim3(c.threads), c.lds, stream>>>(
-      x, ldx, a.qweight, a.scales, a.qzeros, xsum, a.y, a.ldy, (int)a.m, (int)a.n, (int)a.k, tiles_n,
-      items, per_xcd, vec, p.ksplit, p.gps, partials, tickets, a.lora);
+  if (lora)
+    int4_pipe_kernel<NWM, NWN, FM, LSTAGES, PREP, true><<<dim3((unsigned)(per_xcd * 8)), dim3(c.threads), c.lds,
+                                                           stream>>>(
+        x, ldx, a.qweight, a.scales, a.qzeros, xsum, a.y, a.ldy, (int)a.m, (int)a.n, (int)a.k, tiles_n, items,
+        per_xcd, vec, p.ksplit, p.gps, partials, tickets, a.lora);
+  else
+    int4_pipe_kernel<NWM, NWN, FM, STAGES, PREP, false><<<dim3((unsigned)(per_xcd * 8)), dim3(c.threads), c.lds,
+                                                           stream>>>(
+        x, ldx, a.qweight, a.scales, a.qzeros, xsum, a.y, a.ldy, (int)a.m, (int)a.n, (int)a.k, tiles_n, items,
+        per_xcd, vec, p.ksplit, p.gps, partials, tickets, a.lora);
 }
 
 template <bool PREP>

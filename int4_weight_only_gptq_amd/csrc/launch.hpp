@@ -8,13 +8,16 @@
 namespace qg {
 
 // LoRA add in the epilogue of an int4 product: Y += scale * U . B^T with
-// U = X . A^T (fp32 [m][16], columns >= rank zero) computed beforehand.
+// U = X . A^T (fp32, columns >= rank zero).  Either U was computed beforehand
+// (u: [m][16]) or the product's kernel accumulates it from lora_A itself (a).
 struct LoraEpi {
-  const float* u;         // nullptr: no adapter
+  const float* u;         // precomputed U, or nullptr
   const uint16_t* b;      // lora_B bf16 [n][ldb], the first `rank` entries of each row used
   int64_t ldb;
   int rank;
   float scale;
+  const uint16_t* a;      // lora_A bf16 [rank][lda] for U inside the product's launch, or nullptr
+  int64_t lda;
 };
 
 struct Int4Args {
@@ -58,6 +61,10 @@ hipError_t launch_gemv_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipSt
 hipError_t launch_fused_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream);
 // With ws_bytes >= workspace_int4(m, n, k, 3): a preparation pass into ws first.
 hipError_t launch_mfma_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream);
+
+// True when the kernel that path (1 GEMV, 2 fused, 3 MFMA) launches for these
+// arguments and workspace accumulates the LoRA intermediate U itself (lora.a).
+bool lora_in_launch(const Int4Args& a, int path, int64_t ws_bytes);
 
 // Workspace bytes a path (1 GEMV, 2 fused, 3 MFMA) can use; 0 if none.
 int64_t workspace_int4(int64_t m, int64_t n, int64_t k, int path);

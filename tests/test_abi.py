@@ -103,6 +103,7 @@ def lora(lib, x=A16, ldx=256, qw=A16, sc=A16, qz=A16, la=A16, lda=256, lb=A16, l
 @pytest.mark.parametrize("kw,code", [
     (dict(rank=0), SHAPE), (dict(rank=17), SHAPE), (dict(la=0), NULL), (dict(lb=0), NULL),
     (dict(lda=128), SHAPE), (dict(ldb=8), SHAPE), (dict(la=A16 + 8), ALIGN), (dict(lda=260), ALIGN),
+    (dict(lda=(1 << 22) + 8), SHAPE),
     (dict(lb=A16 + 1), ALIGN), (dict(ws=None, wsb=0), SHAPE), (dict(wsb=32), SHAPE),
     (dict(x=MIS), ALIGN), (dict(gs=64), UNSUP), (dict(y=0), NULL),
     (dict(m=0, x=0, qw=0, sc=0, qz=0, la=0, lb=0, y=0, ws=None, wsb=0), OK),

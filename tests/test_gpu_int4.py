@@ -395,7 +395,10 @@ LORA_CASES = [("gemv", 1, 1152, 776, 16), ("fused", 2, 2048, 1040, 16), ("fused"
               ("gemv", 1, 16384, 520, 16), ("fused", 8, 16384, 520, 16), ("mfma", 33, 4096, 520, 16),
               ("auto", 24, 2048, 1040, 16), ("auto", 32, 16384, 520, 5), ("auto", 31, 1152, 776, 1),   # two row tiles
               ("auto", 40, 2048, 1040, 16), ("auto", 64, 16384, 264, 3),   # three / four row tiles
-              ("fused", 4, 16384, 520, 16)]   # idle waves
+              ("fused", 4, 16384, 520, 16),   # idle waves
+              # U accumulated in the product's launch: the LDS-staged kernel with the
+              # activations in registers (two workgroups per CU) and with 64-column strips
+              ("fused", 15, 2048, 5632, 16), ("auto", 1, 4096, 14336, 7), ("fused", 3, 4096, 14336, 16)]
 
 
 @pytest.mark.parametrize("path,m,k,n,rank", LORA_CASES)
@@ -424,7 +427,10 @@ def test_lora_paths_match_oracle(gpu_lib, path, m, k, n, rank):
     assert_accepted(host_u16(y2), ref, ("lora-min-ws", path, m, k, n, rank))
 
 
-@pytest.mark.parametrize("m,k,n", [(1, 4096, 4096), (15, 2048, 8192), (512, 5120, 25600)])
+# (1024 x 1024 x 8192: the 256 x 128 tiles with U in the launch, 2^34 flops; 512 x 2048 x
+# 8192: 128 x 128 tiles, U in the launch; 512 x 5120 x 25600: U in two small launches first)
+@pytest.mark.parametrize("m,k,n", [(1, 4096, 4096), (15, 2048, 8192), (512, 5120, 25600), (512, 2048, 8192),
+                                   (1024, 1024, 8192), (8, 4096, 4096)])
 def test_lora_full_size_sampled(gpu_lib, m, k, n):
     import torch
 
