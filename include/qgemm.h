@@ -162,6 +162,32 @@ int32_t qgemm_int4_lora(const void* x, int64_t ldx, const uint32_t* qweight, con
                         int64_t n, int64_t k, int32_t group_size, int32_t path, void* workspace,
                         int64_t workspace_bytes, void* stream);
 
+/*
+ * qgemm_int4_epilogue -- qgemm_int4 with the fused epilogues of a linear layer
+ * in the product's launch (mi50grad README, "Key Optimizations": the FFN
+ * down-projection's GEMV, all-reduce and RMSNorm in one kernel, the RMSNorm's
+ * sum of squares taken over the whole output row; BC-250 post, "Where the
+ * time went": LoRA adapters on every linear layer):
+ *
+ *   - the LoRA add of qgemm_int4_lora when lora_a != NULL (same arguments,
+ *     limits and workspace rule); lora_a == NULL: no adapter (lora_b, rank and
+ *     lora_scale are ignored; the workspace is optional as in qgemm_int4);
+ *   - the row reduction of an RMSNorm when row_sumsq != NULL: fp32 [m] device
+ *     vector (4-byte aligned), to which the call adds, for every row r,
+ *       row_sumsq[r] += sum_j float(Y[r][j])^2,
+ *     the squares of the rounded bf16 outputs accumulated in fp32.  Zero it
+ *     first for a fresh sum.  The partial sums of the column strips / tiles
+ *     are added with fp32 atomics, so their order (and the last bits) can
+ *     differ from call to call; Y itself is deterministic.
+ *
+ * Other arguments, limits and errors as qgemm_int4 / qgemm_int4_lora.
+ */
+int32_t qgemm_int4_epilogue(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
+                            const uint32_t* qzeros, const void* lora_a, int64_t lda_a, const void* lora_b,
+                            int64_t ldb_b, int32_t rank, float lora_scale, float* row_sumsq, void* y,
+                            int64_t ldy, int64_t m, int64_t n, int64_t k, int32_t group_size, int32_t path,
+                            void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Workspace bytes for qgemm_int4_lora (U plus what the path can use); < 0: -error. */
 int64_t qgemm_int4_lora_workspace_size(int64_t m, int64_t n, int64_t k, int32_t path);
 

@@ -11,7 +11,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["load", "lib_path", "QGemmError", "qgemm_int4", "qgemm_int4_noalloc", "qgemm_int4_lora", "qgemm_int4_dequant", "gemm_dense",
+__all__ = ["load", "lib_path", "QGemmError", "qgemm_int4", "qgemm_int4_noalloc", "qgemm_int4_lora",
+           "qgemm_int4_epilogue", "qgemm_int4_dequant", "gemm_dense",
            "gemm_dense_batched", "describe_int4",
            "workspace_size", "probe_mfma_bf16", "probe_copy", "probe_read",
            "abi_version", "PATHS", "LAYOUTS"]
@@ -71,6 +72,9 @@ def load():
     lib.qgemm_int4_lora.restype = i32
     lib.qgemm_int4_lora.argtypes = [vp, i64, vp, vp, vp, vp, i64, vp, i64, i32, ctypes.c_float, vp, i64,
                                     i64, i64, i64, i32, i32, vp, i64, vp]
+    lib.qgemm_int4_epilogue.restype = i32
+    lib.qgemm_int4_epilogue.argtypes = [vp, i64, vp, vp, vp, vp, i64, vp, i64, i32, ctypes.c_float, vp, vp,
+                                        i64, i64, i64, i64, i32, i32, vp, i64, vp]
     lib.qgemm_int4_lora_workspace_size.restype = i64
     lib.qgemm_int4_lora_workspace_size.argtypes = [i64, i64, i64, i32]
     lib.gemm_dense.restype = i32
@@ -238,6 +242,41 @@ def qgemm_int4_lora(x, qweight, scales, qzeros, lora_a, lora_b, lora_scale: floa
                              float(lora_scale), out.data_ptr(), _ld(out), m, n, k, group_size, PATHS[path],
                              wptr, wbytes, sh)
     _check(st, "qgemm_int4_lora")
+    return out
+
+
+def qgemm_int4_epilogue(x, qweight, scales, qzeros, lora_a=None, lora_b=None, lora_scale: float = 1.0,
+                        row_sumsq=None, out=None, group_size: int = 128, path: str = "auto", workspace=None,
+                        stream=None):
+    """qgemm_int4 with the fused epilogues: the LoRA add (lora_a, lora_b given) and/or
+    the row reduction row_sumsq[r] += sum_j y[r][j]^2 (fp32 [m] tensor, accumulated)."""
+    import torch
+
+    lib = load()
+    m, k = x.shape
+    n = qweight.shape[1]
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if row_sumsq is not None and (row_sumsq.dtype != torch.float32 or row_sumsq.numel() < m):
+        raise TypeError("row_sumsq must be a float32 tensor of m elements")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    sh = _stream(x, stream)
+    rank = 0 if lora_a is None else lora_a.shape[0]
+    if workspace is None:
+        size = (lib.qgemm_int4_lora_workspace_size(m, n, k, PATHS[path]) if lora_a is not None
+                else lib.qgemm_int4_workspace_size(m, n, k, PATHS[path]))
+        if size < 0:
+            raise QGemmError(-size, "qgemm_int4_epilogue workspace size")
+        workspace = _workspace(x.device, stream, size)
+    wptr = None if workspace is None or workspace is False else workspace.data_ptr()
+    wbytes = 0 if wptr is None else workspace.numel() * workspace.element_size()
+    st = lib.qgemm_int4_epilogue(x.data_ptr(), _ld(x), qweight.data_ptr(), scales.data_ptr(), _ptr(qzeros),
+                                 _ptr(lora_a), _ld(lora_a) if lora_a is not None else 0, _ptr(lora_b),
+                                 _ld(lora_b) if lora_b is not None else 0, rank, float(lora_scale),
+                                 _ptr(row_sumsq), out.data_ptr(), _ld(out), m, n, k, group_size, PATHS[path],
+                                 wptr, wbytes, sh)
+    _check(st, "qgemm_int4_epilogue")
     return out
 
 

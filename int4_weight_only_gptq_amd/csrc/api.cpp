@@ -105,7 +105,8 @@ int64_t lora_u_bytes(int64_t m, int64_t k) { return qg::lora_bytes(m, k); }
 int32_t run_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
                  const uint32_t* qzeros, void* y, int64_t ldy, int64_t m, int64_t n, int64_t k,
                  int32_t group_size, int32_t path, void* ws, int64_t ws_bytes, void* stream,
-                 const qg::LoraEpi* lora = nullptr, const void* lora_a = nullptr, int64_t lda_a = 0) {
+                 const qg::LoraEpi* lora = nullptr, const void* lora_a = nullptr, int64_t lda_a = 0,
+                 float* row_ss = nullptr) {
   int32_t st = check_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size);
   if (st != QG_OK) return st;
   st = check_path(m, path);
@@ -116,6 +117,7 @@ int32_t run_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint
   hipStream_t s = (hipStream_t)stream;
   if (k == 0) return hip_status(qg::launch_zero16((uint16_t*)y, m, n, ldy, s));
   qg::Int4Args a{(const uint16_t*)x, ldx, qweight, scales, qzeros, (uint16_t*)y, ldy, m, n, k};
+  a.lora.row_ss = row_ss;
   if (ws == nullptr) ws_bytes = 0;
   const int32_t rp = resolve_path(m, n, k, path);
   if (lora != nullptr) {
@@ -127,6 +129,7 @@ int32_t run_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint
     a.lora = *lora;
     a.lora.a = (const uint16_t*)lora_a;
     a.lora.lda = lda_a;
+    a.lora.row_ss = row_ss;
     if (!qg::lora_in_launch(a, rp, rest)) {
       float* u = (float*)((char*)ws + rest);
       st = hip_status(qg::launch_lora_u((const uint16_t*)x, ldx, (const uint16_t*)lora_a, lda_a, lora->rank, m,
@@ -151,6 +154,12 @@ int32_t run_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
+
+int32_t qgemm_int4_lora_rss(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
+                            const uint32_t* qzeros, const void* lora_a, int64_t lda_a, const void* lora_b,
+                            int64_t ldb_b, int32_t rank, float lora_scale, float* row_sumsq, void* y,
+                            int64_t ldy, int64_t m, int64_t n, int64_t k, int32_t group_size, int32_t path,
+                            void* workspace, int64_t workspace_bytes, void* stream);
 
 int32_t noalloc_scratch(hipStream_t stream, void** out) {
   int dev = -1;
@@ -226,11 +235,43 @@ int32_t qgemm_int4_path(const void* x, int64_t ldx, const uint32_t* qweight,
                   workspace_bytes, stream);
 }
 
+int32_t qgemm_int4_epilogue(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
+                            const uint32_t* qzeros, const void* lora_a, int64_t lda_a, const void* lora_b,
+                            int64_t ldb_b, int32_t rank, float lora_scale, float* row_sumsq, void* y,
+                            int64_t ldy, int64_t m, int64_t n, int64_t k, int32_t group_size, int32_t path,
+                            void* workspace, int64_t workspace_bytes, void* stream) {
+  if (row_sumsq != nullptr && !aligned(row_sumsq, 4)) return QG_ERR_ALIGN;
+  if (lora_a == nullptr) {
+    const int32_t st = check_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size);
+    if (st != QG_OK) return st;
+    if (m == 0 || n == 0 || k == 0)   // k == 0: zeros, whose squares add nothing
+      return run_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size, path, workspace,
+                      workspace_bytes, stream);
+    return run_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size, path, workspace,
+                    workspace_bytes, stream, nullptr, nullptr, 0, row_sumsq);
+  }
+  return qgemm_int4_lora_rss(x, ldx, qweight, scales, qzeros, lora_a, lda_a, lora_b, ldb_b, rank, lora_scale,
+                             row_sumsq, y, ldy, m, n, k, group_size, path, workspace, workspace_bytes, stream);
+}
+
 int32_t qgemm_int4_lora(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
                         const uint32_t* qzeros, const void* lora_a, int64_t lda_a, const void* lora_b,
                         int64_t ldb_b, int32_t rank, float lora_scale, void* y, int64_t ldy, int64_t m,
                         int64_t n, int64_t k, int32_t group_size, int32_t path, void* workspace,
                         int64_t workspace_bytes, void* stream) {
+  return qgemm_int4_lora_rss(x, ldx, qweight, scales, qzeros, lora_a, lda_a, lora_b, ldb_b, rank, lora_scale,
+                             nullptr, y, ldy, m, n, k, group_size, path, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int32_t qgemm_int4_lora_rss(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
+                            const uint32_t* qzeros, const void* lora_a, int64_t lda_a, const void* lora_b,
+                            int64_t ldb_b, int32_t rank, float lora_scale, float* row_sumsq, void* y,
+                            int64_t ldy, int64_t m, int64_t n, int64_t k, int32_t group_size, int32_t path,
+                            void* workspace, int64_t workspace_bytes, void* stream) {
   if (rank < 1 || rank > 16) return QG_ERR_SHAPE;
   if (m > 0 && n > 0 && k > 0) {
     if (lora_a == nullptr || lora_b == nullptr) return QG_ERR_NULL;
@@ -241,10 +282,14 @@ int32_t qgemm_int4_lora(const void* x, int64_t ldx, const uint32_t* qweight, con
   if (m > 0 && n > 0 && k == 0)      // U = 0: the plain product (zeros)
     return run_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size, path, workspace,
                     workspace_bytes, stream);
-  const qg::LoraEpi l{nullptr, (const uint16_t*)lora_b, ldb_b, rank, lora_scale, nullptr, 0};
+  const qg::LoraEpi l{nullptr, (const uint16_t*)lora_b, ldb_b, rank, lora_scale, nullptr, 0, nullptr};
   return run_int4(x, ldx, qweight, scales, qzeros, y, ldy, m, n, k, group_size, path, workspace,
-                  workspace_bytes, stream, &l, lora_a, lda_a);
+                  workspace_bytes, stream, &l, lora_a, lda_a, row_sumsq);
 }
+
+}  // namespace
+
+extern "C" {
 
 int64_t qgemm_int4_lora_workspace_size(int64_t m, int64_t n, int64_t k, int32_t path) {
   const int64_t base = qgemm_int4_workspace_size(m, n, k, path);

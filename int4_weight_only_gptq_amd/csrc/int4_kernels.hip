@@ -189,6 +189,18 @@ __device__ __forceinline__ void load_group(GroupRegs<M, DOT, CPL>& r, const uint
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __builtin_bit_cast(float, h << 16); }
 
+// Row reduction of the epilogue: q is this lane's sum of squares of its
+// rounded outputs of one row (0 without one); the G lanes of an aligned group
+// (all on the same row) add theirs with cross-lane swaps, and the group's
+// first lane adds the total to row_ss[row] with one atomic.  Every lane of a
+// group must come here together.
+template <int G>
+__device__ __forceinline__ void add_row_sumsq(float* row_ss, float q, int64_t row, bool first, bool valid) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) q += __shfl_xor(q, o, G);
+  if (first && valid) atomicAdd(row_ss + row, q);
+}
+
 // The LoRA term of one output (row, col): scale * sum_r U[row][r] B[col][r].
 // All loads are issued before the first use (one round trip): the U row as
 // four 16-byte loads, the B row as two when its 16 entries are aligned (else
@@ -571,7 +583,12 @@ __global__ __launch_bounds__(M > 16 ? 512 : 1024) void skinny_int4_kernel(
       v += jo < 4 ? pre : lora_term(lora, token, cg);
     }
     if (ksplit == 1) {
-      if (cg < n) y[(int64_t)token * ldy + cg] = (uint16_t)f32_to_bf16_bits(v);
+      const uint32_t yb = f32_to_bf16_bits(v);
+      if (cg < n) y[(int64_t)token * ldy + cg] = (uint16_t)yb;
+      if (lora.row_ss) {
+        const float yf = cg < n ? bf16_bits_to_float(yb) : 0.f;
+        add_row_sumsq<SW>(lora.row_ss, yf * yf, token, cc == 0, true);
+      }
     } else {
       // agent-coherent store: visible to any workgroup once it has completed
       __hip_atomic_store(&mine[o], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -603,7 +620,12 @@ __global__ __launch_bounds__(M > 16 ? 512 : 1024) void skinny_int4_kernel(
     float v = 0.f;
 #pragma unroll
     for (int p = 0; p < SK_MAX_SPLIT; ++p) v += part[p];
-    if (cg < n) y[(int64_t)token * ldy + cg] = (uint16_t)f32_to_bf16_bits(v);
+    const uint32_t yb = f32_to_bf16_bits(v);
+    if (cg < n) y[(int64_t)token * ldy + cg] = (uint16_t)yb;
+    if (lora.row_ss) {
+      const float yf = cg < n ? bf16_bits_to_float(yb) : 0.f;
+      add_row_sumsq<SW>(lora.row_ss, yf * yf, token, cc == 0, true);
+    }
   }
   if (tid == 0) __hip_atomic_store(&tickets[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -916,11 +938,15 @@ __global__ __launch_bounds__(1024) void skinny_lds_kernel(
     float v = 0.f;
     for (int w = 0; w < nw; ++w) v += plane[(w * M + token) * SW + cc];
     const int64_t cg = col0 + cc;
+    float yf = 0.f;
     if (cg < n) {
       if constexpr (LORA) v += lora_term_u(lora, utot + token * 16, cg);
       else if (lora.u) v += lora_term(lora, token, cg);
-      y[(int64_t)token * ldy + cg] = (uint16_t)f32_to_bf16_bits(v);
+      const uint32_t yb = f32_to_bf16_bits(v);
+      y[(int64_t)token * ldy + cg] = (uint16_t)yb;
+      yf = bf16_bits_to_float(yb);
     }
+    if (lora.row_ss) add_row_sumsq<SW>(lora.row_ss, yf * yf, token, cc == 0, true);
   }
 }
 
@@ -1412,14 +1438,29 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
   for (int c = tid; c < BM * CPR; c += T) {
     const int r = c / CPR, cc = c - r * CPR;
     const int gr = m0 + r, gc = n0 + 8 * cc;
-    if (gr >= m || gc >= n) continue;
+    const bool in = gr < m && gc < n;
     const uint16_t* src = &osm[r * S::OP + 8 * cc];
-    uint16_t* dst = y + (int64_t)gr * ldy + gc;
-    if (vec_store) {
-      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
-    } else {
-      reinterpret_cast<u32x2*>(dst)[0] = reinterpret_cast<const u32x2*>(src)[0];
-      reinterpret_cast<u32x2*>(dst)[1] = reinterpret_cast<const u32x2*>(src)[1];
+    if (in) {
+      uint16_t* dst = y + (int64_t)gr * ldy + gc;
+      if (vec_store) {
+        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+      } else {
+        reinterpret_cast<u32x2*>(dst)[0] = reinterpret_cast<const u32x2*>(src)[0];
+        reinterpret_cast<u32x2*>(dst)[1] = reinterpret_cast<const u32x2*>(src)[1];
+      }
+    }
+    if (lora.row_ss) {   // the CPR lanes of a row: one aligned group
+      float q = 0.f;
+      if (in) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float lo = bf16_bits_to_float(w[i] & 0xFFFFu), hi = bf16_bits_to_float(w[i] >> 16);
+          q = __builtin_fmaf(lo, lo, q);
+          q = __builtin_fmaf(hi, hi, q);
+        }
+      }
+      add_row_sumsq<CPR>(lora.row_ss, q, gr, cc == 0, gr < m);
     }
   }
 }

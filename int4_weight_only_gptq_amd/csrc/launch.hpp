@@ -18,6 +18,7 @@ struct LoraEpi {
   float scale;
   const uint16_t* a;      // lora_A bf16 [rank][lda] for U inside the product's launch, or nullptr
   int64_t lda;
+  float* row_ss;          // row reduction: += sum over j of y[r][j]^2 (rounded outputs), or nullptr
 };
 
 struct Int4Args {

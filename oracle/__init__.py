@@ -18,6 +18,8 @@ from .qgemm_oracle import (  # noqa: F401
     qgemm_int4_at,
     qgemm_int4_lora,
     qgemm_int4_lora_at,
+    row_sumsq,
+    row_sumsq_bound,
     dense,
     dense_at,
     dense_batched,

@@ -199,6 +199,26 @@ def qgemm_int4_lora_at(x_bits, qweight, scales, qzeros, a_bits, b_bits, lora_sca
     return y + float(lora_scale) * (u @ bf16_value(np.asarray(b_bits)[np.asarray(cols)]).T)
 
 
+def row_sumsq(y_bits, dtype: str = "bf16") -> np.ndarray:
+    """Per-row sum of squares of stored outputs, fp64: r[i] = sum_j y[i][j]^2.
+
+    The reduction an RMSNorm takes over a linear layer's output row (the
+    mi50grad README, "Key Optimizations": the fused GEMV + RMSNorm kernel sums
+    the squares over the whole row), here of the rounded outputs as stored.
+    """
+    y = _value(np.asarray(y_bits), dtype)
+    return np.sum(y * y, axis=-1)
+
+
+def row_sumsq_bound(y_bits, dtype: str = "bf16") -> np.ndarray:
+    """Bound on |fp32 sum - exact sum| for any order of adding the n squares in
+    fp32 (each square rounded once, then n - 1 roundings of partial sums of
+    nonnegative terms): (n + 1) * 2^-24 * sum_j y^2, plus the underflow floor."""
+    y = _value(np.asarray(y_bits), dtype)
+    n = y.shape[-1]
+    return (n + 1) * 2.0 ** -24 * np.sum(y * y, axis=-1) + n * 2.0 ** -149
+
+
 # ----------------------------------------------------------------------------
 # dense products
 # ----------------------------------------------------------------------------

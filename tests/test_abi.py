@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
         "qg_abi_version", "qg_status_str", "qg_last_hip_error", "qgemm_int4", "qgemm_int4_path",
         "qgemm_int4_workspace_size", "qgemm_int4_describe", "qgemm_int4_dequant", "gemm_dense",
         "gemm_dense_batched", "qgemm_int4_lora", "qgemm_int4_lora_workspace_size", "qg_probe_mfma_bf16",
-        "qg_probe_copy", "qg_probe_read", "qgemm_int4_noalloc"])
+        "qg_probe_copy", "qg_probe_read", "qgemm_int4_noalloc", "qgemm_int4_epilogue"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -110,6 +110,26 @@ def lora(lib, x=A16, ldx=256, qw=A16, sc=A16, qz=A16, la=A16, lda=256, lb=A16, l
 ])
 def test_int4_lora_rejects_invalid_arguments(lib, kw, code):
     assert lora(lib, **kw) == code
+
+
+def test_epilogue_rejects_invalid_arguments(lib):
+    f = lib.qgemm_int4_epilogue
+    # (x, ldx, qw, sc, qz, la, lda, lb, ldb, rank, scale, rss, y, ldy, m, n, k, gs, path, ws, wsb, stream)
+    base = [A16, 256, A16, A16, A16, None, 0, None, 0, 0, 1.0, A16, A16, 64, 1, 64, 256, 128, 0, None, 0, None]
+    assert f(*base[:11], A16 + 2, *base[12:]) == ALIGN                # misaligned row_sumsq
+    args = list(base)
+    args[16] = 200
+    assert f(*args) == SHAPE                                          # k % 128
+    args = list(base)
+    args[0] = 0
+    assert f(*args) == NULL
+    args = list(base)
+    args[14], args[0], args[2], args[3], args[4], args[12] = 0, 0, 0, 0, 0, 0
+    assert f(*args) == OK                                             # m == 0: no-op
+    # with an adapter: the LoRA checks (rank 17 is rejected)
+    args = list(base)
+    args[5], args[6], args[7], args[8], args[9], args[19], args[20] = A16, 256, A16, 16, 17, A16, 1 << 20
+    assert f(*args) == SHAPE
 
 
 def test_int4_lora_workspace_size(lib):

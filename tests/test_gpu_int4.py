@@ -500,3 +500,73 @@ def test_max_n(gpu_lib, path, m):
     scp = np.concatenate([scb, np.zeros((1, pad), dtype=np.uint16)], axis=1)
     ref = oracle.qgemm_int4(xb, qwp, scp, qzs, m, k, nq * 8)[:, :len(cols)]
     assert_accepted(host_u16(y[:, ct]), ref, ("max-n", path, m))
+
+
+# ----------------------------------------------------------------------------
+# fused epilogues (qgemm_int4_epilogue): the row reduction of an RMSNorm,
+# row_sumsq[r] += sum_j y[r][j]^2 over the rounded outputs, with and without
+# the LoRA add, on every kernel family (LDS-staged small-M, register-staged
+# small-M with a k split and with row tiles, MFMA tiles with and without a k
+# split); Y is bit-identical to the product without the reduction
+# ----------------------------------------------------------------------------
+EPI_CASES = [("gemv", 1, 1152, 776, 0), ("fused", 8, 2048, 1040, 0), ("fused", 15, 2048, 1040, 16),
+             ("fused", 8, 16384, 520, 0), ("gemv", 1, 16384, 520, 16), ("auto", 24, 2048, 1040, 0),
+             ("auto", 40, 2048, 1040, 5), ("mfma", 130, 1152, 776, 0), ("mfma", 33, 4096, 520, 16),
+             ("mfma", 257, 2048, 1040, 0), ("fused", 3, 4096, 14336, 0)]
+
+
+@pytest.mark.parametrize("path,m,k,n,rank", EPI_CASES)
+def test_epilogue_row_sumsq(gpu_lib, path, m, k, n, rank):
+    import torch
+
+    say("epilogue", path, m, k, n, rank, gpu_lib.describe_int4(m, n, k, path))
+    d = int4_inputs(m, k, n, seed=1300 + m + k + n)
+    t = upload_int4(d)
+    rss = torch.zeros(m, dtype=torch.float32, device="cuda")
+    if rank:
+        l = lora_inputs(k, n, rank, seed=1400 + rank)
+        la, lb = upload_lora(l)
+        ref = oracle.qgemm_int4_lora(d["x"], d["qweight"], d["scales"], d["qzeros"], l["lora_a"], l["lora_b"],
+                                     2.0, m, k, n)
+        y = gpu_lib.qgemm_int4_epilogue(t["x"], t["qweight"], t["scales"], t["qzeros"], la, lb, 2.0,
+                                        row_sumsq=rss, path=path)
+        plain = gpu_lib.qgemm_int4_lora(t["x"], t["qweight"], t["scales"], t["qzeros"], la, lb, 2.0, path=path)
+    else:
+        ref = oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], m, k, n)
+        y = gpu_lib.qgemm_int4_epilogue(t["x"], t["qweight"], t["scales"], t["qzeros"], row_sumsq=rss,
+                                        path=path)
+        plain = gpu_lib.qgemm_int4(t["x"], t["qweight"], t["scales"], t["qzeros"], path=path)
+    torch.cuda.synchronize()
+    yb = host_u16(y)
+    assert_accepted(yb, ref, ("epilogue", path, m, k, n, rank))
+    assert np.array_equal(yb, host_u16(plain))
+    got = rss.cpu().numpy().astype(np.float64)
+    want, bound = oracle.row_sumsq(yb), oracle.row_sumsq_bound(yb)
+    assert np.all(np.abs(got - want) <= bound), (np.max(np.abs(got - want) / np.maximum(bound, 1e-30)))
+    # accumulated: a second call adds the same sums again
+    if rank:
+        gpu_lib.qgemm_int4_epilogue(t["x"], t["qweight"], t["scales"], t["qzeros"], la, lb, 2.0, row_sumsq=rss,
+                                    out=y, path=path)
+    else:
+        gpu_lib.qgemm_int4_epilogue(t["x"], t["qweight"], t["scales"], t["qzeros"], row_sumsq=rss, out=y,
+                                    path=path)
+    torch.cuda.synchronize()
+    got2 = rss.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got2 - 2 * want) <= 2 * bound + 2 * 2.0 ** -24 * 2 * want)
+
+
+@pytest.mark.parametrize("m,k,n", [(15, 4096, 4096), (1, 4096, 28672), (512, 5120, 25600)])
+def test_epilogue_row_sumsq_full_size(gpu_lib, m, k, n):
+    import torch
+
+    say("epilogue-full", m, k, n, gpu_lib.describe_int4(m, n, k))
+    d = int4_inputs(m, k, n, seed=1500 + m)
+    t = upload_int4(d)
+    rss = torch.zeros(m, dtype=torch.float32, device="cuda")
+    y = host_u16(gpu_lib.qgemm_int4_epilogue(t["x"], t["qweight"], t["scales"], t["qzeros"], row_sumsq=rss))
+    torch.cuda.synchronize()
+    rows, cols = sample_indices(m, 16, m), sample_indices(n, 96, m + 1)
+    ref = oracle.qgemm_int4_at(d["x"], d["qweight"], d["scales"], d["qzeros"], k, n, rows, cols)
+    assert_accepted(y[np.ix_(rows, cols)], ref, ("epilogue-full", m, k, n))
+    got = rss.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - oracle.row_sumsq(y)) <= oracle.row_sumsq_bound(y))

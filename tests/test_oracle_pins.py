@@ -565,3 +565,33 @@ def test_dense_dropped_k_slice_is_rejected():
     bad = oracle.round_to_grid(a @ oracle.bf16_value(d["b"]).T, "bf16")
     rep = oracle.compare(f32_to_bf16_bits(bad), c, "bf16")
     assert rep["rms_rel"] > 0.05
+
+
+def test_row_sumsq_closed_forms_and_brute_force():
+    # constant rows: n c^2 exactly (c = 1.5 and -0.25 are bf16 values)
+    y = np.zeros((2, 40), dtype=np.uint16)
+    y[0, :] = 0x3FC0          # 1.5
+    y[1, :] = 0xBE80          # -0.25
+    r = oracle.row_sumsq(y)
+    assert r[0] == 40 * 2.25 and r[1] == 40 * 0.0625
+    # brute force with math.fsum over struct-decoded values, random bf16 rows
+    import math
+    import struct
+
+    from qgemm_inputs import f32_to_bf16_bits
+
+    rng = np.random.default_rng(5)
+    bits = f32_to_bf16_bits((rng.normal(size=(3, 77)) * 3.0).astype(np.float32))
+    for i in range(3):
+        vals = [struct.unpack("<f", struct.pack("<I", int(b) << 16))[0] for b in bits[i]]
+        exact = math.fsum(v * v for v in vals)
+        assert abs(oracle.row_sumsq(bits[i:i + 1])[0] - exact) <= 1e-14 * exact   # fp64 sum order
+    # the bound covers a sequential fp32 sum, and rejects a dropped term
+    v = oracle.bf16_value(bits).astype(np.float32)
+    seq = np.zeros(3, dtype=np.float32)
+    for j in range(77):
+        seq = (seq + v[:, j] * v[:, j]).astype(np.float32)
+    assert np.all(np.abs(seq - oracle.row_sumsq(bits)) <= oracle.row_sumsq_bound(bits))
+    dropped = oracle.row_sumsq(bits[:, 1:])
+    big = np.abs(oracle.bf16_value(bits[:, 0])) ** 2 > oracle.row_sumsq_bound(bits)
+    assert np.all(np.abs(dropped - oracle.row_sumsq(bits))[big] > oracle.row_sumsq_bound(bits)[big])
