@@ -36,7 +36,7 @@ LLC_BYTES = 256 << 20
 # HBM traffic of the small-M kernels, measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
 # and scaled by the same counters on a copy of known size; valid only while the
 # kernel sources hash to the value recorded with the counters.
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "skinny_int4_small_m_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "skinny_lds_small_m_traffic.md")
 KERNEL_SOURCES = ["int4_weight_only_gptq_amd/csrc/int4_kernels.hip",
                   "int4_weight_only_gptq_amd/csrc/common.hpp",
                   "int4_weight_only_gptq_amd/csrc/launch.hpp",

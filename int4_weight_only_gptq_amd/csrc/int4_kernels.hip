@@ -600,7 +600,8 @@ __global__ __launch_bounds__(M > 16 ? 512 : 1024) void skinny_int4_kernel(
   // Every thread waits for its partial stores to complete before the barrier,
   // then one counter increment per workgroup; partials are only written and
   // read with agent-coherent accesses, so no cache-wide maintenance is needed.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("" ::: "memory");             // (no instruction: keeps the stores above the wait)
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
   if (tid == 0)
     last_flag = __hip_atomic_fetch_add(&tickets[strip], 1u, __ATOMIC_RELAXED,
@@ -1673,6 +1674,50 @@ static LdsPlan plan_lds(int64_t m, const SkinnyPlan& p, int64_t k, bool dot, boo
   return r;
 }
 
+// The strip plan without a k split (the strip width by n alone), for the
+// LDS-staged kernel where the register-staged plan would split k.
+static SkinnyPlan plan_whole_k(int64_t m, int64_t n, int64_t k, bool dot) {
+  SkinnyPlan p = plan_skinny(m, n, k, 0, dot);
+  const int cplmax = dot || m <= 32 ? 4 : (m <= 48 ? 2 : 1);
+  int cpl = 1;
+  if ((n + 63) / 64 >= QG_SKINNY_MIN_STRIPS) cpl = 4;
+  else if ((n + 31) / 32 >= QG_SKINNY_MIN_STRIPS) cpl = 2;
+  if (cpl == 2 && (n + 31) / 32 >= 384) {
+    const int64_t s4 = (n + 63) / 64;
+    if (s4 >= 192 && s4 <= 256) cpl = 4;
+  }
+  if (cpl > cplmax) cpl = cplmax;
+  p.cpl = cpl;
+  p.nstrips = (int)((n + 16 * cpl - 1) / (16 * cpl));
+  p.ksplit = 1;
+  p.gwg = (int)(k / 128);
+  p.ws_bytes = 0;
+  p.items_per_xcd = (p.nstrips + 7) / 8;
+  p.blocks = (int64_t)p.items_per_xcd * 8;
+  return p;
+}
+
+#ifndef QG_LDS_PREFER_WHOLE_K
+#define QG_LDS_PREFER_WHOLE_K 1
+#endif
+
+// The plan the small-M paths launch: the register-staged plan, or the
+// LDS-staged kernel over the whole k where the register-staged plan splits k
+// (or has no LDS-staged form) and the whole-k strips fill the CUs.  Measured
+// (cold weights): 32-column strips and the GEMV gain, 16-column strips with
+// m >= 2 lose (the split's extra workgroups hide more latency there):
+// 8192 x 8192 m = 8 / 16 13.0 / 14.5 -> 11.6 / 13.8 µs, 7168 x 8192 m = 15
+// 13.1 -> 12.6 µs, 8192 x 5632 m = 1 13.7 -> 12.9 µs, but 8192 x 5632
+// m = 16 15.6 -> 21.2 µs.
+static SkinnyPlan plan_small_m(int64_t m, int64_t n, int64_t k, int64_t ws_bytes, bool dot) {
+  const SkinnyPlan p = plan_skinny(m, n, k, ws_bytes, dot);
+  if (QG_LDS_PREFER_WHOLE_K && m <= 16 && (p.ksplit > 1 || plan_lds(m, p, k, dot).ng == 0)) {
+    const SkinnyPlan q = plan_whole_k(m, n, k, dot);
+    if (q.nstrips >= QG_SKINNY_MIN_STRIPS && (dot || q.cpl >= 2) && plan_lds(m, q, k, dot).ng > 0) return q;
+  }
+  return p;
+}
+
 template <int M, bool DOT, int CPL, int NG, bool XL, bool LORA>
 static void lds_launch_k(const Int4Args& a, const SkinnyPlan& p, const LdsPlan& l, hipStream_t stream) {
   skinny_lds_kernel<M, DOT, CPL, NG, XL, LORA><<<dim3((unsigned)p.blocks), dim3(64 * l.waves), l.lds, stream>>>(
@@ -1733,18 +1778,18 @@ bool lora_in_launch(const Int4Args& a, int path, int64_t ws_bytes) {
   if (path == 3) return 2.0 * (double)a.m * (double)a.n * (double)a.k <= QG_LORA_TILE_MAX_FLOPS;
   if (a.m > 16) return false;
   const bool dot = path == 1;
-  const SkinnyPlan p = plan_skinny(dot ? 1 : a.m, a.n, a.k, ws_bytes, dot);
+  const SkinnyPlan p = plan_small_m(dot ? 1 : a.m, a.n, a.k, ws_bytes, dot);
   return plan_lds(dot ? 1 : a.m, p, a.k, dot, true).ng > 0;
 }
 
 hipError_t launch_gemv_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream) {
-  const SkinnyPlan p = plan_skinny(1, a.n, a.k, ws ? ws_bytes : 0, true);
+  const SkinnyPlan p = plan_small_m(1, a.n, a.k, ws ? ws_bytes : 0, true);
   if (!lds_launch_c<1, true>(a, p, stream)) skinny_launch_c<1, true>(a, p, ws, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_fused_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipStream_t stream) {
-  const SkinnyPlan p = plan_skinny(a.m, a.n, a.k, ws ? ws_bytes : 0, false);
+  const SkinnyPlan p = plan_small_m(a.m, a.n, a.k, ws ? ws_bytes : 0, false);
   switch (a.m) {
     case 1: if (!lds_launch_c<1, false>(a, p, stream)) skinny_launch_c<1, false>(a, p, ws, stream); break;
     case 2: if (!lds_launch_c<2, false>(a, p, stream)) skinny_launch_c<2, false>(a, p, ws, stream); break;
@@ -2020,14 +2065,14 @@ hipError_t launch_mfma_int4(const Int4Args& a, void* ws, int64_t ws_bytes, hipSt
 int64_t workspace_int4(int64_t m, int64_t n, int64_t k, int path) {
   if (m == 0 || n == 0 || k == 0) return 0;
   if (path == 3) return plan_mfma(m, n, k, INT64_MAX).ws_bytes;
-  return plan_skinny(m, n, k, INT64_MAX, path == 1).ws_bytes;
+  return plan_small_m(m, n, k, INT64_MAX, path == 1).ws_bytes;
 }
 
 void describe_int4(int64_t m, int64_t n, int64_t k, int path, int64_t ws_bytes, char* buf,
                    size_t len) {
   if (path == 1 || path == 2) {
     const int64_t mp = path == 1 ? 1 : m;
-    const SkinnyPlan p = plan_skinny(mp, n, k, ws_bytes, path == 1);
+    const SkinnyPlan p = plan_small_m(mp, n, k, ws_bytes, path == 1);
     const bool dot = path == 1;
     const LdsPlan l = plan_lds(mp, p, k, dot);
     if (l.ng > 0) {

@@ -255,6 +255,16 @@ def test_describe_names_the_dispatch(lib):
     # more strips than one pass holds with all their codes in LDS: the register-staged kernel
     assert qg.describe_int4(8, 28672, 4096).startswith("skinny_int4_kernel<8,mfma,4> grid=448")
     assert qg.describe_int4(16, 28672, 4096).startswith("skinny_int4_kernel<16,mfma,4> grid=448 block=512")
+    # 64 groups would be split over 128 strips of 64 columns; instead 256 strips of 32
+    # columns each take the whole k in the LDS-staged kernel (4 groups per wave, 16
+    # waves): 64 groups x 2 KiB of codes and 16 waves x 16 tokens x 32 columns x 4 bytes
+    assert qg.describe_int4(16, 8192, 8192) == (
+        "skinny_lds_kernel<16,mfma,2,4,xreg> grid=256 block=1024 lds=%d ksplit=1 groups=64"
+        % (64 * 2048 + 16 * 16 * 32 * 4))
+    assert qg.describe_int4(8, 8192, 7168).startswith("skinny_lds_kernel<8,mfma,2,4,xreg> grid=256 block=896 ")
+    assert qg.describe_int4(1, 5632, 8192).startswith("skinny_lds_kernel<1,dot,1,4,xreg> grid=352 block=1024 ")
+    # 16-column strips with m >= 2 keep the split
+    assert qg.describe_int4(8, 5632, 8192).startswith("skinny_int4_kernel<8,mfma,4> grid=264 ")
     # a long k with few strips is split: m >= 8 and 200 groups take 8-wave workgroups,
     # 25 groups per wave -> 7 slices of 29 over 80 strips of 64 columns
     assert qg.describe_int4(16, 5120, 25600).startswith("skinny_int4_kernel<16,mfma,4> grid=560 block=512")

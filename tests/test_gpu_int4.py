@@ -315,6 +315,10 @@ FULL += [(2, ("row-tiles", 20, 25600, 5120, 2020)), (2, ("row-tiles", 24, 5120, 
          (3, ("row-tiles", 32, 8192, 28672, 3032))]
 # 257..383 strips: 8-wave workgroups, two per CU (2048 x 5632: 352 strips)
 FULL += [(1, ("strips", 8, 2048, 5632, 1108)), (1, ("strips", 1, 2048, 5632, 1101))]
+# the LDS-staged kernel over the whole k where the register-staged plan splits it:
+# 32-column strips with 4 groups per wave (16 and 14 waves), and the GEMV's 16-column strips
+FULL += [(1, ("whole-k", 16, 8192, 8192, 1116)), (1, ("whole-k", 8, 7168, 8192, 1118)),
+         (1, ("whole-k", 1, 8192, 5632, 1119))]
 # 33..64 tokens: three and four row tiles in one pass over the CUs (4096 x 4096, 2048 x 8192)
 FULL += [(1, ("row-tiles", 33, 4096, 4096, 1033)), (1, ("row-tiles", 64, 4096, 4096, 1064)),
          (1, ("row-tiles", 48, 2048, 8192, 1048)), (2, ("row-tiles", 40, 14336, 4096, 2040))]   # two passes, k split
@@ -428,9 +432,10 @@ def test_lora_paths_match_oracle(gpu_lib, path, m, k, n, rank):
 
 
 # (1024 x 1024 x 8192: the 256 x 128 tiles with U in the launch, 2^34 flops; 512 x 2048 x
-# 8192: 128 x 128 tiles, U in the launch; 512 x 5120 x 25600: U in two small launches first)
+# 8192: 128 x 128 tiles, U in the launch; 512 x 5120 x 25600: U in two small launches first;
+# 16 x 8192 x 8192: the LDS-staged kernel over the whole k, U in the launch)
 @pytest.mark.parametrize("m,k,n", [(1, 4096, 4096), (15, 2048, 8192), (512, 5120, 25600), (512, 2048, 8192),
-                                   (1024, 1024, 8192), (8, 4096, 4096)])
+                                   (1024, 1024, 8192), (8, 4096, 4096), (16, 8192, 8192)])
 def test_lora_full_size_sampled(gpu_lib, m, k, n):
     import torch
 
