@@ -80,6 +80,36 @@ const char* qg_status_str(int32_t status);
 int32_t qg_last_hip_error(void);
 
 /*
+ * Ordering of the k split's partial-sum exchange on the int4 paths.  When k is
+ * split, every k slice of an output tile stores its fp32 partials, takes a
+ * ticket from a counter in the workspace, and the slice that takes the last
+ * ticket adds the partials in slice order (a deterministic result) and writes
+ * Y; the sums are the same in both orders below, bit for bit.
+ *
+ *   QG_SPLIT_ORDER_HW (the default): partials are stored and read with
+ *     agent-scope atomic accesses, every thread waits for the completion of
+ *     its stores before its workgroup's ticket is taken, and the ticket
+ *     increment is relaxed.  The order rests on the GPU's store-completion
+ *     counter (an agent-scope store completes at the point where every CU
+ *     sees it), not on the HIP memory model.
+ *   QG_SPLIT_ORDER_ACQ_REL: the ticket increment is an agent-scope
+ *     acquire-release read-modify-write, so the memory model itself orders
+ *     the partials before their sum.  On gfx950 it costs an L2 write-back and
+ *     invalidate per workgroup of a split launch: measured (cold weights)
+ *     25600 x 5120 m = 16 26.2 -> 47.6 µs, 14336 x 4096 m = 8 11.8 -> 13.9 µs,
+ *     25600 x 5120 m = 2048 (MFMA tiles) 695 -> 710 µs.
+ *
+ * Process-wide; applies to launches made after the call (calls that overlap
+ * it on another thread may take either order).  qg_set_split_order returns
+ * QG_OK, or QG_ERR_UNSUPPORTED (nothing changed) for another value;
+ * qg_split_order returns the current order.
+ */
+#define QG_SPLIT_ORDER_HW 0
+#define QG_SPLIT_ORDER_ACQ_REL 1
+int32_t qg_set_split_order(int32_t order);
+int32_t qg_split_order(void);
+
+/*
  * qgemm_int4 -- Y = X . W^T with GPTQ int4 weights (GPTQModel #3645, "What
  * changed" and "Accuracy"; mi50grad README, "Model": group size 128).
  *

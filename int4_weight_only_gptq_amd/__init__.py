@@ -21,6 +21,7 @@ _LIB_NAME = "libqgemm_gfx950.so"
 _lib = None
 
 PATHS = {"auto": 0, "gemv": 1, "fused": 2, "mfma": 3}
+SPLIT_ORDERS = {"hw": 0, "acq_rel": 1}
 LAYOUTS = {"NT": 0, "NN": 1, "TN": 2}
 _DTYPES = {"bf16": 0, "fp16": 1, "fp32": 2}
 
@@ -56,6 +57,10 @@ def load():
     lib.qg_status_str.argtypes = [i32]
     lib.qg_last_hip_error.restype = i32
     lib.qg_last_hip_error.argtypes = []
+    lib.qg_set_split_order.restype = i32
+    lib.qg_set_split_order.argtypes = [i32]
+    lib.qg_split_order.restype = i32
+    lib.qg_split_order.argtypes = []
     int4_args = [vp, i64, vp, vp, vp, vp, i64, i64, i64, i64, i32]
     lib.qgemm_int4.restype = i32
     lib.qgemm_int4.argtypes = int4_args + [vp, i64, vp]
@@ -128,6 +133,18 @@ def _check(status, where):
 
 
 _workspaces = {}
+
+
+def set_split_order(order: str) -> None:
+    """Ordering of the k split's partial-sum exchange, process-wide: "hw" (the
+    default: agent-scope atomic partials behind a store-completion wait, relaxed
+    ticket) or "acq_rel" (an acquire-release ticket; slower)."""
+    _check(load().qg_set_split_order(SPLIT_ORDERS[order]), "qg_set_split_order")
+
+
+def split_order() -> str:
+    code = load().qg_split_order()
+    return {v: k for k, v in SPLIT_ORDERS.items()}[code]
 
 
 def workspace_size(m: int, n: int, k: int, path: str = "auto") -> int:

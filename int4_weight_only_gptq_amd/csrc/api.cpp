@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "launch.hpp"
@@ -18,6 +19,7 @@ static __device__ __align__(256) unsigned char scratch[QG_NOALLOC_SCRATCH_BYTES]
 namespace {
 
 thread_local int32_t g_last_hip_error = 0;
+std::atomic<int32_t> g_split_order{QG_SPLIT_ORDER_HW};
 
 int32_t hip_status(hipError_t e) {
   if (e == hipSuccess) return QG_OK;
@@ -117,6 +119,7 @@ int32_t run_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint
   hipStream_t s = (hipStream_t)stream;
   if (k == 0) return hip_status(qg::launch_zero16((uint16_t*)y, m, n, ldy, s));
   qg::Int4Args a{(const uint16_t*)x, ldx, qweight, scales, qzeros, (uint16_t*)y, ldy, m, n, k};
+  a.split_acq_rel = g_split_order.load(std::memory_order_relaxed) == QG_SPLIT_ORDER_ACQ_REL;
   a.lora.row_ss = row_ss;
   if (ws == nullptr) ws_bytes = 0;
   const int32_t rp = resolve_path(m, n, k, path);
@@ -203,6 +206,14 @@ const char* qg_status_str(int32_t status) {
 }
 
 int32_t qg_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t qg_set_split_order(int32_t order) {
+  if (order != QG_SPLIT_ORDER_HW && order != QG_SPLIT_ORDER_ACQ_REL) return QG_ERR_UNSUPPORTED;
+  g_split_order.store(order, std::memory_order_relaxed);
+  return QG_OK;
+}
+
+int32_t qg_split_order(void) { return g_split_order.load(std::memory_order_relaxed); }
 
 int32_t qgemm_int4(const void* x, int64_t ldx, const uint32_t* qweight, const uint16_t* scales,
                    const uint32_t* qzeros, void* y, int64_t ldy, int64_t m, int64_t n, int64_t k,

@@ -360,12 +360,23 @@ hipError_t launch_lora_u(const uint16_t* x, int64_t ldx, const uint16_t* a, int6
   return hipGetLastError();
 }
 
+// One ticket of a k split's counter (agent scope); returns the count before.
+// acq_rel != 0: an acquire-release increment (the memory model orders the
+// slice's partial stores before it and the last slice's reads after it);
+// else relaxed, the partials' order then resting on the store-completion wait
+// before the increment.
+__device__ __forceinline__ uint32_t ticket_add(uint32_t* t, int acq_rel) {
+  return acq_rel ? __hip_atomic_fetch_add(t, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT)
+                 : __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int M, bool DOT, int CPL>
 __global__ __launch_bounds__(M > 16 ? 512 : 1024) void skinny_int4_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
     uint16_t* __restrict__ y, int64_t ldy, int n, int k, int nstrips, int ksplit, int gwg,
-    int items_per_xcd, float* __restrict__ partials, uint32_t* __restrict__ tickets, LoraEpi lora) {
+    int items_per_xcd, float* __restrict__ partials, uint32_t* __restrict__ tickets, int acq_rel,
+    LoraEpi lora) {
   static_assert(!DOT || M == 1, "the VALU variant computes one token");
   constexpr int SW = 16 * CPL;                 // strip width in columns
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -599,13 +610,14 @@ __global__ __launch_bounds__(M > 16 ? 512 : 1024) void skinny_int4_kernel(
   // split k: the last workgroup of the strip adds the partials in k order.
   // Every thread waits for its partial stores to complete before the barrier,
   // then one counter increment per workgroup; partials are only written and
-  // read with agent-coherent accesses, so no cache-wide maintenance is needed.
+  // read with agent-coherent accesses, so no cache-wide maintenance is needed
+  // (acq_rel: the increment orders them by the memory model, at the price of
+  // an L2 write-back and invalidate).
   asm volatile("" ::: "memory");             // (no instruction: keeps the stores above the wait)
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
   if (tid == 0)
-    last_flag = __hip_atomic_fetch_add(&tickets[strip], 1u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(ksplit - 1);
+    last_flag = ticket_add(&tickets[strip], acq_rel) == (uint32_t)(ksplit - 1);
   __syncthreads();
   if (!last_flag) return;
   const float* base = partials + (int64_t)strip * ksplit * (M * SW);
@@ -1011,7 +1023,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
     const float* __restrict__ xsum, uint16_t* __restrict__ y, int64_t ldy, int m, int n, int k,
     int tiles_n, int items, int items_per_xcd, int vec_store, int ksplit, int gps,
-    float* __restrict__ partials, uint32_t* __restrict__ tickets, LoraEpi lora) {
+    float* __restrict__ partials, uint32_t* __restrict__ tickets, int acq_rel, LoraEpi lora) {
   using S = PipeShape<NWM, NWN, FM, PREP, LORA>;
   constexpr int T = S::T, BM = S::BM, BN = S::BN, XL = S::XL, WL = S::WL, LOADS = S::LOADS;
   static_assert(LOADS * (STAGES - 2) <= 63, "vmcnt range");
@@ -1362,7 +1374,8 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
     // stores and takes a ticket; the last slice of the tile to arrive adds the
     // partials in slice order (deterministic) and writes Y.  No fences: the
     // partials are only written and read with agent-coherent accesses, and
-    // every thread waits for its stores before the ticket is taken.
+    // every thread waits for its stores before the ticket is taken (or, with
+    // acq_rel, the ticket orders them).
     // fragment order: element pair (f, v, c / 2) of thread tid at
     // ((f * 4 + v) * 2 + c / 2) * T + tid (8-byte words), so that each store
     // instruction of a wave covers 512 contiguous bytes; the last slice reads
@@ -1385,8 +1398,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
     if (tid == 0)
-      psm_i4[0] = __hip_atomic_fetch_add(&tickets[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                   (uint32_t)(ksplit - 1);
+      psm_i4[0] = ticket_add(&tickets[t], acq_rel) == (uint32_t)(ksplit - 1);
     __syncthreads();
     if (!psm_i4[0]) return;
     const uint64_t* base = reinterpret_cast<const uint64_t*>(partials) + (int64_t)t * ksplit * (BM * BN / 2);
@@ -1601,7 +1613,7 @@ static void skinny_launch(const Int4Args& a, const SkinnyPlan& p, void* ws, hipS
   float* partials = ws ? (float*)((char*)ws + kTicketBytes) : nullptr;
   skinny_int4_kernel<M, DOT, CPL><<<dim3((unsigned)p.blocks), dim3(64 * p.waves), p.lds, stream>>>(
       a.x, a.ldx, a.qweight, a.scales, a.qzeros, a.y, a.ldy, (int)a.n, (int)a.k, p.nstrips,
-      p.ksplit, p.gwg, p.items_per_xcd, partials, tickets, a.lora);
+      p.ksplit, p.gwg, p.items_per_xcd, partials, tickets, a.split_acq_rel, a.lora);
 }
 
 template <int M, bool DOT>
@@ -2027,12 +2039,12 @@ static void pipe_launch(const Int4Args& a, const MfmaPlan& p, const uint16_t* x,
     int4_pipe_kernel<NWM, NWN, FM, LSTAGES, PREP, true><<<dim3((unsigned)(per_xcd * 8)), dim3(c.threads), c.lds,
                                                            stream>>>(
         x, ldx, a.qweight, a.scales, a.qzeros, xsum, a.y, a.ldy, (int)a.m, (int)a.n, (int)a.k, tiles_n, items,
-        per_xcd, vec, p.ksplit, p.gps, partials, tickets, a.lora);
+        per_xcd, vec, p.ksplit, p.gps, partials, tickets, a.split_acq_rel, a.lora);
   else
     int4_pipe_kernel<NWM, NWN, FM, STAGES, PREP, false><<<dim3((unsigned)(per_xcd * 8)), dim3(c.threads), c.lds,
                                                            stream>>>(
         x, ldx, a.qweight, a.scales, a.qzeros, xsum, a.y, a.ldy, (int)a.m, (int)a.n, (int)a.k, tiles_n, items,
-        per_xcd, vec, p.ksplit, p.gps, partials, tickets, a.lora);
+        per_xcd, vec, p.ksplit, p.gps, partials, tickets, a.split_acq_rel, a.lora);
 }
 
 template <bool PREP>

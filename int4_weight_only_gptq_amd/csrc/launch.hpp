@@ -31,6 +31,7 @@ struct Int4Args {
   int64_t ldy;
   int64_t m, n, k;
   LoraEpi lora;           // zero-initialised: no adapter
+  int split_acq_rel = 0;  // 1: the k split's ticket is an acquire-release RMW
 };
 
 // U[m][16] = X . A^T in fp32 for lora_A bf16 [rank][lda] (rank <= 16; the

@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
         "qg_abi_version", "qg_status_str", "qg_last_hip_error", "qgemm_int4", "qgemm_int4_path",
         "qgemm_int4_workspace_size", "qgemm_int4_describe", "qgemm_int4_dequant", "gemm_dense",
         "gemm_dense_batched", "qgemm_int4_lora", "qgemm_int4_lora_workspace_size", "qg_probe_mfma_bf16",
-        "qg_probe_copy", "qg_probe_read", "qgemm_int4_noalloc", "qgemm_int4_epilogue"])
+        "qg_probe_copy", "qg_probe_read", "qgemm_int4_noalloc", "qgemm_int4_epilogue", "qg_set_split_order",
+        "qg_split_order"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -170,6 +171,23 @@ def test_probe_rejects_invalid_arguments(lib):
     assert lib.qg_probe_mfma_bf16(65537, 10, buf, None) == 2                  # too many
     assert lib.qg_probe_mfma_bf16(4, 0, buf, None) == 2                       # no iterations
     assert lib.qg_probe_mfma_bf16(4, 10, ctypes.c_void_p(0x100004), None) == 3  # misaligned
+
+
+def test_split_order_setting(lib):
+    assert defines("QG_SPLIT_ORDER_") == {"QG_SPLIT_ORDER_HW": qg.SPLIT_ORDERS["hw"],
+                                          "QG_SPLIT_ORDER_ACQ_REL": qg.SPLIT_ORDERS["acq_rel"]}
+    assert lib.qg_split_order() == 0                                           # the default
+    try:
+        assert lib.qg_set_split_order(1) == OK and lib.qg_split_order() == 1
+        assert lib.qg_set_split_order(2) == UNSUP and lib.qg_split_order() == 1   # unchanged
+        assert lib.qg_set_split_order(-1) == UNSUP
+        qg.set_split_order("hw")
+        assert qg.split_order() == "hw"
+        with pytest.raises(KeyError):
+            qg.set_split_order("seq_cst")
+    finally:
+        lib.qg_set_split_order(0)
+    assert lib.qg_split_order() == 0
 
 
 def test_bandwidth_probes_reject_invalid_arguments(lib):

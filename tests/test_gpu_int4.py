@@ -230,6 +230,30 @@ def test_mfma_split_k_matches_oracle(gpu_lib, m, k, n):
     assert np.array_equal(host_u16(y1), host_u16(y2))
 
 
+# the k split under both exchange orders: the small-M kernel's strips (16 slices), the
+# GEMV, and the MFMA tiles (a ticket per tile); acquire-release tickets give the same
+# sums, bit for bit
+@pytest.mark.parametrize("path,m,k,n", [("fused", 8, 16384, 520), ("gemv", 1, 20480, 776),
+                                        ("mfma", 130, 8192, 776), ("mfma", 17, 16384, 264)])
+def test_split_orders_agree(gpu_lib, path, m, k, n):
+    desc = gpu_lib.describe_int4(m, n, k, path)
+    say("split-order", path, m, k, n, desc)
+    assert "ksplit=1 " not in desc + " "
+    d = int4_inputs(m, k, n, seed=50 + m)
+    t = upload_int4(d)
+    ref = oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], m, k, n)
+    assert gpu_lib.split_order() == "hw"
+    y_hw = host_u16(run(gpu_lib, t, path))
+    try:
+        gpu_lib.set_split_order("acq_rel")
+        y_ar = host_u16(run(gpu_lib, t, path))
+        y_ar2 = host_u16(run(gpu_lib, t, path))      # the tickets were reset under this order too
+    finally:
+        gpu_lib.set_split_order("hw")
+    assert_accepted(y_ar, ref, ("split-order", path, m, k, n))
+    assert np.array_equal(y_ar, y_hw) and np.array_equal(y_ar2, y_hw)
+
+
 def test_gemv_long_k_without_workspace(gpu_lib):
     # 600 groups on one 16-column strip, no k split: each wave walks a long chain
     m, k, n = 1, 76800, 16
