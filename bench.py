@@ -599,6 +599,18 @@ def run_suite(qg, torch, args, path):
                      "dtype": case["dtype"], "M": M, "N": N, "K": K, "us": us,
                      "gbps": dense_bytes(M, N, K) / us / 1e3, "tflops": 2 * M * N * K / us / 1e6,
                      "mfma_frac": 2 * M * N * K / us / 1e6 / MFMA_BF16_PEAK_TFLOPS})
+        if "dense_vendor" in kinds and min(M, N) > 16:
+            # context: the vendor library (torch.mm -> hipBLASLt) on the same operands
+            # and layout, same timing; 2-D products only
+            lay = case["layout"]
+            lhs = a.t() if lay == "TN" else a
+            rhs = b.t() if lay == "NT" else b
+            ref = torch.empty((M, N), dtype=dt, device="cuda")
+            torch.mm(lhs, rhs, out=ref)
+            vus = time_us(torch, lambda: torch.mm(lhs, rhs, out=ref), iters)
+            rows[-1].update({"vendor_us": vus, "vendor_tflops": 2 * M * N * K / vus / 1e6,
+                             "vendor": "torch.mm (hipBLASLt)"})
+            del ref
         print("suite dense", rows[-1], file=sys.stderr, flush=True)
     # a rank-16 LoRA add in the epilogue (U = X A^T launched first) on the same shapes
     for cfg in ((1, 2) if "int4_lora" in kinds else ()):
