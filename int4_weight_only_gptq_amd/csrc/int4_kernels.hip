@@ -1114,10 +1114,14 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int i = 0; i < S::ML; ++i) {
       const int j = S::NW * i + wave;
-      // without zero points the zero-word slots stay unloaded (and unread)
+      // Every wave issues the same number of loads per stage (the waits count
+      // them).  Without zero points the zero-word slots load a word of the
+      // stage's scale row instead (in bounds: lane offsets stay below n / 2
+      // bytes), which is never read.
       if (j == 0) buffer_to_lds4(scales + g * n + n0, moff[i], wl + S::W_DW + 64 * j);
       else if (j >= 2 && j < S::MSLOTS) buffer_to_lds4(xsum + g * m + m0, moff[i], wl + S::W_DW + 64 * j);
       else if (qzeros) buffer_to_lds4(qzeros + g * (n >> 3) + (n0 >> 3), moff[i], wl + S::W_DW + 64 * j);
+      else buffer_to_lds4(scales + g * n + n0, moff[i], wl + S::W_DW + 64 * j);
     }
     if constexpr (LORA) {
       uint32_t* al = wl + S::W_DW + S::M_DW;
