@@ -257,8 +257,8 @@ __device__ __forceinline__ u32x4 read_mn_frag(const u32x4* region, int kb, int c
   return out;
 }
 
-template <int LAYOUT, int DTYPE, int BM, int BN, int STAGES>
-__global__ __launch_bounds__(256) void dense_pipe_kernel(
+template <int LAYOUT, int DTYPE, int BM, int BN, int STAGES, int NWV = 4>
+__global__ __launch_bounds__(64 * NWV) void dense_pipe_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_n, int tiles,
     int tiles_per_xcd, int vec_store, BatchStrides bs) {
@@ -267,10 +267,14 @@ __global__ __launch_bounds__(256) void dense_pipe_kernel(
   C += blockIdx.y * bs.c;
   constexpr bool A_MN = (LAYOUT == 2);           // A stored [K][M]
   constexpr bool B_MN = (LAYOUT != 0);           // B stored [K][N]
-  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
+  // NWV waves as a 2 x (NWV / 2) grid over the tile: 4 waves (one per SIMD) or
+  // 8 (two per SIMD, half the columns each)
+  constexpr int T = 64 * NWV;
+  constexpr int WM = BM / 2, WN = BN / (NWV / 2), FM = WM / 16, FN = WN / 16;
   constexpr int A_SLOTS = BM * 8, B_SLOTS = BN * 8;           // 16-byte chunks per stage
   constexpr int STAGE = A_SLOTS + B_SLOTS;
-  constexpr int A_LOADS = A_SLOTS / 256, B_LOADS = B_SLOTS / 256;   // per thread per stage
+  constexpr int A_LOADS = A_SLOTS / T, B_LOADS = B_SLOTS / T;   // per thread per stage
+  static_assert(A_SLOTS % T == 0 && B_SLOTS % T == 0 && (NWV == 4 || NWV == 8), "loads per thread");
   constexpr int LOADS = A_LOADS + B_LOADS;
   static_assert(LOADS * (STAGES - 1) <= 63, "vmcnt range");
   extern __shared__ __attribute__((aligned(16))) u32x4 psm[];
@@ -289,7 +293,7 @@ __global__ __launch_bounds__(256) void dense_pipe_kernel(
   const uint16_t* bsrc[B_LOADS];
 #pragma unroll
   for (int i = 0; i < A_LOADS; ++i) {
-    const int slot = tid + 256 * i;
+    const int slot = tid + T * i;
     if constexpr (A_MN) {
       const int k = slot / (BM / 8), c = (slot % (BM / 8)) ^ fmn_r<BM>(k);
       const int64_t gm = m0 + 8 * c < M ? m0 + 8 * c : (int64_t)M - 8;
@@ -302,7 +306,7 @@ __global__ __launch_bounds__(256) void dense_pipe_kernel(
   }
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
-    const int slot = tid + 256 * i;
+    const int slot = tid + T * i;
     if constexpr (B_MN) {
       const int k = slot / (BN / 8), c = (slot % (BN / 8)) ^ fmn_r<BN>(k);
       const int64_t gn = n0 + 8 * c < N ? n0 + 8 * c : (int64_t)N - 8;
@@ -328,10 +332,10 @@ __global__ __launch_bounds__(256) void dense_pipe_kernel(
   auto issue1 = [&](int st, int j) {
     u32x4* base = psm + (size_t)(st % STAGES) * STAGE;
     if (j < A_LOADS)
-      __builtin_amdgcn_global_load_lds((void*)(asrc[j] + st * astep), (void*)(base + 256 * j + 64 * wave), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((void*)(asrc[j] + st * astep), (void*)(base + T * j + 64 * wave), 16, 0, 0);
     else
       __builtin_amdgcn_global_load_lds((void*)(bsrc[j - A_LOADS] + st * bstep),
-                                       (void*)(base + A_SLOTS + 256 * (j - A_LOADS) + 64 * wave), 16, 0, 0);
+                                       (void*)(base + A_SLOTS + T * (j - A_LOADS) + 64 * wave), 16, 0, 0);
   };
   // operand fragment j (0 .. FM-1: rows of A, FM .. FM+FN-1: columns of B) of
   // k step s (32 k) of stage kt
@@ -491,7 +495,7 @@ __global__ __launch_bounds__(256) void dense_pipe_kernel(
       }
   __syncthreads();
   constexpr int CPR = BN / 8;
-  for (int c = tid; c < BM * CPR; c += 256) {
+  for (int c = tid; c < BM * CPR; c += T) {
     const int r = c / CPR, cc = c - r * CPR;
     const int64_t gr = m0 + r, gc = n0 + 8 * cc;
     if (gr >= M || gc >= N) continue;
@@ -943,8 +947,11 @@ static void tile_launch(const DenseArgs& a, hipStream_t stream) {
 #ifndef QG_DENSE_PIPE_STAGES
 #define QG_DENSE_PIPE_STAGES 3
 #endif
+#ifndef QG_DENSE_W256
+#define QG_DENSE_W256 8     // waves of the 256 x 256 tile: two per SIMD, 128 x 64 each (4: one per SIMD, 128 x 128)
+#endif
 
-template <int LAYOUT, int DTYPE, int BM, int BN, int STAGES>
+template <int LAYOUT, int DTYPE, int BM, int BN, int STAGES, int NWV = 4>
 static void pipe_launch(const DenseArgs& a, hipStream_t stream) {
   const int tiles_m = (int)((a.M + BM - 1) / BM), tiles_n = (int)((a.N + BN - 1) / BN);
   const int tiles = tiles_m * tiles_n, per_xcd = (tiles + 7) / 8;
@@ -952,7 +959,8 @@ static void pipe_launch(const DenseArgs& a, hipStream_t stream) {
   const size_t main_bytes = (size_t)STAGES * (BM + BN) * 8 * 16;
   const size_t out_bytes = (size_t)BM * (BN + 8) * 2;
   const size_t lds = main_bytes > out_bytes ? main_bytes : out_bytes;
-  dense_pipe_kernel<LAYOUT, DTYPE, BM, BN, STAGES><<<dim3((unsigned)(per_xcd * 8), (unsigned)a.batch), dim3(256), lds, stream>>>(
+  dense_pipe_kernel<LAYOUT, DTYPE, BM, BN, STAGES, NWV><<<dim3((unsigned)(per_xcd * 8), (unsigned)a.batch),
+                                                          dim3(64 * NWV), lds, stream>>>(
       a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, vec, strides(a));
 }
 
@@ -1048,7 +1056,7 @@ static void dense_dispatch(const DenseArgs& a, hipStream_t stream) {
   } else if (mfma_fits(a) && a.K % DBK == 0 && a.M >= 128 && a.N >= 128) {
     auto launch_tile = [&](int t, const DenseArgs& b) {
       switch (t) {
-        case 2: pipe_launch<LAYOUT, DTYPE, 256, 256, 2>(b, stream); break;
+        case 2: pipe_launch<LAYOUT, DTYPE, 256, 256, 2, QG_DENSE_W256>(b, stream); break;
         case 1: pipe_launch<LAYOUT, DTYPE, 256, 128, QG_DENSE_PIPE_STAGES>(b, stream); break;
         case 0: pipe_launch<LAYOUT, DTYPE, 128, 128, 4>(b, stream); break;
         default: pipe_launch<LAYOUT, DTYPE, 64, 128, 4>(b, stream); break;
