@@ -257,7 +257,7 @@ __device__ __forceinline__ u32x4 read_mn_frag(const u32x4* region, int kb, int c
   return out;
 }
 
-template <int LAYOUT, int DTYPE, int BM, int BN, int STAGES, int NWV = 4>
+template <int LAYOUT, int DTYPE, int BM, int BN, int STAGES, int NWV = 4, int WGM = 2>
 __global__ __launch_bounds__(64 * NWV) void dense_pipe_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_n, int tiles,
@@ -267,10 +267,10 @@ __global__ __launch_bounds__(64 * NWV) void dense_pipe_kernel(
   C += blockIdx.y * bs.c;
   constexpr bool A_MN = (LAYOUT == 2);           // A stored [K][M]
   constexpr bool B_MN = (LAYOUT != 0);           // B stored [K][N]
-  // NWV waves as a 2 x (NWV / 2) grid over the tile: 4 waves (one per SIMD) or
-  // 8 (two per SIMD, half the columns each)
+  // NWV waves as a WGM x (NWV / WGM) grid over the tile: 4 waves (one per
+  // SIMD) or 8 (two per SIMD)
   constexpr int T = 64 * NWV;
-  constexpr int WM = BM / 2, WN = BN / (NWV / 2), FM = WM / 16, FN = WN / 16;
+  constexpr int WM = BM / WGM, WN = BN / (NWV / WGM), FM = WM / 16, FN = WN / 16;
   constexpr int A_SLOTS = BM * 8, B_SLOTS = BN * 8;           // 16-byte chunks per stage
   constexpr int STAGE = A_SLOTS + B_SLOTS;
   constexpr int A_LOADS = A_SLOTS / T, B_LOADS = B_SLOTS / T;   // per thread per stage
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(64 * NWV) void dense_pipe_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cl = lane & 15, ks = lane >> 4;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int wm0 = (wave & 1) * WM, wn0 = (wave >> 1) * WN;
+  const int wm0 = (wave % WGM) * WM, wn0 = (wave / WGM) * WN;
 
   // source of each of this thread's chunks (chunk tid + 256 i of the operand's
   // stage region), at k tile 0; later tiles add k0 (K-contiguous) or k0 * ld
@@ -947,11 +947,24 @@ static void tile_launch(const DenseArgs& a, hipStream_t stream) {
 #ifndef QG_DENSE_PIPE_STAGES
 #define QG_DENSE_PIPE_STAGES 3
 #endif
+// Waves of the 256 x 256 and 256 x 128 tiles: 8, two per SIMD, so that one
+// wave's MFMAs run while the other waits on LDS or the barrier (4: one per
+// SIMD).  Measured against 4 waves (bf16 training trio, same-process A/B):
+// 256 x 256 as 128 x 64 per wave, NN 2048 x 5632 x 2048 73.6 -> 61.9 µs, TN
+// 2-9% faster, NT within 5%; then 256 x 128 as 64 x 64 (NT) or 128 x 32 (NN,
+// TN) per wave, NN 1024 x 5632 x 2048 48.8 -> 41.3 µs, 4096 x 2048 x 5632
+// 121.6 -> 109.0 µs, NT 4096 x 5632 x 2048 97.9 -> 91.9 µs, 2.5% over the trio.
+#ifndef QG_DENSE_W128
+#define QG_DENSE_W128 8     // waves of the 256 x 128 tile
+#endif
+#ifndef QG_DENSE_G128
+#define QG_DENSE_G128 0     // of which along M (0: 4 for NT, 2 for NN / TN)
+#endif
 #ifndef QG_DENSE_W256
-#define QG_DENSE_W256 8     // waves of the 256 x 256 tile: two per SIMD, 128 x 64 each (4: one per SIMD, 128 x 128)
+#define QG_DENSE_W256 8     // waves of the 256 x 256 tile (128 x 64 each)
 #endif
 
-template <int LAYOUT, int DTYPE, int BM, int BN, int STAGES, int NWV = 4>
+template <int LAYOUT, int DTYPE, int BM, int BN, int STAGES, int NWV = 4, int WGM = 2>
 static void pipe_launch(const DenseArgs& a, hipStream_t stream) {
   const int tiles_m = (int)((a.M + BM - 1) / BM), tiles_n = (int)((a.N + BN - 1) / BN);
   const int tiles = tiles_m * tiles_n, per_xcd = (tiles + 7) / 8;
@@ -959,8 +972,8 @@ static void pipe_launch(const DenseArgs& a, hipStream_t stream) {
   const size_t main_bytes = (size_t)STAGES * (BM + BN) * 8 * 16;
   const size_t out_bytes = (size_t)BM * (BN + 8) * 2;
   const size_t lds = main_bytes > out_bytes ? main_bytes : out_bytes;
-  dense_pipe_kernel<LAYOUT, DTYPE, BM, BN, STAGES, NWV><<<dim3((unsigned)(per_xcd * 8), (unsigned)a.batch),
-                                                          dim3(64 * NWV), lds, stream>>>(
+  dense_pipe_kernel<LAYOUT, DTYPE, BM, BN, STAGES, NWV, WGM><<<dim3((unsigned)(per_xcd * 8), (unsigned)a.batch),
+                                                               dim3(64 * NWV), lds, stream>>>(
       a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, vec, strides(a));
 }
 
@@ -1057,7 +1070,10 @@ static void dense_dispatch(const DenseArgs& a, hipStream_t stream) {
     auto launch_tile = [&](int t, const DenseArgs& b) {
       switch (t) {
         case 2: pipe_launch<LAYOUT, DTYPE, 256, 256, 2, QG_DENSE_W256>(b, stream); break;
-        case 1: pipe_launch<LAYOUT, DTYPE, 256, 128, QG_DENSE_PIPE_STAGES>(b, stream); break;
+        case 1:
+          pipe_launch<LAYOUT, DTYPE, 256, 128, QG_DENSE_PIPE_STAGES, QG_DENSE_W128,
+                      QG_DENSE_G128 ? QG_DENSE_G128 : (LAYOUT == 0 ? 4 : 2)>(b, stream);
+          break;
         case 0: pipe_launch<LAYOUT, DTYPE, 128, 128, 4>(b, stream); break;
         default: pipe_launch<LAYOUT, DTYPE, 64, 128, 4>(b, stream); break;
       }
