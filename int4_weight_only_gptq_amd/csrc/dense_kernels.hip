@@ -960,6 +960,18 @@ static void tile_launch(const DenseArgs& a, hipStream_t stream) {
 #ifndef QG_DENSE_G128
 #define QG_DENSE_G128 0     // of which along M (0: 4 for NT, 2 for NN / TN)
 #endif
+// The 128 x 128 tile: 4 stages, 8 waves of 64 x 32 (NN 2048 x 2048 x 5632
+// 82.7 -> 77.3 µs, NT 2048 x 2048 x 5632 58.5 -> 56.5 µs against 4 waves of
+// 64 x 64; 2 stages, so that two workgroups share a CU, were slower).
+#ifndef QG_DENSE_T0_STAGES
+#define QG_DENSE_T0_STAGES 4
+#endif
+#ifndef QG_DENSE_T0_WAVES
+#define QG_DENSE_T0_WAVES 8
+#endif
+#ifndef QG_DENSE_T0_WGM
+#define QG_DENSE_T0_WGM 2
+#endif
 #ifndef QG_DENSE_W256
 #define QG_DENSE_W256 8     // waves of the 256 x 256 tile (128 x 64 each)
 #endif
@@ -1074,7 +1086,7 @@ static void dense_dispatch(const DenseArgs& a, hipStream_t stream) {
           pipe_launch<LAYOUT, DTYPE, 256, 128, QG_DENSE_PIPE_STAGES, QG_DENSE_W128,
                       QG_DENSE_G128 ? QG_DENSE_G128 : (LAYOUT == 0 ? 4 : 2)>(b, stream);
           break;
-        case 0: pipe_launch<LAYOUT, DTYPE, 128, 128, 4>(b, stream); break;
+        case 0: pipe_launch<LAYOUT, DTYPE, 128, 128, QG_DENSE_T0_STAGES, QG_DENSE_T0_WAVES, QG_DENSE_T0_WGM>(b, stream); break;
         default: pipe_launch<LAYOUT, DTYPE, 64, 128, 4>(b, stream); break;
       }
     };
