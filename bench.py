@@ -313,12 +313,13 @@ def cpu_baseline(cases, seconds):
 
     threads = cpu.default_threads()
     t0 = time.perf_counter()
-    done_bytes, calls = 0, 0
+    done_bytes, done_flops, calls = 0, 0, 0
     while True:
         for c in cases:
             d = c.host
             cpu.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], c.m, c.k, c.n, threads=threads)
             done_bytes += c.bytes
+            done_flops += c.flops
             calls += 1
         if time.perf_counter() - t0 >= seconds:
             break
@@ -345,7 +346,9 @@ def cpu_baseline(cases, seconds):
     except OSError:
         pass
     return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "cpu_model": model, "hardware_threads": cpu.hardware_threads(),
+            "kind": "oracle", "us_per_call": round(el / calls * 1e6, 1),
+            "gflops": round(done_flops / el / 1e9, 3), "cpu_model": model,
+            "hardware_threads": cpu.hardware_threads(),
             "single_thread_gemv_us": round(el1 / n1 * 1e6, 1),
             "single_thread_step_s": round(el2, 3),
             "sample": "%d calls of the C++ oracle (dequantise to fp32, accumulate in fp64, %d std::threads "
@@ -456,11 +459,22 @@ def main():
     for c in cases:
         us = time_us(torch, c.launch, args.steps, min_calls=len(c.w))
         per_case.append({"m": c.m, "k": c.k, "n": c.n, "kernel": c.kernel, "us": round(us, 3),
-                         "gbps": round(c.bytes / us / 1e3, 1), "bytes": c.bytes,
+                         "gbps": round(c.bytes / us / 1e3, 1), "tflops": round(c.flops / us / 1e6, 2),
+                         "bytes": c.bytes,
                          "calls_per_replay": max(args.steps, len(c.w)),
                          "bytes_per_replay": max(args.steps, len(c.w)) * c.bytes})
         print("case", per_case[-1], file=sys.stderr, flush=True)
     state1 = gpu_state(qg, torch)
+    # context: the warm regime (one weight copy, resident in the LLC), same timing
+    warm = []
+    for c in cases:
+        w0 = c.w[0]
+
+        def warm_launch(c=c, w0=w0):
+            c.qg.qgemm_int4(c.x, w0[0], w0[1], w0[2], out=c.y)
+
+        us = time_us(torch, warm_launch, args.steps)
+        warm.append({"m": c.m, "k": c.k, "n": c.n, "us": round(us, 3), "gbps": round(c.bytes / us / 1e3, 1)})
     # floor: the smallest kernel the same entry point launches (k = 0 -> a zero fill of 1 x 8)
     fx = torch.empty((1, 0), dtype=torch.bfloat16, device="cuda")
     fw = torch.empty((0, 8), dtype=torch.int32, device="cuda")
@@ -513,7 +527,9 @@ def main():
         "cases": per_case,
         "timing": "HIP graph replay of back-to-back launches, HIP events on the launch stream; the step: one "
                   "replay of exactly K steps; per-case, floor, reference and config figures: median of 7 "
-                  "replays, each touching every weight copy (>= 2x the LLC per replay in the cold regime)",
+                  "replays, each touching every weight copy (>= 2x the LLC per replay in the cold regime); "
+                  "warm_cases: the same calls on one weight copy (LLC-resident), context only",
+        "warm_cases": warm,
         "floor_us": round(floor_us, 3),
         "copy_gbps": bw["copy_gbps"],
         "read_gbps": bw["read_gbps"],
