@@ -254,7 +254,18 @@ def gpu_state(qg, torch):
     mhz = float(np.median(100.0 * (c[:, 2] - c[:, 0]) / np.where(ticks > 0, ticks, np.nan)))
     out = {"sclk_mhz": round(mhz, 1)}
     try:
-        res = subprocess.run(["rocm-smi", "--showtemp", "--json"], capture_output=True, text=True, timeout=15)
+        # rocm-smi is a Python script: start it under this interpreter as a child
+        # process, so that no launcher in between replaces itself with exec()
+        import shutil
+
+        smi = shutil.which("rocm-smi")
+        if smi is None:
+            raise OSError("rocm-smi not found")
+        smi = os.path.realpath(smi)
+        with open(smi, "rb") as f:
+            first = f.readline()
+        cmd = ([sys.executable, smi] if b"python" in first else [smi]) + ["--showtemp", "--json"]
+        res = subprocess.run(cmd, capture_output=True, text=True, timeout=15)
         data = json.loads(res.stdout)
         temps = {}
         for card, vals in data.items():
