@@ -787,7 +787,9 @@ constexpr int FKP = FBK + 4;             // floats per LDS row, K-contiguous ope
 constexpr int FMP = 128 + 4;             // floats per LDS k-row, M/N-contiguous operand
 constexpr int F32_REGION = 128 * FKP > FBK * FMP ? 128 * FKP : FBK * FMP;   // floats per operand buffer
 
-template <int LAYOUT>
+// BM = 128 or 64 rows per tile (waves of 64 x 64 or 32 x 64): the 64-row tile
+// for products whose 128-row tiles would leave CUs idle in their last round.
+template <int LAYOUT, int BM = 128>
 __global__ __launch_bounds__(256) void dense_f32_kernel(const float* __restrict__ A, int64_t lda,
                                                         const float* __restrict__ B, int64_t ldb,
                                                         float* __restrict__ C, int64_t ldc, int M, int N,
@@ -797,7 +799,9 @@ __global__ __launch_bounds__(256) void dense_f32_kernel(const float* __restrict_
   B += blockIdx.y * bs.b;
   C += blockIdx.y * bs.c;
   constexpr bool A_MN = (LAYOUT == 2), B_MN = (LAYOUT != 0);
-  constexpr int FM = 4, FN = 4;
+  static_assert(BM == 128 || BM == 64, "tile rows");
+  constexpr int FM = BM / 32, FN = 4;
+  constexpr int AL = BM / 32;                // float4 loads of A per thread and k tile
   __shared__ __attribute__((aligned(16))) float fsm[2][2][F32_REGION];   // [buffer][A, B]
 
   const int t = (blockIdx.x & 7) * tiles_per_xcd + (blockIdx.x >> 3);
@@ -805,18 +809,21 @@ __global__ __launch_bounds__(256) void dense_f32_kernel(const float* __restrict_
   const int tm = t / tiles_n, tn = t - tm * tiles_n;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cl = lane & 15, ks = lane >> 4;
-  const int64_t m0 = (int64_t)tm * 128, n0 = (int64_t)tn * 128;
-  const int wm0 = (wave & 1) * 64, wn0 = (wave >> 1) * 64;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * 128;
+  const int wm0 = (wave & 1) * (BM / 2), wn0 = (wave >> 1) * 64;
 
-  // 4 float4 per thread per operand and k tile; past the edges: zeros
-  f32x4 ra[4], rb[4];
+  // BM / 32 (A) and 4 (B) float4 per thread and k tile; past the edges: zeros.
+  // An operand of R rows (R = BM or 128): K-contiguous, 8 float4 per row;
+  // M/N-contiguous, R / 4 float4 per k-row.
+  f32x4 ra[AL], rb[4];
   auto load_op = [&](const float* __restrict__ P, int64_t ld, int64_t r0, int64_t rows, bool mn, int64_t k0,
-                     f32x4 (&reg)[4]) {
+                     auto& reg) {
+    constexpr int L = sizeof(reg) / sizeof(reg[0]), R = 32 * L;   // rows of this operand's tile
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < L; ++i) {
       const int c = tid + 256 * i;
       if (mn) {
-        const int64_t gk = k0 + c / 32, gr = r0 + 4 * (c % 32);
+        const int64_t gk = k0 + c / (R / 4), gr = r0 + 4 * (c % (R / 4));
         reg[i] = (gk < K && gr < rows) ? *reinterpret_cast<const f32x4*>(P + gk * ld + gr)
                                        : f32x4{0.f, 0.f, 0.f, 0.f};
       } else {
@@ -826,11 +833,12 @@ __global__ __launch_bounds__(256) void dense_f32_kernel(const float* __restrict_
       }
     }
   };
-  auto store_op = [&](float* region, bool mn, const f32x4 (&reg)[4]) {
+  auto store_op = [&](float* region, bool mn, const auto& reg) {
+    constexpr int L = sizeof(reg) / sizeof(reg[0]), R = 32 * L;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < L; ++i) {
       const int c = tid + 256 * i;
-      if (mn) *reinterpret_cast<f32x4*>(region + (c / 32) * FMP + 4 * (c % 32)) = reg[i];
+      if (mn) *reinterpret_cast<f32x4*>(region + (c / (R / 4)) * FMP + 4 * (c % (R / 4))) = reg[i];
       else *reinterpret_cast<f32x4*>(region + (c / 8) * FKP + 4 * (c % 8)) = reg[i];
     }
   };
@@ -1115,6 +1123,10 @@ static void dense_dispatch(const DenseArgs& a, hipStream_t stream) {
   }
 }
 
+#ifndef QG_F32_T64
+#define QG_F32_T64 0.55   // time of a round of 64 x 128 fp32 tiles relative to 128 x 128
+#endif
+
 template <int LAYOUT>
 static void dense_dispatch_f32(const DenseArgs& a, hipStream_t stream) {
   const float* A = reinterpret_cast<const float*>(a.A);
@@ -1125,10 +1137,20 @@ static void dense_dispatch_f32(const DenseArgs& a, hipStream_t stream) {
                    a.sb % 4 == 0 && a_contig % 4 == 0 && b_contig % 4 == 0 && a.M < (1LL << 31) &&
                    a.N < (1LL << 31) && a.K < (1LL << 31);
   if (vec) {
+    // 64-row tiles where they take fewer rounds of the CUs, weighted by their
+    // relative time per round
     const int tiles_n = (int)((a.N + 127) / 128);
-    const int tiles = (int)(((a.M + 127) / 128) * tiles_n), per_xcd = (tiles + 7) / 8;
-    dense_f32_kernel<LAYOUT><<<dim3((unsigned)(per_xcd * 8), (unsigned)a.batch), dim3(256), 0, stream>>>(
-        A, a.lda, B, a.ldb, C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, strides(a));
+    const int64_t t128 = ((a.M + 127) / 128) * tiles_n, t64 = ((a.M + 63) / 64) * tiles_n;
+    auto rounds = [&](int64_t t) { return (double)((t * a.batch + 255) / 256); };
+    if (rounds(t64) * QG_F32_T64 < rounds(t128)) {
+      const int tiles = (int)t64, per_xcd = (tiles + 7) / 8;
+      dense_f32_kernel<LAYOUT, 64><<<dim3((unsigned)(per_xcd * 8), (unsigned)a.batch), dim3(256), 0, stream>>>(
+          A, a.lda, B, a.ldb, C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, strides(a));
+    } else {
+      const int tiles = (int)t128, per_xcd = (tiles + 7) / 8;
+      dense_f32_kernel<LAYOUT, 128><<<dim3((unsigned)(per_xcd * 8), (unsigned)a.batch), dim3(256), 0, stream>>>(
+          A, a.lda, B, a.ldb, C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, strides(a));
+    }
   } else {
     const int64_t total = a.M * a.N;
     dense_generic_f32_kernel<LAYOUT><<<dim3((unsigned)((total + 255) / 256), (unsigned)a.batch), dim3(256), 0,
