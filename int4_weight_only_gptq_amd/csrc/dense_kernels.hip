@@ -789,8 +789,8 @@ constexpr int F32_REGION = 128 * FKP > FBK * FMP ? 128 * FKP : FBK * FMP;   // f
 
 // BM = 128 or 64 rows per tile (waves of 64 x 64 or 32 x 64): the 64-row tile
 // for products whose 128-row tiles would leave CUs idle in their last round.
-template <int LAYOUT, int BM = 128>
-__global__ __launch_bounds__(256) void dense_f32_kernel(const float* __restrict__ A, int64_t lda,
+template <int LAYOUT, int BM = 128, int NWF = 4>
+__global__ __launch_bounds__(64 * NWF) void dense_f32_kernel(const float* __restrict__ A, int64_t lda,
                                                         const float* __restrict__ B, int64_t ldb,
                                                         float* __restrict__ C, int64_t ldc, int M, int N,
                                                         int K, int tiles_n, int tiles, int tiles_per_xcd,
@@ -800,8 +800,12 @@ __global__ __launch_bounds__(256) void dense_f32_kernel(const float* __restrict_
   C += blockIdx.y * bs.c;
   constexpr bool A_MN = (LAYOUT == 2), B_MN = (LAYOUT != 0);
   static_assert(BM == 128 || BM == 64, "tile rows");
-  constexpr int FM = BM / 32, FN = 4;
-  constexpr int AL = BM / 32;                // float4 loads of A per thread and k tile
+  static_assert(NWF == 4 || NWF == 8, "waves");
+  // NWF waves as 2 x (NWF / 2): 4 waves of (BM / 2) x 64, or 8 of (BM / 2) x 32
+  constexpr int TF = 64 * NWF, WNF = 128 / (NWF / 2);
+  constexpr int FM = BM / 32, FN = WNF / 16;
+  constexpr int AL = BM * 8 / TF;            // float4 loads of A per thread and k tile
+  constexpr int BLD = 128 * 8 / TF;          // of B
   __shared__ __attribute__((aligned(16))) float fsm[2][2][F32_REGION];   // [buffer][A, B]
 
   const int t = (blockIdx.x & 7) * tiles_per_xcd + (blockIdx.x >> 3);
@@ -810,18 +814,18 @@ __global__ __launch_bounds__(256) void dense_f32_kernel(const float* __restrict_
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cl = lane & 15, ks = lane >> 4;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * 128;
-  const int wm0 = (wave & 1) * (BM / 2), wn0 = (wave >> 1) * 64;
+  const int wm0 = (wave & 1) * (BM / 2), wn0 = (wave >> 1) * WNF;
 
-  // BM / 32 (A) and 4 (B) float4 per thread and k tile; past the edges: zeros.
+  // AL (A) and BLD (B) float4 per thread and k tile; past the edges: zeros.
   // An operand of R rows (R = BM or 128): K-contiguous, 8 float4 per row;
   // M/N-contiguous, R / 4 float4 per k-row.
-  f32x4 ra[AL], rb[4];
+  f32x4 ra[AL], rb[BLD];
   auto load_op = [&](const float* __restrict__ P, int64_t ld, int64_t r0, int64_t rows, bool mn, int64_t k0,
                      auto& reg) {
-    constexpr int L = sizeof(reg) / sizeof(reg[0]), R = 32 * L;   // rows of this operand's tile
+    constexpr int L = sizeof(reg) / sizeof(reg[0]), R = L * TF / 8;   // rows of this operand's tile
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + TF * i;
       if (mn) {
         const int64_t gk = k0 + c / (R / 4), gr = r0 + 4 * (c % (R / 4));
         reg[i] = (gk < K && gr < rows) ? *reinterpret_cast<const f32x4*>(P + gk * ld + gr)
@@ -834,10 +838,10 @@ __global__ __launch_bounds__(256) void dense_f32_kernel(const float* __restrict_
     }
   };
   auto store_op = [&](float* region, bool mn, const auto& reg) {
-    constexpr int L = sizeof(reg) / sizeof(reg[0]), R = 32 * L;
+    constexpr int L = sizeof(reg) / sizeof(reg[0]), R = L * TF / 8;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + TF * i;
       if (mn) *reinterpret_cast<f32x4*>(region + (c / (R / 4)) * FMP + 4 * (c % (R / 4))) = reg[i];
       else *reinterpret_cast<f32x4*>(region + (c / 8) * FKP + 4 * (c % 8)) = reg[i];
     }
@@ -1123,6 +1127,13 @@ static void dense_dispatch(const DenseArgs& a, hipStream_t stream) {
   }
 }
 
+// Waves of the 128 x 128 fp32 tile: 8 (two per SIMD, 64 x 32 each) for NN and
+// TN, 4 (64 x 64) for NT.  Eight against four, same-process A/B: NN 2048 x
+// 2048 x 5632 440 -> 405 µs, TN 1-3% faster at every size; NT mixed (2048 x
+// 5632 x 2048 538 -> 464 µs, but 4096 tokens 6-8% slower).
+#ifndef QG_F32_WAVES
+#define QG_F32_WAVES 0    // 0: by layout as above
+#endif
 #ifndef QG_F32_T64
 #define QG_F32_T64 0.55   // time of a round of 64 x 128 fp32 tiles relative to 128 x 128
 #endif
@@ -1148,7 +1159,9 @@ static void dense_dispatch_f32(const DenseArgs& a, hipStream_t stream) {
           A, a.lda, B, a.ldb, C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, strides(a));
     } else {
       const int tiles = (int)t128, per_xcd = (tiles + 7) / 8;
-      dense_f32_kernel<LAYOUT, 128><<<dim3((unsigned)(per_xcd * 8), (unsigned)a.batch), dim3(256), 0, stream>>>(
+      constexpr int W = QG_F32_WAVES ? QG_F32_WAVES : (LAYOUT == 0 ? 4 : 8);
+      dense_f32_kernel<LAYOUT, 128, W><<<dim3((unsigned)(per_xcd * 8), (unsigned)a.batch), dim3(64 * W), 0,
+                                         stream>>>(
           A, a.lda, B, a.ldb, C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, strides(a));
     }
   } else {

@@ -288,8 +288,11 @@ def test_attention_products_sampled(gpu_lib, case):
 from gpu_helpers import host_u32  # noqa: E402
 
 FP32_RMS_GATE = 2e-5
+# the last shape takes the 128 x 128 tile (512 of them; 64-row tiles would need more rounds)
+# with ragged rows, columns and k tile; the others take the 64-row tile or, unaligned, the
+# one-thread-per-output kernel
 FP32_SHAPES = [(1, 1, 1), (13, 17, 19), (128, 128, 64), (130, 264, 200), (256, 136, 520), (1000, 8, 16),
-               (200, 264, 36), (64, 16, 1024)]
+               (200, 264, 36), (64, 16, 1024), (2000, 4000, 100)]
 
 
 def assert_fp32_accepted(c_bits, ref, absd, K, what):
