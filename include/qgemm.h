@@ -311,6 +311,40 @@ int32_t gemm_dense(int32_t layout, int32_t dtype, int64_t M, int64_t N, int64_t 
                    int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream);
 
 /*
+ * gemm_dense_ws -- gemm_dense with a workspace, which lets products with few
+ * output tiles and a long K split K over several workgroups (bf16 / fp16 on
+ * the pipelined tiles: when the 256 x 128 tiles would fill less than three
+ * quarters of the 256 CUs and each of up to 4 k slices keeps at least 1024 k).
+ * Each slice stores its fp32 partial tile; the last slice of a tile to arrive
+ * adds them in slice order (deterministic for a given size) and rounds once,
+ * so the accuracy contract is that of gemm_dense (the summation order
+ * differs).  The exchange is ordered as qg_set_split_order selects.
+ *
+ *   workspace, workspace_bytes
+ *            optional device scratch (16-byte aligned); NULL or fewer bytes
+ *            than gemm_dense_workspace_size asks for: no split.  As for
+ *            qgemm_int4, its first 64 KiB hold the split's counters, which
+ *            must be zero before the first use with this library and are
+ *            zero again after each call (the same workspace may serve both
+ *            entry points); calls that share a workspace must not overlap.
+ *
+ * Other arguments and errors as gemm_dense (plus QG_ERR_SHAPE for a negative
+ * workspace_bytes and QG_ERR_ALIGN for a misaligned workspace).
+ */
+int32_t gemm_dense_ws(int32_t layout, int32_t dtype, int64_t M, int64_t N, int64_t K, const void* A,
+                      int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, void* workspace,
+                      int64_t workspace_bytes, void* stream);
+
+/*
+ * gemm_dense_workspace_size -- bytes of workspace with which gemm_dense_ws
+ * splits K for this (layout, dtype, M, N, K), assuming 16-byte aligned
+ * operands with leading dimensions equal to their contiguous extents; 0 when
+ * it would not split (QG_FP32, short K, enough tiles).  A negative value is
+ * -qg_status for invalid arguments.
+ */
+int64_t gemm_dense_workspace_size(int32_t layout, int32_t dtype, int64_t M, int64_t N, int64_t K);
+
+/*
  * gemm_dense_batched -- `batch` independent gemm_dense products in one launch,
  * the batched products inside attention that the BC-250 tuned-GEMM post tunes
  * and validates ("Tuning the kernels", "Checking the results are right"):

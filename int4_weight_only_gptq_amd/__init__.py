@@ -84,6 +84,10 @@ def load():
     lib.qgemm_int4_lora_workspace_size.argtypes = [i64, i64, i64, i32]
     lib.gemm_dense.restype = i32
     lib.gemm_dense.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
+    lib.gemm_dense_ws.restype = i32
+    lib.gemm_dense_ws.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp]
+    lib.gemm_dense_workspace_size.restype = i64
+    lib.gemm_dense_workspace_size.argtypes = [i32, i32, i64, i64, i64]
     lib.gemm_dense_batched.restype = i32
     lib.gemm_dense_batched.argtypes = [i32, i32, i64, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64,
                                        i64, vp]
@@ -335,9 +339,21 @@ def _dtype_of(a, b):
     return names[a.dtype]
 
 
-def gemm_dense(layout: str, a, b, out=None, stream=None):
+def dense_workspace_size(layout: str, dtype: str, M: int, N: int, K: int) -> int:
+    """Bytes of workspace that let gemm_dense split K for this product (0: no split)."""
+    size = load().gemm_dense_workspace_size(LAYOUTS[layout], _DTYPES[dtype], M, N, K)
+    if size < 0:
+        raise QGemmError(-size, "gemm_dense_workspace_size")
+    return size
+
+
+def gemm_dense(layout: str, a, b, out=None, stream=None, workspace=None):
     """C = op(A) . op(B) for layout "NT", "NN" or "TN" (row-major, see qgemm.h);
-    bf16 / fp16 with fp32 accumulation, or fp32 throughout."""
+    bf16 / fp16 with fp32 accumulation, or fp32 throughout.
+
+    ``workspace``: None = the cached zero-filled buffer of the launch stream when
+    the library asks for one (a k split for few-tile, long-K products); False =
+    none; or a caller-owned uint8 tensor."""
     import torch
 
     lib = load()
@@ -352,8 +368,15 @@ def gemm_dense(layout: str, a, b, out=None, stream=None):
         raise ValueError(layout)
     if out is None:
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
-    st = lib.gemm_dense(LAYOUTS[layout], _DTYPES[dtype], M, N, K, a.data_ptr(), _ld(a),
-                        b.data_ptr(), _ld(b), out.data_ptr(), _ld(out), _stream(a, stream))
+    if workspace is None:
+        workspace = _workspace(a.device, stream, dense_workspace_size(layout, dtype, M, N, K))
+    if workspace is None or workspace is False:
+        st = lib.gemm_dense(LAYOUTS[layout], _DTYPES[dtype], M, N, K, a.data_ptr(), _ld(a),
+                            b.data_ptr(), _ld(b), out.data_ptr(), _ld(out), _stream(a, stream))
+    else:
+        st = lib.gemm_dense_ws(LAYOUTS[layout], _DTYPES[dtype], M, N, K, a.data_ptr(), _ld(a),
+                               b.data_ptr(), _ld(b), out.data_ptr(), _ld(out), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream(a, stream))
     _check(st, "gemm_dense")
     return out
 

@@ -349,7 +349,10 @@ int32_t qgemm_int4_dequant(const uint32_t* qweight, const uint16_t* scales,
 
 static int32_t run_dense(int32_t layout, int32_t dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
                          const void* A, int64_t lda, int64_t sa, const void* B, int64_t ldb, int64_t sb,
-                         void* C, int64_t ldc, int64_t sc, void* stream) {
+                         void* C, int64_t ldc, int64_t sc, void* stream, void* ws = nullptr,
+                         int64_t ws_bytes = 0) {
+  if (ws_bytes < 0) return QG_ERR_SHAPE;
+  if (ws != nullptr && !aligned(ws, 16)) return QG_ERR_ALIGN;
   if (layout < QG_NT || layout > QG_TN) return QG_ERR_LAYOUT;
   if (dtype != QG_BF16 && dtype != QG_FP16 && dtype != QG_FP32) return QG_ERR_DTYPE;
   const uintptr_t esize = dtype == QG_FP32 ? 4 : 2;
@@ -368,14 +371,39 @@ static int32_t run_dense(int32_t layout, int32_t dtype, int64_t batch, int64_t M
     if (!aligned(A, esize) || !aligned(B, esize)) return QG_ERR_ALIGN;
   }
   if (batch == 1) sa = sb = sc = 0;
-  const qg::DenseArgs a{layout, dtype, M, N, K, (const uint16_t*)A, lda, (const uint16_t*)B, ldb,
-                        (uint16_t*)C, ldc, batch, sa, sb, sc};
+  qg::DenseArgs a{layout, dtype, M, N, K, (const uint16_t*)A, lda, (const uint16_t*)B, ldb,
+                  (uint16_t*)C, ldc, batch, sa, sb, sc};
+  a.ws = ws;
+  a.ws_bytes = ws ? ws_bytes : 0;
+  a.split_acq_rel = g_split_order.load(std::memory_order_relaxed) == QG_SPLIT_ORDER_ACQ_REL;
   return hip_status(qg::launch_dense(a, (hipStream_t)stream));
 }
 
 int32_t gemm_dense(int32_t layout, int32_t dtype, int64_t M, int64_t N, int64_t K, const void* A,
                    int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
   return run_dense(layout, dtype, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, stream);
+}
+
+int32_t gemm_dense_ws(int32_t layout, int32_t dtype, int64_t M, int64_t N, int64_t K, const void* A,
+                      int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, void* workspace,
+                      int64_t workspace_bytes, void* stream) {
+  return run_dense(layout, dtype, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, stream, workspace,
+                   workspace_bytes);
+}
+
+int64_t gemm_dense_workspace_size(int32_t layout, int32_t dtype, int64_t M, int64_t N, int64_t K) {
+  if (layout < QG_NT || layout > QG_TN) return -(int64_t)QG_ERR_LAYOUT;
+  if (dtype != QG_BF16 && dtype != QG_FP16 && dtype != QG_FP32) return -(int64_t)QG_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0) return -(int64_t)QG_ERR_SHAPE;
+  if (M == 0 || N == 0 || K == 0 || dtype == QG_FP32) return 0;
+  // the split needs the pipelined tiles, whose 16-byte loads need aligned
+  // operands: the size assumes 16-byte aligned A and B with leading
+  // dimensions equal to the contiguous extents
+  qg::DenseArgs a{layout, dtype, M, N, K, (const uint16_t*)nullptr, 0, (const uint16_t*)nullptr, 0,
+                  (uint16_t*)nullptr, N, 1, 0, 0, 0};
+  a.lda = layout == QG_TN ? M : K;
+  a.ldb = layout == QG_NT ? K : N;
+  return qg::dense_workspace_bytes(a);
 }
 
 int32_t gemm_dense_batched(int32_t layout, int32_t dtype, int64_t batch, int64_t M, int64_t N, int64_t K,

@@ -200,6 +200,16 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 // over distinct banks.
 __device__ __forceinline__ int swz(int r, int c) { return 8 * r + (c ^ (r & 7)); }
 
+// One ticket of a k split's counter (agent scope); returns the count before.
+// acq_rel != 0: an acquire-release increment (the memory model orders the
+// slice's partial stores before it and the last slice's reads after it);
+// else relaxed, the partials' order then resting on the store-completion wait
+// before the increment.
+__device__ __forceinline__ uint32_t ticket_add(uint32_t* t, int acq_rel) {
+  return acq_rel ? __hip_atomic_fetch_add(t, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT)
+                 : __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Workgroup barrier without the memory fence of __syncthreads (which would
 // also wait for every direct global->LDS load in flight).  The empty asm with a
 // memory clobber keeps the compiler from moving LDS reads or writes across it:

@@ -18,6 +18,7 @@
 namespace qg {
 
 constexpr int DBK = 64;
+constexpr int SPLIT_MAX = 4;   // k slices of a dense tile at most (the exchange loads three others at once)
 constexpr int DSTRIDE = DBK + 8;   // 16-bit elements per LDS row (144 bytes)
 
 // 8 x 8 transpose of 16-bit elements: in[r] holds row r (8 elements), out[j]
@@ -257,11 +258,12 @@ __device__ __forceinline__ u32x4 read_mn_frag(const u32x4* region, int kb, int c
   return out;
 }
 
-template <int LAYOUT, int DTYPE, int BM, int BN, int STAGES, int NWV = 4, int WGM = 2>
+template <int LAYOUT, int DTYPE, int BM, int BN, int STAGES, int NWV = 4, int WGM = 2, bool KSPLIT = false>
 __global__ __launch_bounds__(64 * NWV) void dense_pipe_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     uint16_t* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_n, int tiles,
-    int tiles_per_xcd, int vec_store, BatchStrides bs) {
+    int tiles_per_xcd, int vec_store, BatchStrides bs, int ksplit, int kps, float* __restrict__ partials,
+    uint32_t* __restrict__ tickets, int acq_rel, int band_w) {
   A += blockIdx.y * bs.a;   // batch blockIdx.y
   B += blockIdx.y * bs.b;
   C += blockIdx.y * bs.c;
@@ -279,13 +281,25 @@ __global__ __launch_bounds__(64 * NWV) void dense_pipe_kernel(
   static_assert(LOADS * (STAGES - 1) <= 63, "vmcnt range");
   extern __shared__ __attribute__((aligned(16))) u32x4 psm[];
 
-  const int t = (blockIdx.x & 7) * tiles_per_xcd + (blockIdx.x >> 3);
-  if (t >= tiles) return;
-  const int tm = t / tiles_n, tn = t - tm * tiles_n;
+  // item = tile * ksplit + k slice (the slices of a tile are consecutive
+  // items, so they run on one XCD); slice s takes k tiles [s kps, (s + 1) kps)
+  const int item = (blockIdx.x & 7) * tiles_per_xcd + (blockIdx.x >> 3);
+  if (!KSPLIT) ksplit = 1;   // (the exchange below is compiled only into split kernels)
+  if (item >= tiles * ksplit) return;
+  const int t = item / ksplit, kslice = item - t * ksplit;
+  // tile order: bands of band_w tile columns, row-major inside a band, so that
+  // an XCD's run of consecutive tiles is a block of rows x band_w columns
+  // sharing operand panels in its L2 (band_w = tiles_n: plain row-major)
+  const int tiles_m = tiles / tiles_n, band = t / (tiles_m * band_w);
+  const int bw = min(band_w, tiles_n - band * band_w), in_band = t - band * tiles_m * band_w;
+  const int tm = in_band / bw, tn = band * band_w + (in_band - tm * bw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cl = lane & 15, ks = lane >> 4;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int wm0 = (wave % WGM) * WM, wn0 = (wave / WGM) * WN;
+  const int kt0 = kslice * kps;
+  A += A_MN ? (int64_t)kt0 * DBK * lda : (int64_t)kt0 * DBK;
+  B += B_MN ? (int64_t)kt0 * DBK * ldb : (int64_t)kt0 * DBK;
 
   // source of each of this thread's chunks (chunk tid + 256 i of the operand's
   // stage region), at k tile 0; later tiles add k0 (K-contiguous) or k0 * ld
@@ -326,7 +340,7 @@ __global__ __launch_bounds__(64 * NWV) void dense_pipe_kernel(
 #pragma unroll
     for (int c = 0; c < FN; ++c) acc[f][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int ktiles = K / DBK;
+  const int ktiles = K / DBK - kt0 < kps ? K / DBK - kt0 : kps;   // this slice's k tiles
   // direct load j (0 .. LOADS-1) of stage st: each wave-instruction fills 64
   // consecutive chunks of the stage's buffer
   auto issue1 = [&](int st, int j) {
@@ -477,6 +491,86 @@ __global__ __launch_bounds__(64 * NWV) void dense_pipe_kernel(
     for (int kt = 0; kt < ktiles; ++kt) tile(kt, kt + STAGES < ktiles, kt + 1 < ktiles);
   }
   __syncthreads();
+
+  if constexpr (KSPLIT) {
+    // Split k: every slice stores its fp32 accumulators (fragment order:
+    // element pair h of (f, c) of thread tid at ((f FN + c) 2 + h) T + tid,
+    // 8-byte agent-coherent stores, 512 contiguous bytes per wave and store),
+    // waits for them and takes a ticket; the last slice of the tile to arrive
+    // adds the slices in slice order (its own from registers) and goes on to
+    // the epilogue.  The exchange's ordering is that of the int4 split (acq_rel:
+    // an acquire-release ticket).
+    __shared__ int last_slice;
+    uint64_t* part64 = reinterpret_cast<uint64_t*>(partials);
+    uint64_t* mine = part64 + ((int64_t)t * ksplit + kslice) * (FM * FN * 2 * T);
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int c = 0; c < FN; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float lo = acc[f][c][2 * h], hi = acc[f][c][2 * h + 1];
+          const uint64_t pair = (uint64_t)__builtin_bit_cast(uint32_t, lo) |
+                                ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
+          __hip_atomic_store(&mine[((f * FN + c) * 2 + h) * T + tid], pair, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+    asm volatile("" ::: "memory");   // (no instruction: keeps the stores above the wait)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    if (tid == 0) last_slice = ticket_add(&tickets[t], acq_rel) == (uint32_t)(ksplit - 1);
+    __syncthreads();
+    if (!last_slice) return;
+    // the O = ksplit - 1 other slices' pairs, FG row fragments per batch of
+    // loads (at most 32 pairs in flight per thread), added in slice order
+    constexpr int SLICE = FM * FN * 2 * T, PAIRS = FN * 2;
+    const uint64_t* base = part64 + (int64_t)t * ksplit * SLICE;
+    auto reduce = [&](auto o_) {
+      constexpr int O = decltype(o_)::value;
+      constexpr int FG0 = 32 / (O * PAIRS), FG = FG0 < 1 ? 1 : (FG0 > FM ? FM : FG0);
+#pragma unroll
+      for (int f0 = 0; f0 < FM; f0 += FG) {
+        uint64_t w[FG][O][PAIRS];
+#pragma unroll
+        for (int g = 0; g < FG; ++g)
+#pragma unroll
+          for (int j = 0; j < O; ++j) {
+            const int q = j < kslice ? j : j + 1;
+            const uint64_t* src = base + (int64_t)q * SLICE + (f0 + g) * FN * 2 * T + tid;
+#pragma unroll
+            for (int e = 0; e < PAIRS; ++e)
+              w[g][j][e] = f0 + g < FM ? __hip_atomic_load(src + e * T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+          }
+#pragma unroll
+        for (int g = 0; g < FG; ++g) {
+          const int f = f0 + g;
+          if (f >= FM) break;
+#pragma unroll
+          for (int c = 0; c < FN; ++c)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int e = c * 2 + h;
+              float lo = 0.f, hi = 0.f;
+#pragma unroll
+              for (int p = 0; p <= O; ++p) {
+                const int jp = p < kslice ? p : p - 1;   // (selects: no indexed registers)
+                uint64_t v = w[g][0][e];
+#pragma unroll
+                for (int j = 1; j < O; ++j) v = jp == j ? w[g][j][e] : v;
+                lo += p == kslice ? acc[f][c][2 * h] : __builtin_bit_cast(float, (uint32_t)v);
+                hi += p == kslice ? acc[f][c][2 * h + 1] : __builtin_bit_cast(float, (uint32_t)(v >> 32));
+              }
+              acc[f][c][2 * h] = lo;
+              acc[f][c][2 * h + 1] = hi;
+            }
+        }
+      }
+    };
+    if (ksplit == 2) reduce(std::integral_constant<int, 1>{});
+    else if (ksplit == 3) reduce(std::integral_constant<int, 2>{});
+    else reduce(std::integral_constant<int, 3>{});
+    if (tid == 0) __hip_atomic_store(&tickets[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   // epilogue: accumulators -> output tile in LDS -> 16-byte stores
   uint16_t* osm = reinterpret_cast<uint16_t*>(psm);
@@ -988,17 +1082,81 @@ static void tile_launch(const DenseArgs& a, hipStream_t stream) {
 #define QG_DENSE_W256 8     // waves of the 256 x 256 tile (128 x 64 each)
 #endif
 
-template <int LAYOUT, int DTYPE, int BM, int BN, int STAGES, int NWV = 4, int WGM = 2>
-static void pipe_launch(const DenseArgs& a, hipStream_t stream) {
+// Tile columns per band of the pipelined kernels' tile order: an XCD's 32 CUs
+// run about 32 consecutive items at a time, and a block of r rows x w columns
+// of tiles reads r BM + w BN operand rows (of k) into that XCD's L2, least
+// near w = sqrt(32 BM / BN) tiles (power of two, at least 32 / tiles_m).
+#ifndef QG_DENSE_BAND
+#define QG_DENSE_BAND 1      // 0: row-major tile order
+#endif
+static int band_width(int tiles_m, int tiles_n, int per_xcd, int ksplit, int BM, int BN) {
+  if (!QG_DENSE_BAND) return tiles_n;
+  const int conc = (per_xcd < 32 ? per_xcd : 32) / ksplit;
+  const int conc_tiles = conc > 1 ? conc : 1;
+  int w = 1;
+  while ((double)(2 * w) * (2 * w) <= 2.0 * conc_tiles * BM / BN) w *= 2;   // nearest power of two in log
+  const int wmin = (conc_tiles + tiles_m - 1) / tiles_m;
+  if (w < wmin) w = wmin;
+  return w < tiles_n ? w : tiles_n;
+}
+
+template <int LAYOUT, int DTYPE, int BM, int BN, int STAGES, int NWV = 4, int WGM = 2, bool KSPLIT = false>
+static void pipe_launch(const DenseArgs& a, hipStream_t stream, int ksplit = 1) {
+  if (!KSPLIT) ksplit = 1;
   const int tiles_m = (int)((a.M + BM - 1) / BM), tiles_n = (int)((a.N + BN - 1) / BN);
-  const int tiles = tiles_m * tiles_n, per_xcd = (tiles + 7) / 8;
+  const int tiles = tiles_m * tiles_n, per_xcd = (tiles * ksplit + 7) / 8;
+  const int ktiles = (int)(a.K / DBK), kps = (ktiles + ksplit - 1) / ksplit;
+  uint32_t* tickets = ksplit > 1 ? (uint32_t*)a.ws : nullptr;
+  float* partials = ksplit > 1 ? (float*)((char*)a.ws + kSplitCounterBytes) : nullptr;
   const int vec = aligned16(a.C) && a.ldc % 8 == 0 && a.sc % 8 == 0;
   const size_t main_bytes = (size_t)STAGES * (BM + BN) * 8 * 16;
   const size_t out_bytes = (size_t)BM * (BN + 8) * 2;
   const size_t lds = main_bytes > out_bytes ? main_bytes : out_bytes;
-  dense_pipe_kernel<LAYOUT, DTYPE, BM, BN, STAGES, NWV, WGM><<<dim3((unsigned)(per_xcd * 8), (unsigned)a.batch),
-                                                               dim3(64 * NWV), lds, stream>>>(
-      a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, vec, strides(a));
+  dense_pipe_kernel<LAYOUT, DTYPE, BM, BN, STAGES, NWV, WGM, KSPLIT>
+      <<<dim3((unsigned)(per_xcd * 8), (unsigned)a.batch), dim3(64 * NWV), lds, stream>>>(
+      a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, vec, strides(a),
+      ksplit, kps, partials, tickets, a.split_acq_rel, band_width(tiles_m, tiles_n, per_xcd, ksplit, BM, BN));
+}
+
+// k split of the pipelined 256 x 128 tile: when its tiles fill at most half
+// of the 256 CUs and k is long, s = min(4, 256 / tiles) slices of at least 16
+// k tiles (1024 k) each fill them; the slices' fp32 partials (s x 128 KiB per
+// tile) ride behind the split counters.  The exchange costs about 8-9 µs at
+// 256 busy CUs (the partials' HBM traffic), so NT, whose 128 x 128 and 64 x
+// 128 tiles fill the chip well without a split, splits only at up to
+// QG_DENSE_SPLIT_TILES_NT tiles (same-process A/B, bf16, split / no split:
+// NT 512 x 2048 x 5632 0.93, 1024 x 1024 x 8192 0.80, 256 x 2048 x 8192 0.80,
+// but 1024 x 2048 x 5632 1.04, 2048 x 2048 x 5632 1.12; NN and TN 0.52-0.93
+// at every shape that splits).
+#ifndef QG_DENSE_SPLIT_TILES
+#define QG_DENSE_SPLIT_TILES 128
+#endif
+#ifndef QG_DENSE_SPLIT_TILES_NT
+#define QG_DENSE_SPLIT_TILES_NT 32
+#endif
+#ifndef QG_DENSE_SPLIT_MIN_KT
+#define QG_DENSE_SPLIT_MIN_KT 16
+#endif
+static int64_t dense_split_bytes(int64_t tiles, int ksplit) {
+  return kSplitCounterBytes + tiles * ksplit * 256 * 128 * 4;
+}
+// slices for this product, given `ws_bytes` of workspace (1: no split)
+static int pick_dense_split(const DenseArgs& a, int64_t ws_bytes) {
+  if (a.batch != 1 || a.dtype == 2 || a.K % DBK != 0 || a.M < 128 || a.N < 128) return 1;
+  const int64_t tiles = ((a.M + 255) / 256) * ((a.N + 127) / 128);
+  if (tiles > (a.layout == 0 ? QG_DENSE_SPLIT_TILES_NT : QG_DENSE_SPLIT_TILES) || tiles > kSplitCounterBytes / 4)
+    return 1;
+  int s = (int)(256 / tiles);
+  if (s > SPLIT_MAX) s = SPLIT_MAX;
+  while (s > 1 && (a.K / DBK) / s < QG_DENSE_SPLIT_MIN_KT) --s;
+  if (s < 2 || dense_split_bytes(tiles, s) > ws_bytes) return 1;
+  return s;
+}
+
+int64_t dense_workspace_bytes(const DenseArgs& a) {
+  if (!mfma_fits(a)) return 0;
+  const int s = pick_dense_split(a, INT64_MAX);
+  return s > 1 ? dense_split_bytes(((a.M + 255) / 256) * ((a.N + 127) / 128), s) : 0;
 }
 
 #ifndef QG_SPLITK16_MIN_K
@@ -1091,6 +1249,12 @@ static void dense_dispatch(const DenseArgs& a, hipStream_t stream) {
     dense_smallk_kernel<LAYOUT, DTYPE><<<dim3((unsigned)(per_xcd * 8), (unsigned)a.batch), dim3(256), 0, stream>>>(
         a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, vec, strides(a));
   } else if (mfma_fits(a) && a.K % DBK == 0 && a.M >= 128 && a.N >= 128) {
+    const int split = a.ws ? pick_dense_split(a, a.ws_bytes) : 1;
+    if (split > 1) {
+      pipe_launch<LAYOUT, DTYPE, 256, 128, QG_DENSE_PIPE_STAGES, QG_DENSE_W128,
+                  QG_DENSE_G128 ? QG_DENSE_G128 : (LAYOUT == 0 ? 4 : 2), true>(a, stream, split);
+      return;
+    }
     auto launch_tile = [&](int t, const DenseArgs& b) {
       switch (t) {
         case 2: pipe_launch<LAYOUT, DTYPE, 256, 256, 2, QG_DENSE_W256>(b, stream); break;

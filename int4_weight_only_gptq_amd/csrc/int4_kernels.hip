@@ -360,16 +360,6 @@ hipError_t launch_lora_u(const uint16_t* x, int64_t ldx, const uint16_t* a, int6
   return hipGetLastError();
 }
 
-// One ticket of a k split's counter (agent scope); returns the count before.
-// acq_rel != 0: an acquire-release increment (the memory model orders the
-// slice's partial stores before it and the last slice's reads after it);
-// else relaxed, the partials' order then resting on the store-completion wait
-// before the increment.
-__device__ __forceinline__ uint32_t ticket_add(uint32_t* t, int acq_rel) {
-  return acq_rel ? __hip_atomic_fetch_add(t, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT)
-                 : __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 template <int M, bool DOT, int CPL>
 __global__ __launch_bounds__(M > 16 ? 512 : 1024) void skinny_int4_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint32_t* __restrict__ qweight,

@@ -88,7 +88,12 @@ struct DenseArgs {
   int64_t ldc;
   int64_t batch;           // >= 1 products, operand b at A + b sa, B + b sb, C + b sc
   int64_t sa, sb, sc;      // batch strides in elements (0 when batch == 1)
+  void* ws = nullptr;      // optional workspace: k split counters, then fp32 partials
+  int64_t ws_bytes = 0;
+  int split_acq_rel = 0;   // 1: the k split's ticket is an acquire-release RMW
 };
+// Workspace bytes that let a dense product split k (0 when it would not).
+int64_t dense_workspace_bytes(const DenseArgs& a);
 
 // batch strides as one kernel argument
 struct BatchStrides {

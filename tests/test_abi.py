@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
         "qgemm_int4_workspace_size", "qgemm_int4_describe", "qgemm_int4_dequant", "gemm_dense",
         "gemm_dense_batched", "qgemm_int4_lora", "qgemm_int4_lora_workspace_size", "qg_probe_mfma_bf16",
         "qg_probe_copy", "qg_probe_read", "qgemm_int4_noalloc", "qgemm_int4_epilogue", "qg_set_split_order",
-        "qg_split_order"])
+        "qg_split_order", "gemm_dense_ws", "gemm_dense_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -188,6 +188,37 @@ def test_split_order_setting(lib):
     finally:
         lib.qg_set_split_order(0)
     assert lib.qg_split_order() == 0
+
+
+def test_dense_workspace_size(lib):
+    # few 256 x 128 tiles over a long k (NN / TN: up to 128, NT: up to 32): split into
+    # min(4, 256 / tiles) slices of >= 1024 k, the counters (64 KiB) then one fp32 256 x 128
+    # partial tile per tile and slice
+    tile = 256 * 128 * 4
+    assert qg.dense_workspace_size("NN", "bf16", 1024, 2048, 5632) == 65536 + 64 * 4 * tile
+    assert qg.dense_workspace_size("TN", "fp16", 2048, 2048, 5632) == 65536 + 128 * 2 * tile
+    assert qg.dense_workspace_size("NT", "bf16", 512, 2048, 5632) == 65536 + 32 * 4 * tile
+    assert qg.dense_workspace_size("TN", "bf16", 200, 264, 4096) == 65536 + 3 * 4 * tile
+    assert qg.dense_workspace_size("NT", "bf16", 520, 1000, 3072) == 65536 + 24 * 3 * tile   # 48 k tiles: 3 slices
+    # enough tiles, a short k, fp32, an unaligned contiguous extent, or an empty product: none
+    for (lay, dt, M, N, K) in [("NT", "bf16", 4096, 2048, 5632), ("NN", "bf16", 1024, 5632, 2048),
+                               ("NT", "bf16", 1024, 2048, 5632), ("NN", "bf16", 2560, 2048, 5632),
+                               ("NT", "bf16", 1024, 2048, 1024), ("NT", "fp32", 1024, 2048, 5632),
+                               ("NT", "bf16", 1024, 2048, 5630), ("NT", "bf16", 0, 2048, 5632),
+                               ("NT", "bf16", 100, 2048, 5632)]:
+        assert qg.dense_workspace_size(lay, dt, M, N, K) == 0, (lay, dt, M, N, K)
+    assert lib.gemm_dense_workspace_size(3, 0, 8, 8, 8) == -LAYOUT
+    assert lib.gemm_dense_workspace_size(0, 7, 8, 8, 8) == -DTYPE
+    assert lib.gemm_dense_workspace_size(0, 0, -1, 8, 8) == -SHAPE
+
+
+def test_dense_workspace_is_validated(lib):
+    buf = 0x100000
+    f = lib.gemm_dense_ws
+    assert f(0, 0, 8, 8, 8, buf, 8, buf, 8, buf, 8, buf, -1, None) == SHAPE       # negative size
+    assert f(0, 0, 8, 8, 8, buf, 8, buf, 8, buf, 8, buf + 8, 4096, None) == ALIGN   # misaligned
+    assert f(3, 0, 8, 8, 8, buf, 8, buf, 8, buf, 8, None, 0, None) == LAYOUT
+    assert f(0, 0, 8, 8, 8, None, 8, buf, 8, buf, 8, None, 0, None) == NULL
 
 
 def test_bandwidth_probes_reject_invalid_arguments(lib):

@@ -70,10 +70,15 @@ PIPE_SHAPES = [(128, 128, 64), (200, 264, 128), (1000, 136, 192), (2000, 2600, 6
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
 def test_pipeline_shapes_match_oracle(gpu_lib, layout, dtype):
+    import torch
+
     for i, (M, N, K) in enumerate(PIPE_SHAPES):
         say("pipe", layout, dtype, M, N, K)
         d = dense_inputs(layout, dtype, M, N, K, seed=700 + i)
-        c = host_u16(run(gpu_lib, layout, dev(d["a"], tdtype(dtype)), dev(d["b"], tdtype(dtype))))
+        # without a workspace: no k split, the tiles as listed above
+        c = host_u16(gpu_lib.gemm_dense(layout, dev(d["a"], tdtype(dtype)), dev(d["b"], tdtype(dtype)),
+                                        workspace=False))
+        torch.cuda.synchronize()
         if M * N <= 300000:
             ref = oracle.dense(layout, dtype, d["a"], d["b"], M, N, K)
             assert_accepted(c, ref, dtype, (layout, dtype, M, N, K))
@@ -81,6 +86,44 @@ def test_pipeline_shapes_match_oracle(gpu_lib, layout, dtype):
             rows, cols = sample_indices(M, 96, i), sample_indices(N, 96, i + 1)
             ref = oracle.dense_at(layout, dtype, d["a"], d["b"], rows, cols)
             assert_accepted(c[np.ix_(rows, cols)], ref, dtype, (layout, dtype, M, N, K))
+
+
+# the k split of gemm_dense_ws: few 256 x 128 tiles over a long k (2 tiles x 4 slices; 3 ragged
+# tiles x 4 slices; 24 ragged tiles x 3 slices of 16 k tiles), with a caller-owned workspace
+# whose counters are zero again after every call; the same result twice and under both
+# exchange orders; and without a workspace (no split) the oracle accepts it too
+SPLIT_SHAPES = [(256, 256, 8192), (200, 264, 4096), (520, 1000, 3072)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_k_split_matches_oracle(gpu_lib, layout, dtype):
+    import torch
+
+    for i, (M, N, K) in enumerate(SPLIT_SHAPES):
+        need = gpu_lib.dense_workspace_size(layout, dtype, M, N, K)
+        say("dense-split", layout, dtype, M, N, K, need)
+        assert need > 65536
+        d = dense_inputs(layout, dtype, M, N, K, seed=760 + i)
+        a, b = dev(d["a"], tdtype(dtype)), dev(d["b"], tdtype(dtype))
+        ref = oracle.dense(layout, dtype, d["a"], d["b"], M, N, K)
+        ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+        c1 = host_u16(gpu_lib.gemm_dense(layout, a, b, workspace=ws))
+        assert_accepted(c1, ref, dtype, ("split", layout, dtype, M, N, K))
+        assert int(torch.count_nonzero(ws[:65536])) == 0            # counters back at zero
+        c2 = host_u16(gpu_lib.gemm_dense(layout, a, b, workspace=ws))
+        assert np.array_equal(c1, c2)
+        try:
+            gpu_lib.set_split_order("acq_rel")
+            c3 = host_u16(gpu_lib.gemm_dense(layout, a, b, workspace=ws))
+        finally:
+            gpu_lib.set_split_order("hw")
+        assert np.array_equal(c1, c3)
+        c0 = host_u16(gpu_lib.gemm_dense(layout, a, b, workspace=False))
+        assert_accepted(c0, ref, dtype, ("no-split", layout, dtype, M, N, K))
+        # a workspace below the size asked for: no split either
+        c4 = host_u16(gpu_lib.gemm_dense(layout, a, b, workspace=ws[:need - 256]))
+        assert np.array_equal(c0, c4)
 
 
 # shapes for the 16 x 16 split-k kernel (one of M, N <= 16, K >= 256): k tails
