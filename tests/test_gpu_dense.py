@@ -126,6 +126,39 @@ def test_k_split_matches_oracle(gpu_lib, layout, dtype):
         assert np.array_equal(c0, c4)
 
 
+# the split under HIP graph capture: one graph with a caller-owned workspace (zeroed before
+# capture) and one with the binding's per-stream workspace (allocated and zero-filled inside
+# the capture), each replayed three times with eager products on the same workspace in
+# between; every replay gives the eager split result bit for bit and leaves the counters at zero
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_k_split_in_graph_replays(gpu_lib, layout):
+    import torch
+
+    M, N, K = 200, 264, 4096
+    say("dense-split-graph", layout, M, N, K)
+    d = dense_inputs(layout, "bf16", M, N, K, seed=790)
+    a, b = dev(d["a"], torch.bfloat16), dev(d["b"], torch.bfloat16)
+    need = gpu_lib.dense_workspace_size(layout, "bf16", M, N, K)
+    assert need > 65536
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    want = host_u16(gpu_lib.gemm_dense(layout, a, b, workspace=ws))
+    for own in (True, False):
+        out = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            gpu_lib.gemm_dense(layout, a, b, out=out, workspace=ws if own else None)
+        for r in range(3):
+            out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(host_u16(out), want), ("replay", own, r)
+            eager = host_u16(gpu_lib.gemm_dense(layout, a, b, workspace=ws))
+            assert np.array_equal(eager, want)
+        assert int(torch.count_nonzero(ws[:65536])) == 0
+        del g
+
+
 # shapes for the 16 x 16 split-k kernel (one of M, N <= 16, K >= 256): k tails
 # inside a 32-row step, ragged 16-tiles, K not a multiple of 8 (TN only: K is
 # then a row count), and both orientations of the skinny side
