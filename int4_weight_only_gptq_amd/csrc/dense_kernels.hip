@@ -1118,45 +1118,59 @@ static void pipe_launch(const DenseArgs& a, hipStream_t stream, int ksplit = 1) 
       ksplit, kps, partials, tickets, a.split_acq_rel, band_width(tiles_m, tiles_n, per_xcd, ksplit, BM, BN));
 }
 
-// k split of the pipelined 256 x 128 tile: when its tiles fill at most half
-// of the 256 CUs and k is long, s = min(4, 256 / tiles) slices of at least 16
-// k tiles (1024 k) each fill them; the slices' fp32 partials (s x 128 KiB per
-// tile) ride behind the split counters.  The exchange costs about 8-9 µs at
-// 256 busy CUs (the partials' HBM traffic), so NT, whose 128 x 128 and 64 x
-// 128 tiles fill the chip well without a split, splits only at up to
-// QG_DENSE_SPLIT_TILES_NT tiles (same-process A/B, bf16, split / no split:
-// NT 512 x 2048 x 5632 0.93, 1024 x 1024 x 8192 0.80, 256 x 2048 x 8192 0.80,
-// but 1024 x 2048 x 5632 1.04, 2048 x 2048 x 5632 1.12; NN and TN 0.52-0.93
-// at every shape that splits).
+// k split of the pipelined 128 x 128 or 256 x 128 tile, for products whose
+// tiles fill at most half of the 256 CUs over a long k: s = min(4, 256 /
+// tiles) slices of at least 16 k tiles (1024 k) each; the slices' fp32
+// partials (s x BM x 128 x 4 bytes per tile) ride behind the split counters.
+// Of the two tiles the one whose tiles x slices fills more CUs is taken; on a
+// tie, 256 x 128 for NN (its more efficient tile) and 128 x 128 for NT and TN.
+// NT never splits the 256 x 128 tile: its unsplit 128 x 128 and 64 x 128
+// tiles fill the chip well, and the larger exchange (128 KiB per slice, about
+// 8-9 µs at 256 busy CUs) lost (2048 x 2048 x 5632 1.12x, 1024 x 2048 x 5632
+// 1.03x).  Same-process A/B, bf16, split time / best unsplit time: NT
+// 256 x 2048 x 8192 0.53, 1024 x 1024 x 8192 0.58, 512 x 2048 x 5632 0.69,
+// 1024 x 2048 x 5632 0.82, 512 x 4096 x 4096 0.87; NN 512 x 2048 x 5632 0.47
+// (128 x 128 tiles), 1024 x 2048 x 5632 0.66, 2048 x 2048 x 5632 0.84 (256 x
+// 128); TN 256 x 2048 x 8192 0.40, 1024 x 2048 x 5632 0.71, 2048 x 2048 x
+// 5632 0.94.
 #ifndef QG_DENSE_SPLIT_TILES
 #define QG_DENSE_SPLIT_TILES 128
-#endif
-#ifndef QG_DENSE_SPLIT_TILES_NT
-#define QG_DENSE_SPLIT_TILES_NT 32
 #endif
 #ifndef QG_DENSE_SPLIT_MIN_KT
 #define QG_DENSE_SPLIT_MIN_KT 16
 #endif
-static int64_t dense_split_bytes(int64_t tiles, int ksplit) {
-  return kSplitCounterBytes + tiles * ksplit * 256 * 128 * 4;
-}
-// slices for this product, given `ws_bytes` of workspace (1: no split)
-static int pick_dense_split(const DenseArgs& a, int64_t ws_bytes) {
-  if (a.batch != 1 || a.dtype == 2 || a.K % DBK != 0 || a.M < 128 || a.N < 128) return 1;
-  const int64_t tiles = ((a.M + 255) / 256) * ((a.N + 127) / 128);
-  if (tiles > (a.layout == 0 ? QG_DENSE_SPLIT_TILES_NT : QG_DENSE_SPLIT_TILES) || tiles > kSplitCounterBytes / 4)
-    return 1;
-  int s = (int)(256 / tiles);
-  if (s > SPLIT_MAX) s = SPLIT_MAX;
-  while (s > 1 && (a.K / DBK) / s < QG_DENSE_SPLIT_MIN_KT) --s;
-  if (s < 2 || dense_split_bytes(tiles, s) > ws_bytes) return 1;
-  return s;
+struct DenseSplit {
+  int bm = 0;        // rows of the split tile (columns: 128); 0: no split
+  int s = 1;         // k slices
+  int64_t tiles = 0;
+  int64_t bytes() const { return kSplitCounterBytes + tiles * s * bm * 128 * 4; }
+};
+static DenseSplit plan_dense_split(const DenseArgs& a) {
+  DenseSplit best;
+  if (a.batch != 1 || a.dtype == 2 || a.K % DBK != 0 || a.M < 128 || a.N < 128) return best;
+  for (int bm : {256, 128}) {
+    if (bm == 256 && a.layout == 0) continue;
+    const int64_t tiles = ((a.M + bm - 1) / bm) * ((a.N + 127) / 128);
+    if (tiles > QG_DENSE_SPLIT_TILES || tiles > kSplitCounterBytes / 4) continue;
+    int s = (int)(256 / tiles);
+    if (s > SPLIT_MAX) s = SPLIT_MAX;
+    while (s > 1 && (a.K / DBK) / s < QG_DENSE_SPLIT_MIN_KT) --s;
+    if (s < 2) continue;
+    const int64_t items = tiles * s, best_items = best.tiles * best.s;
+    const bool tie_to_this = bm == 128 && a.layout != 1;
+    if (items > best_items || (items == best_items && tie_to_this)) {
+      best.bm = bm;
+      best.s = s;
+      best.tiles = tiles;
+    }
+  }
+  return best;
 }
 
 int64_t dense_workspace_bytes(const DenseArgs& a) {
   if (!mfma_fits(a)) return 0;
-  const int s = pick_dense_split(a, INT64_MAX);
-  return s > 1 ? dense_split_bytes(((a.M + 255) / 256) * ((a.N + 127) / 128), s) : 0;
+  const DenseSplit p = plan_dense_split(a);
+  return p.bm ? p.bytes() : 0;
 }
 
 #ifndef QG_SPLITK16_MIN_K
@@ -1249,10 +1263,15 @@ static void dense_dispatch(const DenseArgs& a, hipStream_t stream) {
     dense_smallk_kernel<LAYOUT, DTYPE><<<dim3((unsigned)(per_xcd * 8), (unsigned)a.batch), dim3(256), 0, stream>>>(
         a.A, a.lda, a.B, a.ldb, a.C, a.ldc, (int)a.M, (int)a.N, (int)a.K, tiles_n, tiles, per_xcd, vec, strides(a));
   } else if (mfma_fits(a) && a.K % DBK == 0 && a.M >= 128 && a.N >= 128) {
-    const int split = a.ws ? pick_dense_split(a, a.ws_bytes) : 1;
-    if (split > 1) {
-      pipe_launch<LAYOUT, DTYPE, 256, 128, QG_DENSE_PIPE_STAGES, QG_DENSE_W128,
-                  QG_DENSE_G128 ? QG_DENSE_G128 : (LAYOUT == 0 ? 4 : 2), true>(a, stream, split);
+    const DenseSplit sp = a.ws ? plan_dense_split(a) : DenseSplit{};
+    if (sp.bm && sp.bytes() <= a.ws_bytes) {
+      const int split = sp.s;
+      if (sp.bm == 128)
+        pipe_launch<LAYOUT, DTYPE, 128, 128, QG_DENSE_T0_STAGES, QG_DENSE_T0_WAVES, QG_DENSE_T0_WGM, true>(a, stream,
+                                                                                                       split);
+      else
+        pipe_launch<LAYOUT, DTYPE, 256, 128, QG_DENSE_PIPE_STAGES, QG_DENSE_W128,
+                    QG_DENSE_G128 ? QG_DENSE_G128 : (LAYOUT == 0 ? 4 : 2), true>(a, stream, split);
       return;
     }
     auto launch_tile = [&](int t, const DenseArgs& b) {

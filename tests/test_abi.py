@@ -191,18 +191,23 @@ def test_split_order_setting(lib):
 
 
 def test_dense_workspace_size(lib):
-    # few 256 x 128 tiles over a long k (NN / TN: up to 128, NT: up to 32): split into
-    # min(4, 256 / tiles) slices of >= 1024 k, the counters (64 KiB) then one fp32 256 x 128
-    # partial tile per tile and slice
-    tile = 256 * 128 * 4
-    assert qg.dense_workspace_size("NN", "bf16", 1024, 2048, 5632) == 65536 + 64 * 4 * tile
-    assert qg.dense_workspace_size("TN", "fp16", 2048, 2048, 5632) == 65536 + 128 * 2 * tile
-    assert qg.dense_workspace_size("NT", "bf16", 512, 2048, 5632) == 65536 + 32 * 4 * tile
-    assert qg.dense_workspace_size("TN", "bf16", 200, 264, 4096) == 65536 + 3 * 4 * tile
-    assert qg.dense_workspace_size("NT", "bf16", 520, 1000, 3072) == 65536 + 24 * 3 * tile   # 48 k tiles: 3 slices
+    # few tiles over a long k: min(4, 256 / tiles) slices of >= 1024 k of the 128 x 128 or
+    # 256 x 128 tile (at most 128 tiles; the tile whose tiles x slices is larger, on a tie
+    # 256 x 128 for NN and 128 x 128 for NT and TN; NT never 256 x 128): the counters (64 KiB)
+    # then one fp32 BM x 128 partial tile per tile and slice
+    t256, t128 = 256 * 128 * 4, 128 * 128 * 4
+    assert qg.dense_workspace_size("NN", "bf16", 1024, 2048, 5632) == 65536 + 64 * 4 * t256   # tie: 256
+    assert qg.dense_workspace_size("TN", "bf16", 1024, 2048, 5632) == 65536 + 128 * 2 * t128  # tie: 128
+    assert qg.dense_workspace_size("TN", "fp16", 2048, 2048, 5632) == 65536 + 128 * 2 * t256  # 256 tiles of 128
+    assert qg.dense_workspace_size("NN", "bf16", 512, 2048, 5632) == 65536 + 64 * 4 * t128    # 256 items > 128
+    assert qg.dense_workspace_size("NT", "bf16", 1024, 2048, 5632) == 65536 + 128 * 2 * t128
+    assert qg.dense_workspace_size("TN", "bf16", 200, 264, 4096) == 65536 + 6 * 4 * t128
+    assert qg.dense_workspace_size("NT", "bf16", 520, 1000, 3072) == 65536 + 40 * 3 * t128   # 48 k tiles: 3 slices
+    assert qg.dense_workspace_size("NN", "bf16", 520, 4000, 2048) == 65536 + 96 * 2 * t256
     # enough tiles, a short k, fp32, an unaligned contiguous extent, or an empty product: none
     for (lay, dt, M, N, K) in [("NT", "bf16", 4096, 2048, 5632), ("NN", "bf16", 1024, 5632, 2048),
-                               ("NT", "bf16", 1024, 2048, 5632), ("NN", "bf16", 2560, 2048, 5632),
+                               ("NT", "bf16", 2048, 2048, 5632), ("NN", "bf16", 2560, 2048, 5632),
+                               ("NT", "bf16", 520, 4000, 2048),
                                ("NT", "bf16", 1024, 2048, 1024), ("NT", "fp32", 1024, 2048, 5632),
                                ("NT", "bf16", 1024, 2048, 5630), ("NT", "bf16", 0, 2048, 5632),
                                ("NT", "bf16", 100, 2048, 5632)]:

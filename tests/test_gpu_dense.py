@@ -88,11 +88,14 @@ def test_pipeline_shapes_match_oracle(gpu_lib, layout, dtype):
             assert_accepted(c[np.ix_(rows, cols)], ref, dtype, (layout, dtype, M, N, K))
 
 
-# the k split of gemm_dense_ws: few 256 x 128 tiles over a long k (2 tiles x 4 slices; 3 ragged
-# tiles x 4 slices; 24 ragged tiles x 3 slices of 16 k tiles), with a caller-owned workspace
-# whose counters are zero again after every call; the same result twice and under both
-# exchange orders; and without a workspace (no split) the oracle accepts it too
-SPLIT_SHAPES = [(256, 256, 8192), (200, 264, 4096), (520, 1000, 3072)]
+# the k split of gemm_dense_ws: few tiles over a long k, split into slices of >= 16 k tiles
+# with a caller-owned workspace whose counters are zero again after every call; the same
+# result twice and under both exchange orders; and without a workspace (no split) the
+# oracle accepts it too.  The first three shapes split the 128 x 128 tile (4 tiles x 4
+# slices; 6 ragged tiles x 4; 40 ragged tiles x 3); the last has 160 such tiles, too many,
+# so NN and TN split its 256 x 128 tile (96 ragged tiles x 2, compared on sampled outputs)
+# and NT does not split it at all
+SPLIT_SHAPES = [(256, 256, 8192), (200, 264, 4096), (520, 1000, 3072), (520, 4000, 2048)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
@@ -103,13 +106,22 @@ def test_k_split_matches_oracle(gpu_lib, layout, dtype):
     for i, (M, N, K) in enumerate(SPLIT_SHAPES):
         need = gpu_lib.dense_workspace_size(layout, dtype, M, N, K)
         say("dense-split", layout, dtype, M, N, K, need)
+        if i == 3 and layout == "NT":
+            assert need == 0
+            continue
         assert need > 65536
         d = dense_inputs(layout, dtype, M, N, K, seed=760 + i)
         a, b = dev(d["a"], tdtype(dtype)), dev(d["b"], tdtype(dtype))
-        ref = oracle.dense(layout, dtype, d["a"], d["b"], M, N, K)
+        if M * N <= 600000:
+            pick = lambda c: c
+            ref = oracle.dense(layout, dtype, d["a"], d["b"], M, N, K)
+        else:
+            rows, cols = sample_indices(M, 96, i), sample_indices(N, 96, i + 1)
+            pick = lambda c: c[np.ix_(rows, cols)]
+            ref = oracle.dense_at(layout, dtype, d["a"], d["b"], rows, cols)
         ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
         c1 = host_u16(gpu_lib.gemm_dense(layout, a, b, workspace=ws))
-        assert_accepted(c1, ref, dtype, ("split", layout, dtype, M, N, K))
+        assert_accepted(pick(c1), ref, dtype, ("split", layout, dtype, M, N, K))
         assert int(torch.count_nonzero(ws[:65536])) == 0            # counters back at zero
         c2 = host_u16(gpu_lib.gemm_dense(layout, a, b, workspace=ws))
         assert np.array_equal(c1, c2)
@@ -120,7 +132,7 @@ def test_k_split_matches_oracle(gpu_lib, layout, dtype):
             gpu_lib.set_split_order("hw")
         assert np.array_equal(c1, c3)
         c0 = host_u16(gpu_lib.gemm_dense(layout, a, b, workspace=False))
-        assert_accepted(c0, ref, dtype, ("no-split", layout, dtype, M, N, K))
+        assert_accepted(pick(c0), ref, dtype, ("no-split", layout, dtype, M, N, K))
         # a workspace below the size asked for: no split either
         c4 = host_u16(gpu_lib.gemm_dense(layout, a, b, workspace=ws[:need - 256]))
         assert np.array_equal(c0, c4)
