@@ -106,6 +106,9 @@ def copies_for(bytes_per_copy, regime):
     return max(2, -(-2 * LLC_BYTES // bytes_per_copy))
 
 
+WARM_S = 0.03   # untimed replays (or calls) before each timing, so that the clocks have left idle
+
+
 def time_us(torch, fn, iters, graph=True, reps=7, min_calls=1):
     """Microseconds per call of fn() over n = max(iters, min_calls) back-to-back
     calls: the median of `reps` timed repetitions.
@@ -115,9 +118,14 @@ def time_us(torch, fn, iters, graph=True, reps=7, min_calls=1):
     (Python, ctypes) is not on the clock; HIP events bracket each replay on the
     same stream.  graph=False times eager launches from Python.  A caller that
     rotates over R buffer copies passes min_calls=R, so every replay touches all
-    of them (the cold regime: R copies span at least twice the LLC).
+    of them (the cold regime: R copies span at least twice the LLC).  Before the
+    timed repetitions the same replays (calls) run untimed for WARM_S seconds:
+    after host-side set-up the GPU clocks start from idle and take milliseconds
+    to rise, which otherwise shows as the first measurement of a pair reading
+    slower.
     """
     import statistics
+    import time
 
     n = max(iters, min_calls)
     s = torch.cuda.current_stream()
@@ -128,8 +136,12 @@ def time_us(torch, fn, iters, graph=True, reps=7, min_calls=1):
         with torch.cuda.graph(g):
             for _ in range(n):
                 fn()
-        g.replay()                       # warm replay
+        g.replay()                       # warm replays
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < WARM_S:
+            g.replay()
+            torch.cuda.synchronize()
         for _ in range(reps):
             e0.record(s)
             g.replay()
@@ -138,6 +150,10 @@ def time_us(torch, fn, iters, graph=True, reps=7, min_calls=1):
             times.append(e0.elapsed_time(e1) * 1e3 / n)
         del g
         return statistics.median(times)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < WARM_S:
+        fn()
+        torch.cuda.synchronize()
     for _ in range(reps):
         e0.record(s)
         for _ in range(n):

@@ -1064,7 +1064,7 @@ static void tile_launch(const DenseArgs& a, hipStream_t stream) {
 #define QG_DENSE_W128 8     // waves of the 256 x 128 tile
 #endif
 #ifndef QG_DENSE_G128
-#define QG_DENSE_G128 0     // of which along M (0: 4 for NT, 2 for NN / TN)
+#define QG_DENSE_G128 0     // of which along M (0: 2 for NN, 4 for NT and TN)
 #endif
 // The 128 x 128 tile: 4 stages, 8 waves of 64 x 32 (NN 2048 x 2048 x 5632
 // 82.7 -> 77.3 µs, NT 2048 x 2048 x 5632 58.5 -> 56.5 µs against 4 waves of
@@ -1271,7 +1271,7 @@ static void dense_dispatch(const DenseArgs& a, hipStream_t stream) {
                                                                                                        split);
       else
         pipe_launch<LAYOUT, DTYPE, 256, 128, QG_DENSE_PIPE_STAGES, QG_DENSE_W128,
-                    QG_DENSE_G128 ? QG_DENSE_G128 : (LAYOUT == 0 ? 4 : 2), true>(a, stream, split);
+                    QG_DENSE_G128 ? QG_DENSE_G128 : (LAYOUT == 1 ? 2 : 4), true>(a, stream, split);
       return;
     }
     auto launch_tile = [&](int t, const DenseArgs& b) {
@@ -1279,7 +1279,7 @@ static void dense_dispatch(const DenseArgs& a, hipStream_t stream) {
         case 2: pipe_launch<LAYOUT, DTYPE, 256, 256, 2, QG_DENSE_W256>(b, stream); break;
         case 1:
           pipe_launch<LAYOUT, DTYPE, 256, 128, QG_DENSE_PIPE_STAGES, QG_DENSE_W128,
-                      QG_DENSE_G128 ? QG_DENSE_G128 : (LAYOUT == 0 ? 4 : 2)>(b, stream);
+                      QG_DENSE_G128 ? QG_DENSE_G128 : (LAYOUT == 1 ? 2 : 4)>(b, stream);
           break;
         case 0: pipe_launch<LAYOUT, DTYPE, 128, 128, QG_DENSE_T0_STAGES, QG_DENSE_T0_WAVES, QG_DENSE_T0_WGM>(b, stream); break;
         default: pipe_launch<LAYOUT, DTYPE, 64, 128, 4>(b, stream); break;
