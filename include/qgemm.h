@@ -312,9 +312,10 @@ int32_t gemm_dense(int32_t layout, int32_t dtype, int64_t M, int64_t N, int64_t 
 
 /*
  * gemm_dense_ws -- gemm_dense with a workspace, which lets products with few
- * output tiles and a long K split K over several workgroups (bf16 / fp16 on
- * the pipelined tiles: when the 256 x 128 tiles would fill less than three
- * quarters of the 256 CUs and each of up to 4 k slices keeps at least 1024 k).
+ * output tiles and a long K split K over several workgroups (bf16 / fp16, batch
+ * 1, on the pipelined 128 x 128 or 256 x 128 tiles: at most 128 tiles, up to 4
+ * k slices of at least 1024 k each, the tile whose tiles x slices covers more
+ * of the 256 CUs; NT splits only the 128 x 128 tile).
  * Each slice stores its fp32 partial tile; the last slice of a tile to arrive
  * adds them in slice order (deterministic for a given size) and rounds once,
  * so the accuracy contract is that of gemm_dense (the summation order
@@ -345,9 +346,9 @@ int32_t gemm_dense_ws(int32_t layout, int32_t dtype, int64_t M, int64_t N, int64
 int64_t gemm_dense_workspace_size(int32_t layout, int32_t dtype, int64_t M, int64_t N, int64_t K);
 
 /*
- * gemm_dense_batched -- `batch` independent gemm_dense products in one launch,
- * the batched products inside attention that the BC-250 tuned-GEMM post tunes
- * and validates ("Tuning the kernels", "Checking the results are right"):
+ * gemm_dense_batched -- `batch` independent gemm_dense products in one launch:
+ * the attention layers' batched products, which the BC-250 tuned-GEMM post
+ * tunes and validates ("Tuning the kernels", "Checking the results are right"):
  *
  *   C_b = op(A_b) . op(B_b),  A_b = A + b * stride_a, B_b = B + b * stride_b,
  *   C_b = C + b * stride_c  (strides in elements), b = 0 .. batch-1,

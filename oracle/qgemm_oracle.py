@@ -28,7 +28,7 @@ What it computes
     NT: C[M][N] = A[M][K] . B[N][K]^T   (forward)
     NN: C[M][N] = A[M][K] . B[K][N]     (input gradient)
     TN: C[M][N] = A[K][M]^T . B[K][N]   (weight gradient)
-  and batches of them (the batched products inside attention), one product per
+  and batches of them (the batched products of attention layers), one product per
   leading index; and the same products in FP32 (the post tunes and validates
   FP32 in all three layouts), accepted under a dot-product error bound
   (accept_fp32).
