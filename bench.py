@@ -13,9 +13,11 @@ weights stream from HBM; --regime warm reuses one copy (cache-resident).
 
 Prints ONE JSON line: effective GB/s over the whole step (algorithmic bytes /
 time), per-call microseconds and GB/s, the roofline of the dominant kernel
-measured live with HIP events on the launch stream, and the CPU oracle timed
-on a bounded sample of the same workload.  ``--suite FILE`` also times every
-int4 and dense workload shape and writes them to FILE.
+measured live with HIP events on the launch stream, the rest of the metric
+per call (``configs``: the int4 prefill and large-weight shapes, the bf16 dense
+training trio), and the CPU oracle timed on a bounded sample of the same
+workload.  ``--suite FILE`` also times every int4 and dense workload shape and
+writes them to FILE.
 """
 from __future__ import annotations
 
@@ -414,8 +416,11 @@ def time_configs(qg, torch, args, bw):
     (4096 x 28672, 4096 x 14336, 8192 x 8192) at m = 1, 8, 16; each row with its
     kernel, µs, GB/s of algorithmic bytes, TFLOP/s and the fraction of its
     roofline (MFMA-bound rows: of the 2.5 PFLOP/s bf16 peak; the others: of the
-    measured copy), plus the shader clock and temperatures after each shape."""
-    from qgemm_inputs.configs import seed_for
+    measured copy), plus the shader clock and temperatures after each shape;
+    then the bf16 dense training trio (forward NT, input gradient NN, weight
+    gradient TN at 1024 / 2048 / 4096 tokens for both weight orientations),
+    with the library's default workspace (the k split where it applies)."""
+    from qgemm_inputs.configs import dense_cases, seed_for
 
     rows, states = [], []
     for cfg, shapes, tokens in ((2, [(25600, 5120), (5120, 25600)], [16, 512, 2048]),
@@ -452,6 +457,26 @@ def time_configs(qg, torch, args, bw):
             st = gpu_state(qg, torch)
             st.update(config=cfg, k=k, n=n)
             states.append(st)
+    # config 3, bf16: operands N(0, 0.02^2) drawn on the device (timing only; the
+    # parity tests use the host generator)
+    g = torch.Generator(device="cuda")
+    for case in dense_cases(3, with_lora=False):
+        if case["dtype"] != "bf16":
+            continue
+        lay, M, N, K = case["layout"], case["M"], case["N"], case["K"]
+        g.manual_seed(case["seed"])
+        a = (torch.randn((K, M) if lay == "TN" else (M, K), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        b = (torch.randn((N, K) if lay == "NT" else (K, N), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        out = qg.gemm_dense(lay, a, b)
+        us = time_us(torch, lambda: qg.gemm_dense(lay, a, b, out=out), args.steps)
+        fl = 2 * M * N * K
+        rows.append({"config": 3, "role": case["role"], "layout": lay, "M": M, "N": N, "K": K,
+                     "us": round(us, 3), "tflops": round(fl / us / 1e6, 1), "bound": "mfma",
+                     "frac_of_mfma_peak": round(fl / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "k_split": qg.dense_workspace_size(lay, "bf16", M, N, K) > 0})
+        print("config", rows[-1], file=sys.stderr, flush=True)
+        del a, b, out
+    torch.cuda.empty_cache()
     return rows, states
 
 
