@@ -138,6 +138,36 @@ def test_k_split_matches_oracle(gpu_lib, layout, dtype):
         assert np.array_equal(c0, c4)
 
 
+# the split with padded leading dimensions (16-byte multiples, so the pipelined tiles and
+# the split still apply) and the output a view inside a larger buffer: the slices offset
+# their k ranges through lda / ldb, and nothing outside the view is written
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_k_split_with_padded_leading_dims(gpu_lib, layout):
+    import torch
+
+    M, N, K = 200, 264, 4096
+    say("dense-split-padded", layout, M, N, K)
+    d = dense_inputs(layout, "bf16", M, N, K, seed=795)
+    (ra, ca), (rb, cb) = d["a"].shape, d["b"].shape
+    pa = torch.zeros((ra, ca + 24), dtype=torch.bfloat16, device="cuda")
+    pb = torch.zeros((rb, cb + 40), dtype=torch.bfloat16, device="cuda")
+    pa[:, 8:8 + ca] = dev(d["a"], torch.bfloat16)
+    pb[:, 16:16 + cb] = dev(d["b"], torch.bfloat16)
+    big = torch.full((M + 2, N + 24), 3.0, dtype=torch.bfloat16, device="cuda")
+    out = big[1:M + 1, 8:8 + N]
+    need = gpu_lib.dense_workspace_size(layout, "bf16", M, N, K)
+    assert need > 65536
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    gpu_lib.gemm_dense(layout, pa[:, 8:8 + ca], pb[:, 16:16 + cb], out=out, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.dense(layout, "bf16", d["a"], d["b"], M, N, K)
+    assert_accepted(host_u16(out), ref, "bf16", ("split-padded", layout))
+    assert int(torch.count_nonzero(ws[:65536])) == 0
+    g = big.float().cpu().numpy()
+    g[1:M + 1, 8:8 + N] = 3.0
+    assert np.all(g == 3.0)
+
+
 # the split under HIP graph capture: one graph with a caller-owned workspace (zeroed before
 # capture) and one with the binding's per-stream workspace (allocated and zero-filled inside
 # the capture), each replayed three times with eager products on the same workspace in
