@@ -63,7 +63,11 @@ hipError_t launch_dequant(const uint32_t* qweight, const uint16_t* scales, const
 // ---------------------------------------------------------------------------
 template <int CPL>
 __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[CPL]) {
-  if constexpr (CPL == 4) {
+  if constexpr (CPL == 8) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p), u = *reinterpret_cast<const u32x4*>(p + 4);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+    w[4] = u[0]; w[5] = u[1]; w[6] = u[2]; w[7] = u[3];
+  } else if constexpr (CPL == 4) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(p);
     w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
   } else if constexpr (CPL == 2) {
@@ -80,14 +84,20 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[CPL]
 // flight.
 template <int CPL>
 struct Meta {
-  uint32_t s[CPL == 4 ? 2 : 1];
+  uint32_t s[CPL >= 4 ? CPL / 2 : 1];
   uint32_t z;
 };
 
 template <int CPL>
 __device__ __forceinline__ Meta<CPL> load_meta(const uint16_t* __restrict__ sp, const uint32_t* __restrict__ zp) {
   Meta<CPL> r;
-  if constexpr (CPL == 4) {
+  if constexpr (CPL == 8) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(sp);
+    r.s[0] = v[0];
+    r.s[1] = v[1];
+    r.s[2] = v[2];
+    r.s[3] = v[3];
+  } else if constexpr (CPL == 4) {
     const u32x2 v = *reinterpret_cast<const u32x2*>(sp);
     r.s[0] = v[0];
     r.s[1] = v[1];
@@ -361,7 +371,7 @@ hipError_t launch_lora_u(const uint16_t* x, int64_t ldx, const uint16_t* a, int6
 }
 
 template <int M, bool DOT, int CPL>
-__global__ __launch_bounds__(M > 16 ? 512 : 1024) void skinny_int4_kernel(
+__global__ __launch_bounds__(M > 16 || CPL > 4 ? 512 : 1024) void skinny_int4_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
     uint16_t* __restrict__ y, int64_t ldy, int n, int k, int nstrips, int ksplit, int gwg,
@@ -588,7 +598,7 @@ __global__ __launch_bounds__(M > 16 ? 512 : 1024) void skinny_int4_kernel(
       if (cg < n) y[(int64_t)token * ldy + cg] = (uint16_t)yb;
       if (lora.row_ss) {
         const float yf = cg < n ? bf16_bits_to_float(yb) : 0.f;
-        add_row_sumsq<SW>(lora.row_ss, yf * yf, token, cc == 0, true);
+        add_row_sumsq<(SW < 64 ? SW : 64)>(lora.row_ss, yf * yf, token, cc % 64 == 0, true);
       }
     } else {
       // agent-coherent store: visible to any workgroup once it has completed
@@ -627,7 +637,7 @@ __global__ __launch_bounds__(M > 16 ? 512 : 1024) void skinny_int4_kernel(
     if (cg < n) y[(int64_t)token * ldy + cg] = (uint16_t)yb;
     if (lora.row_ss) {
       const float yf = cg < n ? bf16_bits_to_float(yb) : 0.f;
-      add_row_sumsq<SW>(lora.row_ss, yf * yf, token, cc == 0, true);
+      add_row_sumsq<(SW < 64 ? SW : 64)>(lora.row_ss, yf * yf, token, cc % 64 == 0, true);
     }
   }
   if (tid == 0) __hip_atomic_store(&tickets[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1500,6 +1510,20 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
 #ifndef QG_SKINNY_LONG_G
 #define QG_SKINNY_LONG_G 48        // groups from which MFMA strips (m >= 8) use 8-wave workgroups
 #endif
+// 128-column strips (m <= 16, MFMA) where k is split anyway and each slice
+// keeps at least QG_SKINNY_CPL8_MIN_GPS groups: half the activation reads per
+// column (every workgroup reads X over its k range), one 512-thread workgroup
+// per CU.  Same-process A/B, cold weights, against 64-column strips:
+// 25600 x 5120 m = 2 / 8 / 16 24.9 / 22.9 / 26.3 -> 18.2 / 20.1 / 23.1 µs,
+// 32768 x 8192 m = 8 41.9 -> 31.2 µs, 25600 x 7168 m = 16 34.9 -> 29.2 µs,
+// 28672 x 4096 m = 16 (28 groups per slice) 23.1 -> 21.2 µs; but 14336 x
+// 4096 m = 16 (14 groups per slice) 13.4 -> 15.7 µs.
+#ifndef QG_SKINNY_CPL8
+#define QG_SKINNY_CPL8 1
+#endif
+#ifndef QG_SKINNY_CPL8_MIN_GPS
+#define QG_SKINNY_CPL8_MIN_GPS 20
+#endif
 
 int64_t split_workspace_bytes(int64_t nstrips, int64_t ksplit, int64_t m, int cpl) {
   return kTicketBytes + nstrips * ksplit * m * 16 * cpl * 4;
@@ -1552,16 +1576,27 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes,
   // 4m / (16 CPL) times the codes' traffic) and wider strips load more code
   // bytes per instruction.  Measured at k = 25600, n = 5120: m = 1 40 -> 29 µs,
   // m = 2 39 -> 27 µs, m = 16 57 -> 35 µs.
-  if ((dot || m >= QG_SKINNY_WIDE_M) && ks > 1 && p.cpl < 4) {
-    for (int c = cplmax; c > p.cpl; c /= 2) {
+  const int cplwide = QG_SKINNY_CPL8 && !dot && m <= 16 ? 8 : cplmax;
+  if ((dot || m >= QG_SKINNY_WIDE_M) && ks > 1 && p.cpl < cplwide) {
+    for (int c = cplwide; c > p.cpl; c /= 2) {
       const int64_t strips = (n + 16 * c - 1) / (16 * c);
-      const int64_t wc = (strips >= QG_SKINNY_MANY_STRIPS || long_k || m > 16) ? (QG_SKINNY_WAVES < 8 ? QG_SKINNY_WAVES : 8)
-                                                             : QG_SKINNY_WAVES;
+      // (128-column strips: 512-thread workgroups, twice the accumulators)
+      const int64_t wc = (strips >= QG_SKINNY_MANY_STRIPS || long_k || m > 16 || c > 4)
+                             ? (QG_SKINNY_WAVES < 8 ? QG_SKINNY_WAVES : 8)
+                             : QG_SKINNY_WAVES;
       const int64_t wv = G < QG_SKINNY_GPW_MIN ? 1 : (G / QG_SKINNY_GPW_MIN < wc ? G / QG_SKINNY_GPW_MIN : wc);
       const int64_t pw = (G + wv - 1) / wv;
       int64_t kc = (pw + 3) / 4;
       const int64_t fill = (QG_SKINNY_MIN_STRIPS + strips - 1) / strips;
       if (kc < fill) kc = fill;
+      if (c == 8) {
+        // one 512-thread workgroup per CU (the registers allow no second): as
+        // many slices as fit one pass, and only when each slice keeps a long
+        // chain of groups
+        kc = 256 / strips;
+        if (kc < 2 || G / kc < QG_SKINNY_CPL8_MIN_GPS) continue;
+        if (split_workspace_bytes(strips, kc, m, c) > workspace_bytes) continue;   // (no split: not these)
+      }
       if (kc > SK_MAX_SPLIT || kc > G || strips * 4 > kTicketBytes) continue;
       p.cpl = c;
       p.nstrips = (int)strips;
@@ -1613,6 +1648,12 @@ static void skinny_launch(const Int4Args& a, const SkinnyPlan& p, void* ws, hipS
 template <int M, bool DOT>
 static void skinny_launch_c(const Int4Args& a, const SkinnyPlan& p, void* ws, hipStream_t stream) {
   if constexpr (M <= 32) {
+    if constexpr (M <= 16 && !DOT && QG_SKINNY_CPL8) {
+      if (p.cpl == 8) {
+        skinny_launch<M, DOT, 8>(a, p, ws, stream);
+        return;
+      }
+    }
     if (p.cpl == 4) skinny_launch<M, DOT, 4>(a, p, ws, stream);
     else if (p.cpl == 2) skinny_launch<M, DOT, 2>(a, p, ws, stream);
     else skinny_launch<M, DOT, 1>(a, p, ws, stream);
@@ -1646,7 +1687,7 @@ struct LdsPlan {
 static LdsPlan plan_lds(int64_t m, const SkinnyPlan& p, int64_t k, bool dot, bool lora = false) {
   LdsPlan r{0, 0, 0, false, 0};
   const int64_t G = k / 128;
-  if (m > 16 || p.ksplit != 1 || G < 1) return r;
+  if (m > 16 || p.ksplit != 1 || G < 1 || p.cpl > 4) return r;
   int ng = G <= 16 ? 1 : (G <= 32 ? 2 : (G <= 64 ? 4 : 0));
   if (p.nstrips > 256 && ng > 0 && ng < QG_LDS_MANY_NG && G > 8) ng = G <= 32 ? 2 : 4;
   const int la = lora ? 4 : 0;                                 // lora_A loads per group

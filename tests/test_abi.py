@@ -319,10 +319,17 @@ def test_describe_names_the_dispatch(lib):
     assert qg.describe_int4(1, 5632, 8192).startswith("skinny_lds_kernel<1,dot,1,4,xreg> grid=352 block=1024 ")
     # 16-column strips with m >= 2 keep the split
     assert qg.describe_int4(8, 5632, 8192).startswith("skinny_int4_kernel<8,mfma,4> grid=264 ")
-    # a long k with few strips is split: m >= 8 and 200 groups take 8-wave workgroups,
-    # 25 groups per wave -> 7 slices of 29 over 80 strips of 64 columns
-    assert qg.describe_int4(16, 5120, 25600).startswith("skinny_int4_kernel<16,mfma,4> grid=560 block=512")
-    assert "ksplit=7 groups=29" in qg.describe_int4(16, 5120, 25600)
+    # a long k with few strips is split: 200 groups over 40 strips of 128 columns in 256 / 40 =
+    # 6 slices of 34 groups, one 512-thread workgroup per CU; where 128-column strips would keep
+    # fewer than 20 groups per slice (112 groups over 32 strips: 8 slices of 14), 64-column
+    # strips as before (m >= 8: 8-wave workgroups, 28 groups per slice over 64 strips)
+    assert qg.describe_int4(16, 5120, 25600).startswith("skinny_int4_kernel<16,mfma,8> grid=240 block=512")
+    assert "ksplit=6 groups=34" in qg.describe_int4(16, 5120, 25600)
+    assert qg.describe_int4(16, 4096, 14336).startswith("skinny_int4_kernel<16,mfma,4> grid=256 block=512")
+    assert "ksplit=4 groups=28" in qg.describe_int4(16, 4096, 14336)
+    # the GEMV keeps 64-column strips; without a workspace no split and no 128-column strips
+    assert qg.describe_int4(1, 5120, 25600).startswith("skinny_int4_kernel<1,dot,4> ")
+    assert qg.describe_int4(16, 5120, 25600, workspace_bytes=0).startswith("skinny_int4_kernel<16,mfma,4> grid=80 ")
     assert "ksplit=1 groups=200" in qg.describe_int4(16, 5120, 25600, workspace_bytes=0)
     # pipelined MFMA kernel: 64-token tiles for small m, 256 x 128 once there are enough of them
     # (lds = 4 stages x (activations + words + metadata) dwords x 4 bytes)
@@ -351,8 +358,8 @@ def test_describe_names_the_dispatch(lib):
 
 
 def test_workspace_size(lib):
-    # 64 KiB of counters, then 80 strips x 7 slices x 16 tokens x 64 columns x 4 bytes
-    assert qg.workspace_size(16, 5120, 25600) == 65536 + 80 * 7 * 16 * 64 * 4
+    # 64 KiB of counters, then 40 strips x 6 slices x 16 tokens x 128 columns x 4 bytes
+    assert qg.workspace_size(16, 5120, 25600) == 65536 + 40 * 6 * 16 * 128 * 4
     assert qg.workspace_size(8, 4096, 4096) == 0           # no split needed
     # MFMA tiles: 64 KiB of counters, prepared activations, group sums, then the k split's
     # partial tiles (tiles x slices x BM x 128 fp32)

@@ -254,6 +254,32 @@ def test_split_orders_agree(gpu_lib, path, m, k, n):
     assert np.array_equal(y_ar, y_hw) and np.array_equal(y_ar2, y_hw)
 
 
+# 128-column strips (m <= 16, k split anyway, long slices): ragged last strip (4104 = 32 x 128
+# + 8 columns), 7 slices of 23 groups; every output against the C++ oracle, the same bits
+# again (tickets reset) and under acquire-release tickets; without a workspace the plan
+# falls back to 64-column strips without a split
+@pytest.mark.parametrize("m,k,n", [(3, 20480, 4104), (16, 20480, 4104)])
+def test_wide_strips_match_oracle(gpu_lib, m, k, n):
+    desc = gpu_lib.describe_int4(m, n, k)
+    say("wide-strips", m, k, n, desc)
+    assert ",mfma,8>" in desc and "ksplit=1 " not in desc + " "
+    d = int4_inputs(m, k, n, seed=1700 + m)
+    t = upload_int4(d)
+    ref = cpp_oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], m, k, n)
+    y1 = host_u16(run(gpu_lib, t))
+    assert_accepted(y1, ref, ("wide-strips", m, k, n))
+    assert np.array_equal(y1, host_u16(run(gpu_lib, t)))
+    try:
+        gpu_lib.set_split_order("acq_rel")
+        y_ar = host_u16(run(gpu_lib, t))
+    finally:
+        gpu_lib.set_split_order("hw")
+    assert np.array_equal(y1, y_ar)
+    assert ",mfma,8>" not in gpu_lib.describe_int4(m, n, k, "auto", 0)
+    y0 = host_u16(run(gpu_lib, t, workspace=False))
+    assert_accepted(y0, ref, ("wide-strips no-ws", m, k, n))
+
+
 def test_gemv_long_k_without_workspace(gpu_lib):
     # 600 groups on one 16-column strip, no k split: each wave walks a long chain
     m, k, n = 1, 76800, 16
@@ -541,7 +567,7 @@ def test_max_n(gpu_lib, path, m):
 EPI_CASES = [("gemv", 1, 1152, 776, 0), ("fused", 8, 2048, 1040, 0), ("fused", 15, 2048, 1040, 16),
              ("fused", 8, 16384, 520, 0), ("gemv", 1, 16384, 520, 16), ("auto", 24, 2048, 1040, 0),
              ("auto", 40, 2048, 1040, 5), ("mfma", 130, 1152, 776, 0), ("mfma", 33, 4096, 520, 16),
-             ("mfma", 257, 2048, 1040, 0), ("fused", 3, 4096, 14336, 0)]
+             ("mfma", 257, 2048, 1040, 0), ("fused", 3, 4096, 14336, 0), ("fused", 2, 20480, 4104, 16)]
 
 
 @pytest.mark.parametrize("path,m,k,n,rank", EPI_CASES)
