@@ -1524,6 +1524,9 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
 #ifndef QG_SKINNY_CPL8_MIN_GPS
 #define QG_SKINNY_CPL8_MIN_GPS 20
 #endif
+#ifndef QG_SKINNY_CPL8_MIN_STRIPS
+#define QG_SKINNY_CPL8_MIN_STRIPS 192   // 128-column strips without a split: at least this many
+#endif
 
 int64_t split_workspace_bytes(int64_t nstrips, int64_t ksplit, int64_t m, int cpl) {
   return kTicketBytes + nstrips * ksplit * m * 16 * cpl * 4;
@@ -1569,6 +1572,20 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int64_t workspace_bytes,
   if (per_wave > QG_SKINNY_MAX_GPW && (int64_t)p.nstrips * 4 <= kTicketBytes) {
     ks = (per_wave + 3) / 4;
     if (ks > SK_MAX_SPLIT) ks = SK_MAX_SPLIT;
+  }
+  // Without a split, 64-column strips that need two workgroups per CU (more
+  // than 256) become 128-column strips in one pass of one 8-wave workgroup per
+  // CU when those still cover most CUs (same-process A/B, cold weights:
+  // 4096 x 28672 m = 4 / 8 / 16 16.3 / 17.0 / 19.2 -> 15.8 / 16.3 / 18.1 µs,
+  // 5120 x 25600 m = 8 / 16 20.2 / 23.5 -> 18.7 / 21.6 µs, 4096 x 32768 m = 16
+  // 19.2 -> 18.2 µs).
+  if (QG_SKINNY_CPL8 && !dot && m <= 16 && ks == 1 && p.cpl == 4 && p.nstrips > 256) {
+    const int64_t s8 = (n + 127) / 128;
+    if (s8 >= QG_SKINNY_CPL8_MIN_STRIPS && s8 <= 256 && G <= 8 * QG_SKINNY_MAX_GPW) {
+      p.cpl = 8;
+      p.nstrips = (int)s8;
+      p.waves = (int)(G < 8 ? (G > 0 ? G : 1) : 8);
+    }
   }
   // When k is long enough to be split anyway, take the widest strip whose
   // count, times a split of at most SK_MAX_SPLIT, still fills the CUs: every

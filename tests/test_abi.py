@@ -306,9 +306,12 @@ def test_describe_names_the_dispatch(lib):
         "skinny_lds_kernel<15,mfma,1,2,xlds> grid=256 block=1024 lds=%d ksplit=1 groups=32" % (160 * 1024))
     # 8192 columns: 256 strips of 32, one group per wave (16 groups)
     assert qg.describe_int4(8, 8192, 2048).startswith("skinny_lds_kernel<8,mfma,2,1,xlds> grid=256 block=1024")
-    # more strips than one pass holds with all their codes in LDS: the register-staged kernel
-    assert qg.describe_int4(8, 28672, 4096).startswith("skinny_int4_kernel<8,mfma,4> grid=448")
-    assert qg.describe_int4(16, 28672, 4096).startswith("skinny_int4_kernel<16,mfma,4> grid=448 block=512")
+    # more strips than one pass holds with all their codes in LDS: the register-staged kernel,
+    # 224 strips of 128 columns (one 8-wave workgroup per CU) instead of 448 of 64; the GEMV
+    # keeps 64-column strips
+    assert qg.describe_int4(8, 28672, 4096).startswith("skinny_int4_kernel<8,mfma,8> grid=224 block=512")
+    assert qg.describe_int4(16, 28672, 4096).startswith("skinny_int4_kernel<16,mfma,8> grid=224 block=512")
+    assert qg.describe_int4(1, 28672, 4096).startswith("skinny_int4_kernel<1,dot,4> grid=448")
     # 64 groups would be split over 128 strips of 64 columns; instead 256 strips of 32
     # columns each take the whole k in the LDS-staged kernel (4 groups per wave, 16
     # waves): 64 groups x 2 KiB of codes and 16 waves x 16 tokens x 32 columns x 4 bytes

@@ -280,6 +280,20 @@ def test_wide_strips_match_oracle(gpu_lib, m, k, n):
     assert_accepted(y0, ref, ("wide-strips no-ws", m, k, n))
 
 
+# 128-column strips without a split (more 64-column strips than two per CU hold in one
+# pass, 193 of 128 columns with a ragged last one): every output against the C++ oracle
+@pytest.mark.parametrize("m,k,n", [(5, 4096, 24584), (16, 6144, 24584)])
+def test_wide_strips_unsplit_match_oracle(gpu_lib, m, k, n):
+    desc = gpu_lib.describe_int4(m, n, k)
+    say("wide-strips-unsplit", m, k, n, desc)
+    assert ",mfma,8> grid=" in desc and "ksplit=1 " in desc + " "
+    d = int4_inputs(m, k, n, seed=1750 + m)
+    t = upload_int4(d)
+    ref = cpp_oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], m, k, n)
+    y = host_u16(run(gpu_lib, t))
+    assert_accepted(y, ref, ("wide-strips-unsplit", m, k, n))
+
+
 def test_gemv_long_k_without_workspace(gpu_lib):
     # 600 groups on one 16-column strip, no k split: each wave walks a long chain
     m, k, n = 1, 76800, 16
