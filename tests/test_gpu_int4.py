@@ -258,40 +258,42 @@ def test_split_orders_agree(gpu_lib, path, m, k, n):
 # + 8 columns), 7 slices of 23 groups; every output against the C++ oracle, the same bits
 # again (tickets reset) and under acquire-release tickets; without a workspace the plan
 # falls back to 64-column strips without a split
-@pytest.mark.parametrize("m,k,n", [(3, 20480, 4104), (16, 20480, 4104)])
-def test_wide_strips_match_oracle(gpu_lib, m, k, n):
-    desc = gpu_lib.describe_int4(m, n, k)
-    say("wide-strips", m, k, n, desc)
+@pytest.mark.parametrize("path,m,k,n", [("auto", 3, 20480, 4104), ("auto", 16, 20480, 4104),
+                                        ("fused", 1, 20480, 4104)])
+def test_wide_strips_match_oracle(gpu_lib, path, m, k, n):
+    desc = gpu_lib.describe_int4(m, n, k, path)
+    say("wide-strips", path, m, k, n, desc)
     assert ",mfma,8>" in desc and "ksplit=1 " not in desc + " "
     d = int4_inputs(m, k, n, seed=1700 + m)
     t = upload_int4(d)
     ref = cpp_oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], m, k, n)
-    y1 = host_u16(run(gpu_lib, t))
-    assert_accepted(y1, ref, ("wide-strips", m, k, n))
-    assert np.array_equal(y1, host_u16(run(gpu_lib, t)))
+    y1 = host_u16(run(gpu_lib, t, path))
+    assert_accepted(y1, ref, ("wide-strips", path, m, k, n))
+    assert np.array_equal(y1, host_u16(run(gpu_lib, t, path)))
     try:
         gpu_lib.set_split_order("acq_rel")
-        y_ar = host_u16(run(gpu_lib, t))
+        y_ar = host_u16(run(gpu_lib, t, path))
     finally:
         gpu_lib.set_split_order("hw")
     assert np.array_equal(y1, y_ar)
-    assert ",mfma,8>" not in gpu_lib.describe_int4(m, n, k, "auto", 0)
-    y0 = host_u16(run(gpu_lib, t, workspace=False))
-    assert_accepted(y0, ref, ("wide-strips no-ws", m, k, n))
+    assert ",mfma,8>" not in gpu_lib.describe_int4(m, n, k, path, 0)
+    y0 = host_u16(run(gpu_lib, t, path, workspace=False))
+    assert_accepted(y0, ref, ("wide-strips no-ws", path, m, k, n))
 
 
 # 128-column strips without a split (more 64-column strips than two per CU hold in one
 # pass, 193 of 128 columns with a ragged last one): every output against the C++ oracle
-@pytest.mark.parametrize("m,k,n", [(5, 4096, 24584), (16, 6144, 24584)])
-def test_wide_strips_unsplit_match_oracle(gpu_lib, m, k, n):
-    desc = gpu_lib.describe_int4(m, n, k)
-    say("wide-strips-unsplit", m, k, n, desc)
+@pytest.mark.parametrize("path,m,k,n", [("auto", 5, 4096, 24584), ("auto", 16, 6144, 24584),
+                                        ("fused", 1, 4096, 24584)])
+def test_wide_strips_unsplit_match_oracle(gpu_lib, path, m, k, n):
+    desc = gpu_lib.describe_int4(m, n, k, path)
+    say("wide-strips-unsplit", path, m, k, n, desc)
     assert ",mfma,8> grid=" in desc and "ksplit=1 " in desc + " "
     d = int4_inputs(m, k, n, seed=1750 + m)
     t = upload_int4(d)
     ref = cpp_oracle.qgemm_int4(d["x"], d["qweight"], d["scales"], d["qzeros"], m, k, n)
-    y = host_u16(run(gpu_lib, t))
-    assert_accepted(y, ref, ("wide-strips-unsplit", m, k, n))
+    y = host_u16(run(gpu_lib, t, path))
+    assert_accepted(y, ref, ("wide-strips-unsplit", path, m, k, n))
 
 
 def test_gemv_long_k_without_workspace(gpu_lib):
